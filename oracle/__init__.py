@@ -1,0 +1,111 @@
+"""CPU oracle for serial-episode counting -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library's product path never does;
+it shares no code with the HIP path.
+
+The arithmetic lives in ``alpha0.c`` (the reference serial state machine
+alpha_0 of the page "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
+Episodes Using Graphics Processors", Fig. 3 text and the opening section's
+Algorithm 1, restated from its description).  This module only compiles it with
+gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "alpha0.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile alpha0.c into liboracle.so with plain gcc (no GPU code)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+             "-pthread", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_count_one.restype = ctypes.c_int64
+        lib.oracle_count_one.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_count_batch.restype = ctypes.c_int
+        lib.oracle_count_batch.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _prep(times, types, ep_types, t_low, t_high):
+    times = np.ascontiguousarray(times, dtype=np.int32)
+    types = np.ascontiguousarray(types, dtype=np.uint16)
+    ep_types = np.ascontiguousarray(ep_types, dtype=np.uint16)
+    if ep_types.ndim == 1:
+        ep_types = ep_types[None, :]
+    S, N = ep_types.shape
+    t_low = np.ascontiguousarray(t_low, dtype=np.int32).reshape(S, max(N - 1, 0))
+    t_high = np.ascontiguousarray(t_high, dtype=np.int32).reshape(S, max(N - 1, 0))
+    if times.shape != types.shape:
+        raise ValueError("times and types differ in length")
+    if np.any(t_low < 0) or np.any(t_low >= t_high):
+        raise ValueError("intervals must satisfy 0 <= t_low < t_high")
+    if times.size > 1 and np.any(np.diff(times.astype(np.int64)) < 0):
+        raise ValueError("times must be non-decreasing")
+    return times, types, ep_types, t_low, t_high
+
+
+def count(times, types, ep_types, t_low, t_high, n_threads: int | None = None):
+    """Counts of S episodes (rows of ``ep_types``) over one stream, as int64[S].
+
+    ``ep_types``: [S, N] event types; ``t_low``/``t_high``: [S, N-1] delay
+    bounds of the half-open intervals (t_low, t_high].
+    """
+    times, types, ep_types, t_low, t_high = _prep(times, types, ep_types, t_low, t_high)
+    S, N = ep_types.shape
+    out = np.zeros(S, dtype=np.int64)
+    if S == 0:
+        return out
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    lib = _load()
+    lib.oracle_count_batch(times.ctypes.data, types.ctypes.data, times.size, N,
+                           ep_types.ctypes.data, t_low.ctypes.data, t_high.ctypes.data,
+                           S, out.ctypes.data, int(n_threads))
+    if np.any(out < 0):
+        raise MemoryError("oracle ran out of memory")
+    return out
+
+
+def count_timed(times, types, ep_types, t_low, t_high, n_threads: int | None = None):
+    """Like :func:`count`, also returning (seconds, threads used)."""
+    times, types, ep_types, t_low, t_high = _prep(times, types, ep_types, t_low, t_high)
+    S, N = ep_types.shape
+    out = np.zeros(S, dtype=np.int64)
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    lib = _load()
+    t0 = time.perf_counter()
+    used = lib.oracle_count_batch(times.ctypes.data, types.ctypes.data, times.size, N,
+                                  ep_types.ctypes.data, t_low.ctypes.data,
+                                  t_high.ctypes.data, S, out.ctypes.data, int(n_threads))
+    dt = time.perf_counter() - t0
+    return out, dt, used
