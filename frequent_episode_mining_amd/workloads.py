@@ -84,7 +84,7 @@ def _sorted_uniform_ticks(rng, count: int, t_first: int, t_last: int) -> np.ndar
     acc = 0.0
     step = 1 << 24
     for s in range(0, count, step):
-        c = np.cumsum(e[s:s + step]) + acc
+        c = np.cumsum(e[s:min(s + step, count)]) + acc
         acc = c[-1]
         u = c / total
         out[s:s + step] = t_first + np.minimum((u * span).astype(np.int64), span - 1)
