@@ -1,1 +1,189 @@
-"""MI355X-native serial-episode counting (binding is added with the HIP library)."""
+"""MI355X-native serial-episode counting: Python binding of libepcount.so.
+
+Argument marshalling only: every step of the counting runs in the library's
+HIP kernels.  PyTorch provides device memory and the stream.  The library is
+loaded from this package directory; if it is missing, every call raises.
+
+Page: "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent Episodes
+Using Graphics Processors" -- counting the non-overlapped occurrences of serial
+episodes E(1) -(t_low,t_high]-> ... -> E(N) in a time-sorted event stream,
+with the thread-per-episode (PTPE) and MapConcatenate schemes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libepcount.so")
+
+EP_OK = 0
+STATUS = {
+    0: "EP_OK", -1: "EP_ERR_ARG", -2: "EP_ERR_NODES", -3: "EP_ERR_INTERVAL",
+    -4: "EP_ERR_UNSORTED", -5: "EP_ERR_WORKSPACE", -6: "EP_ERR_HIP", -7: "EP_ERR_UNSUPPORTED",
+}
+MODES = {"auto": 0, "ptpe": 1, "mapconcat": 2}
+MODE_NAMES = {v: k for k, v in MODES.items()}
+MAX_NODES = 16
+
+
+class EpEpisodes(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("types", ctypes.c_void_p),
+                ("t_low", ctypes.c_void_p), ("t_high", ctypes.c_void_p)]
+
+
+class EpStats(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("max_runs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("repairs", ctypes.c_int64), ("fallbacks", ctypes.c_int64)]
+
+
+class EpOptions(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("validate", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("stats", ctypes.POINTER(EpStats))]
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libepcount.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libepcount.so is not built (%s); run __graft_entry__.build()" % p)
+    lib = ctypes.CDLL(p)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.ep_count_episodes.restype = ctypes.c_int
+    lib.ep_count_episodes.argtypes = [vp, vp, i64, EpEpisodes, i64, vp, vp]
+    lib.ep_count_episodes_ex.restype = ctypes.c_int
+    lib.ep_count_episodes_ex.argtypes = [vp, vp, i64, EpEpisodes, i64, vp, vp,
+                                         ctypes.POINTER(EpOptions)]
+    lib.ep_plan.restype = ctypes.c_int
+    lib.ep_plan.argtypes = [i64, i32, i64, i32, i32, i32, i32,
+                            ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.ep_segment_cut.restype = i64
+    lib.ep_segment_cut.argtypes = [i32, i32, i32, i32]
+    lib.ep_status_string.restype = ctypes.c_char_p
+    lib.ep_status_string.argtypes = [ctypes.c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ep_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != EP_OK:
+        raise EpError(status, status_string(status))
+
+
+class EpisodeTable:
+    """Host-side candidate episode set (uint16 types [S,N], int32 bounds [S,N-1])."""
+
+    def __init__(self, ep_types, t_low, t_high):
+        ep_types = np.ascontiguousarray(ep_types, dtype=np.uint16)
+        if ep_types.ndim == 1:
+            ep_types = ep_types[None, :]
+        S, N = ep_types.shape
+        self.types = ep_types
+        self.t_low = np.ascontiguousarray(np.asarray(t_low, dtype=np.int32).reshape(S, max(N - 1, 0)))
+        self.t_high = np.ascontiguousarray(np.asarray(t_high, dtype=np.int32).reshape(S, max(N - 1, 0)))
+
+    @property
+    def n_episodes(self) -> int:
+        return self.types.shape[0]
+
+    @property
+    def n_nodes(self) -> int:
+        return self.types.shape[1]
+
+    def as_struct(self) -> EpEpisodes:
+        return EpEpisodes(self.n_nodes, self.types.ctypes.data,
+                          self.t_low.ctypes.data if self.t_low.size else None,
+                          self.t_high.ctypes.data if self.t_high.size else None)
+
+
+def _device_ptr(t, dtype_ok, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU torch tensor" % name)
+    if t.dtype not in dtype_ok:
+        raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtype_ok))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr() if t.numel() else None
+
+
+def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str = "auto",
+                   n_segments: int = 0, validate: bool = False, stats: bool = False,
+                   out=None, stream=None):
+    """Counts of S episodes over one GPU-resident event stream.
+
+    times: int32 [n] GPU tensor, non-decreasing.  types: uint16 (or int16, same
+    bits) [n] GPU tensor.  ep_types: [S, N] host array (or an EpisodeTable);
+    t_low/t_high: [S, N-1] host arrays.  Returns an int64 [S] GPU tensor (and
+    the ep_stats dict if ``stats``).  Enqueued on ``stream`` (default: torch's
+    current stream); ``validate``/``stats`` synchronise that stream.
+    """
+    import torch
+    table = ep_types if isinstance(ep_types, EpisodeTable) else EpisodeTable(ep_types, t_low, t_high)
+    tp = _device_ptr(times, (torch.int32,), "times")
+    yp = _device_ptr(types, (torch.int16, getattr(torch, "uint16", torch.int16)), "types")
+    n = times.numel()
+    if types.numel() != n:
+        raise ValueError("times and types differ in length")
+    S = table.n_episodes
+    if out is None:
+        out = torch.empty(S, dtype=torch.int64, device=times.device)
+    op = _device_ptr(out, (torch.int64,), "out") if S else None
+    if stream is None:
+        stream = torch.cuda.current_stream(times.device)
+    sp = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    lib = load_library()
+    st = EpStats()
+    opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), 0,
+                    ctypes.pointer(st) if stats else None)
+    with torch.cuda.device(times.device):
+        status = lib.ep_count_episodes_ex(tp, yp, n, table.as_struct(), S, op, sp, ctypes.byref(opt))
+    _check(status)
+    if stats:
+        return out, {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,
+                     "max_runs": st.max_runs, "repairs": st.repairs, "fallbacks": st.fallbacks}
+    return out
+
+
+def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_segments: int = 0,
+         cu_count: int = 256, lanes_per_cu: int = 2048):
+    """The planner on a described device (no GPU needed): (mode name, segments)."""
+    lib = load_library()
+    m = ctypes.c_int32()
+    p = ctypes.c_int32()
+    _check(lib.ep_plan(n_episodes, n_nodes, n_events, MODES[mode], n_segments, cu_count,
+                       lanes_per_cu, ctypes.byref(m), ctypes.byref(p)))
+    return MODE_NAMES[m.value], p.value
+
+
+def segment_cut(t_min: int, t_max: int, n_segments: int, p: int) -> int:
+    return int(load_library().ep_segment_cut(t_min, t_max, n_segments, p))
+
+
+def to_device(times: np.ndarray, types: np.ndarray, device="cuda"):
+    """Copy a host stream to GPU tensors in the layout the library reads."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(times, dtype=np.int32)).to(device)
+    y = torch.from_numpy(np.ascontiguousarray(types, dtype=np.uint16).view(np.int16)).to(device)
+    return t, y

@@ -1,0 +1,500 @@
+// Host side of the serial-episode counting library: argument checks, the
+// scheme planner, scratch layout, the small non-templated kernels (cuts,
+// Concatenate tree levels, result extraction) and the C ABI of epcount.h.
+//
+// Source page: "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
+// Episodes Using Graphics Processors".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "ep_device.hpp"
+#include "epcount.h"
+
+namespace epk {
+const Launchers* launchers_n1();
+const Launchers* launchers_n2();
+const Launchers* launchers_n3();
+const Launchers* launchers_n4();
+const Launchers* launchers_n5();
+const Launchers* launchers_n6();
+const Launchers* launchers_n7();
+const Launchers* launchers_n8();
+const Launchers* launchers_n9();
+const Launchers* launchers_n10();
+const Launchers* launchers_n11();
+const Launchers* launchers_n12();
+const Launchers* launchers_n13();
+const Launchers* launchers_n14();
+const Launchers* launchers_n15();
+const Launchers* launchers_n16();
+
+namespace {
+
+const Launchers* launchers_for(int N) {
+  switch (N) {
+    case 1: return launchers_n1();
+    case 2: return launchers_n2();
+    case 3: return launchers_n3();
+    case 4: return launchers_n4();
+    case 5: return launchers_n5();
+    case 6: return launchers_n6();
+    case 7: return launchers_n7();
+    case 8: return launchers_n8();
+    case 9: return launchers_n9();
+    case 10: return launchers_n10();
+    case 11: return launchers_n11();
+    case 12: return launchers_n12();
+    case 13: return launchers_n13();
+    case 14: return launchers_n14();
+    case 15: return launchers_n15();
+    case 16: return launchers_n16();
+    default: return nullptr;
+  }
+}
+
+// ------------------------------------------------------------ small kernels
+
+// Equal-time cuts and each segment's event index range.  tau_p for p = 0..P;
+// segment p needs the events in (tau_p - maxSpan, tau_{p+1} + maxSpan]: its
+// machines start up to maxSpan before the left cut and look up to maxSpan past
+// the right cut for the exit b.
+__global__ __launch_bounds__(kBlock) void cuts_kernel(const int32_t* times, int64_t n, int32_t P,
+                                                      int64_t max_span, int64_t* tau,
+                                                      int32_t* beg, int32_t* end) {
+  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (p > P) return;
+  const int64_t t_min = times[0];
+  const int64_t t_max = times[n - 1];
+  const int64_t width = t_max - t_min + 1;
+  const int64_t cut = t_min - 1 + (p * width) / P;
+  tau[p] = cut;
+  if (p < P) {
+    const int64_t next = t_min - 1 + ((p + 1) * width) / P;
+    beg[p] = (int32_t)upper_bound_time(times, 0, n, cut - max_span);
+    end[p] = (int32_t)upper_bound_time(times, 0, n, next + max_span);
+  }
+}
+
+// One Concatenate level (rules 2-3, Fig. 6): block j spans segments
+// [j*2h, j*2h + 2h); its left half starts at L = j*2h, its right half at
+// R = L + h.  Every tuple of the left half is joined with the right half's
+// tuple whose key equals its exit: (a, c, b) -> (a, c + c', b').  Tuples of a
+// block are keyed by its first segment's keys, so the join is in place.
+__global__ __launch_bounds__(kBlock) void concat_level_kernel(Tuple* T, const int32_t* nslots,
+                                                              int32_t* flags, int64_t S, int32_t P,
+                                                              int32_t slots, int64_t half) {
+  const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t per_block = S * slots;
+  const int64_t j = item / per_block;
+  const int64_t rem = item - j * per_block;
+  const int64_t e = rem / slots;
+  const int32_t s = (int32_t)(rem - e * slots);
+  const int64_t L = j * 2 * half;
+  const int64_t R = L + half;
+  if (R >= P) return;
+  const int32_t nl = min(nslots[L * S + e], slots);
+  if (s >= nl) return;
+  Tuple* lt = T + (L * S + e) * slots + s;
+  Tuple x = *lt;
+  const Tuple* rt = T + (R * S + e) * slots;
+  const int32_t nr = min(nslots[R * S + e], slots);
+  for (int32_t m = 0; m < nr; ++m) {
+    const Tuple y = rt[m];
+    if (y.a == x.b) {
+      x.c += y.c;
+      x.b = y.b;
+      *lt = x;
+      return;
+    }
+  }
+  atomicOr(&flags[e], 2);
+}
+
+// The answer is the chain entering segment 0 through machine 0: segment 0's
+// machines start before the first event, so each of them is the page's
+// reference machine alpha_0 on the whole stream (Fig. 3 text).
+__global__ __launch_bounds__(kBlock) void extract_kernel(const Tuple* T, int64_t S, int32_t slots,
+                                                         int64_t* out) {
+  const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (e < S) out[e] = T[e * slots].c;
+}
+
+__global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n, int64_t v) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* times, int64_t n,
+                                                              int32_t* bad) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i + 1 < n && times[i] > times[i + 1]) atomicOr(bad, 1);
+}
+
+inline unsigned grid_for(int64_t items) { return (unsigned)((items + kBlock - 1) / kBlock); }
+
+// ------------------------------------------------------------ host helpers
+
+struct DeviceInfo {
+  bool ok = false;
+  int cu_count = 0;
+  int occ[EP_MAX_NODES + 1][3] = {};  // blocks per CU of map_kernel<N, K>, K index 0/1/2
+};
+
+std::mutex g_info_mu;
+DeviceInfo g_info[64];
+
+int k_index(int K) { return K == 1 ? 0 : (K == 2 ? 1 : 2); }
+
+// Pinned staging for the episode table upload; the event guards reuse.
+struct Staging {
+  std::mutex mu;
+  void* buf = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+Staging g_staging[64];
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int mode;
+  int32_t P;
+  int M, G, R, CH;
+  int slots;
+};
+
+int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments, int32_t cu_count,
+              int32_t lanes_per_cu, int32_t* out_mode, int32_t* out_segments) {
+  const int64_t full = (int64_t)std::max(cu_count, 1) * std::max(lanes_per_cu, 1);
+  int m = mode;
+  if (m == EP_MODE_AUTO) m = (S >= full) ? EP_MODE_PTPE : EP_MODE_MAPCONCAT;
+  int64_t P = 1;
+  if (m == EP_MODE_MAPCONCAT) {
+    if (n_segments > 0) {
+      P = n_segments;
+    } else {
+      const int64_t need = (full + S * N - 1) / std::max<int64_t>(S * N, 1);
+      const int64_t cap_by_events = std::max<int64_t>(1, n / 256);
+      P = 2;
+      while (P < need && P < (1 << 20)) P <<= 1;
+      while (P > 1 && P > cap_by_events) P >>= 1;
+    }
+  }
+  *out_mode = m;
+  *out_segments = (int32_t)P;
+  return EP_OK;
+}
+
+}  // namespace
+}  // namespace epk
+
+using namespace epk;
+
+extern "C" const char* ep_status_string(int status) {
+  switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_ARG: return "invalid argument";
+    case EP_ERR_NODES: return "episode size outside 1..EP_MAX_NODES";
+    case EP_ERR_INTERVAL: return "delay interval violates 0 <= t_low < t_high or the span overflows";
+    case EP_ERR_UNSORTED: return "event times are not non-decreasing";
+    case EP_ERR_WORKSPACE: return "scratch allocation failed";
+    case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_UNSUPPORTED: return "a delay window needs more candidate runs than EP_MAX_RUNS";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int64_t ep_segment_cut(int32_t t_min, int32_t t_max, int32_t n_segments, int32_t p) {
+  if (n_segments <= 0) return (int64_t)t_min - 1;
+  const int64_t width = (int64_t)t_max - (int64_t)t_min + 1;
+  return (int64_t)t_min - 1 + ((int64_t)p * width) / n_segments;
+}
+
+extern "C" int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, int32_t mode,
+                       int32_t n_segments, int32_t cu_count, int32_t lanes_per_cu,
+                       int32_t* out_mode, int32_t* out_segments) {
+  if (!out_mode || !out_segments || n_episodes < 0 || n_events < 0 || n_segments < 0)
+    return EP_ERR_ARG;
+  if (n_nodes < 1 || n_nodes > EP_MAX_NODES) return EP_ERR_NODES;
+  if (mode < EP_MODE_AUTO || mode > EP_MODE_MAPCONCAT) return EP_ERR_ARG;
+  return plan_rule(n_episodes, n_nodes, n_events, mode, n_segments, cu_count, lanes_per_cu,
+                   out_mode, out_segments);
+}
+
+namespace {
+
+#define EP_HIP(call)                                      \
+  do {                                                    \
+    hipError_t err_ = (call);                             \
+    if (err_ != hipSuccess) {                             \
+      if (getenv("EP_LOG"))                               \
+        fprintf(stderr, "epcount: %s failed: %s\n", #call, \
+                hipGetErrorString(err_));                 \
+      return EP_ERR_HIP;                                  \
+    }                                                     \
+  } while (0)
+
+int device_info(int dev, DeviceInfo** out) {
+  if (dev < 0 || dev >= 64) return EP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_info_mu);
+  DeviceInfo& d = g_info[dev];
+  if (!d.ok) {
+    int cus = 0;
+    EP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    d.cu_count = cus;
+    for (int N = 1; N <= EP_MAX_NODES; ++N)
+      for (int ki = 0; ki < 3; ++ki) {
+        int b = 0;
+        EP_HIP(launchers_for(N)->map_occupancy(ki == 0 ? 1 : (ki == 1 ? 2 : 4), &b));
+        d.occ[N][ki] = std::max(b, 1);
+      }
+    d.ok = true;
+  }
+  *out = &d;
+  return EP_OK;
+}
+
+// Copy `bytes` of host data to `dst` on `stream` through pinned staging.
+int upload(int dev, void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  Staging& s = g_staging[dev];
+  std::lock_guard<std::mutex> lock(s.mu);
+  if (s.pending) {
+    EP_HIP(hipEventSynchronize(s.ev));
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.buf) EP_HIP(hipHostFree(s.buf));
+    s.buf = nullptr;
+    s.cap = 0;
+    size_t cap = std::max<size_t>(bytes, 1 << 16);
+    EP_HIP(hipHostMalloc(&s.buf, cap, hipHostMallocDefault));
+    s.cap = cap;
+  }
+  if (!s.ev) EP_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  memcpy(s.buf, src, bytes);
+  EP_HIP(hipMemcpyAsync(dst, s.buf, bytes, hipMemcpyHostToDevice, stream));
+  EP_HIP(hipEventRecord(s.ev, stream));
+  s.pending = true;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
+                                    ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                                    hipStream_t stream, const ep_options* opt) {
+  // ---- host-side argument checks (nothing is enqueued before they pass)
+  const int32_t N = episodes.n_nodes;
+  const int64_t S = n_episodes;
+  if (n_events < 0 || S < 0 || n_events > INT32_MAX) return EP_ERR_ARG;
+  if (N < 1 || N > EP_MAX_NODES) return EP_ERR_NODES;
+  if (S > 0 && (!out_counts || !episodes.types)) return EP_ERR_ARG;
+  if (S > 0 && N > 1 && (!episodes.t_low || !episodes.t_high)) return EP_ERR_ARG;
+  if (n_events > 0 && S > 0 && (!times || !types)) return EP_ERR_ARG;
+  const int mode = opt ? opt->mode : EP_MODE_AUTO;
+  if (mode < EP_MODE_AUTO || mode > EP_MODE_MAPCONCAT) return EP_ERR_ARG;
+  if (opt && opt->n_segments < 0) return EP_ERR_ARG;
+
+  int64_t max_span = 0;
+  int K = 1;
+  for (int64_t e = 0; e < S; ++e) {
+    int64_t span = 0;
+    for (int j = 0; j < N - 1; ++j) {
+      const int64_t lo = episodes.t_low[e * (N - 1) + j];
+      const int64_t hi = episodes.t_high[e * (N - 1) + j];
+      if (lo < 0 || lo >= hi) return EP_ERR_INTERVAL;
+      span += hi;
+      // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1
+      const int64_t runs = hi / (hi - lo + 1) + 1;
+      if (runs > EP_MAX_RUNS) return EP_ERR_UNSUPPORTED;
+      while (K < runs) K <<= 1;
+    }
+    if (span > INT32_MAX) return EP_ERR_INTERVAL;
+    max_span = std::max(max_span, span);
+  }
+  if (S == 0) return EP_OK;
+
+  int dev = 0;
+  EP_HIP(hipGetDevice(&dev));
+  if (n_events == 0) {
+    hipLaunchKernelGGL(fill_i64_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, out_counts, S,
+                       (int64_t)0);
+    EP_HIP(hipGetLastError());
+    if (opt && opt->stats) {
+      EP_HIP(hipStreamSynchronize(stream));
+      memset(opt->stats, 0, sizeof(ep_stats));
+      opt->stats->mode = EP_MODE_PTPE;
+      opt->stats->n_segments = 1;
+      opt->stats->max_runs = K;
+    }
+    return EP_OK;
+  }
+
+  DeviceInfo* info = nullptr;
+  if (int st = device_info(dev, &info)) return st;
+  const Launchers* L = launchers_for(N);
+
+  // ---- plan (hybrid rule)
+  const int lanes_per_cu = info->occ[N][k_index(K)] * kBlock;
+  int32_t pmode = 0, P = 1;
+  plan_rule(S, N, n_events, mode, opt ? opt->n_segments : 0, info->cu_count, lanes_per_cu, &pmode,
+            &P);
+  const int M = (pmode == EP_MODE_PTPE) ? 1 : N;
+  int G = (int)std::min<int64_t>(S, kBlock / M);
+  int R = 1;
+  if (G == S) R = std::max(1, kBlock / (G * M));
+  R = (int)std::min<int64_t>(R, P);
+  const int CH = kTile / R;
+  const int slots = (pmode == EP_MODE_PTPE) ? 1 : 2 * N;
+  if (getenv("EP_LOG"))
+    fprintf(stderr, "epcount: S=%lld N=%d n=%lld mode=%s P=%d K=%d M=%d G=%d R=%d CH=%d maxSpan=%lld\n",
+            (long long)S, N, (long long)n_events, pmode == EP_MODE_PTPE ? "ptpe" : "mapconcat", P, K,
+            M, G, R, CH, (long long)max_span);
+
+  // ---- scratch layout (one stream-ordered allocation)
+  const size_t sz_types = align_up(sizeof(uint16_t) * S * N, 256);
+  const size_t sz_lohi = align_up(sizeof(int32_t) * S * std::max(N - 1, 1), 256);
+  const size_t sz_span = align_up(sizeof(int32_t) * S, 256);
+  const size_t sz_tau = align_up(sizeof(int64_t) * (P + 1), 256);
+  const size_t sz_seg = align_up(sizeof(int32_t) * P, 256);
+  const size_t sz_tuples = align_up(sizeof(Tuple) * (size_t)P * S * slots, 256);
+  const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);
+  const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
+  const size_t sz_cnt = 256;
+  const size_t host_bytes = sz_types + 2 * sz_lohi + sz_span;
+  const size_t total = host_bytes + sz_tau + 2 * sz_seg + sz_tuples + sz_nslots + sz_flags + sz_cnt;
+
+  char* ws = nullptr;
+  if (hipMallocAsync((void**)&ws, total, stream) != hipSuccess || !ws) return EP_ERR_WORKSPACE;
+  int status = EP_OK;
+  do {
+    size_t off = 0;
+    uint16_t* d_types = (uint16_t*)(ws + off); off += sz_types;
+    int32_t* d_lo = (int32_t*)(ws + off); off += sz_lohi;
+    int32_t* d_hi = (int32_t*)(ws + off); off += sz_lohi;
+    int32_t* d_span = (int32_t*)(ws + off); off += sz_span;
+    int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
+    int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
+    int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
+    Tuple* d_tuples = (Tuple*)(ws + off); off += sz_tuples;
+    int32_t* d_nslots = (int32_t*)(ws + off); off += sz_nslots;
+    int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
+    unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
+
+    // episode table: packed on the host, one upload
+    std::vector<char> host(host_bytes, 0);
+    memcpy(host.data(), episodes.types, sizeof(uint16_t) * S * N);
+    if (N > 1) {
+      memcpy(host.data() + sz_types, episodes.t_low, sizeof(int32_t) * S * (N - 1));
+      memcpy(host.data() + sz_types + sz_lohi, episodes.t_high, sizeof(int32_t) * S * (N - 1));
+    }
+    int32_t* spans = (int32_t*)(host.data() + sz_types + 2 * sz_lohi);
+    for (int64_t e = 0; e < S; ++e) {
+      int64_t s = 0;
+      for (int j = 0; j < N - 1; ++j) s += episodes.t_high[e * (N - 1) + j];
+      spans[e] = (int32_t)s;
+    }
+    if ((status = upload(dev, ws, host.data(), host_bytes, stream))) break;
+
+    if (opt && opt->validate) {
+      hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kBlock), 0, stream, d_flags + S, (int64_t)1, 0);
+      hipLaunchKernelGGL(check_sorted_kernel, dim3(grid_for(n_events)), dim3(kBlock), 0, stream, times,
+                         n_events, d_flags + S);
+      int32_t bad = 0;
+      if (hipMemcpyAsync(&bad, d_flags + S, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+      if (bad) {
+        status = EP_ERR_UNSORTED;
+        break;
+      }
+    }
+
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_flags, S, 0);
+    hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, (int64_t*)d_cnt, (int64_t)4,
+                       (int64_t)0);
+    hipLaunchKernelGGL(cuts_kernel, dim3(grid_for((int64_t)P + 1)), dim3(kBlock), 0, stream, times,
+                       n_events, P, max_span, d_tau, d_beg, d_end);
+    if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
+
+    MapArgs ma;
+    ma.times = times; ma.types = types;
+    ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
+    ma.tau = d_tau; ma.seg_beg = d_beg; ma.seg_end = d_end;
+    ma.tuples = d_tuples; ma.nslots = d_nslots;
+    ma.S = S; ma.P = P; ma.M = M; ma.G = G; ma.R = R; ma.CH = CH; ma.slots = slots;
+    dim3 mgrid((unsigned)((P + R - 1) / R), (unsigned)((S + G - 1) / G));
+    if (L->map(ma, K, mgrid, stream) != hipSuccess) { status = EP_ERR_HIP; break; }
+
+    if (P > 1) {
+      ClosureArgs ca;
+      ca.times = times; ca.types = types;
+      ca.ep_types = d_types; ca.ep_lo = d_lo; ca.ep_hi = d_hi; ca.ep_span = d_span;
+      ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
+      ca.tuples = d_tuples; ca.nslots = d_nslots; ca.flags = d_flags; ca.repairs = d_cnt;
+      ca.S = S; ca.P = P; ca.slots = slots;
+      if (L->closure(ca, K, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+      for (int64_t half = 1; half < P; half <<= 1) {
+        const int64_t blocks = (P + 2 * half - 1) / (2 * half);
+        hipLaunchKernelGGL(concat_level_kernel, dim3(grid_for(blocks * S * slots)), dim3(kBlock), 0,
+                           stream, d_tuples, d_nslots, d_flags, S, P, slots, half);
+      }
+    }
+    hipLaunchKernelGGL(extract_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_tuples, S, slots,
+                       out_counts);
+    if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
+
+    FallbackArgs fa;
+    fa.times = times; fa.types = types;
+    fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
+    fa.flags = d_flags; fa.fallbacks = d_cnt + 1; fa.out = out_counts;
+    fa.n = n_events; fa.S = S;
+    if (L->fallback(fa, K, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+      status = EP_ERR_HIP;
+      break;
+    }
+
+    if (opt && opt->stats) {
+      unsigned long long cnt[2] = {0, 0};
+      if (hipMemcpyAsync(cnt, d_cnt, sizeof(cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+          hipStreamSynchronize(stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+      opt->stats->mode = pmode;
+      opt->stats->n_segments = P;
+      opt->stats->max_runs = K;
+      opt->stats->reserved = 0;
+      opt->stats->repairs = (int64_t)cnt[0];
+      opt->stats->fallbacks = (int64_t)cnt[1];
+    }
+  } while (0);
+
+  if (hipFreeAsync(ws, stream) != hipSuccess && status == EP_OK) status = EP_ERR_HIP;
+  return status;
+}
+
+extern "C" int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_events,
+                                 ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                                 hipStream_t stream) {
+  return ep_count_episodes_ex(times, types, n_events, episodes, n_episodes, out_counts, stream,
+                              nullptr);
+}

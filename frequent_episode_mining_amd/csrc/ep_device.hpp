@@ -1,0 +1,529 @@
+// Device code of the serial-episode counting library (gfx950 / CDNA4).
+//
+// Source page: "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
+// Episodes Using Graphics Processors".
+//
+// The counting machine is the page's serial state machine (opening section,
+// Algorithm 1; Fig. 3 text: alpha_0), kept in registers: for every node j < N-1
+// a window of candidate times t' of node j whose continuation intervals
+// (t' + t_low_j, t' + t_high_j] are merged into at most K disjoint runs.  A run
+// is stored as its first and last candidate time (f, l); it covers
+// (f + t_low, l + t_high].  Because event times only grow, runs whose end lies
+// before the current time are dropped from the front, and at most
+// floor(t_high / (t_high - t_low + 1)) + 1 runs are ever live, so a window of
+// that capacity is exact.  All time differences are formed as uint32 of
+// non-negative int32 differences, so no int32 arithmetic can overflow.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epk {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;   // threads per workgroup of every kernel here
+constexpr int kTile = 2048;   // events staged in LDS per chunk by a Map workgroup
+
+// One (a, count, b) tuple of the Map step (Map rules 1-4, Fig. 5), with a and b
+// stored as offsets from the segment's left and right cut; 0 is the sentinel
+// "no completion within Span after the cut".
+struct alignas(16) Tuple {
+  int32_t a;
+  int32_t c;
+  int32_t b;
+  int32_t pad;
+};
+
+// Episode parameters of one lane, in registers.
+template <int N>
+struct EpParams {
+  uint32_t ty[N];
+  uint32_t lo[N > 1 ? N - 1 : 1];
+  uint32_t hi[N > 1 ? N - 1 : 1];
+  uint32_t width[N > 1 ? N - 1 : 1];  // hi - lo: merge distance of two candidates
+  int32_t span;                        // hi_1 + ... + hi_{N-1}
+
+  __device__ void load(const uint16_t* ep_types, const int32_t* ep_lo, const int32_t* ep_hi,
+                       const int32_t* ep_span, int64_t e) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) ty[j] = ep_types[e * N + j];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      lo[j] = (uint32_t)ep_lo[e * (N - 1) + j];
+      hi[j] = (uint32_t)ep_hi[e * (N - 1) + j];
+      width[j] = hi[j] - lo[j];
+    }
+    span = ep_span[e];
+  }
+
+  // Bit j set iff node j has event type y (a type may sit at several nodes).
+  __device__ uint32_t level_mask(uint32_t y) const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) m |= (uint32_t)(ty[j] == y) << j;
+    return m;
+  }
+
+  // hi_1 + ... + hi_k: machine k of a segment is reset this long before the cut.
+  __device__ int64_t prefix_hi(int k) const {
+    int64_t s = 0;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) s += (j < k) ? (int64_t)hi[j] : 0;
+    return s;
+  }
+};
+
+template <int K>
+struct Window {
+  int32_t f[K];
+  int32_t l[K];
+  int32_t n;
+
+  __device__ void clear() { n = 0; }
+
+  // Drop runs that ended before t: a run (f, l] + (lo, hi] is dead once t - l > hi.
+  __device__ void expire(int32_t t, uint32_t hi) {
+#pragma unroll
+    for (int it = 0; it < K; ++it) {
+      const bool dead = n > 0 && ((uint32_t)t - (uint32_t)l[0]) > hi;
+      if (dead) {
+#pragma unroll
+        for (int i = 0; i + 1 < K; ++i) {
+          f[i] = f[i + 1];
+          l[i] = l[i + 1];
+        }
+        --n;
+      }
+    }
+  }
+
+  // Is t inside (t' + lo, t' + hi] for some candidate t' of this window?
+  __device__ bool contains(int32_t t, uint32_t lo, uint32_t hi) {
+    expire(t, hi);
+    return n > 0 && ((uint32_t)t - (uint32_t)f[0]) > lo;
+  }
+
+  // Add candidate t (t is not older than any stored candidate).
+  __device__ void insert(int32_t t, uint32_t hi, uint32_t width) {
+    expire(t, hi);
+    int32_t last_l = l[0];
+#pragma unroll
+    for (int i = 1; i < K; ++i) last_l = (i == n - 1) ? l[i] : last_l;
+    const bool merge = n > 0 && ((uint32_t)t - (uint32_t)last_l) <= width;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (merge && i == n - 1) l[i] = t;
+      if (!merge && i == n) {
+        f[i] = t;
+        l[i] = t;
+      }
+    }
+    n += merge ? 0 : 1;
+  }
+};
+
+// The serial counting machine of one episode.
+template <int N, int K>
+struct Machine {
+  int64_t r;  // time of the last reset (last completion, or the start)
+  Window<K> w[N > 1 ? N - 1 : 1];
+
+  __device__ void reset(int64_t at) {
+    r = at;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) w[j].clear();
+  }
+
+  // Feed an event at time t with level mask lm (non-zero).  Returns true if it
+  // completes an occurrence; the machine is then reset at t.  Events at or
+  // before the last reset are ignored: occurrences must start strictly after
+  // the previous counted one ends.
+  __device__ bool step(int32_t t, uint32_t lm, const EpParams<N>& P) {
+    if ((int64_t)t <= r) return false;
+    if ((lm >> (N - 1)) & 1u) {
+      bool done = true;
+      if constexpr (N > 1) done = w[N - 2].contains(t, P.lo[N - 2], P.hi[N - 2]);
+      if (done) {
+        reset(t);
+        return true;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      if ((lm >> j) & 1u) {
+        bool ok = true;
+        if (j > 0) ok = w[j - 1].contains(t, P.lo[j - 1], P.hi[j - 1]);
+        if (ok) w[j].insert(t, P.hi[j], P.width[j]);
+      }
+    }
+    return false;
+  }
+};
+
+// A machine bound to one segment (tau_lo, tau_hi]: it produces the segment's
+// (a, count, b) tuple.  a = first completion in (tau_lo, tau_lo + Span] (else
+// 0), count = completions in (tau_lo, tau_hi], b = first completion in
+// (tau_hi, tau_hi + Span] (else 0); the windows are closed on the right.
+template <int N, int K>
+struct SegMachine {
+  Machine<N, K> m;
+  int64_t tau_lo;
+  int64_t tau_hi;
+  int64_t stop;  // tau_hi + Span: nothing after it can change the tuple
+  int32_t count;
+  int32_t a_off;
+  int32_t b_off;
+  bool first_found;
+  bool finished;
+
+  __device__ void init(int64_t reset_at, int64_t lo_cut, int64_t hi_cut, int32_t span) {
+    m.reset(reset_at);
+    tau_lo = lo_cut;
+    tau_hi = hi_cut;
+    stop = hi_cut + span;
+    count = 0;
+    a_off = 0;
+    b_off = 0;
+    first_found = false;
+    finished = false;
+  }
+
+  __device__ void feed(int32_t t, uint32_t lm, const EpParams<N>& P) {
+    if (finished || lm == 0) return;
+    if ((int64_t)t > stop) {
+      finished = true;
+      return;
+    }
+    if (m.step(t, lm, P) && (int64_t)t > tau_lo) {
+      if (!first_found) {
+        first_found = true;
+        const int64_t d = (int64_t)t - tau_lo;
+        a_off = d <= (int64_t)P.span ? (int32_t)d : 0;
+      }
+      if ((int64_t)t <= tau_hi) {
+        ++count;
+      } else {
+        b_off = (int32_t)((int64_t)t - tau_hi);
+        finished = true;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- Map kernel
+
+struct MapArgs {
+  const int32_t* times;
+  const uint16_t* types;
+  const uint16_t* ep_types;  // [S*N]
+  const int32_t* ep_lo;      // [S*(N-1)]
+  const int32_t* ep_hi;      // [S*(N-1)]
+  const int32_t* ep_span;    // [S]
+  const int64_t* tau;        // [P+1] cuts
+  const int32_t* seg_beg;    // [P] first event index with time > tau_p - maxSpan
+  const int32_t* seg_end;    // [P] first event index with time > tau_{p+1} + maxSpan
+  Tuple* tuples;             // [P*S*slots]
+  int32_t* nslots;           // [P*S]
+  int64_t S;
+  int32_t P;
+  int32_t M;      // machines per (segment, episode): N for MapConcatenate, 1 for PTPE
+  int32_t G;      // episodes per workgroup
+  int32_t R;      // segments per workgroup
+  int32_t CH;     // events per segment per chunk (R * CH <= kTile)
+  int32_t slots;  // tuple slots per (segment, episode)
+};
+
+// One lane = one machine (segment p, episode e, machine k).  A workgroup holds R
+// consecutive segments x G episodes x M machines; it streams the R segments'
+// event ranges through LDS in lockstep chunks of CH events each, and every
+// lane feeds its own segment's chunk to its machine.
+template <int N, int K>
+__global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
+  __shared__ int32_t s_t[kTile];
+  __shared__ uint16_t s_y[kTile];
+  __shared__ int32_t s_beg[kBlock];
+  __shared__ int32_t s_len[kBlock];
+  __shared__ int32_t s_chunks;
+
+  const int tid = threadIdx.x;
+  const int per_seg = A.G * A.M;
+  const int r_idx = tid / per_seg;
+  const int g = (tid / A.M) % A.G;
+  const int k = tid % A.M;
+  const int64_t p = (int64_t)blockIdx.x * A.R + r_idx;
+  const int64_t e = (int64_t)blockIdx.y * A.G + g;
+  const bool active = tid < A.R * per_seg && p < A.P && e < A.S;
+
+  if (tid == 0) s_chunks = 0;
+  __syncthreads();
+  if (tid < A.R) {
+    const int64_t pp = (int64_t)blockIdx.x * A.R + tid;
+    int32_t b = 0, len = 0;
+    if (pp < A.P) {
+      b = A.seg_beg[pp];
+      len = A.seg_end[pp] - b;
+    }
+    s_beg[tid] = b;
+    s_len[tid] = len;
+    atomicMax(&s_chunks, (len + A.CH - 1) / A.CH);
+  }
+
+  EpParams<N> prm;
+  SegMachine<N, K> sm;
+  if (active) {
+    prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
+    const int64_t lo_cut = A.tau[p];
+    const int64_t hi_cut = A.tau[p + 1];
+    sm.init(lo_cut - prm.prefix_hi(k), lo_cut, hi_cut, prm.span);
+  }
+  __syncthreads();
+  const int n_chunks = s_chunks;
+
+  for (int c = 0; c < n_chunks; ++c) {
+    if (c > 0) __syncthreads();  // previous chunk fully consumed
+    for (int r = 0; r < A.R; ++r) {
+      const int32_t base = s_beg[r] + c * A.CH;
+      const int32_t avail = s_len[r] - c * A.CH;
+      for (int i = tid; i < A.CH; i += kBlock) {
+        if (i < avail) {
+          s_t[r * A.CH + i] = A.times[base + i];
+          s_y[r * A.CH + i] = A.types[base + i];
+        }
+      }
+    }
+    __syncthreads();
+    if (active && !sm.finished) {
+      int32_t len = s_len[r_idx] - c * A.CH;
+      len = len < A.CH ? len : A.CH;
+      const int off = r_idx * A.CH;
+      for (int i = 0; i < len; ++i) {
+        const int32_t t = s_t[off + i];
+        const uint32_t lm = prm.level_mask(s_y[off + i]);
+        sm.feed(t, lm, prm);
+      }
+    }
+  }
+
+  if (active) {
+    const int64_t pe = p * A.S + e;
+    Tuple tu;
+    tu.a = sm.a_off;
+    tu.c = sm.count;
+    tu.b = sm.b_off;
+    tu.pad = 0;
+    A.tuples[pe * A.slots + k] = tu;
+    if (k == 0) A.nslots[pe] = A.M;
+  }
+}
+
+// ------------------------------------------- wave-cooperative single machine
+
+// All 64 lanes hold the same machine; they load 64 events at a time with one
+// coalesced access, ballot the events whose type sits on a node of the
+// episode, and feed those, in order, to the (uniform) machine.
+template <int N, int K>
+__device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int64_t i0,
+                                int64_t i1, SegMachine<N, K>& sm, const EpParams<N>& prm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int64_t base = i0; base < i1 && !sm.finished; base += kWave) {
+    const int64_t i = base + lane;
+    const bool valid = i < i1;
+    const int32_t t = valid ? times[i] : 0;
+    const uint32_t lm = valid ? prm.level_mask(types[i]) : 0u;
+    uint64_t mask = __ballot(lm != 0u);
+    while (mask != 0 && !sm.finished) {
+      const int src = __ffsll((unsigned long long)mask) - 1;
+      mask &= mask - 1;
+      const int32_t tt = __shfl(t, src);
+      const uint32_t ll = (uint32_t)__shfl((int)lm, src);
+      sm.feed(tt, ll, prm);
+    }
+  }
+}
+
+// First index in [lo, hi) whose time is > v (hi if none).
+__device__ inline int64_t upper_bound_time(const int32_t* times, int64_t lo, int64_t hi, int64_t v) {
+  while (lo < hi) {
+    const int64_t mid = lo + ((hi - lo) >> 1);
+    if ((int64_t)times[mid] > v)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------ closure (match + repair)
+
+struct ClosureArgs {
+  const int32_t* times;
+  const uint16_t* types;
+  const uint16_t* ep_types;
+  const int32_t* ep_lo;
+  const int32_t* ep_hi;
+  const int32_t* ep_span;
+  const int64_t* tau;
+  const int32_t* seg_beg;
+  const int32_t* seg_end;
+  Tuple* tuples;
+  int32_t* nslots;
+  int32_t* flags;              // [S] non-zero: recount this episode with the fallback
+  unsigned long long* repairs; // repair-tuple counter
+  int64_t S;
+  int32_t P;
+  int32_t slots;
+};
+
+// The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
+// machine reset at x runs over segment q.  Its count includes the completion
+// at x itself when x <= tau_{q+1}.
+template <int N, int K>
+__device__ Tuple repair_tuple(const ClosureArgs& A, const EpParams<N>& prm, int64_t q, int64_t x) {
+  const int64_t lo_cut = A.tau[q];
+  const int64_t hi_cut = A.tau[q + 1];
+  Tuple tu;
+  tu.a = (int32_t)(x - lo_cut);
+  tu.pad = 0;
+  if (x > hi_cut) {
+    tu.c = 0;
+    tu.b = (int32_t)(x - hi_cut);
+    return tu;
+  }
+  SegMachine<N, K> sm;
+  sm.init(x, lo_cut, hi_cut, prm.span);
+  const int64_t i0 = upper_bound_time(A.times, A.seg_beg[q], A.seg_end[q], x);
+  wave_feed_range<N, K>(A.times, A.types, i0, A.seg_end[q], sm, prm);
+  tu.c = sm.count + 1;
+  tu.b = sm.b_off;
+  return tu;
+}
+
+template <int N>
+__device__ bool has_map_key(const ClosureArgs& A, int64_t q, int64_t e, int32_t key) {
+  const Tuple* T = A.tuples + (q * A.S + e) * A.slots;
+  bool hit = false;
+#pragma unroll
+  for (int m = 0; m < N; ++m) hit |= (T[m].a == key);
+  return hit;
+}
+
+// For every boundary p -> p+1 and episode e: each distinct exit b of segment
+// p's Map tuples must be a key a of segment p+1 (Concatenate rule 2 needs
+// b_s = a_t).  A missing exit gets a repair tuple in segment p+1, and the
+// repair's own exit is checked against segment p+2, and so on.  Items are one
+// per lane; the repairs of a wave's items run one after another with the
+// whole wave cooperating on each.
+template <int N, int K>
+__global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
+  const int64_t n_items = (int64_t)(A.P - 1) * A.S;
+  const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  uint32_t missing = 0;
+  if (item < n_items) {
+    const int64_t p = item / A.S;
+    const int64_t e = item - p * A.S;
+    const Tuple* L = A.tuples + (p * A.S + e) * A.slots;
+    const Tuple* R = A.tuples + ((p + 1) * A.S + e) * A.slots;
+    int32_t keys[N];
+#pragma unroll
+    for (int m = 0; m < N; ++m) keys[m] = R[m].a;
+    int32_t exits[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) exits[k] = L[k].b;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      bool hit = false, dup = false;
+#pragma unroll
+      for (int m = 0; m < N; ++m) hit |= keys[m] == exits[k];
+#pragma unroll
+      for (int j = 0; j < k; ++j) dup |= exits[j] == exits[k];
+      if (!hit && !dup) missing |= 1u << k;
+    }
+  }
+  uint64_t wmask = __ballot(missing != 0u);
+  const int lane = threadIdx.x & (kWave - 1);
+  while (wmask != 0) {
+    const int src = __ffsll((unsigned long long)wmask) - 1;
+    wmask &= wmask - 1;
+    const int64_t it = (int64_t)__shfl((long long)item, src);
+    uint32_t miss = (uint32_t)__shfl((int)missing, src);
+    const int64_t p = it / A.S;
+    const int64_t e = it - p * A.S;
+    EpParams<N> prm;
+    prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
+    while (miss != 0u) {
+      const int k = __ffs((int)miss) - 1;
+      miss &= miss - 1;
+      int32_t x_off = A.tuples[(p * A.S + e) * A.slots + k].b;
+      int64_t q = p + 1;
+      for (;;) {
+        if (x_off <= 0) {  // a sentinel exit always has a sentinel key; never repair it
+          if (lane == 0) atomicOr(&A.flags[e], 1);
+          break;
+        }
+        const Tuple tu = repair_tuple<N, K>(A, prm, q, A.tau[q] + x_off);
+        int slot = 0;
+        if (lane == 0) slot = atomicAdd(&A.nslots[q * A.S + e], 1);
+        slot = __shfl(slot, 0);
+        if (slot >= A.slots) {
+          if (lane == 0) atomicOr(&A.flags[e], 1);
+          break;
+        }
+        if (lane == 0) {
+          A.tuples[(q * A.S + e) * A.slots + slot] = tu;
+          atomicAdd(A.repairs, 1ull);
+        }
+        if (q + 1 >= A.P) break;
+        if (has_map_key<N>(A, q + 1, e, tu.b)) break;
+        x_off = tu.b;
+        ++q;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- fallback
+
+struct FallbackArgs {
+  const int32_t* times;
+  const uint16_t* types;
+  const uint16_t* ep_types;
+  const int32_t* ep_lo;
+  const int32_t* ep_hi;
+  const int32_t* ep_span;
+  const int32_t* flags;
+  unsigned long long* fallbacks;
+  int64_t* out;
+  int64_t n;
+  int64_t S;
+};
+
+// Exact safety net: one wave recounts a flagged episode over the whole
+// stream with a single machine (the page's alpha_0 on the unsegmented stream).
+template <int N, int K>
+__global__ __launch_bounds__(kBlock) void fallback_kernel(FallbackArgs A) {
+  const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (e >= A.S) return;
+  if (A.flags[e] == 0) return;
+  EpParams<N> prm;
+  prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
+  const int64_t before = (int64_t)A.times[0] - 1;
+  SegMachine<N, K> sm;
+  sm.init(before, before, INT64_MAX / 4, prm.span);
+  wave_feed_range<N, K>(A.times, A.types, 0, A.n, sm, prm);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    A.out[e] = sm.count;
+    atomicAdd(A.fallbacks, 1ull);
+  }
+}
+
+// ----------------------------------------------------------- launchers
+
+// Per-N entry points, defined in ep_inst.hip (one translation unit per N).
+struct Launchers {
+  hipError_t (*map)(const MapArgs&, int K, dim3 grid, hipStream_t);
+  hipError_t (*closure)(const ClosureArgs&, int K, dim3 grid, hipStream_t);
+  hipError_t (*fallback)(const FallbackArgs&, int K, dim3 grid, hipStream_t);
+  hipError_t (*map_occupancy)(int K, int* blocks_per_cu);
+};
+
+}  // namespace epk

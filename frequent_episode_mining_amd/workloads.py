@@ -27,7 +27,8 @@ embedded causal chains), scaled to five configurations:
               segments.
 
 Every generator takes ``n`` so that tests can draw the same shape at a size the
-oracle finishes in seconds.  Events are sorted by (time, type).
+oracle finishes in seconds.  Events are sorted by time; events that share a
+tick are in random order (the count does not depend on that order).
 """
 from __future__ import annotations
 
@@ -96,7 +97,11 @@ def _random_episodes(rng, S: int, N: int, n_types: int) -> np.ndarray:
 
 
 def _merge_planted(times_bg, types_bg, pt, py, n, rng):
-    """Merge planted events into a background stream and trim/pad to exactly n."""
+    """Merge planted events into a time-sorted background and trim/pad to exactly n.
+
+    The result is sorted by time; events sharing a tick keep the background's
+    random order, with planted events after them.
+    """
     pt = np.asarray(pt, dtype=np.int64)
     py = np.asarray(py, dtype=np.int64)
     keep = n - pt.size
@@ -110,13 +115,17 @@ def _merge_planted(times_bg, types_bg, pt, py, n, rng):
         times_bg, types_bg = times_bg[mask], types_bg[mask]
     elif bg_n < keep:
         lo, hi = int(times_bg.min()), int(times_bg.max())
-        extra_t = rng.integers(lo, hi + 1, size=keep - bg_n)
+        extra_t = np.sort(rng.integers(lo, hi + 1, size=keep - bg_n))
         extra_y = rng.integers(0, int(types_bg.max()) + 1, size=keep - bg_n)
-        times_bg = np.concatenate([times_bg, extra_t])
-        types_bg = np.concatenate([types_bg, extra_y])
-    t = np.concatenate([times_bg.astype(np.int64), pt])
-    y = np.concatenate([types_bg.astype(np.int64), py])
-    return _sort_events(t.astype(np.int32), y.astype(np.uint16))
+        pos = np.searchsorted(times_bg, extra_t, side="right")
+        times_bg = np.insert(times_bg, pos, extra_t.astype(times_bg.dtype))
+        types_bg = np.insert(types_bg, pos, extra_y.astype(types_bg.dtype))
+    order = np.argsort(pt, kind="stable")
+    pt, py = pt[order], py[order]
+    pos = np.searchsorted(times_bg, pt, side="right")
+    times = np.insert(np.asarray(times_bg, dtype=np.int32), pos, pt.astype(np.int32))
+    types = np.insert(np.asarray(types_bg, dtype=np.uint16), pos, py.astype(np.uint16))
+    return np.ascontiguousarray(times), np.ascontiguousarray(types)
 
 
 def tiny(n: int = 10_000, seed: int = BASE_SEED + 0, n_types: int = 26,
@@ -245,8 +254,7 @@ def level2(n: int = 10_000_000, seed: int = BASE_SEED + 3, n_types: int = 64) ->
     with each delay bin (0,5],(5,10],(10,20],(20,40]: n_types^2 * 4 episodes,
     ordered by (first type, second type, bin)."""
     rng = np.random.default_rng(seed)
-    t_bg, y_bg, T = _poisson_background(rng, n, n_types, 0.02)
-    times, types = _sort_events(t_bg, y_bg)
+    times, types, T = _poisson_background(rng, n, n_types, 0.02)
     a = np.repeat(np.arange(n_types), n_types * len(LEVEL2_BINS))
     b = np.tile(np.repeat(np.arange(n_types), len(LEVEL2_BINS)), n_types)
     bins = np.tile(np.arange(len(LEVEL2_BINS)), n_types * n_types)

@@ -1,0 +1,185 @@
+/*
+ * epcount.h -- C ABI of the MI355X (gfx950) serial-episode counting library.
+ *
+ * Source page: "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
+ * Episodes Using Graphics Processors".
+ *
+ * The library counts, for each of S candidate episodes, the number of
+ * non-overlapped occurrences of the serial episode
+ *     E(1) -(t_low_1, t_high_1]-> E(2) -> ... -> E(N)
+ * in one time-sorted event stream (opening section: support counting for M
+ * episodes, each counted independently; "Design of MapConcatenate": the
+ * episode with half-open inter-event delay intervals, Fig. 3 text: the
+ * reference serial machine alpha_0 and non-overlapped occurrences).
+ *
+ * Definitions used by every entry point:
+ *   - An occurrence is a choice of events (t_1,E(1)),...,(t_N,E(N)) of the
+ *     stream with t_low_i < t_{i+1} - t_i <= t_high_i for i = 1..N-1.
+ *   - Two occurrences are non-overlapped when one starts strictly after the
+ *     other ends (equal times overlap).
+ *   - The count of an episode is the largest number of pairwise
+ *     non-overlapped occurrences.  It is an exact integer; the result does
+ *     not depend on the order of events that share a time.
+ *
+ * The work runs on the GPU in one of two schemes (both exact, same result):
+ *   PTPE       one GPU lane runs the serial counting machine for one episode
+ *              over the whole stream (opening section, Algorithm 1 per thread).
+ *   MAPCONCAT  the stream is cut into P time segments; each segment runs N
+ *              machines per episode, machine k reset at
+ *              tau_p - (t_high_1 + ... + t_high_k), that emit (a, count, b)
+ *              tuples (Map rules 1-4, Figs. 4-5); a log-depth tree joins
+ *              adjacent segments where the left exit b equals the right key a
+ *              (Concatenate rules 1-3, Fig. 6).
+ * AUTO picks PTPE when the episodes alone fill the GPU and MAPCONCAT
+ * otherwise (hybrid-algorithm section: "fully utilized" test on episodes,
+ * threads per block, multiprocessors and resident blocks per multiprocessor).
+ *
+ * Conventions shared by all calls:
+ *   - Device pointers point into memory of the current HIP device; host
+ *     pointers into ordinary host memory.  The caller owns every pointer; the
+ *     library keeps none of them after the call returns.
+ *   - Calls are asynchronous on `stream` unless stated otherwise: on EP_OK the
+ *     outputs are valid once the stream has reached the end of the work the
+ *     call enqueued.  Host-side argument errors are returned before anything
+ *     is enqueued.  Scratch memory is taken from and returned to the stream-
+ *     ordered allocator (hipMallocAsync / hipFreeAsync) on `stream`.
+ *   - Inputs outside the documented domain (unsorted times) give unspecified
+ *     counts unless `validate` is set in ep_options.
+ *   - The library is thread-safe: concurrent calls on different streams do
+ *     not share mutable state except a pinned staging buffer guarded by a lock.
+ */
+#ifndef EPCOUNT_H
+#define EPCOUNT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest supported episode size N. */
+#define EP_MAX_NODES 16
+
+/* Status codes returned by every entry point (0 = success). */
+typedef enum {
+  EP_OK = 0,
+  EP_ERR_ARG = -1,         /* null pointer with a non-zero size, negative size, n_events > INT32_MAX */
+  EP_ERR_NODES = -2,       /* n_nodes outside 1..EP_MAX_NODES */
+  EP_ERR_INTERVAL = -3,    /* some t_low < 0, t_low >= t_high, or t_high_1+...+t_high_{N-1} > INT32_MAX */
+  EP_ERR_UNSORTED = -4,    /* validate: times are not non-decreasing */
+  EP_ERR_WORKSPACE = -5,   /* scratch allocation failed */
+  EP_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+  EP_ERR_UNSUPPORTED = -7  /* a delay window needs more candidate runs than the kernels hold (see EP_MAX_RUNS) */
+} ep_status;
+
+/*
+ * Candidate runs per node window.  A node window holds the union of the
+ * intervals (t'+t_low, t'+t_high] over the candidate times t' of the previous
+ * node; at most floor(t_high/(t_high-t_low+1)) + 1 disjoint runs of it can
+ * be live at once, and the kernels keep up to EP_MAX_RUNS of them per node.
+ */
+#define EP_MAX_RUNS 4
+
+/*
+ * The candidate episode set, S episodes of the same size N.  HOST memory:
+ * the planner reads the delay bounds to size the kernels' windows, then the
+ * library copies the table to the device itself.
+ *   n_nodes  N, 1 <= N <= EP_MAX_NODES.
+ *   types    [S * N] event types, row-major: episode e's node k is types[e*N+k].
+ *            A type may repeat inside an episode.
+ *   t_low    [S * (N-1)] lower delay bounds, row-major (may be NULL if N == 1).
+ *   t_high   [S * (N-1)] upper delay bounds, 0 <= t_low < t_high.
+ */
+typedef struct {
+  int32_t n_nodes;
+  const uint16_t* types;
+  const int32_t* t_low;
+  const int32_t* t_high;
+} ep_episodes;
+
+/*
+ * Count S episodes over one event stream (the operation of the opening
+ * section; scheme chosen by the hybrid rule).
+ *   times       DEVICE, int32[n_events], non-decreasing event times (ticks).
+ *   types       DEVICE, uint16[n_events], event types; SoA with `times`.
+ *   n_events    0 <= n_events <= INT32_MAX.  0 gives all-zero counts.
+ *   episodes    HOST table described above.
+ *   n_episodes  S >= 0.  0 is a no-op.
+ *   out_counts  DEVICE, int64[n_episodes], written with the counts.
+ *   stream      HIP stream all work is enqueued on (0 = default stream).
+ * Returns EP_OK or an ep_status error; on error `out_counts` is untouched
+ * unless the error is EP_ERR_HIP.
+ */
+int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_events,
+                      ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                      hipStream_t stream);
+
+/* Scheme selection for ep_count_episodes_ex. */
+enum { EP_MODE_AUTO = 0, EP_MODE_PTPE = 1, EP_MODE_MAPCONCAT = 2 };
+
+/* Optional statistics filled by ep_count_episodes_ex when `stats` is set. */
+typedef struct {
+  int32_t mode;         /* scheme that ran: EP_MODE_PTPE or EP_MODE_MAPCONCAT */
+  int32_t n_segments;   /* P (1 for PTPE) */
+  int32_t max_runs;     /* run capacity per node window the kernels were built with */
+  int32_t reserved;
+  int64_t repairs;      /* repair tuples made for unmatched segment exits */
+  int64_t fallbacks;    /* episodes recounted by the whole-stream fallback */
+} ep_stats;
+
+/*
+ * Options for ep_count_episodes_ex.
+ *   mode        EP_MODE_AUTO, EP_MODE_PTPE or EP_MODE_MAPCONCAT.
+ *   n_segments  MAPCONCAT only: P >= 1, 0 = chosen by the planner.  Any P is
+ *               valid; the planner picks powers of two (Concatenate section).
+ *   validate    non-zero: check on the device that times are non-decreasing
+ *               and return EP_ERR_UNSORTED if not.  Synchronises `stream`.
+ *   stats       if non-NULL, filled after the work completes.  Synchronises
+ *               `stream`.
+ */
+typedef struct {
+  int32_t mode;
+  int32_t n_segments;
+  int32_t validate;
+  int32_t reserved;
+  ep_stats* stats;
+} ep_options;
+
+/* ep_count_episodes with explicit options (opt may be NULL = defaults). */
+int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
+                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                         hipStream_t stream, const ep_options* opt);
+
+/*
+ * The planner alone, on a described device (no GPU needed): which scheme and
+ * segment count a call would use.
+ *   n_episodes, n_nodes, n_events  sizes of the call.
+ *   mode, n_segments               as in ep_options.
+ *   cu_count                       multiprocessors of the device (MP).
+ *   lanes_per_cu                   resident lanes per multiprocessor of the
+ *                                  counting kernel (T_B * B_MP).
+ *   out_mode, out_segments         results (host pointers).
+ * Rule (hybrid-algorithm section): PTPE iff n_episodes >= cu_count *
+ * lanes_per_cu; otherwise MAPCONCAT with the smallest power-of-two P such
+ * that n_episodes * n_nodes * P >= cu_count * lanes_per_cu, capped so that a
+ * segment keeps at least 256 events on average and P <= 2^20.
+ */
+int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, int32_t mode,
+            int32_t n_segments, int32_t cu_count, int32_t lanes_per_cu,
+            int32_t* out_mode, int32_t* out_segments);
+
+/* Equal-time cut p (0 <= p <= P) of a stream spanning [t_min, t_max]:
+ * t_min - 1 + floor(p * (t_max - t_min + 1) / P).  Segment p (0-based) holds
+ * the events with time in (cut(p), cut(p+1)] ("Design of MapConcatenate":
+ * events of segment p lie in (tau_p, tau_{p+1}]). */
+int64_t ep_segment_cut(int32_t t_min, int32_t t_max, int32_t n_segments, int32_t p);
+
+/* Static text for a status code. */
+const char* ep_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPCOUNT_H */

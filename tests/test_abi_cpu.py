@@ -1,0 +1,98 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/epcount.h declares, and rejects bad arguments on the host before
+anything touches a GPU.  Also the planner (hybrid rule of the page "Towards
+Chip-on-Chip Neuroscience: Fast Mining of Frequent Episodes Using Graphics
+Processors": PTPE when the episodes fill the GPU, else MapConcatenate) on
+described devices, and the documented equal-time cut rule."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import frequent_episode_mining_amd as fem
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "epcount.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(ep_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fem.load_library()
+    names = declared_functions()
+    assert {"ep_count_episodes", "ep_count_episodes_ex", "ep_plan", "ep_segment_cut",
+            "ep_status_string"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in fem.STATUS:
+        assert fem.status_string(code)
+    assert fem.status_string(12345) == "unknown status"
+
+
+def _call(n_events=10, S=1, N=2, lo=(0,), hi=(5,), times=1, types=1, out=1, opt=None):
+    lib = fem.load_library()
+    ep_t = np.zeros(max(S, 1) * N, np.uint16)
+    lo_a = np.array(list(lo) * max(S, 1), np.int32)
+    hi_a = np.array(list(hi) * max(S, 1), np.int32)
+    eps = fem.EpEpisodes(N, ep_t.ctypes.data, lo_a.ctypes.data if lo_a.size else None,
+                         hi_a.ctypes.data if hi_a.size else None)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case here fails on the host
+    return lib.ep_count_episodes_ex(fake if times else None, fake if types else None, n_events, eps,
+                                    S, fake if out else None, None, opt)
+
+
+def test_host_argument_errors():
+    assert _call(n_events=-1) == -1
+    assert _call(S=-1) == -1
+    assert _call(n_events=2 ** 31) == -1
+    assert _call(out=0) == -1
+    assert _call(times=0) == -1
+    assert _call(N=0, lo=(), hi=()) == -2
+    assert _call(N=17, lo=(0,) * 16, hi=(5,) * 16) == -2
+    assert _call(lo=(5,), hi=(5,)) == -3
+    assert _call(lo=(-1,), hi=(5,)) == -3
+    assert _call(N=3, lo=(0, 0), hi=(2 ** 31 - 1, 2)) == -3
+    # a window with more live runs than EP_MAX_RUNS: (9,10] has up to 6
+    assert _call(lo=(9,), hi=(10,)) == -7
+    bad_mode = fem.EpOptions(7, 0, 0, 0, None)
+    assert _call(opt=ctypes.byref(bad_mode)) == -1
+    bad_p = fem.EpOptions(2, -4, 0, 0, None)
+    assert _call(opt=ctypes.byref(bad_p)) == -1
+    # no episodes: a no-op that needs no device at all
+    assert _call(S=0, out=0) == 0
+
+
+def test_planner_rule():
+    # episodes alone fill 256 CUs x 2048 lanes -> PTPE
+    assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
+    # 1,024 four-node episodes: MapConcatenate with the smallest 2^q filling the device
+    mode, P = fem.plan(1024, 4, 10 ** 6, cu_count=256, lanes_per_cu=2048)
+    assert mode == "mapconcat" and P == 128 and 1024 * 4 * P >= 256 * 2048
+    # few episodes, long stream
+    assert fem.plan(8, 5, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 16384)
+    # the segment count is capped so a segment keeps >= 256 events on average
+    assert fem.plan(1, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 32)
+    # forced choices pass through
+    assert fem.plan(8, 5, 10 ** 8, mode="mapconcat", n_segments=4096) == ("mapconcat", 4096)
+    assert fem.plan(8, 5, 10 ** 8, mode="ptpe") == ("ptpe", 1)
+    # a smaller device needs fewer segments
+    m1, p1 = fem.plan(64, 3, 10 ** 7, cu_count=8, lanes_per_cu=1024)
+    m2, p2 = fem.plan(64, 3, 10 ** 7, cu_count=256, lanes_per_cu=1024)
+    assert m1 == m2 == "mapconcat" and p1 < p2
+
+
+def test_segment_cut_rule():
+    # cut p of [t_min, t_max] into P equal-time segments
+    assert fem.segment_cut(1, 100, 4, 0) == 0
+    assert fem.segment_cut(1, 100, 4, 4) == 100
+    assert [fem.segment_cut(90, 111, 2, p) for p in range(3)] == [89, 100, 111]
+    cuts = [fem.segment_cut(-2 ** 31, 2 ** 31 - 1, 1024, p) for p in range(1025)]
+    assert cuts[0] == -2 ** 31 - 1 and cuts[-1] == 2 ** 31 - 1
+    assert all(b >= a for a, b in zip(cuts, cuts[1:]))

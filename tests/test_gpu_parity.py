@@ -1,0 +1,155 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Counts are integers, so the bar is bit-exact equality for every episode.
+Each case runs AUTO, forced PTPE and forced MapConcatenate with several
+segment counts (page "Towards Chip-on-Chip Neuroscience: Fast Mining of
+Frequent Episodes Using Graphics Processors": the two schemes and the hybrid
+choice must agree with the reference serial machine alpha_0).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import all_cases
+from frequent_episode_mining_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fem():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import frequent_episode_mining_amd as m
+    m.load_library()
+    return m
+
+
+def _gpu(fem, times, types, ep, lo, hi, mode, P=0, stats=False):
+    t, y = fem.to_device(times, types, "cuda")
+    res = fem.count_episodes(t, y, ep, lo, hi, mode=mode, n_segments=P, stats=stats)
+    torch.cuda.synchronize()
+    if stats:
+        return res[0].cpu().numpy(), res[1]
+    return res.cpu().numpy()
+
+
+def _check(got, want, label):
+    if not np.array_equal(got, want):
+        bad = np.nonzero(got != want)[0][:8]
+        raise AssertionError("%s: %d mismatches, episodes %s got %s want %s" % (
+            label, int((got != want).sum()), bad.tolist(), got[bad].tolist(), want[bad].tolist()))
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 1), ("mapconcat", 2), ("mapconcat", 3),
+         ("mapconcat", 4), ("mapconcat", 7), ("mapconcat", 16), ("mapconcat", 64)]
+
+
+@pytest.mark.parametrize("case", all_cases(), ids=lambda c: c["name"])
+def test_golden(fem, case):
+    _log("golden %s" % case["name"])
+    want = np.array(case["expect"]["count"], np.int64)
+    for mode, P in MODES:
+        got = _gpu(fem, case["times"], case["types"], case["ep_types"][None], case["t_low"][None],
+                   case["t_high"][None], mode, P)
+        _check(got, want, "%s %s P=%d" % (case["name"], mode, P))
+
+
+def test_boundary_miss_is_repaired(fem):
+    case = [c for c in all_cases() if c["name"] == "boundary_miss_lower_bound"][0]
+    got, st = _gpu(fem, case["times"], case["types"], case["ep_types"][None], case["t_low"][None],
+                   case["t_high"][None], "mapconcat", 2, stats=True)
+    assert got[0] == 2
+    assert st["repairs"] >= 1 and st["fallbacks"] == 0 and st["n_segments"] == 2
+
+
+def test_fuzz_small_streams(fem):
+    rng = np.random.default_rng(31)
+    checked = 0
+    for trial in range(60):
+        n = int(rng.integers(1, 400))
+        n_types = int(rng.integers(1, 6))
+        N = int(rng.integers(1, 6))
+        times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 4)))
+        # windows whose live runs fit the kernels (at most 4)
+        ep, lo, hi = W.random_episodes(rng, int(rng.integers(1, 80)), N, n_types, max_hi=6)
+        ok = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1) if N > 1 else np.ones(ep.shape[0], bool)
+        ep, lo, hi = ep[ok], lo[ok], hi[ok]
+        if ep.shape[0] == 0:
+            continue
+        want = oracle.count(times, types, ep, lo, hi)
+        for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 2), ("mapconcat", 5),
+                        ("mapconcat", 16), ("mapconcat", max(1, n))]:
+            got = _gpu(fem, times, types, ep, lo, hi, mode, P)
+            _check(got, want, "fuzz trial %d n=%d N=%d %s P=%d" % (trial, n, N, mode, P))
+            checked += 1
+    assert checked > 200
+
+
+def test_empty_stream_and_no_episodes(fem):
+    e = np.zeros(0, np.int32)
+    got = _gpu(fem, e, e.astype(np.uint16), np.array([[1, 2]], np.uint16), np.array([[0]], np.int32),
+               np.array([[5]], np.int32), "auto")
+    assert got.tolist() == [0]
+    t, y = fem.to_device(np.array([1, 2], np.int32), np.array([1, 2], np.uint16), "cuda")
+    out = fem.count_episodes(t, y, np.zeros((0, 2), np.uint16), np.zeros((0, 1), np.int32),
+                             np.zeros((0, 1), np.int32))
+    assert out.numel() == 0
+
+
+def test_validate_rejects_unsorted(fem):
+    t, y = fem.to_device(np.array([5, 3, 9], np.int32), np.array([0, 1, 0], np.uint16), "cuda")
+    with pytest.raises(fem.EpError) as ei:
+        fem.count_episodes(t, y, np.array([[0, 1]], np.uint16), [[0]], [[5]], validate=True)
+    assert ei.value.status == -4
+
+
+def test_extreme_times(fem):
+    # times at both ends of the int32 range: cut and window arithmetic must not overflow
+    lo32, hi32 = -2 ** 31, 2 ** 31 - 1
+    times = np.array([lo32, lo32, lo32 + 1, lo32 + 3, 0, 1, 2, hi32 - 3, hi32 - 1, hi32, hi32], np.int32)
+    types = np.array([0, 1, 1, 2, 0, 1, 2, 0, 1, 2, 0], np.uint16)
+    ep = np.array([[0, 1, 2], [0, 1], [1, 2], [0, 0]], dtype=object)
+    for row, lo, hi in [([0, 1, 2], [0, 0], [3, 3]), ([0, 1], [0], [2]), ([1, 2], [1], [4]),
+                        ([0, 0], [0], [2 ** 31 - 1])]:
+        e = np.array([row], np.uint16)
+        lo = np.array([lo], np.int32)
+        hi = np.array([hi], np.int32)
+        want = oracle.count(times, types, e, lo, hi)
+        for mode, P in MODES:
+            _check(_gpu(fem, times, types, e, lo, hi, mode, P), want, "extreme %s %s P=%d" % (row, mode, P))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "level2", "longchain"])
+def test_config_small(fem, name):
+    wl = W.make_small(name)
+    _log("config %s small: n=%d S=%d N=%d" % (name, wl.n_events, wl.n_episodes, wl.n_nodes))
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    runs = [("auto", 0), ("ptpe", 0), ("mapconcat", 0), ("mapconcat", 64), ("mapconcat", 1000)]
+    if wl.n_segments:
+        runs.append(("mapconcat", wl.n_segments))
+    for mode, P in runs:
+        got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, stats=True)
+        _check(got, want, "%s %s P=%d" % (name, mode, P))
+        assert st["fallbacks"] == 0
+
+
+def test_ptpe_config_full_size(fem):
+    # the benchmarked configuration at full size, AUTO launch (as bench.py times it)
+    wl = W.make("ptpe")
+    _log("config ptpe full: n=%d S=%d" % (wl.n_events, wl.n_episodes))
+    t0 = time.time()
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    _log("oracle %.1fs" % (time.time() - t0))
+    got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "auto", stats=True)
+    _log("gpu plan %s" % st)
+    _check(got, want, "ptpe full auto")
+    assert want[0] >= 200  # the planted chains

@@ -170,7 +170,8 @@ MUTANTS = {
                              "tlist_has_predecessor(&L[k - 1], t, lo[0], hi[0])"),
     "completion_also_extends": ("        r = t;\n        for (int k = 0; k < N - 1; ++k) L[k].head = L[k].size = 0;\n        continue;",
                                 "        r = t;\n        for (int k = 0; k < N - 1; ++k) L[k].head = L[k].size = 0;"),
-    "first_level_needs_predecessor": ("int ok = (k == 0) ||", "int ok = (k == 0 && N == 1) ||"),
+    "append_to_wrong_list": ("if (ok && tlist_push(&L[k], (int32_t)t) != 0)",
+                             "if (ok && tlist_push(&L[k > 0 ? k - 1 : 0], (int32_t)t) != 0)"),
     "prune_too_early": ("t - (int64_t)L->v[L->head] > hi", "t - (int64_t)L->v[L->head] >= hi"),
 }
 
