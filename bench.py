@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the serial-episode counting library on one MI355X.
+
+One step = one ep_count_episodes call (every kernel of the scheme the planner
+picks, plus its scratch allocation and episode-table upload) over one batch of
+synthetic, GPU-resident input.  Default workload: 1,000,000 events, 64 types
+firing at 20 Hz on a 1 ms tick, 200 planted four-node chains, 1,024 four-node
+candidate episodes with (2,8] delays.
+
+Prints ONE JSON line: episode-events/s (events x episodes / step time), the
+roofline of the dominant kernel (Map) measured live with HIP events, and the
+CPU oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X figures: 256 CUs x 4 SIMDs x 16 int32 lanes per clock x 2.4 GHz.
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+HBM_PEAK_GBS = 8000.0
+# Algorithmic work of the counting machine per (episode, relevant event): the
+# node-type test, the window check and the window update, ~10 int32 ops.
+OPS_PER_RELEVANT_PAIR = 10
+KERNEL_SOURCES = ["frequent_episode_mining_amd/csrc/ep_device.hpp",
+                  "frequent_episode_mining_amd/csrc/ep_inst.hip"]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def relevant_pairs(wl) -> int:
+    """Sum over episodes of the events whose type sits on one of its nodes."""
+    cnt = np.bincount(wl.types, minlength=65536).astype(np.int64)
+    total = 0
+    for row in wl.ep_types:
+        total += int(cnt[np.unique(row)].sum())
+    return total
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per Map launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "map_kernel_%s_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_val or m_sha.group(1) != kernel_source_sha():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(wl, gpu_counts, target_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload's episodes."""
+    import oracle
+    threads = min(os.cpu_count() or 1, 16)
+    S = wl.n_episodes
+    probe = min(S, max(threads, 8))
+    _, dt, _ = oracle.count_timed(wl.times, wl.types, wl.ep_types[:probe], wl.t_low[:probe],
+                                  wl.t_high[:probe], n_threads=threads)
+    per_ep = dt / probe
+    m = int(min(S, max(probe, target_s / max(per_ep, 1e-9))))
+    # spread the sample over the whole episode list
+    idx = np.unique(np.linspace(0, S - 1, m).astype(np.int64))
+    want, dt, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
+                                        wl.t_high[idx], n_threads=threads)
+    ok = bool(np.array_equal(gpu_counts[idx], want))
+    value = wl.n_events * idx.size / dt
+    return {"value": value, "unit": "episode-events/s", "cores": int(used), "kind": "oracle",
+            "sample": "%d of %d episodes (evenly spaced) over all %d events, %.2f s"
+                      % (idx.size, S, wl.n_events, dt)}, ok, idx.size
+
+
+def calibrate_copy(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="ptpe",
+                    choices=["tiny", "ptpe", "mapconcat", "level2", "longchain"])
+    ap.add_argument("--mode", default="auto", choices=["auto", "ptpe", "mapconcat"])
+    ap.add_argument("--segments", type=int, default=-1,
+                    help="MapConcatenate segment count (-1: the workload's own, 0: planner)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 5)
+        return
+
+    import frequent_episode_mining_amd as fem
+    from frequent_episode_mining_amd import workloads as W
+
+    fem.load_library()
+    t0 = time.time()
+    wl = W.make(args.config)
+    log("workload %s: %s (%.1fs to generate)" % (wl.name, wl.description, time.time() - t0))
+    seg = wl.n_segments if args.segments < 0 else args.segments
+    mode = args.mode
+    if mode == "auto" and args.segments >= 0 and args.segments != 0:
+        mode = "mapconcat"
+    if mode == "auto" and args.segments < 0 and wl.n_segments:
+        mode = "mapconcat"  # the workload names its segment count
+    if mode == "auto":
+        seg = 0
+
+    dev = torch.device("cuda:0")
+    times, types = fem.to_device(wl.times, wl.types, dev)
+    table = fem.EpisodeTable(wl.ep_types, wl.t_low, wl.t_high)
+    out = torch.empty(wl.n_episodes, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    _, st = fem.count_episodes(times, types, table, mode=mode, n_segments=seg, stats=True, out=out)
+    log("plan: %s" % st)
+    for _ in range(args.warmup):
+        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
+    torch.cuda.synchronize(dev)
+
+    fem.profile_begin()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    w1 = time.perf_counter()
+    prof = fem.profile_end()
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    wall_ms = (w1 - w0) * 1000.0 / args.steps
+    ms_per_step = max(gpu_ms, wall_ms)
+    counts = out.cpu().numpy()
+    log("step %.4f ms (gpu events %.4f, wall %.4f); phases per call: map %.4f closure %.4f "
+        "concat %.4f other %.4f ms" % (ms_per_step, gpu_ms, wall_ms, prof["map_ms"] / prof["calls"],
+                                       prof["closure_ms"] / prof["calls"],
+                                       prof["concat_ms"] / prof["calls"], prof["other_ms"] / prof["calls"]))
+
+    n, S = wl.n_events, wl.n_episodes
+    value = n * S / (ms_per_step / 1000.0)
+
+    map_s = prof["map_ms"] / prof["calls"] / 1000.0
+    rel = relevant_pairs(wl)
+    achieved = OPS_PER_RELEVANT_PAIR * rel / map_s / 1e12
+    traffic = stored_traffic(wl.name)
+    roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
+                "frac": achieved / ALU_PEAK_TOPS, "traffic": traffic,
+                "kernel": "map_kernel", "kernel_ms": map_s * 1000.0,
+                "work": "%d int32 ops x %d (episode, relevant event) pairs"
+                        % (OPS_PER_RELEVANT_PAIR, rel),
+                "hbm_one_pass_frac": 6.0 * n / map_s / 1e9 / HBM_PEAK_GBS}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, ok, m = cpu_baseline(wl, counts, args.cpu_seconds)
+        parity = "bit-exact on %d sampled episodes" % m if ok else "MISMATCH"
+        log("cpu oracle: %s; parity %s" % (cpu["sample"], parity))
+        if not ok:
+            print("bench: GPU counts differ from the oracle", file=sys.stderr)
+
+    line = {
+        "metric": "episode-events/sec (events x episodes counted)",
+        "value": value,
+        "unit": "episode-events/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "n_events": n,
+                   "n_episodes": S, "n_nodes": wl.n_nodes, "mode": st["mode"],
+                   "segments": st["n_segments"], "window_runs": st["max_runs"],
+                   "repairs": st["repairs"], "fallbacks": st["fallbacks"],
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line))
+    if parity == "MISMATCH":
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

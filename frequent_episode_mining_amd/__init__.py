@@ -46,6 +46,12 @@ class EpOptions(ctypes.Structure):
                 ("stats", ctypes.POINTER(EpStats))]
 
 
+class EpProfile(ctypes.Structure):
+    _fields_ = [("map_ms", ctypes.c_double), ("closure_ms", ctypes.c_double),
+                ("concat_ms", ctypes.c_double), ("other_ms", ctypes.c_double),
+                ("calls", ctypes.c_int64)]
+
+
 class EpError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
@@ -75,6 +81,10 @@ def load_library(path: str | None = None):
                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.ep_segment_cut.restype = i64
     lib.ep_segment_cut.argtypes = [i32, i32, i32, i32]
+    lib.ep_profile_begin.restype = ctypes.c_int
+    lib.ep_profile_begin.argtypes = []
+    lib.ep_profile_end.restype = ctypes.c_int
+    lib.ep_profile_end.argtypes = [ctypes.POINTER(EpProfile)]
     lib.ep_status_string.restype = ctypes.c_char_p
     lib.ep_status_string.argtypes = [ctypes.c_int]
     if path is None:
@@ -175,6 +185,19 @@ def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_
     _check(lib.ep_plan(n_episodes, n_nodes, n_events, MODES[mode], n_segments, cu_count,
                        lanes_per_cu, ctypes.byref(m), ctypes.byref(p)))
     return MODE_NAMES[m.value], p.value
+
+
+def profile_begin():
+    """Start recording per-phase GPU durations (HIP events) of later calls."""
+    _check(load_library().ep_profile_begin())
+
+
+def profile_end() -> dict:
+    """Wait for the recorded events; summed per-phase milliseconds and calls."""
+    p = EpProfile()
+    _check(load_library().ep_profile_end(ctypes.byref(p)))
+    return {"map_ms": p.map_ms, "closure_ms": p.closure_ms, "concat_ms": p.concat_ms,
+            "other_ms": p.other_ms, "calls": p.calls}
 
 
 def segment_cut(t_min: int, t_max: int, n_segments: int, p: int) -> int:

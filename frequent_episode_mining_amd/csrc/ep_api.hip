@@ -144,18 +144,32 @@ __global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* tim
 
 inline unsigned grid_for(int64_t items) { return (unsigned)((items + kBlock - 1) / kBlock); }
 
+// type -> node slot (1..U), 0 for types on no node: binary search of the
+// sorted distinct node types.
+__global__ __launch_bounds__(kBlock) void remap_kernel(const uint16_t* distinct, int32_t U,
+                                                       uint8_t* remap) {
+  const int32_t y = blockIdx.x * kBlock + threadIdx.x;
+  if (y >= 65536) return;
+  int32_t lo = 0, hi = U;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) >> 1;
+    if ((int32_t)distinct[mid] < y)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  remap[y] = (lo < U && (int32_t)distinct[lo] == y) ? (uint8_t)(lo + 1) : (uint8_t)0;
+}
+
 // ------------------------------------------------------------ host helpers
 
 struct DeviceInfo {
   bool ok = false;
   int cu_count = 0;
-  int occ[EP_MAX_NODES + 1][3] = {};  // blocks per CU of map_kernel<N, K>, K index 0/1/2
 };
 
 std::mutex g_info_mu;
 DeviceInfo g_info[64];
-
-int k_index(int K) { return K == 1 ? 0 : (K == 2 ? 1 : 2); }
 
 // Pinned staging for the episode table upload; the event guards reuse.
 struct Staging {
@@ -169,13 +183,31 @@ Staging g_staging[64];
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-struct Plan {
-  int mode;
-  int32_t P;
-  int M, G, R, CH;
-  int slots;
+// Profiling session: per counting call, events around its phases.
+struct ProfRecord {
+  hipEvent_t ev[5];  // start, before Map, after Map, after closure, after Concatenate
+  hipEvent_t end;
 };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
 
+int prof_record_start(ProfRecord* r, hipStream_t s) {
+  for (int i = 0; i < 5; ++i) {
+    if (hipEventCreate(&r->ev[i]) != hipSuccess) return EP_ERR_HIP;
+  }
+  if (hipEventCreate(&r->end) != hipSuccess) return EP_ERR_HIP;
+  return hipEventRecord(r->ev[0], s) == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+// Lanes per (segment, episode) of the counting kernels: one lane carries all N
+// machines up to N = 8, one machine per lane beyond.
+constexpr int kMaxClassNodes = 8;
+
+// The hybrid rule (hybrid-algorithm section): the GPU is fully utilised by
+// PTPE when the episodes alone give every resident lane of every CU work.
+// Otherwise MapConcatenate with the smallest power-of-two P that does, kept
+// to >= 256 events per segment on average and P <= 2^20.
 int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments, int32_t cu_count,
               int32_t lanes_per_cu, int32_t* out_mode, int32_t* out_segments) {
   const int64_t full = (int64_t)std::max(cu_count, 1) * std::max(lanes_per_cu, 1);
@@ -186,7 +218,8 @@ int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments,
     if (n_segments > 0) {
       P = n_segments;
     } else {
-      const int64_t need = (full + S * N - 1) / std::max<int64_t>(S * N, 1);
+      const int64_t per_seg = std::max<int64_t>(S, 1) * (N <= kMaxClassNodes ? 1 : N);
+      const int64_t need = (full + per_seg - 1) / per_seg;
       const int64_t cap_by_events = std::max<int64_t>(1, n / 256);
       P = 2;
       while (P < need && P < (1 << 20)) P <<= 1;
@@ -255,12 +288,6 @@ int device_info(int dev, DeviceInfo** out) {
     int cus = 0;
     EP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     d.cu_count = cus;
-    for (int N = 1; N <= EP_MAX_NODES; ++N)
-      for (int ki = 0; ki < 3; ++ki) {
-        int b = 0;
-        EP_HIP(launchers_for(N)->map_occupancy(ki == 0 ? 1 : (ki == 1 ? 2 : 4), &b));
-        d.occ[N][ki] = std::max(b, 1);
-      }
     d.ok = true;
   }
   *out = &d;
@@ -291,6 +318,32 @@ int upload(int dev, void* dst, const void* src, size_t bytes, hipStream_t stream
   return EP_OK;
 }
 
+const char* win_name(int w) {
+  switch (w) {
+    case kRuns1: return "runs1";
+    case kRuns2: return "runs2";
+    case kRuns4: return "runs4";
+    case kBits32: return "bits32";
+    case kBits64: return "bits64";
+    default: return "?";
+  }
+}
+
+// Everything the launch sequence needs, decided on the host.
+struct Launch {
+  int mode;        // EP_MODE_PTPE / EP_MODE_MAPCONCAT
+  int32_t P;       // segments
+  int win;         // window kind of the Map kernel and of the wave machines
+  bool bits;       // bit Map kernel (else the scan Map kernel)
+  bool all_mach;   // bit kernel: one lane holds all machines of a (segment, episode)
+  int M;           // lanes per (segment, episode)
+  int G, R, CH;    // episodes and segments per workgroup, events per segment per chunk
+  int block;
+  size_t lds;
+  int slots;
+  int n_machines;
+};
+
 }  // namespace
 
 extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
@@ -308,7 +361,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   if (mode < EP_MODE_AUTO || mode > EP_MODE_MAPCONCAT) return EP_ERR_ARG;
   if (opt && opt->n_segments < 0) return EP_ERR_ARG;
 
-  int64_t max_span = 0;
+  int64_t max_span = 0, max_hi = 0;
   int K = 1;
   for (int64_t e = 0; e < S; ++e) {
     int64_t span = 0;
@@ -317,15 +370,31 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       const int64_t hi = episodes.t_high[e * (N - 1) + j];
       if (lo < 0 || lo >= hi) return EP_ERR_INTERVAL;
       span += hi;
+      max_hi = std::max(max_hi, hi);
       // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1
       const int64_t runs = hi / (hi - lo + 1) + 1;
-      if (runs > EP_MAX_RUNS) return EP_ERR_UNSUPPORTED;
-      while (K < runs) K <<= 1;
+      while (K < runs && K <= EP_MAX_RUNS) K <<= 1;
     }
     if (span > INT32_MAX) return EP_ERR_INTERVAL;
     max_span = std::max(max_span, span);
   }
+  // window kind: bit windows when every t_high fits one mask, else run windows
+  int win;
+  if (max_hi <= 31)
+    win = kBits32;
+  else if (max_hi <= 63)
+    win = kBits64;
+  else if (K <= EP_MAX_RUNS)
+    win = K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4);
+  else
+    return EP_ERR_UNSUPPORTED;
   if (S == 0) return EP_OK;
+
+  // distinct node types -> slots 1..U
+  std::vector<uint16_t> distinct(episodes.types, episodes.types + S * N);
+  std::sort(distinct.begin(), distinct.end());
+  distinct.erase(std::unique(distinct.begin(), distinct.end()), distinct.end());
+  const int U = (int)distinct.size();
 
   int dev = 0;
   EP_HIP(hipGetDevice(&dev));
@@ -338,44 +407,90 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       memset(opt->stats, 0, sizeof(ep_stats));
       opt->stats->mode = EP_MODE_PTPE;
       opt->stats->n_segments = 1;
-      opt->stats->max_runs = K;
+      opt->stats->max_runs = win >= kBits32 ? (win == kBits32 ? 32 : 64) : K;
     }
     return EP_OK;
   }
 
   DeviceInfo* info = nullptr;
   if (int st = device_info(dev, &info)) return st;
-  const Launchers* L = launchers_for(N);
+  const Launchers* Lr = launchers_for(N);
 
-  // ---- plan (hybrid rule)
-  const int lanes_per_cu = info->occ[N][k_index(K)] * kBlock;
+  // ---- plan: scheme, segments, kernel and workgroup layout
+  Launch L{};
+  L.win = win;
+  L.bits = (win == kBits32 || win == kBits64) && U <= 255 && !getenv("EP_FORCE_SCAN");
+  if (!L.bits && win >= kBits32) {
+    // many node types: the scan kernel with bit windows is not built; use runs if they fit
+    if (K > EP_MAX_RUNS) return EP_ERR_UNSUPPORTED;
+    L.win = K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4);
+  }
+  const int lanes_per_cu_est = 2048;  // 8 waves on each of 4 SIMDs
   int32_t pmode = 0, P = 1;
-  plan_rule(S, N, n_events, mode, opt ? opt->n_segments : 0, info->cu_count, lanes_per_cu, &pmode,
-            &P);
-  const int M = (pmode == EP_MODE_PTPE) ? 1 : N;
-  int G = (int)std::min<int64_t>(S, kBlock / M);
-  int R = 1;
-  if (G == S) R = std::max(1, kBlock / (G * M));
-  R = (int)std::min<int64_t>(R, P);
-  const int CH = kTile / R;
-  const int slots = (pmode == EP_MODE_PTPE) ? 1 : 2 * N;
+  plan_rule(S, N, n_events, mode, opt ? opt->n_segments : 0, info->cu_count, lanes_per_cu_est,
+            &pmode, &P);
+  L.mode = pmode;
+  L.P = P;
+  L.n_machines = (pmode == EP_MODE_PTPE) ? 1 : N;
+  L.block = kBlock;
+  if (L.bits) {
+    // one lane per (segment, episode) holding every machine, unless that
+    // leaves the GPU with too few lanes for a fixed segment count
+    const int64_t target = (int64_t)info->cu_count * lanes_per_cu_est;
+    L.all_mach = L.n_machines > 1 && N <= kMaxClassNodes && S * (int64_t)P * 4 >= target;
+    const char* lanes_env = getenv("EP_LANES");
+    if (lanes_env && N <= kMaxClassNodes && L.n_machines > 1)
+      L.all_mach = strcmp(lanes_env, "machine") != 0;
+    L.M = L.all_mach ? 1 : L.n_machines;
+    L.G = (int)std::min<int64_t>(S, L.block / L.M);
+    L.R = (L.G == S) ? std::max(1, L.block / (L.G * L.M)) : 1;
+    L.R = (int)std::min<int64_t>(L.R, P);
+    // LDS per workgroup: U presence bitmaps + times + slots of one chunk, <= 64 KiB
+    for (;;) {
+      L.CH = std::max((2048 / L.R) & ~63, 64);
+      const int tile = L.R * L.CH;
+      L.lds = (size_t)U * (tile / 64) * 8 + (size_t)tile * 5;
+      if (L.lds <= 65536 || L.R == 1) break;
+      L.R = (L.R + 1) / 2;
+    }
+    if (L.lds > 65536) {
+      L.CH = 64;
+      L.lds = (size_t)U * 8 + 64 * 5;
+    }
+  } else {
+    L.all_mach = false;
+    L.M = L.n_machines;
+    L.G = (int)std::min<int64_t>(S, L.block / L.M);
+    L.R = (L.G == S) ? std::max(1, L.block / (L.G * L.M)) : 1;
+    L.R = (int)std::min<int64_t>(L.R, P);
+    L.CH = kTile / L.R;
+    L.lds = 0;
+  }
+  L.slots = (pmode == EP_MODE_PTPE) ? 1 : 2 * N;
   if (getenv("EP_LOG"))
-    fprintf(stderr, "epcount: S=%lld N=%d n=%lld mode=%s P=%d K=%d M=%d G=%d R=%d CH=%d maxSpan=%lld\n",
-            (long long)S, N, (long long)n_events, pmode == EP_MODE_PTPE ? "ptpe" : "mapconcat", P, K,
-            M, G, R, CH, (long long)max_span);
+    fprintf(stderr,
+            "epcount: S=%lld N=%d n=%lld U=%d mode=%s P=%d win=%s kernel=%s lanes=%s M=%d G=%d R=%d "
+            "CH=%d lds=%zu maxSpan=%lld\n",
+            (long long)S, N, (long long)n_events, U, pmode == EP_MODE_PTPE ? "ptpe" : "mapconcat", P,
+            win_name(L.win), L.bits ? "bits" : "scan", L.all_mach ? "class" : "machine", L.M, L.G, L.R,
+            L.CH, L.lds, (long long)max_span);
 
   // ---- scratch layout (one stream-ordered allocation)
   const size_t sz_types = align_up(sizeof(uint16_t) * S * N, 256);
   const size_t sz_lohi = align_up(sizeof(int32_t) * S * std::max(N - 1, 1), 256);
   const size_t sz_span = align_up(sizeof(int32_t) * S, 256);
+  const size_t sz_slot = align_up((size_t)S * N, 256);
+  const size_t sz_dist = align_up(sizeof(uint16_t) * U, 256);
+  const size_t host_bytes = sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_dist;
+  const size_t sz_remap = 65536;
   const size_t sz_tau = align_up(sizeof(int64_t) * (P + 1), 256);
   const size_t sz_seg = align_up(sizeof(int32_t) * P, 256);
-  const size_t sz_tuples = align_up(sizeof(Tuple) * (size_t)P * S * slots, 256);
+  const size_t sz_tuples = align_up(sizeof(Tuple) * (size_t)P * S * L.slots, 256);
   const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
-  const size_t host_bytes = sz_types + 2 * sz_lohi + sz_span;
-  const size_t total = host_bytes + sz_tau + 2 * sz_seg + sz_tuples + sz_nslots + sz_flags + sz_cnt;
+  const size_t total =
+      host_bytes + sz_remap + sz_tau + 2 * sz_seg + sz_tuples + sz_nslots + sz_flags + sz_cnt;
 
   char* ws = nullptr;
   if (hipMallocAsync((void**)&ws, total, stream) != hipSuccess || !ws) return EP_ERR_WORKSPACE;
@@ -386,6 +501,9 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     int32_t* d_lo = (int32_t*)(ws + off); off += sz_lohi;
     int32_t* d_hi = (int32_t*)(ws + off); off += sz_lohi;
     int32_t* d_span = (int32_t*)(ws + off); off += sz_span;
+    uint8_t* d_slot = (uint8_t*)(ws + off); off += sz_slot;
+    uint16_t* d_dist = (uint16_t*)(ws + off); off += sz_dist;
+    uint8_t* d_remap = (uint8_t*)(ws + off); off += sz_remap;
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
@@ -394,7 +512,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
 
-    // episode table: packed on the host, one upload
+    // episode table, spans, node slots and the distinct types: one upload
     std::vector<char> host(host_bytes, 0);
     memcpy(host.data(), episodes.types, sizeof(uint16_t) * S * N);
     if (N > 1) {
@@ -402,11 +520,19 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       memcpy(host.data() + sz_types + sz_lohi, episodes.t_high, sizeof(int32_t) * S * (N - 1));
     }
     int32_t* spans = (int32_t*)(host.data() + sz_types + 2 * sz_lohi);
+    uint8_t* slots = (uint8_t*)(host.data() + sz_types + 2 * sz_lohi + sz_span);
     for (int64_t e = 0; e < S; ++e) {
-      int64_t s = 0;
-      for (int j = 0; j < N - 1; ++j) s += episodes.t_high[e * (N - 1) + j];
-      spans[e] = (int32_t)s;
+      int64_t sp = 0;
+      for (int j = 0; j < N - 1; ++j) sp += episodes.t_high[e * (N - 1) + j];
+      spans[e] = (int32_t)sp;
+      for (int j = 0; j < N; ++j) {
+        const uint16_t y = episodes.types[e * N + j];
+        const size_t u = std::lower_bound(distinct.begin(), distinct.end(), y) - distinct.begin();
+        slots[e * N + j] = (uint8_t)(U <= 255 ? u + 1 : 0);
+      }
     }
+    memcpy(host.data() + sz_types + 2 * sz_lohi + sz_span + sz_slot, distinct.data(),
+           sizeof(uint16_t) * U);
     if ((status = upload(dev, ws, host.data(), host_bytes, stream))) break;
 
     if (opt && opt->validate) {
@@ -425,9 +551,19 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       }
     }
 
+    bool prof = false;
+    ProfRecord rec{};
+    {
+      std::lock_guard<std::mutex> lock(g_prof_mu);
+      prof = g_prof_on;
+    }
+    if (prof && (status = prof_record_start(&rec, stream))) break;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_flags, S, 0);
     hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, (int64_t*)d_cnt, (int64_t)4,
                        (int64_t)0);
+    if (L.bits)
+      hipLaunchKernelGGL(remap_kernel, dim3(65536 / kBlock), dim3(kBlock), 0, stream, d_dist, U,
+                         d_remap);
     hipLaunchKernelGGL(cuts_kernel, dim3(grid_for((int64_t)P + 1)), dim3(kBlock), 0, stream, times,
                        n_events, P, max_span, d_tau, d_beg, d_end);
     if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
@@ -435,11 +571,17 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     MapArgs ma;
     ma.times = times; ma.types = types;
     ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
+    ma.ep_slot = d_slot; ma.remap = d_remap;
     ma.tau = d_tau; ma.seg_beg = d_beg; ma.seg_end = d_end;
     ma.tuples = d_tuples; ma.nslots = d_nslots;
-    ma.S = S; ma.P = P; ma.M = M; ma.G = G; ma.R = R; ma.CH = CH; ma.slots = slots;
-    dim3 mgrid((unsigned)((P + R - 1) / R), (unsigned)((S + G - 1) / G));
-    if (L->map(ma, K, mgrid, stream) != hipSuccess) { status = EP_ERR_HIP; break; }
+    ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH; ma.slots = L.slots;
+    ma.U = U; ma.n_machines = L.n_machines;
+    dim3 mgrid((unsigned)((P + L.R - 1) / L.R), (unsigned)((S + L.G - 1) / L.G));
+    if (prof) hipEventRecord(rec.ev[1], stream);
+    hipError_t le = L.bits ? Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream)
+                           : Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
+    if (le != hipSuccess) { status = EP_ERR_HIP; break; }
+    if (prof) hipEventRecord(rec.ev[2], stream);
 
     if (P > 1) {
       ClosureArgs ca;
@@ -447,18 +589,23 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       ca.ep_types = d_types; ca.ep_lo = d_lo; ca.ep_hi = d_hi; ca.ep_span = d_span;
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
       ca.tuples = d_tuples; ca.nslots = d_nslots; ca.flags = d_flags; ca.repairs = d_cnt;
-      ca.S = S; ca.P = P; ca.slots = slots;
-      if (L->closure(ca, K, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
+      ca.S = S; ca.P = P; ca.slots = L.slots;
+      if (Lr->closure(ca, L.win, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
       }
+      if (prof) hipEventRecord(rec.ev[3], stream);
       for (int64_t half = 1; half < P; half <<= 1) {
         const int64_t blocks = (P + 2 * half - 1) / (2 * half);
-        hipLaunchKernelGGL(concat_level_kernel, dim3(grid_for(blocks * S * slots)), dim3(kBlock), 0,
-                           stream, d_tuples, d_nslots, d_flags, S, P, slots, half);
+        hipLaunchKernelGGL(concat_level_kernel, dim3(grid_for(blocks * S * L.slots)), dim3(kBlock), 0,
+                           stream, d_tuples, d_nslots, d_flags, S, P, L.slots, half);
       }
     }
-    hipLaunchKernelGGL(extract_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_tuples, S, slots,
+    if (prof) {
+      if (P <= 1) hipEventRecord(rec.ev[3], stream);
+      hipEventRecord(rec.ev[4], stream);
+    }
+    hipLaunchKernelGGL(extract_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_tuples, S, L.slots,
                        out_counts);
     if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
 
@@ -467,9 +614,14 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
     fa.flags = d_flags; fa.fallbacks = d_cnt + 1; fa.out = out_counts;
     fa.n = n_events; fa.S = S;
-    if (L->fallback(fa, K, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+    if (Lr->fallback(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
       status = EP_ERR_HIP;
       break;
+    }
+    if (prof) {
+      hipEventRecord(rec.end, stream);
+      std::lock_guard<std::mutex> lock(g_prof_mu);
+      g_prof.push_back(rec);
     }
 
     if (opt && opt->stats) {
@@ -481,14 +633,49 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       }
       opt->stats->mode = pmode;
       opt->stats->n_segments = P;
-      opt->stats->max_runs = K;
-      opt->stats->reserved = 0;
+      opt->stats->max_runs = L.win >= kBits32 ? (L.win == kBits32 ? 32 : 64) : K;
+      opt->stats->reserved = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0);
       opt->stats->repairs = (int64_t)cnt[0];
       opt->stats->fallbacks = (int64_t)cnt[1];
     }
   } while (0);
 
   if (hipFreeAsync(ws, stream) != hipSuccess && status == EP_OK) status = EP_ERR_HIP;
+  return status;
+}
+
+extern "C" int ep_profile_begin(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof.clear();
+  g_prof_on = true;
+  return EP_OK;
+}
+
+extern "C" int ep_profile_end(ep_profile* out) {
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof_on) return EP_ERR_ARG;
+    g_prof_on = false;
+    recs.swap(g_prof);
+  }
+  ep_profile acc{};
+  int status = EP_OK;
+  for (ProfRecord& r : recs) {
+    float ms[5] = {0, 0, 0, 0, 0};
+    if (hipEventSynchronize(r.end) != hipSuccess) status = EP_ERR_HIP;
+    hipEvent_t seq[6] = {r.ev[0], r.ev[1], r.ev[2], r.ev[3], r.ev[4], r.end};
+    for (int i = 0; i < 5 && status == EP_OK; ++i)
+      if (hipEventElapsedTime(&ms[i], seq[i], seq[i + 1]) != hipSuccess) status = EP_ERR_HIP;
+    acc.other_ms += ms[0] + ms[4];
+    acc.map_ms += ms[1];
+    acc.closure_ms += ms[2];
+    acc.concat_ms += ms[3];
+    acc.calls += 1;
+    for (int i = 0; i < 5; ++i) hipEventDestroy(r.ev[i]);
+    hipEventDestroy(r.end);
+  }
+  if (out) *out = acc;
   return status;
 }
 

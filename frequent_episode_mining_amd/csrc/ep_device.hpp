@@ -4,15 +4,25 @@
 // Episodes Using Graphics Processors".
 //
 // The counting machine is the page's serial state machine (opening section,
-// Algorithm 1; Fig. 3 text: alpha_0), kept in registers: for every node j < N-1
-// a window of candidate times t' of node j whose continuation intervals
-// (t' + t_low_j, t' + t_high_j] are merged into at most K disjoint runs.  A run
-// is stored as its first and last candidate time (f, l); it covers
-// (f + t_low, l + t_high].  Because event times only grow, runs whose end lies
-// before the current time are dropped from the front, and at most
-// floor(t_high / (t_high - t_low + 1)) + 1 runs are ever live, so a window of
-// that capacity is exact.  All time differences are formed as uint32 of
-// non-negative int32 differences, so no int32 arithmetic can overflow.
+// Algorithm 1; Fig. 3 text: alpha_0).  For every node j < N-1 it keeps a
+// window of candidate times t' (events of type E(j) that end a valid prefix
+// started after the last reset); an event of type E(j+1) at time t extends a
+// prefix iff some candidate has t_low_j < t - t' <= t_high_j.  Two exact
+// representations of a window are used:
+//
+//   bit windows  (t_high < W, W = 32 or 64): one W-bit mask per node whose bit
+//                d stands for a candidate at time B - d, B being the time of
+//                the last event the machine looked at.  Moving to time t
+//                shifts every mask left by t - B; the test is a single AND
+//                with the bits (t_low, t_high].  Exact for any t_low.
+//   run windows  (any t_high): the continuation intervals (t'+t_low, t'+t_high]
+//                merged into disjoint runs, each stored as its first and last
+//                candidate (f, l) and covering (f+t_low, l+t_high].  At most
+//                floor(t_high/(t_high-t_low+1)) + 1 runs are ever live, so a
+//                capacity of K runs is exact when that bound is <= K.
+//
+// All time differences are formed as uint32 of non-negative differences of
+// int32 times, and cut arithmetic is int64, so nothing can overflow.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,8 +31,8 @@
 namespace epk {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 256;   // threads per workgroup of every kernel here
-constexpr int kTile = 2048;   // events staged in LDS per chunk by a Map workgroup
+constexpr int kBlock = 256;  // largest workgroup of every kernel here
+constexpr int kTile = 2048;  // events staged in LDS per chunk by the scan Map kernel
 
 // One (a, count, b) tuple of the Map step (Map rules 1-4, Fig. 5), with a and b
 // stored as offsets from the segment's left and right cut; 0 is the sentinel
@@ -34,25 +44,26 @@ struct alignas(16) Tuple {
   int32_t pad;
 };
 
-// Episode parameters of one lane, in registers.
-template <int N>
-struct EpParams {
-  uint32_t ty[N];
-  uint32_t lo[N > 1 ? N - 1 : 1];
-  uint32_t hi[N > 1 ? N - 1 : 1];
-  uint32_t width[N > 1 ? N - 1 : 1];  // hi - lo: merge distance of two candidates
-  int32_t span;                        // hi_1 + ... + hi_{N-1}
+template <int W>
+struct BitsOf;
+template <>
+struct BitsOf<32> {
+  using type = uint32_t;
+};
+template <>
+struct BitsOf<64> {
+  using type = uint64_t;
+};
 
-  __device__ void load(const uint16_t* ep_types, const int32_t* ep_lo, const int32_t* ep_hi,
-                       const int32_t* ep_span, int64_t e) {
+// Event types of an episode's nodes and its span, in registers.
+template <int N>
+struct EpTypes {
+  uint32_t ty[N];
+  int32_t span;  // t_high_1 + ... + t_high_{N-1}
+
+  __device__ void load_types(const uint16_t* ep_types, const int32_t* ep_span, int64_t e) {
 #pragma unroll
     for (int j = 0; j < N; ++j) ty[j] = ep_types[e * N + j];
-#pragma unroll
-    for (int j = 0; j < N - 1; ++j) {
-      lo[j] = (uint32_t)ep_lo[e * (N - 1) + j];
-      hi[j] = (uint32_t)ep_hi[e * (N - 1) + j];
-      width[j] = hi[j] - lo[j];
-    }
     span = ep_span[e];
   }
 
@@ -63,25 +74,47 @@ struct EpParams {
     for (int j = 0; j < N; ++j) m |= (uint32_t)(ty[j] == y) << j;
     return m;
   }
+};
 
-  // hi_1 + ... + hi_k: machine k of a segment is reset this long before the cut.
-  __device__ int64_t prefix_hi(int k) const {
-    int64_t s = 0;
+// hi_1 + ... + hi_k: machine k of a segment is reset this long before the cut
+// (Map step, Fig. 4: alpha_p^k starts at tau_p - sum_{i<=k} t_high).
+template <int N>
+__device__ inline int64_t prefix_hi(const int32_t* ep_hi, int64_t e, int k) {
+  int64_t s = 0;
 #pragma unroll
-    for (int j = 0; j < N - 1; ++j) s += (j < k) ? (int64_t)hi[j] : 0;
-    return s;
+  for (int j = 0; j < N - 1; ++j) s += (j < k) ? (int64_t)ep_hi[e * (N - 1) + j] : 0;
+  return s;
+}
+
+// ------------------------------------------------------------ run windows
+
+template <int N>
+struct RunParams : EpTypes<N> {
+  uint32_t lo[N > 1 ? N - 1 : 1];
+  uint32_t hi[N > 1 ? N - 1 : 1];
+  uint32_t width[N > 1 ? N - 1 : 1];  // hi - lo: merge distance of two candidates
+
+  __device__ void load(const uint16_t* ep_types, const int32_t* ep_lo, const int32_t* ep_hi,
+                       const int32_t* ep_span, int64_t e) {
+    this->load_types(ep_types, ep_span, e);
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      lo[j] = (uint32_t)ep_lo[e * (N - 1) + j];
+      hi[j] = (uint32_t)ep_hi[e * (N - 1) + j];
+      width[j] = hi[j] - lo[j];
+    }
   }
 };
 
 template <int K>
-struct Window {
+struct RunWindow {
   int32_t f[K];
   int32_t l[K];
   int32_t n;
 
   __device__ void clear() { n = 0; }
 
-  // Drop runs that ended before t: a run (f, l] + (lo, hi] is dead once t - l > hi.
+  // Drop runs that ended before t: a run is dead once t - l > hi.
   __device__ void expire(int32_t t, uint32_t hi) {
 #pragma unroll
     for (int it = 0; it < K; ++it) {
@@ -97,13 +130,11 @@ struct Window {
     }
   }
 
-  // Is t inside (t' + lo, t' + hi] for some candidate t' of this window?
   __device__ bool contains(int32_t t, uint32_t lo, uint32_t hi) {
     expire(t, hi);
     return n > 0 && ((uint32_t)t - (uint32_t)f[0]) > lo;
   }
 
-  // Add candidate t (t is not older than any stored candidate).
   __device__ void insert(int32_t t, uint32_t hi, uint32_t width) {
     expire(t, hi);
     int32_t last_l = l[0];
@@ -122,11 +153,11 @@ struct Window {
   }
 };
 
-// The serial counting machine of one episode.
 template <int N, int K>
-struct Machine {
+struct RunMachine {
+  using Params = RunParams<N>;
   int64_t r;  // time of the last reset (last completion, or the start)
-  Window<K> w[N > 1 ? N - 1 : 1];
+  RunWindow<K> w[N > 1 ? N - 1 : 1];
 
   __device__ void reset(int64_t at) {
     r = at;
@@ -134,11 +165,11 @@ struct Machine {
     for (int j = 0; j < N - 1; ++j) w[j].clear();
   }
 
-  // Feed an event at time t with level mask lm (non-zero).  Returns true if it
-  // completes an occurrence; the machine is then reset at t.  Events at or
-  // before the last reset are ignored: occurrences must start strictly after
-  // the previous counted one ends.
-  __device__ bool step(int32_t t, uint32_t lm, const EpParams<N>& P) {
+  // Feed an event at time t with level mask lm.  Returns true if it completes
+  // an occurrence; the machine is then reset at t.  Events at or before the
+  // last reset are ignored: an occurrence must start strictly after the
+  // previous counted one ends.
+  __device__ bool step(int32_t t, uint32_t lm, const Params& P) {
     if ((int64_t)t <= r) return false;
     if ((lm >> (N - 1)) & 1u) {
       bool done = true;
@@ -160,13 +191,83 @@ struct Machine {
   }
 };
 
+// ------------------------------------------------------------ bit windows
+
+// Bits (lo, hi] of a W-bit window: candidate ages d with lo < d <= hi.
+template <int W>
+__device__ inline typename BitsOf<W>::type window_bits(uint32_t lo, uint32_t hi) {
+  using Bits = typename BitsOf<W>::type;
+  const Bits upto_hi = (~(Bits)0) >> (W - 1 - hi);          // bits 0..hi
+  const Bits upto_lo = (~(Bits)0) >> (W - 1 - lo);          // bits 0..lo
+  return upto_hi & ~upto_lo;
+}
+
+template <int N, int W>
+struct BitParams : EpTypes<N> {
+  using Bits = typename BitsOf<W>::type;
+  Bits win[N > 1 ? N - 1 : 1];
+
+  __device__ void load(const uint16_t* ep_types, const int32_t* ep_lo, const int32_t* ep_hi,
+                       const int32_t* ep_span, int64_t e) {
+    this->load_types(ep_types, ep_span, e);
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      win[j] = window_bits<W>((uint32_t)ep_lo[e * (N - 1) + j], (uint32_t)ep_hi[e * (N - 1) + j]);
+  }
+};
+
+// Shift a window from base time B to time t (d = t - B >= 0 ticks later).
+template <int W>
+__device__ inline typename BitsOf<W>::type age(typename BitsOf<W>::type m, uint32_t d) {
+  return d >= (uint32_t)W ? 0 : (m << d);
+}
+
+template <int N, int W>
+struct BitMachine {
+  using Params = BitParams<N, W>;
+  using Bits = typename BitsOf<W>::type;
+  int64_t r;
+  int32_t B;
+  Bits m[N > 1 ? N - 1 : 1];
+
+  __device__ void reset(int64_t at) {
+    r = at;
+    B = at < (int64_t)INT32_MIN ? INT32_MIN : (at > (int64_t)INT32_MAX ? INT32_MAX : (int32_t)at);
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) m[j] = 0;
+  }
+
+  __device__ bool step(int32_t t, uint32_t lm, const Params& P) {
+    if ((int64_t)t <= r) return false;
+    const uint32_t d = (uint32_t)t - (uint32_t)B;
+    B = t;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) m[j] = age<W>(m[j], d);
+    if ((lm >> (N - 1)) & 1u) {
+      bool done = true;
+      if constexpr (N > 1) done = (m[N - 2] & P.win[N - 2]) != 0;
+      if (done) {
+        reset(t);
+        return true;
+      }
+    }
+    bool hit[N > 1 ? N - 1 : 1];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) hit[j] = (m[j] & P.win[j]) != 0;
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[j] |= (Bits)1;
+    return false;
+  }
+};
+
 // A machine bound to one segment (tau_lo, tau_hi]: it produces the segment's
 // (a, count, b) tuple.  a = first completion in (tau_lo, tau_lo + Span] (else
 // 0), count = completions in (tau_lo, tau_hi], b = first completion in
 // (tau_hi, tau_hi + Span] (else 0); the windows are closed on the right.
-template <int N, int K>
+template <class Mach>
 struct SegMachine {
-  Machine<N, K> m;
+  Mach m;
   int64_t tau_lo;
   int64_t tau_hi;
   int64_t stop;  // tau_hi + Span: nothing after it can change the tuple
@@ -188,7 +289,7 @@ struct SegMachine {
     finished = false;
   }
 
-  __device__ void feed(int32_t t, uint32_t lm, const EpParams<N>& P) {
+  __device__ void feed(int32_t t, uint32_t lm, const typename Mach::Params& P) {
     if (finished || lm == 0) return;
     if ((int64_t)t > stop) {
       finished = true;
@@ -210,7 +311,7 @@ struct SegMachine {
   }
 };
 
-// ---------------------------------------------------------------- Map kernel
+// ---------------------------------------------------------------- Map step
 
 struct MapArgs {
   const int32_t* times;
@@ -219,6 +320,8 @@ struct MapArgs {
   const int32_t* ep_lo;      // [S*(N-1)]
   const int32_t* ep_hi;      // [S*(N-1)]
   const int32_t* ep_span;    // [S]
+  const uint8_t* ep_slot;    // [S*N] node type -> 1..U (bit kernels)
+  const uint8_t* remap;      // [65536] event type -> slot, 0 = on no node (bit kernels)
   const int64_t* tau;        // [P+1] cuts
   const int32_t* seg_beg;    // [P] first event index with time > tau_p - maxSpan
   const int32_t* seg_end;    // [P] first event index with time > tau_{p+1} + maxSpan
@@ -226,19 +329,22 @@ struct MapArgs {
   int32_t* nslots;           // [P*S]
   int64_t S;
   int32_t P;
-  int32_t M;      // machines per (segment, episode): N for MapConcatenate, 1 for PTPE
+  int32_t M;      // lanes per (segment, episode): machines spread over lanes
   int32_t G;      // episodes per workgroup
   int32_t R;      // segments per workgroup
-  int32_t CH;     // events per segment per chunk (R * CH <= kTile)
+  int32_t CH;     // events per segment per chunk
   int32_t slots;  // tuple slots per (segment, episode)
+  int32_t U;      // distinct node types (bit kernels)
+  int32_t n_machines;  // machines per (segment, episode): N (MapConcatenate) or 1 (PTPE)
 };
 
-// One lane = one machine (segment p, episode e, machine k).  A workgroup holds R
-// consecutive segments x G episodes x M machines; it streams the R segments'
-// event ranges through LDS in lockstep chunks of CH events each, and every
-// lane feeds its own segment's chunk to its machine.
+// Scan Map kernel (run windows): one lane = one machine (segment p, episode e,
+// machine k).  A workgroup holds R consecutive segments x G episodes x M
+// machines; it streams the R segments' event ranges through LDS in lockstep
+// chunks of CH events, and every lane feeds each event of its own segment's
+// chunk to its machine.
 template <int N, int K>
-__global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
+__global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   __shared__ int32_t s_t[kTile];
   __shared__ uint16_t s_y[kTile];
   __shared__ int32_t s_beg[kBlock];
@@ -268,13 +374,14 @@ __global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
     atomicMax(&s_chunks, (len + A.CH - 1) / A.CH);
   }
 
-  EpParams<N> prm;
-  SegMachine<N, K> sm;
+  using Mach = RunMachine<N, K>;
+  typename Mach::Params prm;
+  SegMachine<Mach> sm;
   if (active) {
     prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
     const int64_t lo_cut = A.tau[p];
     const int64_t hi_cut = A.tau[p + 1];
-    sm.init(lo_cut - prm.prefix_hi(k), lo_cut, hi_cut, prm.span);
+    sm.init(lo_cut - prefix_hi<N>(A.ep_hi, e, k), lo_cut, hi_cut, prm.span);
   }
   __syncthreads();
   const int n_chunks = s_chunks;
@@ -284,7 +391,7 @@ __global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
     for (int r = 0; r < A.R; ++r) {
       const int32_t base = s_beg[r] + c * A.CH;
       const int32_t avail = s_len[r] - c * A.CH;
-      for (int i = tid; i < A.CH; i += kBlock) {
+      for (int i = tid; i < A.CH; i += blockDim.x) {
         if (i < avail) {
           s_t[r * A.CH + i] = A.times[base + i];
           s_y[r * A.CH + i] = A.types[base + i];
@@ -296,11 +403,7 @@ __global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
       int32_t len = s_len[r_idx] - c * A.CH;
       len = len < A.CH ? len : A.CH;
       const int off = r_idx * A.CH;
-      for (int i = 0; i < len; ++i) {
-        const int32_t t = s_t[off + i];
-        const uint32_t lm = prm.level_mask(s_y[off + i]);
-        sm.feed(t, lm, prm);
-      }
+      for (int i = 0; i < len; ++i) sm.feed(s_t[off + i], prm.level_mask(s_y[off + i]), prm);
     }
   }
 
@@ -316,14 +419,266 @@ __global__ __launch_bounds__(kBlock) void map_kernel(MapArgs A) {
   }
 }
 
+// Bit Map kernel (bit windows, relevant events only).
+//
+// Each chunk of events is staged in LDS with, for every node type slot u, a
+// presence bitmap over the chunk's positions (bit i of word w: event 64w+i has
+// a type on slot u).  A lane ORs the bitmaps of its episode's node types and
+// visits only the set bits, in order (the machines ignore every other event
+// anyway).  Lanes of one workgroup share the staged chunk.
+//
+// MCH = N: one lane holds all N machines of a (segment, episode).  Machines
+// that reset at the same time are identical from then on, and so are machines
+// whose last reset lies more than Span before the current event (every
+// occurrence that can still complete starts after both resets), so the lane
+// keeps machines in equivalence classes and advances one window state per
+// class; after the boundary halo a lane usually carries a single class.
+// MCH = 1: one lane per machine (M lanes per (segment, episode)).
+template <int N, int W, int MCH>
+__global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
+  using Bits = typename BitsOf<W>::type;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int32_t s_beg[kBlock];
+  __shared__ int32_t s_len[kBlock];
+  __shared__ int32_t s_chunks;
+
+  const int tile = A.R * A.CH;
+  const int words = tile >> 6;
+  uint64_t* s_bits = (uint64_t*)smem;                       // [U][words]
+  int32_t* s_t = (int32_t*)(s_bits + (size_t)A.U * words);  // [tile]
+  uint8_t* s_s = (uint8_t*)(s_t + tile);                    // [tile]
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int per_seg = A.G * A.M;
+  const int r_idx = tid / per_seg;
+  const int g = (tid / A.M) % A.G;
+  const int k_lane = tid % A.M;
+  const int64_t p = (int64_t)blockIdx.x * A.R + r_idx;
+  const int64_t e = (int64_t)blockIdx.y * A.G + g;
+  const bool active = tid < A.R * per_seg && p < A.P && e < A.S;
+
+  if (tid == 0) s_chunks = 0;
+  __syncthreads();
+  if (tid < A.R) {
+    const int64_t pp = (int64_t)blockIdx.x * A.R + tid;
+    int32_t b = 0, len = 0;
+    if (pp < A.P) {
+      b = A.seg_beg[pp];
+      len = A.seg_end[pp] - b;
+    }
+    s_beg[tid] = b;
+    s_len[tid] = len;
+    atomicMax(&s_chunks, (len + A.CH - 1) / A.CH);
+  }
+
+  // ---- lane state
+  uint32_t slot[N];
+  Bits win[N > 1 ? N - 1 : 1];
+  int32_t span = 0;
+  Bits m[MCH][N > 1 ? N - 1 : 1];
+  int64_t r[MCH];
+  uint32_t mem[MCH];  // machines in class c (bit k); a class lives while mem != 0
+  int32_t cnt[MCH], a_off[MCH], b_off[MCH];
+  uint32_t found = 0, fin = 0;
+  const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
+  int64_t tau_lo = 0, tau_hi = 0, stop = 0, check_at = INT64_MAX;
+  int32_t B = INT32_MIN;
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      win[j] = window_bits<W>((uint32_t)A.ep_lo[e * (N - 1) + j], (uint32_t)A.ep_hi[e * (N - 1) + j]);
+    span = A.ep_span[e];
+    tau_lo = A.tau[p];
+    tau_hi = A.tau[p + 1];
+    stop = tau_hi + span;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int k = (MCH == 1) ? k_lane : c;
+      r[c] = tau_lo - prefix_hi<N>(A.ep_hi, e, k);
+      mem[c] = 1u << c;
+      cnt[c] = 0;
+      a_off[c] = 0;
+      b_off[c] = 0;
+#pragma unroll
+      for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
+      if (MCH > 1) check_at = min(check_at, r[c] + span + 1);
+    }
+  } else {
+    fin = all;
+  }
+  __syncthreads();
+  const int n_chunks = s_chunks;
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    if (ch > 0) __syncthreads();  // previous chunk fully consumed
+    for (int i = tid; i < A.U * words; i += nthr) s_bits[i] = 0;
+    __syncthreads();
+    for (int rr = 0; rr < A.R; ++rr) {
+      const int32_t base = s_beg[rr] + ch * A.CH;
+      const int32_t avail = s_len[rr] - ch * A.CH;
+      for (int i = tid; i < A.CH; i += nthr) {
+        if (i < avail) {
+          const int pos = rr * A.CH + i;
+          const uint32_t u = A.remap[A.types[base + i]];
+          s_t[pos] = A.times[base + i];
+          s_s[pos] = (uint8_t)u;
+          if (u) atomicOr((unsigned long long*)&s_bits[(u - 1) * words + (pos >> 6)],
+                          1ull << (pos & 63));
+        }
+      }
+    }
+    __syncthreads();
+    if (fin == all) continue;
+    int32_t len = s_len[r_idx] - ch * A.CH;
+    len = len < A.CH ? len : A.CH;
+    if (len <= 0) continue;
+    const int w0 = (r_idx * A.CH) >> 6;
+    const int w1 = w0 + ((len + 63) >> 6);
+    int w = w0;
+    uint64_t word = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) word |= s_bits[(slot[j] - 1) * words + w];
+    for (;;) {
+      while (word == 0 && ++w < w1) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) word |= s_bits[(slot[j] - 1) * words + w];
+      }
+      if (word == 0) break;
+      const int pos = (w << 6) + (__ffsll((unsigned long long)word) - 1);
+      word &= word - 1;
+      const int32_t t = s_t[pos];
+      const uint32_t u = s_s[pos];
+      uint32_t lm = 0;
+#pragma unroll
+      for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
+
+      if ((int64_t)t > stop) {
+        fin = all;
+        break;
+      }
+      const uint32_t d = (uint32_t)t - (uint32_t)B;
+      B = t;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c)
+        if (mem[c]) {
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
+        }
+      if (MCH > 1 && (int64_t)t >= check_at) {
+        // classes whose last reset lies more than Span back are identical: merge
+        uint32_t stale = 0, acc = 0;
+        int64_t next = INT64_MAX;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if (mem[c]) {
+            if (r[c] + span < (int64_t)t) {
+              stale |= 1u << c;
+              acc |= mem[c];
+            } else {
+              next = min(next, r[c] + span + 1);
+            }
+          }
+        if (__popc(stale) >= 2) {
+          const int lowest = __ffs((int)stale) - 1;
+#pragma unroll
+          for (int c = 0; c < MCH; ++c)
+            if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+        }
+        check_at = next;
+      }
+      uint32_t done = 0;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        if (mem[c] && (int64_t)t > r[c]) {
+          bool hit[N > 1 ? N - 1 : 1];
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) hit[j] = (m[c][j] & win[j]) != 0;
+          bool complete = (lm >> (N - 1)) & 1u;
+          if constexpr (N > 1) complete = complete && hit[N - 2];
+          if (complete) {
+            done |= 1u << c;
+          } else {
+#pragma unroll
+            for (int j = 0; j < N - 1; ++j)
+              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[c][j] |= (Bits)1;
+          }
+        }
+      }
+      if (done) {
+        // every machine of a completing class completes at t and resets
+        uint32_t members = 0;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((done >> c) & 1u) {
+            members |= mem[c];
+            r[c] = t;
+#pragma unroll
+            for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
+          }
+        const uint32_t live = members & ~fin;  // machines still recording their tuple
+#pragma unroll
+        for (int k = 0; k < MCH; ++k) {
+          if ((live >> k) & 1u) {
+            if ((int64_t)t > tau_lo) {
+              if (!((found >> k) & 1u)) {
+                found |= 1u << k;
+                const int64_t dd = (int64_t)t - tau_lo;
+                a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+              }
+              if ((int64_t)t <= tau_hi) {
+                ++cnt[k];
+              } else {
+                b_off[k] = (int32_t)((int64_t)t - tau_hi);
+                fin |= 1u << k;
+              }
+            }
+          }
+        }
+        if (MCH > 1) {
+          // classes that completed together are identical from now on
+          if (__popc(done) >= 2) {
+            const int lowest = __ffs((int)done) - 1;
+#pragma unroll
+            for (int c = 0; c < MCH; ++c)
+              if ((done >> c) & 1u) mem[c] = (c == lowest) ? members : 0u;
+          }
+          check_at = min(check_at, (int64_t)t + span + 1);
+        }
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
+        if (fin == all) break;
+      }
+    }
+  }
+
+  if (active) {
+    const int64_t pe = p * A.S + e;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int k = (MCH == 1) ? k_lane : c;
+      Tuple tu;
+      tu.a = a_off[c];
+      tu.c = cnt[c];
+      tu.b = b_off[c];
+      tu.pad = 0;
+      A.tuples[pe * A.slots + k] = tu;
+    }
+    if (k_lane == 0) A.nslots[pe] = A.n_machines;
+  }
+}
+
 // ------------------------------------------- wave-cooperative single machine
 
 // All 64 lanes hold the same machine; they load 64 events at a time with one
 // coalesced access, ballot the events whose type sits on a node of the
 // episode, and feed those, in order, to the (uniform) machine.
-template <int N, int K>
-__device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int64_t i0,
-                                int64_t i1, SegMachine<N, K>& sm, const EpParams<N>& prm) {
+template <class Mach>
+__device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int64_t i0, int64_t i1,
+                                SegMachine<Mach>& sm, const typename Mach::Params& prm) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int64_t base = i0; base < i1 && !sm.finished; base += kWave) {
     const int64_t i = base + lane;
@@ -367,8 +722,8 @@ struct ClosureArgs {
   const int32_t* seg_end;
   Tuple* tuples;
   int32_t* nslots;
-  int32_t* flags;              // [S] non-zero: recount this episode with the fallback
-  unsigned long long* repairs; // repair-tuple counter
+  int32_t* flags;               // [S] non-zero: recount this episode with the fallback
+  unsigned long long* repairs;  // repair-tuple counter
   int64_t S;
   int32_t P;
   int32_t slots;
@@ -377,8 +732,9 @@ struct ClosureArgs {
 // The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
 // machine reset at x runs over segment q.  Its count includes the completion
 // at x itself when x <= tau_{q+1}.
-template <int N, int K>
-__device__ Tuple repair_tuple(const ClosureArgs& A, const EpParams<N>& prm, int64_t q, int64_t x) {
+template <class Mach>
+__device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params& prm, int64_t q,
+                              int64_t x) {
   const int64_t lo_cut = A.tau[q];
   const int64_t hi_cut = A.tau[q + 1];
   Tuple tu;
@@ -389,10 +745,10 @@ __device__ Tuple repair_tuple(const ClosureArgs& A, const EpParams<N>& prm, int6
     tu.b = (int32_t)(x - hi_cut);
     return tu;
   }
-  SegMachine<N, K> sm;
+  SegMachine<Mach> sm;
   sm.init(x, lo_cut, hi_cut, prm.span);
   const int64_t i0 = upper_bound_time(A.times, A.seg_beg[q], A.seg_end[q], x);
-  wave_feed_range<N, K>(A.times, A.types, i0, A.seg_end[q], sm, prm);
+  wave_feed_range<Mach>(A.times, A.types, i0, A.seg_end[q], sm, prm);
   tu.c = sm.count + 1;
   tu.b = sm.b_off;
   return tu;
@@ -413,7 +769,7 @@ __device__ bool has_map_key(const ClosureArgs& A, int64_t q, int64_t e, int32_t 
 // repair's own exit is checked against segment p+2, and so on.  Items are one
 // per lane; the repairs of a wave's items run one after another with the
 // whole wave cooperating on each.
-template <int N, int K>
+template <int N, class Mach>
 __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
   const int64_t n_items = (int64_t)(A.P - 1) * A.S;
   const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -448,7 +804,7 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
     uint32_t miss = (uint32_t)__shfl((int)missing, src);
     const int64_t p = it / A.S;
     const int64_t e = it - p * A.S;
-    EpParams<N> prm;
+    typename Mach::Params prm;
     prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
     while (miss != 0u) {
       const int k = __ffs((int)miss) - 1;
@@ -460,7 +816,7 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
           if (lane == 0) atomicOr(&A.flags[e], 1);
           break;
         }
-        const Tuple tu = repair_tuple<N, K>(A, prm, q, A.tau[q] + x_off);
+        const Tuple tu = repair_tuple<Mach>(A, prm, q, A.tau[q] + x_off);
         int slot = 0;
         if (lane == 0) slot = atomicAdd(&A.nslots[q * A.S + e], 1);
         slot = __shfl(slot, 0);
@@ -499,17 +855,17 @@ struct FallbackArgs {
 
 // Exact safety net: one wave recounts a flagged episode over the whole
 // stream with a single machine (the page's alpha_0 on the unsegmented stream).
-template <int N, int K>
+template <class Mach>
 __global__ __launch_bounds__(kBlock) void fallback_kernel(FallbackArgs A) {
   const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (e >= A.S) return;
   if (A.flags[e] == 0) return;
-  EpParams<N> prm;
+  typename Mach::Params prm;
   prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
   const int64_t before = (int64_t)A.times[0] - 1;
-  SegMachine<N, K> sm;
+  SegMachine<Mach> sm;
   sm.init(before, before, INT64_MAX / 4, prm.span);
-  wave_feed_range<N, K>(A.times, A.types, 0, A.n, sm, prm);
+  wave_feed_range<Mach>(A.times, A.types, 0, A.n, sm, prm);
   if ((threadIdx.x & (kWave - 1)) == 0) {
     A.out[e] = sm.count;
     atomicAdd(A.fallbacks, 1ull);
@@ -518,12 +874,20 @@ __global__ __launch_bounds__(kBlock) void fallback_kernel(FallbackArgs A) {
 
 // ----------------------------------------------------------- launchers
 
+// Window kinds: run windows with K = 1, 2, 4 runs, or bit windows of 32 / 64 bits.
+enum WinKind { kRuns1 = 0, kRuns2 = 1, kRuns4 = 2, kBits32 = 3, kBits64 = 4, kNumWin = 5 };
+
 // Per-N entry points, defined in ep_inst.hip (one translation unit per N).
 struct Launchers {
-  hipError_t (*map)(const MapArgs&, int K, dim3 grid, hipStream_t);
-  hipError_t (*closure)(const ClosureArgs&, int K, dim3 grid, hipStream_t);
-  hipError_t (*fallback)(const FallbackArgs&, int K, dim3 grid, hipStream_t);
-  hipError_t (*map_occupancy)(int K, int* blocks_per_cu);
+  // scan Map kernel (run windows; win must be a run kind)
+  hipError_t (*map_scan)(const MapArgs&, int win, dim3 grid, dim3 block, hipStream_t);
+  // bit Map kernel (win must be a bit kind); all_machines: one lane holds N machines
+  hipError_t (*map_bits)(const MapArgs&, int win, bool all_machines, dim3 grid, dim3 block,
+                         size_t lds, hipStream_t);
+  hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
+  hipError_t (*fallback)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
+  // resident workgroups per CU of a Map kernel for a block size and LDS size
+  hipError_t (*occupancy)(int win, bool all_machines, int block, size_t lds, int* blocks_per_cu);
 };
 
 }  // namespace epk

@@ -1,8 +1,8 @@
 // Instantiates the N-node kernels (Map, closure, fallback) for one episode
-// size N, with window capacities K = 1, 2, 4.  The build compiles this file
-// once per N in 1..EP_MAX_NODES with -DEP_N=<N>, so the per-N units compile in
-// parallel and every kernel has N fixed at compile time (all register arrays
-// are indexed statically).
+// size N and every window kind.  The build compiles this file once per N in
+// 1..EP_MAX_NODES with -DEP_N=<N>, so the per-N units compile in parallel and
+// every kernel has N fixed at compile time (register arrays are indexed
+// statically).
 #include "ep_device.hpp"
 
 #ifndef EP_N
@@ -12,61 +12,99 @@
 namespace epk {
 namespace {
 
+// One lane holding all N machines of a (segment, episode) is built up to N = 8.
+constexpr int kMaxClassNodes = 8;
+constexpr int kClassMch = EP_N <= kMaxClassNodes ? EP_N : 1;
+
 template <int K>
-hipError_t launch_map_k(const MapArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((map_kernel<EP_N, K>), grid, dim3(kBlock), 0, s, a);
+hipError_t launch_scan_k(const MapArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((map_scan_kernel<EP_N, K>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_map(const MapArgs& a, int K, dim3 grid, hipStream_t s) {
-  switch (K) {
-    case 1: return launch_map_k<1>(a, grid, s);
-    case 2: return launch_map_k<2>(a, grid, s);
-    case 4: return launch_map_k<4>(a, grid, s);
+hipError_t launch_scan(const MapArgs& a, int win, dim3 grid, dim3 block, hipStream_t s) {
+  switch (win) {
+    case kRuns1: return launch_scan_k<1>(a, grid, block, s);
+    case kRuns2: return launch_scan_k<2>(a, grid, block, s);
+    case kRuns4: return launch_scan_k<4>(a, grid, block, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int K>
-hipError_t launch_closure_k(const ClosureArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((closure_kernel<EP_N, K>), grid, dim3(kBlock), 0, s, a);
+template <int W, int MCH>
+hipError_t launch_bits_wm(const MapArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((map_bits_kernel<EP_N, W, MCH>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_closure(const ClosureArgs& a, int K, dim3 grid, hipStream_t s) {
-  switch (K) {
-    case 1: return launch_closure_k<1>(a, grid, s);
-    case 2: return launch_closure_k<2>(a, grid, s);
-    case 4: return launch_closure_k<4>(a, grid, s);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_bits(const MapArgs& a, int win, bool all_machines, dim3 grid, dim3 block,
+                       size_t lds, hipStream_t s) {
+  if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
+  if (win == kBits32)
+    return all_machines ? launch_bits_wm<32, kClassMch>(a, grid, block, lds, s)
+                        : launch_bits_wm<32, 1>(a, grid, block, lds, s);
+  if (win == kBits64)
+    return all_machines ? launch_bits_wm<64, kClassMch>(a, grid, block, lds, s)
+                        : launch_bits_wm<64, 1>(a, grid, block, lds, s);
+  return hipErrorInvalidValue;
 }
 
-template <int K>
-hipError_t launch_fallback_k(const FallbackArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((fallback_kernel<EP_N, K>), grid, dim3(kBlock), 0, s, a);
+template <class Mach>
+hipError_t launch_closure_m(const ClosureArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((closure_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fallback(const FallbackArgs& a, int K, dim3 grid, hipStream_t s) {
-  switch (K) {
-    case 1: return launch_fallback_k<1>(a, grid, s);
-    case 2: return launch_fallback_k<2>(a, grid, s);
-    case 4: return launch_fallback_k<4>(a, grid, s);
+hipError_t launch_closure(const ClosureArgs& a, int win, dim3 grid, hipStream_t s) {
+  switch (win) {
+    case kRuns1: return launch_closure_m<RunMachine<EP_N, 1>>(a, grid, s);
+    case kRuns2: return launch_closure_m<RunMachine<EP_N, 2>>(a, grid, s);
+    case kRuns4: return launch_closure_m<RunMachine<EP_N, 4>>(a, grid, s);
+    case kBits32: return launch_closure_m<BitMachine<EP_N, 32>>(a, grid, s);
+    case kBits64: return launch_closure_m<BitMachine<EP_N, 64>>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t map_occupancy(int K, int* blocks) {
-  switch (K) {
-    case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, map_kernel<EP_N, 1>, kBlock, 0);
-    case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, map_kernel<EP_N, 2>, kBlock, 0);
-    case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, map_kernel<EP_N, 4>, kBlock, 0);
+template <class Mach>
+hipError_t launch_fallback_m(const FallbackArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((fallback_kernel<Mach>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fallback(const FallbackArgs& a, int win, dim3 grid, hipStream_t s) {
+  switch (win) {
+    case kRuns1: return launch_fallback_m<RunMachine<EP_N, 1>>(a, grid, s);
+    case kRuns2: return launch_fallback_m<RunMachine<EP_N, 2>>(a, grid, s);
+    case kRuns4: return launch_fallback_m<RunMachine<EP_N, 4>>(a, grid, s);
+    case kBits32: return launch_fallback_m<BitMachine<EP_N, 32>>(a, grid, s);
+    case kBits64: return launch_fallback_m<BitMachine<EP_N, 64>>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-const Launchers kLaunchers = {launch_map, launch_closure, launch_fallback, map_occupancy};
+template <class F>
+hipError_t occ(F f, int block, size_t lds, int* out) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, block, lds);
+}
+
+hipError_t occupancy(int win, bool all_machines, int block, size_t lds, int* out) {
+  if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
+  switch (win) {
+    case kRuns1: return occ(map_scan_kernel<EP_N, 1>, block, 0, out);
+    case kRuns2: return occ(map_scan_kernel<EP_N, 2>, block, 0, out);
+    case kRuns4: return occ(map_scan_kernel<EP_N, 4>, block, 0, out);
+    case kBits32:
+      return all_machines ? occ(map_bits_kernel<EP_N, 32, kClassMch>, block, lds, out)
+                          : occ(map_bits_kernel<EP_N, 32, 1>, block, lds, out);
+    case kBits64:
+      return all_machines ? occ(map_bits_kernel<EP_N, 64, kClassMch>, block, lds, out)
+                          : occ(map_bits_kernel<EP_N, 64, 1>, block, lds, out);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+const Launchers kLaunchers = {launch_scan, launch_bits, launch_closure, launch_fallback, occupancy};
 
 }  // namespace
 

@@ -175,6 +175,30 @@ int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, int32_t mode,
  * events of segment p lie in (tau_p, tau_{p+1}]). */
 int64_t ep_segment_cut(int32_t t_min, int32_t t_max, int32_t n_segments, int32_t p);
 
+/*
+ * Per-phase GPU durations for measurement.  Between ep_profile_begin() and
+ * ep_profile_end(), every counting call also records HIP events on its stream
+ * around its phases; nothing is synchronised until ep_profile_end(), which
+ * waits for the recorded events and returns the summed durations.  Calls made
+ * outside a session record nothing.  Sessions are process-wide (one at a
+ * time); ep_profile_end() returns EP_ERR_ARG if none is open.
+ *   map_ms      Map kernel (PTPE: the whole count)
+ *   closure_ms  boundary match + repair
+ *   concat_ms   all Concatenate tree levels
+ *   other_ms    cuts, fills, extraction, fallback
+ *   calls       counting calls recorded
+ */
+typedef struct {
+  double map_ms;
+  double closure_ms;
+  double concat_ms;
+  double other_ms;
+  int64_t calls;
+} ep_profile;
+
+int ep_profile_begin(void);
+int ep_profile_end(ep_profile* out);
+
 /* Static text for a status code. */
 const char* ep_status_string(int status);
 

@@ -59,8 +59,9 @@ def test_host_argument_errors():
     assert _call(lo=(5,), hi=(5,)) == -3
     assert _call(lo=(-1,), hi=(5,)) == -3
     assert _call(N=3, lo=(0, 0), hi=(2 ** 31 - 1, 2)) == -3
-    # a window with more live runs than EP_MAX_RUNS: (9,10] has up to 6
-    assert _call(lo=(9,), hi=(10,)) == -7
+    # a window longer than 63 ticks with more live runs than EP_MAX_RUNS:
+    # (99,100] can hold 51 disjoint runs; (9,10] fits a bit window and is fine
+    assert _call(lo=(99,), hi=(100,)) == -7
     bad_mode = fem.EpOptions(7, 0, 0, 0, None)
     assert _call(opt=ctypes.byref(bad_mode)) == -1
     bad_p = fem.EpOptions(2, -4, 0, 0, None)
@@ -72,11 +73,14 @@ def test_host_argument_errors():
 def test_planner_rule():
     # episodes alone fill 256 CUs x 2048 lanes -> PTPE
     assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
-    # 1,024 four-node episodes: MapConcatenate with the smallest 2^q filling the device
+    # 1,024 four-node episodes: MapConcatenate; a lane carries the N machines of
+    # one (segment, episode), so P is the smallest 2^q with S * P filling the device
     mode, P = fem.plan(1024, 4, 10 ** 6, cu_count=256, lanes_per_cu=2048)
-    assert mode == "mapconcat" and P == 128 and 1024 * 4 * P >= 256 * 2048
+    assert mode == "mapconcat" and P == 512 and 1024 * P >= 256 * 2048 > 1024 * P // 2
     # few episodes, long stream
-    assert fem.plan(8, 5, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 16384)
+    assert fem.plan(8, 5, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 65536)
+    # beyond 8 nodes a lane carries one machine: S * N * P lanes
+    assert fem.plan(100, 12, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
     # the segment count is capped so a segment keeps >= 256 events on average
     assert fem.plan(1, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 32)
     # forced choices pass through

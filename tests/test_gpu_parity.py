@@ -142,6 +142,49 @@ def test_config_small(fem, name):
         assert st["fallbacks"] == 0
 
 
+@pytest.mark.parametrize("layout", ["scan", "machine-lanes"])
+@pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "longchain"])
+def test_config_small_other_kernels(fem, name, layout, monkeypatch):
+    # the same counts from the scan Map kernel (run windows, every event) and
+    # from the bit kernel with one machine per lane
+    if layout == "scan":
+        monkeypatch.setenv("EP_FORCE_SCAN", "1")
+    else:
+        monkeypatch.setenv("EP_LANES", "machine")
+    wl = W.make_small(name)
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    for mode, P in [("auto", 0), ("mapconcat", 64), ("mapconcat", 1000)]:
+        got = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P)
+        _check(got, want, "%s %s %s P=%d" % (name, layout, mode, P))
+
+
+def test_fuzz_wide_windows(fem):
+    # t_high up to 60 (64-bit windows) and beyond 63 (run windows), t_low near t_high
+    rng = np.random.default_rng(41)
+    for trial in range(30):
+        n = int(rng.integers(50, 3000))
+        times, types = W.random_stream(rng, n, 4, max_gap=int(rng.integers(1, 12)))
+        N = int(rng.integers(2, 6))
+        ep = rng.integers(0, 4, size=(40, N)).astype(np.uint16)
+        hi = rng.integers(20, 120, size=(40, N - 1)).astype(np.int32)
+        lo = (hi - rng.integers(1, 60, size=hi.shape)).clip(0).astype(np.int32)
+        lo = np.minimum(lo, hi - 1)
+        if trial % 2 == 0:
+            # within 64-bit windows: any t_low works
+            sel = (hi <= 63).all(axis=1)
+        else:
+            # a call with a window beyond 63 ticks uses run windows for every
+            # episode, so each must fit 4 runs
+            sel = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1)
+        ep, lo, hi = ep[sel], lo[sel], hi[sel]
+        if ep.shape[0] == 0:
+            continue
+        want = oracle.count(times, types, ep, lo, hi)
+        for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 7), ("mapconcat", 64)]:
+            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
+                   "wide trial %d %s P=%d" % (trial, mode, P))
+
+
 def test_ptpe_config_full_size(fem):
     # the benchmarked configuration at full size, AUTO launch (as bench.py times it)
     wl = W.make("ptpe")
