@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
 
   const int tile = A.R * A.CH;
   const int words = tile >> 6;
-  uint64_t* s_bits = (uint64_t*)smem;                       // [U][words]
+  uint64_t* s_bits = (uint64_t*)smem;                       // [words][U], word-major
   int32_t* s_t = (int32_t*)(s_bits + (size_t)A.U * words);  // [tile]
   uint8_t* s_s = (uint8_t*)(s_t + tile);                    // [tile]
 
@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
   int64_t tau_lo = 0, tau_hi = 0, stop = 0, check_at = INT64_MAX;
   int32_t B = INT32_MIN;
+  bool single = MCH == 1;  // exactly one class left, held in slot 0
   if (active) {
 #pragma unroll
     for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
           const uint32_t u = A.remap[A.types[base + i]];
           s_t[pos] = A.times[base + i];
           s_s[pos] = (uint8_t)u;
-          if (u) atomicOr((unsigned long long*)&s_bits[(u - 1) * words + (pos >> 6)],
+          if (u) atomicOr((unsigned long long*)&s_bits[(pos >> 6) * A.U + (u - 1)],
                           1ull << (pos & 63));
         }
       }
@@ -540,11 +541,11 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
     int w = w0;
     uint64_t word = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) word |= s_bits[(slot[j] - 1) * words + w];
+    for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
     for (;;) {
       while (word == 0 && ++w < w1) {
 #pragma unroll
-        for (int j = 0; j < N; ++j) word |= s_bits[(slot[j] - 1) * words + w];
+        for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
       }
       if (word == 0) break;
       const int pos = (w << 6) + (__ffsll((unsigned long long)word) - 1);
@@ -561,49 +562,69 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
       }
       const uint32_t d = (uint32_t)t - (uint32_t)B;
       B = t;
-#pragma unroll
-      for (int c = 0; c < MCH; ++c)
-        if (mem[c]) {
-#pragma unroll
-          for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
-        }
-      if (MCH > 1 && (int64_t)t >= check_at) {
-        // classes whose last reset lies more than Span back are identical: merge
-        uint32_t stale = 0, acc = 0;
-        int64_t next = INT64_MAX;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if (mem[c]) {
-            if (r[c] + span < (int64_t)t) {
-              stale |= 1u << c;
-              acc |= mem[c];
-            } else {
-              next = min(next, r[c] + span + 1);
-            }
-          }
-        if (__popc(stale) >= 2) {
-          const int lowest = __ffs((int)stale) - 1;
-#pragma unroll
-          for (int c = 0; c < MCH; ++c)
-            if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
-        }
-        check_at = next;
-      }
       uint32_t done = 0;
+      if (single) {
+        // one class left, in slot 0: no class bookkeeping on this path
 #pragma unroll
-      for (int c = 0; c < MCH; ++c) {
-        if (mem[c] && (int64_t)t > r[c]) {
+        for (int j = 0; j < N - 1; ++j) m[0][j] = age<W>(m[0][j], d);
+        if ((int64_t)t > r[0]) {
           bool hit[N > 1 ? N - 1 : 1];
 #pragma unroll
-          for (int j = 0; j < N - 1; ++j) hit[j] = (m[c][j] & win[j]) != 0;
+          for (int j = 0; j < N - 1; ++j) hit[j] = (m[0][j] & win[j]) != 0;
           bool complete = (lm >> (N - 1)) & 1u;
           if constexpr (N > 1) complete = complete && hit[N - 2];
           if (complete) {
-            done |= 1u << c;
+            done = 1u;
           } else {
 #pragma unroll
             for (int j = 0; j < N - 1; ++j)
-              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[c][j] |= (Bits)1;
+              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[0][j] |= (Bits)1;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if (mem[c]) {
+#pragma unroll
+            for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
+          }
+        if ((int64_t)t >= check_at) {
+          // classes whose last reset lies more than Span back are identical: merge
+          uint32_t stale = 0, acc = 0;
+          int64_t next = INT64_MAX;
+#pragma unroll
+          for (int c = 0; c < MCH; ++c)
+            if (mem[c]) {
+              if (r[c] + span < (int64_t)t) {
+                stale |= 1u << c;
+                acc |= mem[c];
+              } else {
+                next = min(next, r[c] + span + 1);
+              }
+            }
+          if (__popc(stale) >= 2) {
+            const int lowest = __ffs((int)stale) - 1;
+#pragma unroll
+            for (int c = 0; c < MCH; ++c)
+              if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+          }
+          check_at = next;
+        }
+#pragma unroll
+        for (int c = 0; c < MCH; ++c) {
+          if (mem[c] && (int64_t)t > r[c]) {
+            bool hit[N > 1 ? N - 1 : 1];
+#pragma unroll
+            for (int j = 0; j < N - 1; ++j) hit[j] = (m[c][j] & win[j]) != 0;
+            bool complete = (lm >> (N - 1)) & 1u;
+            if constexpr (N > 1) complete = complete && hit[N - 2];
+            if (complete) {
+              done |= 1u << c;
+            } else {
+#pragma unroll
+              for (int j = 0; j < N - 1; ++j)
+                if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[c][j] |= (Bits)1;
+            }
           }
         }
       }
@@ -637,7 +658,7 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
             }
           }
         }
-        if (MCH > 1) {
+        if (MCH > 1 && !single) {
           // classes that completed together are identical from now on
           if (__popc(done) >= 2) {
             const int lowest = __ffs((int)done) - 1;
@@ -651,6 +672,24 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
         for (int c = 0; c < MCH; ++c)
           if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
         if (fin == all) break;
+      }
+      if (MCH > 1 && !single) {
+        // classes never split; once one is left, move it to slot 0 for the lean path
+        uint32_t alive = 0;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
+        if (__popc(alive) == 1) {
+#pragma unroll
+          for (int c = 1; c < MCH; ++c)
+            if ((alive >> c) & 1u) {
+#pragma unroll
+              for (int j = 0; j < N - 1; ++j) m[0][j] = m[c][j];
+              r[0] = r[c];
+              mem[0] = mem[c];
+              mem[c] = 0u;
+            }
+          single = true;
+        }
       }
     }
   }
