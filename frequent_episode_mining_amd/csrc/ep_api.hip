@@ -61,74 +61,145 @@ const Launchers* launchers_for(int N) {
 
 // ------------------------------------------------------------ small kernels
 
-// Equal-time cuts and each segment's event index range.  tau_p for p = 0..P;
-// segment p needs the events in (tau_p - maxSpan, tau_{p+1} + maxSpan]: its
-// machines start up to maxSpan before the left cut and look up to maxSpan past
-// the right cut for the exit b.
-__global__ __launch_bounds__(kBlock) void cuts_kernel(const int32_t* times, int64_t n, int32_t P,
-                                                      int64_t max_span, int64_t* tau,
-                                                      int32_t* beg, int32_t* end) {
-  const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (p > P) return;
-  const int64_t t_min = times[0];
-  const int64_t t_max = times[n - 1];
-  const int64_t width = t_max - t_min + 1;
-  const int64_t cut = t_min - 1 + (p * width) / P;
-  tau[p] = cut;
-  if (p < P) {
-    const int64_t next = t_min - 1 + ((p + 1) * width) / P;
-    beg[p] = (int32_t)upper_bound_time(times, 0, n, cut - max_span);
-    end[p] = (int32_t)upper_bound_time(times, 0, n, next + max_span);
+// Per-call set-up in one launch: the type -> node-slot map, the equal-time
+// cuts with each segment's event range, and the flag and counter words.
+//   remap  : slot of event type y = 1 + its rank among the sorted distinct node
+//            types, 0 for a type on no node (binary search of `distinct`).
+//   cuts   : tau_p = t_min - 1 + floor(p (t_max - t_min + 1) / P) for p = 0..P
+//            ("Design of MapConcatenate": segment p holds (tau_p, tau_{p+1}]);
+//            segment p needs the events in (tau_p - maxSpan, tau_{p+1} + maxSpan]
+//            since its machines start up to maxSpan before the left cut and
+//            look up to maxSpan past the right cut for the exit b.
+struct SetupArgs {
+  const int32_t* times;
+  int64_t n;
+  int32_t P;
+  int64_t max_span;
+  int64_t* tau;
+  int32_t* beg;
+  int32_t* end;
+  const uint16_t* distinct;
+  int32_t U;
+  uint8_t* remap;  // null: not needed
+  int32_t* flags;  // [S + 1]
+  int64_t S;
+  unsigned long long* counters;  // [4]
+};
+
+__global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
+  int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t n_remap = A.remap ? 65536 : 0;
+  if (i < n_remap) {
+    const int32_t y = (int32_t)i;
+    int32_t lo = 0, hi = A.U;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi) >> 1;
+      if ((int32_t)A.distinct[mid] < y)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    A.remap[y] = (lo < A.U && (int32_t)A.distinct[lo] == y) ? (uint8_t)(lo + 1) : (uint8_t)0;
+    return;
   }
+  i -= n_remap;
+  if (i <= A.P) {
+    const int64_t p = i;
+    const int64_t t_min = A.times[0];
+    const int64_t t_max = A.times[A.n - 1];
+    const int64_t width = t_max - t_min + 1;
+    const int64_t cut = t_min - 1 + (p * width) / A.P;
+    A.tau[p] = cut;
+    if (p < A.P) {
+      const int64_t next = t_min - 1 + ((p + 1) * width) / A.P;
+      A.beg[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut - A.max_span);
+      A.end[p] = (int32_t)upper_bound_time(A.times, 0, A.n, next + A.max_span);
+    }
+    return;
+  }
+  i -= (int64_t)A.P + 1;
+  if (i <= A.S) {
+    A.flags[i] = 0;
+    return;
+  }
+  i -= A.S + 1;
+  if (i < 4) A.counters[i] = 0ull;
 }
 
-// One Concatenate level (rules 2-3, Fig. 6): block j spans segments
-// [j*2h, j*2h + 2h); its left half starts at L = j*2h, its right half at
-// R = L + h.  Every tuple of the left half is joined with the right half's
-// tuple whose key equals its exit: (a, c, b) -> (a, c + c', b').  Tuples of a
-// block are keyed by its first segment's keys, so the join is in place.
-__global__ __launch_bounds__(kBlock) void concat_level_kernel(Tuple* T, const int32_t* nslots,
-                                                              int32_t* flags, int64_t S, int32_t P,
-                                                              int32_t slots, int64_t half) {
-  const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t per_block = S * slots;
-  const int64_t j = item / per_block;
-  const int64_t rem = item - j * per_block;
-  const int64_t e = rem / slots;
-  const int32_t s = (int32_t)(rem - e * slots);
-  const int64_t L = j * 2 * half;
-  const int64_t R = L + half;
-  if (R >= P) return;
-  const int32_t nl = min(nslots[L * S + e], slots);
-  if (s >= nl) return;
-  Tuple* lt = T + (L * S + e) * slots + s;
-  Tuple x = *lt;
-  const Tuple* rt = T + (R * S + e) * slots;
-  const int32_t nr = min(nslots[R * S + e], slots);
-  for (int32_t m = 0; m < nr; ++m) {
-    const Tuple y = rt[m];
-    if (y.a == x.b) {
-      x.c += y.c;
-      x.b = y.b;
-      *lt = x;
-      return;
+// ------------------------------------------------------------- Concatenate
+
+// One workgroup joins G consecutive members (segments p0, p0 + stride, ...)
+// of one episode in LDS, level by level (Concatenate rules 1-3, Fig. 6), and
+// writes the merged tuples back to the first member.  Members hold their
+// tuple list keyed by their first segment's keys; joining left block L with
+// right block R maps each (a, c, b) of L to (a, c + c', b') for the tuple of R
+// whose key a' equals b.  Launched with stride 1, then `members`, then
+// members^2, ..., until one member is left.
+constexpr int kConcatMembers = 256;
+
+__global__ __launch_bounds__(kBlock) void concat_tree_kernel(Tuple* T, int32_t* nslots, int32_t* flags,
+                                                             int64_t S, int32_t P, int32_t slots,
+                                                             int64_t stride, int32_t members) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* s_a = (int32_t*)smem;                      // [members][slots]
+  int32_t* s_c = s_a + members * slots;
+  int32_t* s_b = s_c + members * slots;
+  int32_t* s_n = s_b + members * slots;               // [members]
+  __shared__ int32_t s_miss;
+  const int64_t e = (int64_t)blockIdx.x % S;
+  const int64_t span_members = stride * members;
+  const int64_t p0 = ((int64_t)blockIdx.x / S) * span_members;
+  const int i = threadIdx.x;
+  const int64_t p = p0 + (int64_t)i * stride;
+  if (i == 0) s_miss = 0;
+  int n = 0;
+  if (p < P) {
+    n = min(nslots[p * S + e], slots);
+    const Tuple* src = T + (p * S + e) * slots;
+    for (int k = 0; k < n; ++k) {
+      const Tuple tu = src[k];
+      s_a[i * slots + k] = tu.a;
+      s_c[i * slots + k] = tu.c;
+      s_b[i * slots + k] = tu.b;
     }
   }
-  atomicOr(&flags[e], 2);
+  s_n[i] = n;
+  __syncthreads();
+  for (int h = 1; h < members; h <<= 1) {
+    if ((i & (2 * h - 1)) == 0 && i + h < members && p + (int64_t)h * stride < P) {
+      const int nl = s_n[i];
+      const int nr = s_n[i + h];
+      for (int k = 0; k < nl; ++k) {
+        const int32_t b = s_b[i * slots + k];
+        int hit = -1;
+        for (int m = 0; m < nr; ++m)
+          if (hit < 0 && s_a[(i + h) * slots + m] == b) hit = m;
+        if (hit >= 0) {
+          s_c[i * slots + k] += s_c[(i + h) * slots + hit];
+          s_b[i * slots + k] = s_b[(i + h) * slots + hit];
+        } else {
+          s_miss = 1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (i == 0 && p < P) {
+    Tuple* dst = T + (p * S + e) * slots;
+    for (int k = 0; k < s_n[0]; ++k) {
+      Tuple tu;
+      tu.a = s_a[k];
+      tu.c = s_c[k];
+      tu.b = s_b[k];
+      tu.pad = 0;
+      dst[k] = tu;
+    }
+    if (s_miss) atomicOr(&flags[e], 2);
+  }
 }
 
-// The answer is the chain entering segment 0 through machine 0: segment 0's
-// machines start before the first event, so each of them is the page's
-// reference machine alpha_0 on the whole stream (Fig. 3 text).
-__global__ __launch_bounds__(kBlock) void extract_kernel(const Tuple* T, int64_t S, int32_t slots,
-                                                         int64_t* out) {
-  const int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (e < S) out[e] = T[e * slots].c;
-}
-
-__global__ __launch_bounds__(kBlock) void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i < n) p[i] = v;
+inline int64_t setup_items(const SetupArgs& A) {
+  return (A.remap ? 65536 : 0) + (int64_t)A.P + 1 + A.S + 1 + 4;
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n, int64_t v) {
@@ -143,23 +214,6 @@ __global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* tim
 }
 
 inline unsigned grid_for(int64_t items) { return (unsigned)((items + kBlock - 1) / kBlock); }
-
-// type -> node slot (1..U), 0 for types on no node: binary search of the
-// sorted distinct node types.
-__global__ __launch_bounds__(kBlock) void remap_kernel(const uint16_t* distinct, int32_t U,
-                                                       uint8_t* remap) {
-  const int32_t y = blockIdx.x * kBlock + threadIdx.x;
-  if (y >= 65536) return;
-  int32_t lo = 0, hi = U;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    if ((int32_t)distinct[mid] < y)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  remap[y] = (lo < U && (int32_t)distinct[lo] == y) ? (uint8_t)(lo + 1) : (uint8_t)0;
-}
 
 // ------------------------------------------------------------ host helpers
 
@@ -486,11 +540,11 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   const size_t sz_tau = align_up(sizeof(int64_t) * (P + 1), 256);
   const size_t sz_seg = align_up(sizeof(int32_t) * P, 256);
   const size_t sz_tuples = align_up(sizeof(Tuple) * (size_t)P * S * L.slots, 256);
-  const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);
+  const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);  // also nmap
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
   const size_t total =
-      host_bytes + sz_remap + sz_tau + 2 * sz_seg + sz_tuples + sz_nslots + sz_flags + sz_cnt;
+      host_bytes + sz_remap + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt;
 
   char* ws = nullptr;
   if (hipMallocAsync((void**)&ws, total, stream) != hipSuccess || !ws) return EP_ERR_WORKSPACE;
@@ -509,6 +563,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
     Tuple* d_tuples = (Tuple*)(ws + off); off += sz_tuples;
     int32_t* d_nslots = (int32_t*)(ws + off); off += sz_nslots;
+    int32_t* d_nmap = (int32_t*)(ws + off); off += sz_nslots;
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
 
@@ -536,11 +591,12 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     if ((status = upload(dev, ws, host.data(), host_bytes, stream))) break;
 
     if (opt && opt->validate) {
-      hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(kBlock), 0, stream, d_flags + S, (int64_t)1, 0);
+      hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, (int64_t*)d_cnt, (int64_t)1,
+                         (int64_t)0);
       hipLaunchKernelGGL(check_sorted_kernel, dim3(grid_for(n_events)), dim3(kBlock), 0, stream, times,
-                         n_events, d_flags + S);
+                         n_events, (int32_t*)d_cnt);
       int32_t bad = 0;
-      if (hipMemcpyAsync(&bad, d_flags + S, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      if (hipMemcpyAsync(&bad, d_cnt, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
           hipStreamSynchronize(stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
@@ -558,14 +614,12 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       prof = g_prof_on;
     }
     if (prof && (status = prof_record_start(&rec, stream))) break;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_flags, S, 0);
-    hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, (int64_t*)d_cnt, (int64_t)4,
-                       (int64_t)0);
-    if (L.bits)
-      hipLaunchKernelGGL(remap_kernel, dim3(65536 / kBlock), dim3(kBlock), 0, stream, d_dist, U,
-                         d_remap);
-    hipLaunchKernelGGL(cuts_kernel, dim3(grid_for((int64_t)P + 1)), dim3(kBlock), 0, stream, times,
-                       n_events, P, max_span, d_tau, d_beg, d_end);
+    SetupArgs sa;
+    sa.times = times; sa.n = n_events; sa.P = P; sa.max_span = max_span;
+    sa.tau = d_tau; sa.beg = d_beg; sa.end = d_end;
+    sa.distinct = d_dist; sa.U = U; sa.remap = L.bits ? d_remap : nullptr;
+    sa.flags = d_flags; sa.S = S; sa.counters = d_cnt;
+    hipLaunchKernelGGL(setup_kernel, dim3(grid_for(setup_items(sa))), dim3(kBlock), 0, stream, sa);
     if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
 
     MapArgs ma;
@@ -573,10 +627,12 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
     ma.ep_slot = d_slot; ma.remap = d_remap;
     ma.tau = d_tau; ma.seg_beg = d_beg; ma.seg_end = d_end;
-    ma.tuples = d_tuples; ma.nslots = d_nslots;
+    ma.tuples = d_tuples; ma.nmap = d_nmap; ma.nslots = d_nslots;
     ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH; ma.slots = L.slots;
     ma.U = U; ma.n_machines = L.n_machines;
-    dim3 mgrid((unsigned)((P + L.R - 1) / L.R), (unsigned)((S + L.G - 1) / L.G));
+    // workgroups: (segment group, episode group), episode group fastest
+    ma.n_egroups = (S + L.G - 1) / L.G;
+    dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));
     if (prof) hipEventRecord(rec.ev[1], stream);
     hipError_t le = L.bits ? Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream)
                            : Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
@@ -588,33 +644,37 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       ca.times = times; ca.types = types;
       ca.ep_types = d_types; ca.ep_lo = d_lo; ca.ep_hi = d_hi; ca.ep_span = d_span;
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
-      ca.tuples = d_tuples; ca.nslots = d_nslots; ca.flags = d_flags; ca.repairs = d_cnt;
+      ca.tuples = d_tuples; ca.nmap = d_nmap; ca.nslots = d_nslots; ca.flags = d_flags;
+      ca.repairs = d_cnt;
       ca.S = S; ca.P = P; ca.slots = L.slots;
       if (Lr->closure(ca, L.win, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
       }
       if (prof) hipEventRecord(rec.ev[3], stream);
-      for (int64_t half = 1; half < P; half <<= 1) {
-        const int64_t blocks = (P + 2 * half - 1) / (2 * half);
-        hipLaunchKernelGGL(concat_level_kernel, dim3(grid_for(blocks * S * L.slots)), dim3(kBlock), 0,
-                           stream, d_tuples, d_nslots, d_flags, S, P, L.slots, half);
+      // Concatenate tree: each launch joins groups of `members` blocks in LDS
+      int members = kConcatMembers;
+      while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
+      const size_t lds = (size_t)members * (12 * L.slots + 4);
+      for (int64_t stride = 1; stride < P; stride *= members) {
+        const int64_t groups = (P + stride * members - 1) / (stride * members);
+        hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(members), lds,
+                           stream, d_tuples, d_nslots, d_flags, S, P, L.slots, stride, members);
+        if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
       }
+      if (status != EP_OK) break;
     }
     if (prof) {
       if (P <= 1) hipEventRecord(rec.ev[3], stream);
       hipEventRecord(rec.ev[4], stream);
     }
-    hipLaunchKernelGGL(extract_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, d_tuples, S, L.slots,
-                       out_counts);
-    if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
-
     FallbackArgs fa;
     fa.times = times; fa.types = types;
     fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
-    fa.flags = d_flags; fa.fallbacks = d_cnt + 1; fa.out = out_counts;
+    fa.flags = d_flags; fa.tuples = d_tuples; fa.slots = L.slots;
+    fa.fallbacks = d_cnt + 1; fa.out = out_counts;
     fa.n = n_events; fa.S = S;
-    if (Lr->fallback(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+    if (Lr->finish(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
       status = EP_ERR_HIP;
       break;
     }

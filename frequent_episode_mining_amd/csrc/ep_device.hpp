@@ -326,7 +326,8 @@ struct MapArgs {
   const int32_t* seg_beg;    // [P] first event index with time > tau_p - maxSpan
   const int32_t* seg_end;    // [P] first event index with time > tau_{p+1} + maxSpan
   Tuple* tuples;             // [P*S*slots]
-  int32_t* nslots;           // [P*S]
+  int32_t* nmap;             // [P*S] tuples written by the Map step
+  int32_t* nslots;           // [P*S] tuples in use (Map + repairs)
   int64_t S;
   int32_t P;
   int32_t M;      // lanes per (segment, episode): machines spread over lanes
@@ -336,6 +337,7 @@ struct MapArgs {
   int32_t slots;  // tuple slots per (segment, episode)
   int32_t U;      // distinct node types (bit kernels)
   int32_t n_machines;  // machines per (segment, episode): N (MapConcatenate) or 1 (PTPE)
+  int64_t n_egroups;   // episode groups: workgroup b covers segment group b / n_egroups
 };
 
 // Scan Map kernel (run windows): one lane = one machine (segment p, episode e,
@@ -356,14 +358,16 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   const int r_idx = tid / per_seg;
   const int g = (tid / A.M) % A.G;
   const int k = tid % A.M;
-  const int64_t p = (int64_t)blockIdx.x * A.R + r_idx;
-  const int64_t e = (int64_t)blockIdx.y * A.G + g;
+  const int64_t seg_group = (int64_t)blockIdx.x / A.n_egroups;
+  const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
+  const int64_t p = seg_group * A.R + r_idx;
+  const int64_t e = ep_group * A.G + g;
   const bool active = tid < A.R * per_seg && p < A.P && e < A.S;
 
   if (tid == 0) s_chunks = 0;
   __syncthreads();
   if (tid < A.R) {
-    const int64_t pp = (int64_t)blockIdx.x * A.R + tid;
+    const int64_t pp = seg_group * A.R + tid;
     int32_t b = 0, len = 0;
     if (pp < A.P) {
       b = A.seg_beg[pp];
@@ -415,7 +419,10 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
     tu.b = sm.b_off;
     tu.pad = 0;
     A.tuples[pe * A.slots + k] = tu;
-    if (k == 0) A.nslots[pe] = A.M;
+    if (k == 0) {
+      A.nmap[pe] = A.M;
+      A.nslots[pe] = A.M;
+    }
   }
 }
 
@@ -454,14 +461,16 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   const int r_idx = tid / per_seg;
   const int g = (tid / A.M) % A.G;
   const int k_lane = tid % A.M;
-  const int64_t p = (int64_t)blockIdx.x * A.R + r_idx;
-  const int64_t e = (int64_t)blockIdx.y * A.G + g;
+  const int64_t seg_group = (int64_t)blockIdx.x / A.n_egroups;
+  const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
+  const int64_t p = seg_group * A.R + r_idx;
+  const int64_t e = ep_group * A.G + g;
   const bool active = tid < A.R * per_seg && p < A.P && e < A.S;
 
   if (tid == 0) s_chunks = 0;
   __syncthreads();
   if (tid < A.R) {
-    const int64_t pp = (int64_t)blockIdx.x * A.R + tid;
+    const int64_t pp = seg_group * A.R + tid;
     int32_t b = 0, len = 0;
     if (pp < A.P) {
       b = A.seg_beg[pp];
@@ -536,52 +545,74 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
     int32_t len = s_len[r_idx] - ch * A.CH;
     len = len < A.CH ? len : A.CH;
     if (len <= 0) continue;
+    // cursor over this lane's relevant events of the chunk: word w of the
+    // OR of its node slots' presence bitmaps, with `word` its unvisited bits
     const int w0 = (r_idx * A.CH) >> 6;
     const int w1 = w0 + ((len + 63) >> 6);
     int w = w0;
     uint64_t word = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
-    for (;;) {
-      while (word == 0 && ++w < w1) {
+    // next relevant position, or -1 when the chunk is exhausted
+    auto next_pos = [&]() -> int {
+      while (word == 0) {
+        if (++w >= w1) return -1;
 #pragma unroll
         for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
       }
-      if (word == 0) break;
       const int pos = (w << 6) + (__ffsll((unsigned long long)word) - 1);
       word &= word - 1;
-      const int32_t t = s_t[pos];
-      const uint32_t u = s_s[pos];
-      uint32_t lm = 0;
+      return pos;
+    };
+    // completion of class c at t: every member machine completes and resets
+    auto complete_class = [&](uint32_t done, int32_t t) {
+      uint32_t members = 0;
 #pragma unroll
-      for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
-
-      if ((int64_t)t > stop) {
-        fin = all;
-        break;
-      }
-      const uint32_t d = (uint32_t)t - (uint32_t)B;
-      B = t;
-      uint32_t done = 0;
-      if (single) {
-        // one class left, in slot 0: no class bookkeeping on this path
+      for (int c = 0; c < MCH; ++c)
+        if ((done >> c) & 1u) {
+          members |= mem[c];
+          r[c] = t;
 #pragma unroll
-        for (int j = 0; j < N - 1; ++j) m[0][j] = age<W>(m[0][j], d);
-        if ((int64_t)t > r[0]) {
-          bool hit[N > 1 ? N - 1 : 1];
+          for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
+        }
+      const uint32_t live = members & ~fin;  // machines still recording their tuple
 #pragma unroll
-          for (int j = 0; j < N - 1; ++j) hit[j] = (m[0][j] & win[j]) != 0;
-          bool complete = (lm >> (N - 1)) & 1u;
-          if constexpr (N > 1) complete = complete && hit[N - 2];
-          if (complete) {
-            done = 1u;
-          } else {
-#pragma unroll
-            for (int j = 0; j < N - 1; ++j)
-              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[0][j] |= (Bits)1;
+      for (int k = 0; k < MCH; ++k) {
+        if ((live >> k) & 1u) {
+          if ((int64_t)t > tau_lo) {
+            if (!((found >> k) & 1u)) {
+              found |= 1u << k;
+              const int64_t dd = (int64_t)t - tau_lo;
+              a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+            }
+            if ((int64_t)t <= tau_hi) {
+              ++cnt[k];
+            } else {
+              b_off[k] = (int32_t)((int64_t)t - tau_hi);
+              fin |= 1u << k;
+            }
           }
         }
-      } else {
+      }
+      return members;
+    };
+
+    // ---- loop A: several classes (boundary halo only; MCH > 1)
+    if (MCH > 1 && !single) {
+      for (;;) {
+        const int pos = next_pos();
+        if (pos < 0) break;
+        const int32_t t = s_t[pos];
+        const uint32_t u = s_s[pos];
+        uint32_t lm = 0;
+#pragma unroll
+        for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
+        if ((int64_t)t > stop) {
+          fin = all;
+          break;
+        }
+        const uint32_t d = (uint32_t)t - (uint32_t)B;
+        B = t;
 #pragma unroll
         for (int c = 0; c < MCH; ++c)
           if (mem[c]) {
@@ -610,6 +641,7 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
           }
           check_at = next;
         }
+        uint32_t done = 0;
 #pragma unroll
         for (int c = 0; c < MCH; ++c) {
           if (mem[c] && (int64_t)t > r[c]) {
@@ -627,38 +659,8 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
             }
           }
         }
-      }
-      if (done) {
-        // every machine of a completing class completes at t and resets
-        uint32_t members = 0;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if ((done >> c) & 1u) {
-            members |= mem[c];
-            r[c] = t;
-#pragma unroll
-            for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
-          }
-        const uint32_t live = members & ~fin;  // machines still recording their tuple
-#pragma unroll
-        for (int k = 0; k < MCH; ++k) {
-          if ((live >> k) & 1u) {
-            if ((int64_t)t > tau_lo) {
-              if (!((found >> k) & 1u)) {
-                found |= 1u << k;
-                const int64_t dd = (int64_t)t - tau_lo;
-                a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
-              }
-              if ((int64_t)t <= tau_hi) {
-                ++cnt[k];
-              } else {
-                b_off[k] = (int32_t)((int64_t)t - tau_hi);
-                fin |= 1u << k;
-              }
-            }
-          }
-        }
-        if (MCH > 1 && !single) {
+        if (done) {
+          const uint32_t members = complete_class(done, t);
           // classes that completed together are identical from now on
           if (__popc(done) >= 2) {
             const int lowest = __ffs((int)done) - 1;
@@ -667,14 +669,12 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
               if ((done >> c) & 1u) mem[c] = (c == lowest) ? members : 0u;
           }
           check_at = min(check_at, (int64_t)t + span + 1);
-        }
 #pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
-        if (fin == all) break;
-      }
-      if (MCH > 1 && !single) {
-        // classes never split; once one is left, move it to slot 0 for the lean path
+          for (int c = 0; c < MCH; ++c)
+            if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
+          if (fin == all) break;
+        }
+        // classes never split; once one is left, move it to slot 0
         uint32_t alive = 0;
 #pragma unroll
         for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
@@ -689,6 +689,51 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
               mem[c] = 0u;
             }
           single = true;
+          break;
+        }
+      }
+    }
+
+    // ---- loop B: one class, in slot 0; the next event's LDS reads are issued
+    // before the current event is processed
+    if (single && fin != all) {
+      int pos = next_pos();
+      int32_t t_next = pos >= 0 ? s_t[pos] : 0;
+      uint32_t u_next = pos >= 0 ? s_s[pos] : 0u;
+      while (pos >= 0) {
+        const int32_t t = t_next;
+        const uint32_t u = u_next;
+        pos = next_pos();
+        if (pos >= 0) {
+          t_next = s_t[pos];
+          u_next = s_s[pos];
+        }
+        uint32_t lm = 0;
+#pragma unroll
+        for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
+        if ((int64_t)t > stop) {
+          fin = all;
+          break;
+        }
+        const uint32_t d = (uint32_t)t - (uint32_t)B;
+        B = t;
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) m[0][j] = age<W>(m[0][j], d);
+        if ((int64_t)t > r[0]) {
+          bool hit[N > 1 ? N - 1 : 1];
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) hit[j] = (m[0][j] & win[j]) != 0;
+          bool complete = (lm >> (N - 1)) & 1u;
+          if constexpr (N > 1) complete = complete && hit[N - 2];
+          if (complete) {
+            complete_class(1u, t);
+            if ((mem[0] & ~fin) == 0u) mem[0] = 0u;
+            if (fin == all) break;
+          } else {
+#pragma unroll
+            for (int j = 0; j < N - 1; ++j)
+              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[0][j] |= (Bits)1;
+          }
         }
       }
     }
@@ -696,17 +741,40 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
 
   if (active) {
     const int64_t pe = p * A.S + e;
-#pragma unroll
-    for (int c = 0; c < MCH; ++c) {
-      const int k = (MCH == 1) ? k_lane : c;
+    if (MCH == 1) {
       Tuple tu;
-      tu.a = a_off[c];
-      tu.c = cnt[c];
-      tu.b = b_off[c];
+      tu.a = a_off[0];
+      tu.c = cnt[0];
+      tu.b = b_off[0];
       tu.pad = 0;
-      A.tuples[pe * A.slots + k] = tu;
+      A.tuples[pe * A.slots + k_lane] = tu;
+      if (k_lane == 0) {
+        A.nmap[pe] = A.n_machines;
+        A.nslots[pe] = A.n_machines;
+      }
+    } else {
+      // Equal keys mean identical tuples (same first completion after the cut,
+      // or none within Span), so only distinct keys are kept; machine 0's
+      // tuple stays first.
+      int d = 0;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        bool dup = false;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
+        if (!dup) {
+          Tuple tu;
+          tu.a = a_off[c];
+          tu.c = cnt[c];
+          tu.b = b_off[c];
+          tu.pad = 0;
+          A.tuples[pe * A.slots + d] = tu;
+          ++d;
+        }
+      }
+      A.nmap[pe] = d;
+      A.nslots[pe] = d;
     }
-    if (k_lane == 0) A.nslots[pe] = A.n_machines;
   }
 }
 
@@ -718,19 +786,42 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
 template <class Mach>
 __device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int64_t i0, int64_t i1,
                                 SegMachine<Mach>& sm, const typename Mach::Params& prm) {
+  // Blocks of kDepth x 64 events; the next block's loads are issued before
+  // the current one is fed, so one load latency covers kDepth x 64 events.
+  constexpr int kDepth = 4;
   const int lane = threadIdx.x & (kWave - 1);
-  for (int64_t base = i0; base < i1 && !sm.finished; base += kWave) {
-    const int64_t i = base + lane;
-    const bool valid = i < i1;
-    const int32_t t = valid ? times[i] : 0;
-    const uint32_t lm = valid ? prm.level_mask(types[i]) : 0u;
-    uint64_t mask = __ballot(lm != 0u);
-    while (mask != 0 && !sm.finished) {
-      const int src = __ffsll((unsigned long long)mask) - 1;
-      mask &= mask - 1;
-      const int32_t tt = __shfl(t, src);
-      const uint32_t ll = (uint32_t)__shfl((int)lm, src);
-      sm.feed(tt, ll, prm);
+  int32_t t_cur[kDepth], t_nxt[kDepth];
+  uint32_t y_cur[kDepth], y_nxt[kDepth];
+  auto load = [&](int64_t base, int32_t* tt, uint32_t* yy) {
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      const int64_t i = base + q * kWave + lane;
+      const bool valid = i < i1;
+      tt[q] = valid ? times[i] : 0;
+      yy[q] = valid ? (uint32_t)types[i] : 0xffffffffu;
+    }
+  };
+  if (i0 >= i1) return;
+  load(i0, t_cur, y_cur);
+  for (int64_t base = i0; base < i1 && !sm.finished; base += kDepth * kWave) {
+    const int64_t nb = base + kDepth * kWave;
+    if (nb < i1) load(nb, t_nxt, y_nxt);
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      const uint32_t lm = y_cur[q] == 0xffffffffu ? 0u : prm.level_mask(y_cur[q]);
+      uint64_t mask = __ballot(lm != 0u);
+      while (mask != 0 && !sm.finished) {
+        const int src = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        const int32_t tt = __shfl(t_cur[q], src);
+        const uint32_t ll = (uint32_t)__shfl((int)lm, src);
+        sm.feed(tt, ll, prm);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      t_cur[q] = t_nxt[q];
+      y_cur[q] = y_nxt[q];
     }
   }
 }
@@ -760,6 +851,7 @@ struct ClosureArgs {
   const int32_t* seg_beg;
   const int32_t* seg_end;
   Tuple* tuples;
+  const int32_t* nmap;
   int32_t* nslots;
   int32_t* flags;               // [S] non-zero: recount this episode with the fallback
   unsigned long long* repairs;  // repair-tuple counter
@@ -796,18 +888,13 @@ __device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params&
 template <int N>
 __device__ bool has_map_key(const ClosureArgs& A, int64_t q, int64_t e, int32_t key) {
   const Tuple* T = A.tuples + (q * A.S + e) * A.slots;
+  const int nm = A.nmap[q * A.S + e];
   bool hit = false;
 #pragma unroll
-  for (int m = 0; m < N; ++m) hit |= (T[m].a == key);
+  for (int m = 0; m < N; ++m) hit |= (m < nm) && (T[m].a == key);
   return hit;
 }
 
-// For every boundary p -> p+1 and episode e: each distinct exit b of segment
-// p's Map tuples must be a key a of segment p+1 (Concatenate rule 2 needs
-// b_s = a_t).  A missing exit gets a repair tuple in segment p+1, and the
-// repair's own exit is checked against segment p+2, and so on.  Items are one
-// per lane; the repairs of a wave's items run one after another with the
-// whole wave cooperating on each.
 template <int N, class Mach>
 __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
   const int64_t n_items = (int64_t)(A.P - 1) * A.S;
@@ -818,12 +905,14 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
     const int64_t e = item - p * A.S;
     const Tuple* L = A.tuples + (p * A.S + e) * A.slots;
     const Tuple* R = A.tuples + ((p + 1) * A.S + e) * A.slots;
+    const int nl = A.nmap[p * A.S + e];
+    const int nr = A.nmap[(p + 1) * A.S + e];
     int32_t keys[N];
 #pragma unroll
-    for (int m = 0; m < N; ++m) keys[m] = R[m].a;
+    for (int m = 0; m < N; ++m) keys[m] = m < nr ? R[m].a : -1;
     int32_t exits[N];
 #pragma unroll
-    for (int k = 0; k < N; ++k) exits[k] = L[k].b;
+    for (int k = 0; k < N; ++k) exits[k] = k < nl ? L[k].b : -1;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       bool hit = false, dup = false;
@@ -831,7 +920,7 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
       for (int m = 0; m < N; ++m) hit |= keys[m] == exits[k];
 #pragma unroll
       for (int j = 0; j < k; ++j) dup |= exits[j] == exits[k];
-      if (!hit && !dup) missing |= 1u << k;
+      if (k < nl && !hit && !dup) missing |= 1u << k;
     }
   }
   uint64_t wmask = __ballot(missing != 0u);
@@ -886,26 +975,36 @@ struct FallbackArgs {
   const int32_t* ep_hi;
   const int32_t* ep_span;
   const int32_t* flags;
+  const Tuple* tuples;  // segment 0's first tuple holds the answer
+  int32_t slots;
   unsigned long long* fallbacks;
   int64_t* out;
   int64_t n;
   int64_t S;
 };
 
-// Exact safety net: one wave recounts a flagged episode over the whole
-// stream with a single machine (the page's alpha_0 on the unsegmented stream).
+// Result extraction, one wave per episode.  The answer is the chain entering
+// segment 0 through machine 0: segment 0's machines all start before the
+// first event, so each is the page's reference machine alpha_0 (Fig. 3 text).
+// An episode flagged by a repair-slot overflow or a tree miss is instead
+// recounted exactly over the whole stream by the wave (alpha_0 on the
+// unsegmented stream).
 template <class Mach>
-__global__ __launch_bounds__(kBlock) void fallback_kernel(FallbackArgs A) {
+__global__ __launch_bounds__(kBlock) void finish_kernel(FallbackArgs A) {
   const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (e >= A.S) return;
-  if (A.flags[e] == 0) return;
+  const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
+  if (A.flags[e] == 0) {
+    if (lane0) A.out[e] = A.tuples[e * A.slots].c;
+    return;
+  }
   typename Mach::Params prm;
   prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
   const int64_t before = (int64_t)A.times[0] - 1;
   SegMachine<Mach> sm;
   sm.init(before, before, INT64_MAX / 4, prm.span);
   wave_feed_range<Mach>(A.times, A.types, 0, A.n, sm, prm);
-  if ((threadIdx.x & (kWave - 1)) == 0) {
+  if (lane0) {
     A.out[e] = sm.count;
     atomicAdd(A.fallbacks, 1ull);
   }
@@ -924,7 +1023,7 @@ struct Launchers {
   hipError_t (*map_bits)(const MapArgs&, int win, bool all_machines, dim3 grid, dim3 block,
                          size_t lds, hipStream_t);
   hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
-  hipError_t (*fallback)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
+  hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
   // resident workgroups per CU of a Map kernel for a block size and LDS size
   hipError_t (*occupancy)(int win, bool all_machines, int block, size_t lds, int* blocks_per_cu);
 };

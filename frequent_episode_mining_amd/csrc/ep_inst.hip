@@ -1,4 +1,4 @@
-// Instantiates the N-node kernels (Map, closure, fallback) for one episode
+// Instantiates the N-node kernels (Map, closure, finish) for one episode
 // size N and every window kind.  The build compiles this file once per N in
 // 1..EP_MAX_NODES with -DEP_N=<N>, so the per-N units compile in parallel and
 // every kernel has N fixed at compile time (register arrays are indexed
@@ -67,18 +67,18 @@ hipError_t launch_closure(const ClosureArgs& a, int win, dim3 grid, hipStream_t 
 }
 
 template <class Mach>
-hipError_t launch_fallback_m(const FallbackArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((fallback_kernel<Mach>), grid, dim3(kBlock), 0, s, a);
+hipError_t launch_finish_m(const FallbackArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((finish_kernel<Mach>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fallback(const FallbackArgs& a, int win, dim3 grid, hipStream_t s) {
+hipError_t launch_finish(const FallbackArgs& a, int win, dim3 grid, hipStream_t s) {
   switch (win) {
-    case kRuns1: return launch_fallback_m<RunMachine<EP_N, 1>>(a, grid, s);
-    case kRuns2: return launch_fallback_m<RunMachine<EP_N, 2>>(a, grid, s);
-    case kRuns4: return launch_fallback_m<RunMachine<EP_N, 4>>(a, grid, s);
-    case kBits32: return launch_fallback_m<BitMachine<EP_N, 32>>(a, grid, s);
-    case kBits64: return launch_fallback_m<BitMachine<EP_N, 64>>(a, grid, s);
+    case kRuns1: return launch_finish_m<RunMachine<EP_N, 1>>(a, grid, s);
+    case kRuns2: return launch_finish_m<RunMachine<EP_N, 2>>(a, grid, s);
+    case kRuns4: return launch_finish_m<RunMachine<EP_N, 4>>(a, grid, s);
+    case kBits32: return launch_finish_m<BitMachine<EP_N, 32>>(a, grid, s);
+    case kBits64: return launch_finish_m<BitMachine<EP_N, 64>>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -104,7 +104,7 @@ hipError_t occupancy(int win, bool all_machines, int block, size_t lds, int* out
   }
 }
 
-const Launchers kLaunchers = {launch_scan, launch_bits, launch_closure, launch_fallback, occupancy};
+const Launchers kLaunchers = {launch_scan, launch_bits, launch_closure, launch_finish, occupancy};
 
 }  // namespace
 
