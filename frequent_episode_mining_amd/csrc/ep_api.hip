@@ -394,6 +394,9 @@ struct Launch {
   int G, R, CH;    // episodes and segments per workgroup, events per segment per chunk
   int block;
   size_t lds;
+  int CW;          // tick kernel: 64-tick words per segment per chunk
+  size_t lds_ticks;
+  int split;       // 0: per-segment choice between tick and position kernels; 1: ticks; 2: positions
   int slots;
   int n_machines;
 };
@@ -510,6 +513,14 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     if (L.lds > 65536) {
       L.CH = 64;
       L.lds = (size_t)U * 8 + 64 * 5;
+    }
+    // tick kernel: per chunk, R segments x CW words x U slot bitmaps, <= 32 KiB
+    L.CW = (int)std::max<int64_t>(1, std::min<int64_t>(64, 32768 / ((int64_t)L.R * U * 8)));
+    L.lds_ticks = (size_t)L.R * L.CW * U * 8;
+    L.split = 0;
+    if (const char* sp = getenv("EP_SPLIT")) {
+      if (!strcmp(sp, "ticks")) L.split = 1;
+      if (!strcmp(sp, "positions")) L.split = 2;
     }
   } else {
     L.all_mach = false;
@@ -630,12 +641,20 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     ma.tuples = d_tuples; ma.nmap = d_nmap; ma.nslots = d_nslots;
     ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH; ma.slots = L.slots;
     ma.U = U; ma.n_machines = L.n_machines;
+    ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split;
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;
     dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));
     if (prof) hipEventRecord(rec.ev[1], stream);
-    hipError_t le = L.bits ? Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream)
-                           : Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
+    hipError_t le = hipSuccess;
+    if (!L.bits) {
+      le = Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
+    } else {
+      // each segment goes to the tick or the position kernel (segment_uses_ticks)
+      if (L.split != 2) le = Lr->map_ticks(ma, L.all_mach, mgrid, dim3(L.block), L.lds_ticks, stream);
+      if (le == hipSuccess && L.split != 1)
+        le = Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream);
+    }
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
     if (prof) hipEventRecord(rec.ev[2], stream);
 

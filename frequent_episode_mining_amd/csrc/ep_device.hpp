@@ -86,6 +86,18 @@ __device__ inline int64_t prefix_hi(const int32_t* ep_hi, int64_t e, int k) {
   return s;
 }
 
+// First index in [lo, hi) whose time is > v (hi if none).
+__device__ inline int64_t upper_bound_time(const int32_t* times, int64_t lo, int64_t hi, int64_t v) {
+  while (lo < hi) {
+    const int64_t mid = lo + ((hi - lo) >> 1);
+    if ((int64_t)times[mid] > v)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
 // ------------------------------------------------------------ run windows
 
 template <int N>
@@ -338,7 +350,22 @@ struct MapArgs {
   int32_t U;      // distinct node types (bit kernels)
   int32_t n_machines;  // machines per (segment, episode): N (MapConcatenate) or 1 (PTPE)
   int64_t n_egroups;   // episode groups: workgroup b covers segment group b / n_egroups
+  int64_t max_span;    // largest Span of the call
+  int32_t CW;          // tick kernel: 64-tick words per segment per chunk
+  int32_t split;       // 0: each segment to the kernel segment_uses_ticks picks; 1: all to
+                       // the tick kernel; 2: all to the position kernel
 };
+
+// Which Map kernel counts a segment: the tick kernel costs ~(N-1) bit
+// operations per 64 ticks of the segment, the position kernel ~1 step per
+// relevant event, so ticks win where events are dense in time.  Both kernels
+// evaluate this on the same inputs, so each segment is counted exactly once.
+__device__ inline bool segment_uses_ticks(const MapArgs& A, int64_t p, int N) {
+  if (A.split != 0) return A.split == 1;
+  const int64_t tick_span = A.tau[p + 1] - A.tau[p] + 2 * A.max_span;
+  const int64_t events = (int64_t)A.seg_end[p] - A.seg_beg[p];
+  return tick_span * (int64_t)(N > 1 ? N - 1 : 1) <= 4 * events;
+}
 
 // Scan Map kernel (run windows): one lane = one machine (segment p, episode e,
 // machine k).  A workgroup holds R consecutive segments x G episodes x M
@@ -465,14 +492,14 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
   const int64_t p = seg_group * A.R + r_idx;
   const int64_t e = ep_group * A.G + g;
-  const bool active = tid < A.R * per_seg && p < A.P && e < A.S;
+  const bool active = tid < A.R * per_seg && p < A.P && e < A.S && !segment_uses_ticks(A, p, N);
 
   if (tid == 0) s_chunks = 0;
   __syncthreads();
   if (tid < A.R) {
     const int64_t pp = seg_group * A.R + tid;
     int32_t b = 0, len = 0;
-    if (pp < A.P) {
+    if (pp < A.P && !segment_uses_ticks(A, pp, N)) {
       b = A.seg_beg[pp];
       len = A.seg_end[pp] - b;
     }
@@ -778,6 +805,356 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   }
 }
 
+
+// ------------------------------------------------------- tick Map kernel
+
+// Candidates of node j+1 in one 64-tick word from node j's candidates in the
+// previous word (prev) and this word (cur): bit i is set iff some node-j
+// candidate lies d ticks earlier with lo < d <= hi (hi <= 63).  The 128-bit
+// stream prev:cur is shifted by lo + 1 and then smeared over hi - lo shifts
+// by doubling.
+__device__ inline uint64_t dilate(uint64_t prev, uint64_t cur, uint32_t lo, uint32_t hi) {
+  const uint32_t a = lo + 1;                   // 1..63
+  uint64_t y = (cur << a) | (prev >> (64 - a));
+  uint64_t z = prev << a;                      // only its top hi - lo bits are used
+  const uint32_t W = hi - lo;                  // shifts 0..W-1 are ORed
+  uint32_t width = 1;
+#pragma unroll
+  for (int it = 0; it < 6; ++it) {
+    if (width * 2 <= W) {
+      y |= (y << width) | (z >> (64 - width));
+      z |= z << width;
+      width *= 2;
+    }
+  }
+  const uint32_t rest = W - width;             // 0 <= rest < width
+  if (rest) y |= (y << rest) | (z >> (64 - rest));
+  return y;
+}
+
+// Bits i of a word starting at tick t0 with lo_tick <= t0 + i <= hi_tick.
+__device__ inline uint64_t tick_range_mask(int64_t t0, int64_t lo_tick, int64_t hi_tick) {
+  int64_t a = lo_tick - t0;
+  int64_t b = hi_tick - t0;
+  if (a > 63 || b < 0 || a > b) return 0;
+  if (a < 0) a = 0;
+  if (b > 63) b = 63;
+  const uint64_t upto_b = (~0ull) >> (63 - b);
+  const uint64_t below_a = a == 0 ? 0ull : ((~0ull) >> (64 - a));
+  return upto_b & ~below_a;
+}
+
+// The candidate chain of one word: node 0 candidates are its events within
+// `keep`; node j+1 candidates are its events within `keep` that a node-j
+// candidate can precede.  Writes nodes 0..N-2 to cur, returns node N-1
+// (completions).
+template <int N>
+__device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep, const uint64_t* prev,
+                                      uint64_t* cur, const uint32_t* lo, const uint32_t* hi) {
+  uint64_t c = E[0] & keep;
+#pragma unroll
+  for (int j = 1; j < N; ++j) {
+    cur[j - 1] = c;
+    c = E[j] & keep & dilate(prev[j - 1], c, lo[j - 1], hi[j - 1]);
+  }
+  return c;
+}
+
+// Tick Map kernel (bit-parallel over time, t_high <= 63).
+//
+// Each chunk of a segment's time range is staged in LDS as one bitmap per node
+// type slot over 64-tick words (events of one type on one tick are
+// interchangeable, so a bit per (type, tick) is exact).  A machine's state is,
+// per node, the candidate bitmap of the previous word; one word advances all
+// 64 ticks at once with shifts and ANDs (word_chain).  A completion (rare)
+// resets the machine: the rest of the word is recomputed from an empty state.
+// Lanes, machine classes and tuples are as in the position kernel.
+template <int N, int MCH>
+__global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int64_t s_cur[kBlock];     // first tick of segment r's current chunk
+  __shared__ int32_t s_nw[kBlock];      // words of segment r in the current chunk (0: none)
+  __shared__ int32_t s_skip[kBlock];    // the chunk starts >= 64 ticks after the last word
+  __shared__ int32_t s_ev[kBlock];      // next event index of segment r
+  __shared__ int32_t s_ev_end[kBlock];  // end of this chunk's events of segment r
+  __shared__ int32_t s_more;
+  uint64_t* s_tb = (uint64_t*)smem;     // [R*CW words][U], word-major
+
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int per_seg = A.G * A.M;
+  const int r_idx = tid / per_seg;
+  const int g = (tid / A.M) % A.G;
+  const int k_lane = tid % A.M;
+  const int64_t seg_group = (int64_t)blockIdx.x / A.n_egroups;
+  const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
+  const int64_t p = seg_group * A.R + r_idx;
+  const int64_t e = ep_group * A.G + g;
+  const bool active = tid < A.R * per_seg && p < A.P && e < A.S && segment_uses_ticks(A, p, N);
+  const int CW = A.CW;
+
+  if (tid < A.R) {
+    const int64_t pp = seg_group * A.R + tid;
+    int32_t ev = 0, ev_end = 0;
+    if (pp < A.P && segment_uses_ticks(A, pp, N)) {
+      ev = A.seg_beg[pp];
+      ev_end = A.seg_end[pp];
+    }
+    s_ev[tid] = ev;
+    s_ev_end[tid] = ev_end;                      // segment end until the first chunk
+    s_cur[tid] = INT64_MIN / 2;                  // no word processed yet
+    s_nw[tid] = 0;
+  }
+
+  // ---- lane state
+  uint32_t slot[N];
+  uint32_t lo[N > 1 ? N - 1 : 1], hi[N > 1 ? N - 1 : 1];
+  int32_t span = 0;
+  uint64_t prv[MCH][N > 1 ? N - 1 : 1];  // per class: node candidates of the previous word
+  int64_t r[MCH];
+  uint32_t mem[MCH];
+  int32_t cnt[MCH], a_off[MCH], b_off[MCH];
+  uint32_t found = 0, fin = 0;
+  const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
+  int64_t tau_lo = 0, tau_hi = 0, stop = 0;
+  bool single = MCH == 1;
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      lo[j] = (uint32_t)A.ep_lo[e * (N - 1) + j];
+      hi[j] = (uint32_t)A.ep_hi[e * (N - 1) + j];
+    }
+    span = A.ep_span[e];
+    tau_lo = A.tau[p];
+    tau_hi = A.tau[p + 1];
+    stop = tau_hi + span;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int k = (MCH == 1) ? k_lane : c;
+      r[c] = tau_lo - prefix_hi<N>(A.ep_hi, e, k);
+      mem[c] = 1u << c;
+      cnt[c] = 0;
+      a_off[c] = 0;
+      b_off[c] = 0;
+#pragma unroll
+      for (int j = 0; j < N - 1; ++j) prv[c][j] = 0;
+    }
+  } else {
+    fin = all;
+  }
+
+  // completion of the machines of class c at tick t
+  auto complete_members = [&](uint32_t members, int64_t t) {
+    const uint32_t live = members & ~fin;
+#pragma unroll
+    for (int k = 0; k < MCH; ++k) {
+      if ((live >> k) & 1u) {
+        if (t > tau_lo) {
+          if (!((found >> k) & 1u)) {
+            found |= 1u << k;
+            const int64_t dd = t - tau_lo;
+            a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+          }
+          if (t <= tau_hi) {
+            ++cnt[k];
+          } else {
+            b_off[k] = (int32_t)(t - tau_hi);
+            fin |= 1u << k;
+          }
+        }
+      }
+    }
+  };
+
+  // Chunks are event-driven: a segment's next chunk starts right after its
+  // last processed word, or at its next event when that lies 64 or more ticks
+  // later (no event in between, and every candidate is then older than any
+  // t_high <= 63, so the windows are simply emptied).  A chunk ends at the word
+  // of its last event, so the work is bounded by the events, not the ticks.
+  for (;;) {
+    __syncthreads();  // previous chunk fully consumed; segment cursors final
+    if (tid == 0) s_more = 0;
+    __syncthreads();
+    if (tid < A.R) {
+      const int64_t pp = seg_group * A.R + tid;
+      const int32_t ev = s_ev[tid];
+      int32_t nw = 0;
+      if (pp < A.P && ev < A.seg_end[pp] && segment_uses_ticks(A, pp, N)) {
+        const int64_t next_t = A.times[ev];
+        const int64_t contiguous = s_cur[tid] + (int64_t)s_nw[tid] * 64;
+        const bool skip = next_t >= contiguous + 64;
+        const int64_t start = skip ? next_t : contiguous;
+        const int64_t last_tick = start + (int64_t)CW * 64 - 1;
+        const int32_t end = (int32_t)upper_bound_time(A.times, ev, A.seg_end[pp], last_tick);
+        const int64_t last_t = A.times[end - 1];
+        nw = (int32_t)((last_t - start) / 64 + 1);
+        s_cur[tid] = start;
+        s_skip[tid] = skip ? 1 : 0;
+        s_ev_end[tid] = end;
+        s_more = 1;
+      } else {
+        s_ev_end[tid] = ev;
+        s_skip[tid] = 0;
+      }
+      s_nw[tid] = nw;
+    }
+    for (int i = tid; i < A.R * CW * A.U; i += nthr) s_tb[i] = 0;
+    __syncthreads();
+    if (!s_more) break;
+    for (int rr = 0; rr < A.R; ++rr) {
+      const int32_t b0 = s_ev[rr];
+      const int32_t cnt_ev = s_ev_end[rr] - b0;
+      const int64_t chunk_t0 = s_cur[rr];
+      for (int i = tid; i < cnt_ev; i += nthr) {
+        const uint32_t u = A.remap[A.types[b0 + i]];
+        if (u) {
+          const int64_t o = (int64_t)A.times[b0 + i] - chunk_t0;  // 0 <= o < CW*64
+          atomicOr((unsigned long long*)&s_tb[((int64_t)rr * CW + (o >> 6)) * A.U + (u - 1)],
+                   1ull << (o & 63));
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < A.R) s_ev[tid] = s_ev_end[tid];
+    if (fin == all) continue;
+    const int nw = s_nw[r_idx];
+    if (nw == 0) continue;
+    const int64_t chunk_t0 = s_cur[r_idx];
+    if (s_skip[r_idx]) {
+#pragma unroll
+      for (int c = 0; c < MCH; ++c)
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) prv[c][j] = 0;
+    }
+    for (int wi = 0; wi < nw; ++wi) {
+      const int64_t t0 = chunk_t0 + (int64_t)wi * 64;
+      if (t0 > stop) {
+        fin = all;
+        break;
+      }
+      const uint64_t* row = s_tb + ((int64_t)r_idx * CW + wi) * A.U;
+      uint64_t E[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) E[j] = row[slot[j] - 1];
+      if (!single) {
+        // classes whose last reset lies more than Span before this word are
+        // identical for the rest of the stream: merge them
+        uint32_t stale = 0, acc = 0;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if (mem[c] && r[c] + span < t0) {
+            stale |= 1u << c;
+            acc |= mem[c];
+          }
+        if (__popc(stale) >= 2) {
+          const int lowest = __ffs((int)stale) - 1;
+#pragma unroll
+          for (int c = 0; c < MCH; ++c)
+            if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+        }
+      }
+      uint32_t done = 0;  // classes that completed in this word (for merging)
+      int64_t done_at[MCH];
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        done_at[c] = -1;
+        if (c > 0 && single) continue;
+        if (!mem[c]) continue;
+        uint64_t keep = tick_range_mask(t0, r[c] + 1, stop);
+        uint64_t cur[N > 1 ? N - 1 : 1];
+        uint64_t last = word_chain<N>(E, keep, prv[c], cur, lo, hi);
+        while (last != 0) {
+          const int bit = __ffsll((unsigned long long)last) - 1;
+          const int64_t t = t0 + bit;
+          complete_members(mem[c], t);
+          r[c] = t;
+          done |= 1u << c;
+          done_at[c] = t;
+          keep = bit == 63 ? 0ull : (keep & ~((~0ull) >> (63 - bit)));
+          uint64_t zero[N > 1 ? N - 1 : 1];
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) zero[j] = 0;
+          last = word_chain<N>(E, keep, zero, cur, lo, hi);
+        }
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) prv[c][j] = cur[j];
+      }
+      if (done) {
+        if (!single) {
+          // classes that last reset on the same tick are identical
+#pragma unroll
+          for (int c = 0; c < MCH; ++c)
+#pragma unroll
+            for (int c2 = 0; c2 < c; ++c2)
+              if (mem[c] && mem[c2] && ((done >> c) & 1u) && ((done >> c2) & 1u) &&
+                  done_at[c] == done_at[c2]) {
+                mem[c2] |= mem[c];
+                mem[c] = 0u;
+              }
+        }
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
+        if (fin == all) break;
+      }
+      if (!single) {
+        uint32_t alive = 0;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
+        if (__popc(alive) == 1) {
+#pragma unroll
+          for (int c = 1; c < MCH; ++c)
+            if ((alive >> c) & 1u) {
+#pragma unroll
+              for (int j = 0; j < N - 1; ++j) prv[0][j] = prv[c][j];
+              r[0] = r[c];
+              mem[0] = mem[c];
+              mem[c] = 0u;
+            }
+          single = true;
+        }
+      }
+    }
+  }
+
+  if (active) {
+    const int64_t pe = p * A.S + e;
+    if (MCH == 1) {
+      Tuple tu;
+      tu.a = a_off[0];
+      tu.c = cnt[0];
+      tu.b = b_off[0];
+      tu.pad = 0;
+      A.tuples[pe * A.slots + k_lane] = tu;
+      if (k_lane == 0) {
+        A.nmap[pe] = A.n_machines;
+        A.nslots[pe] = A.n_machines;
+      }
+    } else {
+      int d = 0;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        bool dup = false;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
+        if (!dup) {
+          Tuple tu;
+          tu.a = a_off[c];
+          tu.c = cnt[c];
+          tu.b = b_off[c];
+          tu.pad = 0;
+          A.tuples[pe * A.slots + d] = tu;
+          ++d;
+        }
+      }
+      A.nmap[pe] = d;
+      A.nslots[pe] = d;
+    }
+  }
+}
+
 // ------------------------------------------- wave-cooperative single machine
 
 // All 64 lanes hold the same machine; they load 64 events at a time with one
@@ -824,18 +1201,6 @@ __device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int
       y_cur[q] = y_nxt[q];
     }
   }
-}
-
-// First index in [lo, hi) whose time is > v (hi if none).
-__device__ inline int64_t upper_bound_time(const int32_t* times, int64_t lo, int64_t hi, int64_t v) {
-  while (lo < hi) {
-    const int64_t mid = lo + ((hi - lo) >> 1);
-    if ((int64_t)times[mid] > v)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return lo;
 }
 
 // ------------------------------------------------ closure (match + repair)
@@ -1022,6 +1387,9 @@ struct Launchers {
   // bit Map kernel (win must be a bit kind); all_machines: one lane holds N machines
   hipError_t (*map_bits)(const MapArgs&, int win, bool all_machines, dim3 grid, dim3 block,
                          size_t lds, hipStream_t);
+  // tick Map kernel (bit windows up to 63 ticks)
+  hipError_t (*map_ticks)(const MapArgs&, bool all_machines, dim3 grid, dim3 block, size_t lds,
+                          hipStream_t);
   hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
   hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
   // resident workgroups per CU of a Map kernel for a block size and LDS size

@@ -49,6 +49,16 @@ hipError_t launch_bits(const MapArgs& a, int win, bool all_machines, dim3 grid, 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_ticks(const MapArgs& a, bool all_machines, dim3 grid, dim3 block, size_t lds,
+                        hipStream_t s) {
+  if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
+  if (all_machines)
+    hipLaunchKernelGGL((map_ticks_kernel<EP_N, kClassMch>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((map_ticks_kernel<EP_N, 1>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
 template <class Mach>
 hipError_t launch_closure_m(const ClosureArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((closure_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
@@ -104,7 +114,7 @@ hipError_t occupancy(int win, bool all_machines, int block, size_t lds, int* out
   }
 }
 
-const Launchers kLaunchers = {launch_scan, launch_bits, launch_closure, launch_finish, occupancy};
+const Launchers kLaunchers = {launch_scan, launch_bits, launch_ticks, launch_closure, launch_finish, occupancy};
 
 }  // namespace
 
