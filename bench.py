@@ -169,6 +169,7 @@ def main():
     for _ in range(args.steps):
         fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
     ev1.record(stream)
+    we = time.perf_counter()
     torch.cuda.synchronize(dev)
     w1 = time.perf_counter()
     prof = fem.profile_end()
@@ -176,6 +177,7 @@ def main():
     wall_ms = (w1 - w0) * 1000.0 / args.steps
     ms_per_step = max(gpu_ms, wall_ms)
     counts = out.cpu().numpy()
+    log("host enqueue %.4f ms per call" % ((we - w0) * 1000.0 / args.steps))
     log("step %.4f ms (gpu events %.4f, wall %.4f); phases per call: map %.4f closure %.4f "
         "concat %.4f other %.4f ms" % (ms_per_step, gpu_ms, wall_ms, prof["map_ms"] / prof["calls"],
                                        prof["closure_ms"] / prof["calls"],

@@ -167,8 +167,12 @@ def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str
     st = EpStats()
     opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), 0,
                     ctypes.pointer(st) if stats else None)
-    with torch.cuda.device(times.device):
+    if torch.cuda.current_device() == times.device.index:
         status = lib.ep_count_episodes_ex(tp, yp, n, table.as_struct(), S, op, sp, ctypes.byref(opt))
+    else:
+        with torch.cuda.device(times.device):
+            status = lib.ep_count_episodes_ex(tp, yp, n, table.as_struct(), S, op, sp,
+                                              ctypes.byref(opt))
     _check(status)
     if stats:
         return out, {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,

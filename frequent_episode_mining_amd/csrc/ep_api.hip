@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <climits>
 #include <cstdio>
 #include <cstdlib>
@@ -225,19 +226,104 @@ struct DeviceInfo {
 std::mutex g_info_mu;
 DeviceInfo g_info[64];
 
-// Pinned staging for the episode table upload; the event guards reuse.
-struct Staging {
-  std::mutex mu;
+// Pinned staging for the episode-table upload: a ring of slots per device,
+// each guarded by the event recorded after its copy, so the host can prepare
+// a few calls ahead of the GPU.
+constexpr int kStagingSlots = 4;
+struct StagingSlot {
   void* buf = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
+struct Staging {
+  std::mutex mu;
+  StagingSlot slot[kStagingSlots];
+  int next = 0;
+};
 Staging g_staging[64];
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Profiling session: per counting call, events around its phases.
+// Scratch blocks cached per device.  A call takes a block no other host call
+// holds; if the block was last used on another stream, the new stream waits
+// for that use on the GPU (hipStreamWaitEvent), never on the host.  Returning
+// a block records an event after the call's last kernel.  Blocks grow when a
+// call needs more and are kept until the process ends.
+struct ScratchBlock {
+  void* ptr = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool used = false;  // ev has been recorded at least once
+  bool held = false;
+};
+struct ScratchPool {
+  std::mutex mu;
+  std::vector<ScratchBlock*> blocks;
+};
+ScratchPool g_scratch[64];
+
+int scratch_acquire(int dev, size_t bytes, hipStream_t stream, ScratchBlock** out) {
+  ScratchPool& pool = g_scratch[dev];
+  ScratchBlock* b = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(pool.mu);
+    for (ScratchBlock* c : pool.blocks)  // a big enough block, same stream preferred
+      if (!c->held && c->cap >= bytes && (!b || c->last_stream == stream)) b = c;
+    if (!b)
+      for (ScratchBlock* c : pool.blocks)  // else any free block, to grow
+        if (!c->held) {
+          b = c;
+          break;
+        }
+    if (!b) {
+      b = new ScratchBlock();
+      pool.blocks.push_back(b);
+    }
+    b->held = true;
+  }
+  if (b->used && b->last_stream != stream && hipStreamWaitEvent(stream, b->ev, 0) != hipSuccess) {
+    b->held = false;
+    return EP_ERR_HIP;
+  }
+  if (b->cap < bytes) {
+    // the old block may still be read by kernels queued on `stream` (ordered
+    // after the wait above): free it stream-ordered, then take a bigger one
+    if (b->ptr && hipFreeAsync(b->ptr, stream) != hipSuccess) {
+      b->held = false;
+      return EP_ERR_HIP;
+    }
+    b->ptr = nullptr;
+    b->cap = 0;
+    const size_t cap = bytes + bytes / 4;
+    if (hipMallocAsync(&b->ptr, cap, stream) != hipSuccess || !b->ptr) {
+      b->ptr = nullptr;
+      b->held = false;
+      return EP_ERR_WORKSPACE;
+    }
+    b->cap = cap;
+  }
+  if (!b->ev && hipEventCreateWithFlags(&b->ev, hipEventDisableTiming) != hipSuccess) {
+    b->held = false;
+    return EP_ERR_HIP;
+  }
+  *out = b;
+  return EP_OK;
+}
+
+int scratch_release(int dev, ScratchBlock* b, hipStream_t stream) {
+  const bool ok = hipEventRecord(b->ev, stream) == hipSuccess;
+  std::lock_guard<std::mutex> lock(g_scratch[dev].mu);
+  b->last_stream = stream;
+  b->used = b->used || ok;
+  b->held = false;
+  return ok ? EP_OK : EP_ERR_HIP;
+}
+
+// Profiling session: per counting call, events around its phases.  Events
+// come from a pool that lives as long as the process, so recording adds no
+// event creation to the timed calls once the pool is warm.
 struct ProfRecord {
   hipEvent_t ev[5];  // start, before Map, after Map, after closure, after Concatenate
   hipEvent_t end;
@@ -245,12 +331,27 @@ struct ProfRecord {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  // called with g_prof_mu held
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
 
 int prof_record_start(ProfRecord* r, hipStream_t s) {
-  for (int i = 0; i < 5; ++i) {
-    if (hipEventCreate(&r->ev[i]) != hipSuccess) return EP_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    for (int i = 0; i < 5; ++i)
+      if (!(r->ev[i] = pooled_event())) return EP_ERR_HIP;
+    if (!(r->end = pooled_event())) return EP_ERR_HIP;
   }
-  if (hipEventCreate(&r->end) != hipSuccess) return EP_ERR_HIP;
   return hipEventRecord(r->ev[0], s) == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -277,6 +378,8 @@ int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments,
       const int64_t cap_by_events = std::max<int64_t>(1, n / 256);
       P = 2;
       while (P < need && P < (1 << 20)) P <<= 1;
+      // keep segments to <= 65,536 events on average: a repair rescans one segment
+      while (P * 65536 < n && P < (1 << 20)) P <<= 1;
       while (P > 1 && P > cap_by_events) P >>= 1;
     }
   }
@@ -348,28 +451,54 @@ int device_info(int dev, DeviceInfo** out) {
   return EP_OK;
 }
 
-// Copy `bytes` of host data to `dst` on `stream` through pinned staging.
-int upload(int dev, void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  Staging& s = g_staging[dev];
-  std::lock_guard<std::mutex> lock(s.mu);
+// Pinned staging in two steps: staging_acquire() locks the device's ring,
+// waits until its next slot's previous copy has finished and hands out the
+// slot; staging_commit() enqueues the copy to `dst`, records the slot's event
+// and unlocks.  Every acquire is followed by exactly one commit or abort.
+int staging_acquire(int dev, size_t bytes, char** out) {
+  Staging& st = g_staging[dev];
+  st.mu.lock();
+  StagingSlot& s = st.slot[st.next];
+  int status = EP_OK;
   if (s.pending) {
-    EP_HIP(hipEventSynchronize(s.ev));
+    if (hipEventSynchronize(s.ev) != hipSuccess) status = EP_ERR_HIP;
     s.pending = false;
   }
-  if (s.cap < bytes) {
-    if (s.buf) EP_HIP(hipHostFree(s.buf));
+  if (status == EP_OK && s.cap < bytes) {
+    if (s.buf) hipHostFree(s.buf);
     s.buf = nullptr;
     s.cap = 0;
-    size_t cap = std::max<size_t>(bytes, 1 << 16);
-    EP_HIP(hipHostMalloc(&s.buf, cap, hipHostMallocDefault));
-    s.cap = cap;
+    const size_t cap = std::max<size_t>(bytes, 1 << 16);
+    if (hipHostMalloc(&s.buf, cap, hipHostMallocDefault) != hipSuccess) {
+      s.buf = nullptr;
+      status = EP_ERR_HIP;
+    } else {
+      s.cap = cap;
+    }
   }
-  if (!s.ev) EP_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
-  memcpy(s.buf, src, bytes);
-  EP_HIP(hipMemcpyAsync(dst, s.buf, bytes, hipMemcpyHostToDevice, stream));
-  EP_HIP(hipEventRecord(s.ev, stream));
-  s.pending = true;
+  if (status == EP_OK && !s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess)
+    status = EP_ERR_HIP;
+  if (status != EP_OK) {
+    st.mu.unlock();
+    return status;
+  }
+  *out = (char*)s.buf;
   return EP_OK;
+}
+
+int staging_commit(int dev, void* dst, size_t bytes, hipStream_t stream) {
+  Staging& st = g_staging[dev];
+  StagingSlot& s = st.slot[st.next];
+  int status = EP_OK;
+  if (hipMemcpyAsync(dst, s.buf, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(s.ev, stream) != hipSuccess) {
+    status = EP_ERR_HIP;
+  } else {
+    s.pending = true;
+  }
+  st.next = (st.next + 1) % kStagingSlots;
+  st.mu.unlock();
+  return status;
 }
 
 const char* win_name(int w) {
@@ -403,9 +532,17 @@ struct Launch {
 
 }  // namespace
 
-extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
-                                    ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
-                                    hipStream_t stream, const ep_options* opt) {
+namespace {
+// phase timestamps of the current call, printed when EP_LOG_TIME is set
+thread_local std::chrono::steady_clock::time_point g_tp[16];
+thread_local int g_ntp = 0;
+inline void mark() {
+  if (g_ntp < 16) g_tp[g_ntp++] = std::chrono::steady_clock::now();
+}
+
+int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
+                        ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                        hipStream_t stream, const ep_options* opt) {
   // ---- host-side argument checks (nothing is enqueued before they pass)
   const int32_t N = episodes.n_nodes;
   const int64_t S = n_episodes;
@@ -447,11 +584,20 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     return EP_ERR_UNSUPPORTED;
   if (S == 0) return EP_OK;
 
-  // distinct node types -> slots 1..U
-  std::vector<uint16_t> distinct(episodes.types, episodes.types + S * N);
-  std::sort(distinct.begin(), distinct.end());
-  distinct.erase(std::unique(distinct.begin(), distinct.end()), distinct.end());
-  const int U = (int)distinct.size();
+  // distinct node types -> slots 1..U by rank (a 65,536-bit set with prefix counts)
+  uint64_t seen[1024];
+  uint32_t rank_base[1024];
+  memset(seen, 0, sizeof(seen));
+  for (int64_t i = 0; i < S * N; ++i) seen[episodes.types[i] >> 6] |= 1ull << (episodes.types[i] & 63);
+  int U = 0;
+  for (int w = 0; w < 1024; ++w) {
+    rank_base[w] = (uint32_t)U;
+    U += __builtin_popcountll(seen[w]);
+  }
+  auto slot_of = [&](uint16_t y) -> uint32_t {
+    const uint64_t below = seen[y >> 6] & ((1ull << (y & 63)) - 1);
+    return rank_base[y >> 6] + (uint32_t)__builtin_popcountll(below) + 1;
+  };
 
   int dev = 0;
   EP_HIP(hipGetDevice(&dev));
@@ -473,6 +619,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   if (int st = device_info(dev, &info)) return st;
   const Launchers* Lr = launchers_for(N);
 
+  mark();  // checks, slots
   // ---- plan: scheme, segments, kernel and workgroup layout
   Launch L{};
   L.win = win;
@@ -557,9 +704,12 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   const size_t total =
       host_bytes + sz_remap + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt;
 
-  char* ws = nullptr;
-  if (hipMallocAsync((void**)&ws, total, stream) != hipSuccess || !ws) return EP_ERR_WORKSPACE;
+  mark();  // plan
+  ScratchBlock* block = nullptr;
+  if (int st = scratch_acquire(dev, total, stream, &block)) return st;
+  char* ws = (char*)block->ptr;
   int status = EP_OK;
+  mark();  // malloc
   do {
     size_t off = 0;
     uint16_t* d_types = (uint16_t*)(ws + off); off += sz_types;
@@ -578,28 +728,31 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
 
-    // episode table, spans, node slots and the distinct types: one upload
-    std::vector<char> host(host_bytes, 0);
-    memcpy(host.data(), episodes.types, sizeof(uint16_t) * S * N);
-    if (N > 1) {
-      memcpy(host.data() + sz_types, episodes.t_low, sizeof(int32_t) * S * (N - 1));
-      memcpy(host.data() + sz_types + sz_lohi, episodes.t_high, sizeof(int32_t) * S * (N - 1));
-    }
-    int32_t* spans = (int32_t*)(host.data() + sz_types + 2 * sz_lohi);
-    uint8_t* slots = (uint8_t*)(host.data() + sz_types + 2 * sz_lohi + sz_span);
-    for (int64_t e = 0; e < S; ++e) {
-      int64_t sp = 0;
-      for (int j = 0; j < N - 1; ++j) sp += episodes.t_high[e * (N - 1) + j];
-      spans[e] = (int32_t)sp;
-      for (int j = 0; j < N; ++j) {
-        const uint16_t y = episodes.types[e * N + j];
-        const size_t u = std::lower_bound(distinct.begin(), distinct.end(), y) - distinct.begin();
-        slots[e * N + j] = (uint8_t)(U <= 255 ? u + 1 : 0);
+    // episode table, spans, node slots and the distinct types, written
+    // straight into pinned staging: one upload
+    {
+      char* host = nullptr;
+      if ((status = staging_acquire(dev, host_bytes, &host))) break;
+      memcpy(host, episodes.types, sizeof(uint16_t) * S * N);
+      if (N > 1) {
+        memcpy(host + sz_types, episodes.t_low, sizeof(int32_t) * S * (N - 1));
+        memcpy(host + sz_types + sz_lohi, episodes.t_high, sizeof(int32_t) * S * (N - 1));
       }
+      int32_t* spans = (int32_t*)(host + sz_types + 2 * sz_lohi);
+      uint8_t* slots = (uint8_t*)(host + sz_types + 2 * sz_lohi + sz_span);
+      for (int64_t e = 0; e < S; ++e) {
+        int64_t sp = 0;
+        for (int j = 0; j < N - 1; ++j) sp += episodes.t_high[e * (N - 1) + j];
+        spans[e] = (int32_t)sp;
+        for (int j = 0; j < N; ++j)
+          slots[e * N + j] = (uint8_t)(U <= 255 ? slot_of(episodes.types[e * N + j]) : 0);
+      }
+      uint16_t* dist = (uint16_t*)(host + sz_types + 2 * sz_lohi + sz_span + sz_slot);
+      int k = 0;
+      for (int w = 0; w < 1024; ++w)
+        for (uint64_t m = seen[w]; m; m &= m - 1) dist[k++] = (uint16_t)(w * 64 + __builtin_ctzll(m));
+      if ((status = staging_commit(dev, ws, host_bytes, stream))) break;
     }
-    memcpy(host.data() + sz_types + 2 * sz_lohi + sz_span + sz_slot, distinct.data(),
-           sizeof(uint16_t) * U);
-    if ((status = upload(dev, ws, host.data(), host_bytes, stream))) break;
 
     if (opt && opt->validate) {
       hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, (int64_t*)d_cnt, (int64_t)1,
@@ -618,6 +771,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       }
     }
 
+    mark();  // upload
     bool prof = false;
     ProfRecord rec{};
     {
@@ -633,6 +787,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     hipLaunchKernelGGL(setup_kernel, dim3(grid_for(setup_items(sa))), dim3(kBlock), 0, stream, sa);
     if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
 
+    mark();  // setup launch
     MapArgs ma;
     ma.times = times; ma.types = types;
     ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
@@ -658,6 +813,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
     if (prof) hipEventRecord(rec.ev[2], stream);
 
+    mark();  // map launches
     if (P > 1) {
       ClosureArgs ca;
       ca.times = times; ca.types = types;
@@ -687,6 +843,7 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
       if (P <= 1) hipEventRecord(rec.ev[3], stream);
       hipEventRecord(rec.ev[4], stream);
     }
+    mark();  // closure + tree launches
     FallbackArgs fa;
     fa.times = times; fa.types = types;
     fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
@@ -719,9 +876,13 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
     }
   } while (0);
 
-  if (hipFreeAsync(ws, stream) != hipSuccess && status == EP_OK) status = EP_ERR_HIP;
+  mark();  // finish launch
+  if (scratch_release(dev, block, stream) != EP_OK && status == EP_OK) status = EP_ERR_HIP;
+  mark();  // free
   return status;
 }
+
+}  // namespace
 
 extern "C" int ep_profile_begin(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
@@ -751,11 +912,32 @@ extern "C" int ep_profile_end(ep_profile* out) {
     acc.closure_ms += ms[2];
     acc.concat_ms += ms[3];
     acc.calls += 1;
-    for (int i = 0; i < 5; ++i) hipEventDestroy(r.ev[i]);
-    hipEventDestroy(r.end);
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    for (int i = 0; i < 5; ++i) g_event_pool.push_back(r.ev[i]);
+    g_event_pool.push_back(r.end);
   }
   if (out) *out = acc;
   return status;
+}
+
+extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
+                                    ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                                    hipStream_t stream, const ep_options* opt) {
+  static const bool log_time = getenv("EP_LOG_TIME") != nullptr;
+  if (!log_time)
+    return count_episodes_impl(times, types, n_events, episodes, n_episodes, out_counts, stream, opt);
+  const auto t0 = std::chrono::steady_clock::now();
+  g_ntp = 0;
+  const int st = count_episodes_impl(times, types, n_events, episodes, n_episodes, out_counts, stream, opt);
+  const auto t1 = std::chrono::steady_clock::now();
+  fprintf(stderr, "epcount: host %.1f us:", std::chrono::duration<double, std::micro>(t1 - t0).count());
+  auto prev = t0;
+  for (int i = 0; i < g_ntp; ++i) {
+    fprintf(stderr, " %.1f", std::chrono::duration<double, std::micro>(g_tp[i] - prev).count());
+    prev = g_tp[i];
+  }
+  fprintf(stderr, "\n");
+  return st;
 }
 
 extern "C" int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_events,

@@ -41,12 +41,15 @@
  *   - Calls are asynchronous on `stream` unless stated otherwise: on EP_OK the
  *     outputs are valid once the stream has reached the end of the work the
  *     call enqueued.  Host-side argument errors are returned before anything
- *     is enqueued.  Scratch memory is taken from and returned to the stream-
- *     ordered allocator (hipMallocAsync / hipFreeAsync) on `stream`.
+ *     is enqueued.  Scratch memory comes from blocks the library keeps per
+ *     device until the process ends: a call reuses a free block (a block last
+ *     used on another stream is waited for on the GPU with an event) and
+ *     grows it with hipMallocAsync on `stream` when it is too small.
  *   - Inputs outside the documented domain (unsorted times) give unspecified
  *     counts unless `validate` is set in ep_options.
- *   - The library is thread-safe: concurrent calls on different streams do
- *     not share mutable state except a pinned staging buffer guarded by a lock.
+ *   - The library is thread-safe: concurrent calls never share a scratch
+ *     block, and the pinned staging ring for the episode table is guarded by
+ *     a lock.
  */
 #ifndef EPCOUNT_H
 #define EPCOUNT_H
@@ -162,8 +165,12 @@ int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_
  *   out_mode, out_segments         results (host pointers).
  * Rule (hybrid-algorithm section): PTPE iff n_episodes >= cu_count *
  * lanes_per_cu; otherwise MAPCONCAT with the smallest power-of-two P such
- * that n_episodes * n_nodes * P >= cu_count * lanes_per_cu, capped so that a
- * segment keeps at least 256 events on average and P <= 2^20.
+ * that lanes(P) >= cu_count * lanes_per_cu, where a lane carries the N
+ * machines of one (segment, episode) for N <= 8 (lanes = n_episodes * P) and
+ * one machine beyond (lanes = n_episodes * n_nodes * P); P is then raised
+ * until segments hold <= 65,536 events on average (a boundary repair rescans
+ * one segment), and capped so that a segment keeps >= 256 events on average
+ * and P <= 2^20.
  */
 int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, int32_t mode,
             int32_t n_segments, int32_t cu_count, int32_t lanes_per_cu,

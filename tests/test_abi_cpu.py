@@ -79,8 +79,10 @@ def test_planner_rule():
     assert mode == "mapconcat" and P == 512 and 1024 * P >= 256 * 2048 > 1024 * P // 2
     # few episodes, long stream
     assert fem.plan(8, 5, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 65536)
+    # many episodes, long stream: segments are kept to <= 65,536 events
+    assert fem.plan(16384, 2, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 256)
     # beyond 8 nodes a lane carries one machine: S * N * P lanes
-    assert fem.plan(100, 12, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
+    assert fem.plan(100, 12, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
     # the segment count is capped so a segment keeps >= 256 events on average
     assert fem.plan(1, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 32)
     # forced choices pass through
