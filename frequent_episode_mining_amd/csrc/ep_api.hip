@@ -138,27 +138,26 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
 // members^2, ..., until one member is left.
 constexpr int kConcatMembers = 256;
 
-__global__ __launch_bounds__(kBlock) void concat_tree_kernel(Tuple* T, int32_t* nslots, int32_t* flags,
-                                                             int64_t S, int32_t P, int32_t slots,
-                                                             int64_t stride, int32_t members) {
+__global__ __launch_bounds__(kBlock) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
+                                                             int32_t P, int64_t stride, int32_t members,
+                                                             int64_t groups) {
   extern __shared__ __align__(16) unsigned char smem[];
+  const int slots = ts.slots;
   int32_t* s_a = (int32_t*)smem;                      // [members][slots]
   int32_t* s_c = s_a + members * slots;
   int32_t* s_b = s_c + members * slots;
   int32_t* s_n = s_b + members * slots;               // [members]
   __shared__ int32_t s_miss;
-  const int64_t e = (int64_t)blockIdx.x % S;
-  const int64_t span_members = stride * members;
-  const int64_t p0 = ((int64_t)blockIdx.x / S) * span_members;
+  const int64_t e = (int64_t)blockIdx.x / groups;
+  const int64_t p0 = ((int64_t)blockIdx.x - e * groups) * stride * members;
   const int i = threadIdx.x;
   const int64_t p = p0 + (int64_t)i * stride;
   if (i == 0) s_miss = 0;
   int n = 0;
   if (p < P) {
-    n = min(nslots[p * S + e], slots);
-    const Tuple* src = T + (p * S + e) * slots;
+    n = min(ts.nslots[ts.idx(e, p)], slots);
     for (int k = 0; k < n; ++k) {
-      const Tuple tu = src[k];
+      const Tuple tu = *ts.at(e, p, k);
       s_a[i * slots + k] = tu.a;
       s_c[i * slots + k] = tu.c;
       s_b[i * slots + k] = tu.b;
@@ -186,14 +185,13 @@ __global__ __launch_bounds__(kBlock) void concat_tree_kernel(Tuple* T, int32_t* 
     __syncthreads();
   }
   if (i == 0 && p < P) {
-    Tuple* dst = T + (p * S + e) * slots;
     for (int k = 0; k < s_n[0]; ++k) {
       Tuple tu;
       tu.a = s_a[k];
       tu.c = s_c[k];
       tu.b = s_b[k];
       tu.pad = 0;
-      dst[k] = tu;
+      *ts.at(e, p, k) = tu;
     }
     if (s_miss) atomicOr(&flags[e], 2);
   }
@@ -697,7 +695,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_remap = 65536;
   const size_t sz_tau = align_up(sizeof(int64_t) * (P + 1), 256);
   const size_t sz_seg = align_up(sizeof(int32_t) * P, 256);
-  const size_t sz_tuples = align_up(sizeof(Tuple) * (size_t)P * S * L.slots, 256);
+  const size_t sz_t0 = align_up(sizeof(Tuple) * (size_t)P * S, 256);
+  const size_t sz_tx = align_up(sizeof(Tuple) * (size_t)P * S * (L.slots - 1), 256);
+  const size_t sz_tuples = sz_t0 + sz_tx;
   const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);  // also nmap
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
@@ -722,9 +722,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
-    Tuple* d_tuples = (Tuple*)(ws + off); off += sz_tuples;
+    Tuple* d_t0 = (Tuple*)(ws + off); off += sz_t0;
+    Tuple* d_tx = (Tuple*)(ws + off); off += sz_tx;
     int32_t* d_nslots = (int32_t*)(ws + off); off += sz_nslots;
     int32_t* d_nmap = (int32_t*)(ws + off); off += sz_nslots;
+    TupleStore ts;
+    ts.T0 = d_t0; ts.TX = d_tx; ts.nmap = d_nmap; ts.nslots = d_nslots; ts.P = P; ts.slots = L.slots;
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
 
@@ -793,8 +796,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
     ma.ep_slot = d_slot; ma.remap = d_remap;
     ma.tau = d_tau; ma.seg_beg = d_beg; ma.seg_end = d_end;
-    ma.tuples = d_tuples; ma.nmap = d_nmap; ma.nslots = d_nslots;
-    ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH; ma.slots = L.slots;
+    ma.ts = ts;
+    ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH;
     ma.U = U; ma.n_machines = L.n_machines;
     ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split;
     // workgroups: (segment group, episode group), episode group fastest
@@ -819,9 +822,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       ca.times = times; ca.types = types;
       ca.ep_types = d_types; ca.ep_lo = d_lo; ca.ep_hi = d_hi; ca.ep_span = d_span;
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
-      ca.tuples = d_tuples; ca.nmap = d_nmap; ca.nslots = d_nslots; ca.flags = d_flags;
-      ca.repairs = d_cnt;
-      ca.S = S; ca.P = P; ca.slots = L.slots;
+      ca.ts = ts; ca.flags = d_flags; ca.repairs = d_cnt;
+      ca.S = S; ca.P = P;
       if (Lr->closure(ca, L.win, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
@@ -834,7 +836,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       for (int64_t stride = 1; stride < P; stride *= members) {
         const int64_t groups = (P + stride * members - 1) / (stride * members);
         hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(members), lds,
-                           stream, d_tuples, d_nslots, d_flags, S, P, L.slots, stride, members);
+                           stream, ts, d_flags, S, P, stride, members, groups);
         if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
       }
       if (status != EP_OK) break;
@@ -847,7 +849,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     FallbackArgs fa;
     fa.times = times; fa.types = types;
     fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
-    fa.flags = d_flags; fa.tuples = d_tuples; fa.slots = L.slots;
+    fa.flags = d_flags; fa.T0 = d_t0; fa.P = P;
     fa.fallbacks = d_cnt + 1; fa.out = out_counts;
     fa.n = n_events; fa.S = S;
     if (Lr->finish(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {

@@ -44,6 +44,25 @@ struct alignas(16) Tuple {
   int32_t pad;
 };
 
+// Tuples of all (episode, segment) pairs.  The first tuple of each pair sits
+// in T0, episode-major ([e][p]), so that passes over consecutive segments of
+// one episode read contiguous memory; further tuples (more than one distinct
+// Map key, or repairs) sit in TX.
+struct TupleStore {
+  Tuple* T0;        // [S*P]
+  Tuple* TX;        // [S*P*(slots-1)]
+  int32_t* nmap;    // [S*P] tuples written by the Map step
+  int32_t* nslots;  // [S*P] tuples in use (Map + repairs)
+  int64_t P;
+  int32_t slots;    // capacity per pair
+
+  __device__ int64_t idx(int64_t e, int64_t p) const { return e * P + p; }
+  __device__ Tuple* at(int64_t e, int64_t p, int k) const {
+    const int64_t i = e * P + p;
+    return k == 0 ? T0 + i : TX + i * (slots - 1) + (k - 1);
+  }
+};
+
 template <int W>
 struct BitsOf;
 template <>
@@ -337,16 +356,13 @@ struct MapArgs {
   const int64_t* tau;        // [P+1] cuts
   const int32_t* seg_beg;    // [P] first event index with time > tau_p - maxSpan
   const int32_t* seg_end;    // [P] first event index with time > tau_{p+1} + maxSpan
-  Tuple* tuples;             // [P*S*slots]
-  int32_t* nmap;             // [P*S] tuples written by the Map step
-  int32_t* nslots;           // [P*S] tuples in use (Map + repairs)
+  TupleStore ts;
   int64_t S;
   int32_t P;
   int32_t M;      // lanes per (segment, episode): machines spread over lanes
   int32_t G;      // episodes per workgroup
   int32_t R;      // segments per workgroup
   int32_t CH;     // events per segment per chunk
-  int32_t slots;  // tuple slots per (segment, episode)
   int32_t U;      // distinct node types (bit kernels)
   int32_t n_machines;  // machines per (segment, episode): N (MapConcatenate) or 1 (PTPE)
   int64_t n_egroups;   // episode groups: workgroup b covers segment group b / n_egroups
@@ -439,16 +455,15 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   }
 
   if (active) {
-    const int64_t pe = p * A.S + e;
     Tuple tu;
     tu.a = sm.a_off;
     tu.c = sm.count;
     tu.b = sm.b_off;
     tu.pad = 0;
-    A.tuples[pe * A.slots + k] = tu;
+    *A.ts.at(e, p, k) = tu;
     if (k == 0) {
-      A.nmap[pe] = A.M;
-      A.nslots[pe] = A.M;
+      A.ts.nmap[A.ts.idx(e, p)] = A.M;
+      A.ts.nslots[A.ts.idx(e, p)] = A.M;
     }
   }
 }
@@ -767,17 +782,17 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   }
 
   if (active) {
-    const int64_t pe = p * A.S + e;
+    const int64_t pe = A.ts.idx(e, p);
     if (MCH == 1) {
       Tuple tu;
       tu.a = a_off[0];
       tu.c = cnt[0];
       tu.b = b_off[0];
       tu.pad = 0;
-      A.tuples[pe * A.slots + k_lane] = tu;
+      *A.ts.at(e, p, k_lane) = tu;
       if (k_lane == 0) {
-        A.nmap[pe] = A.n_machines;
-        A.nslots[pe] = A.n_machines;
+        A.ts.nmap[pe] = A.n_machines;
+        A.ts.nslots[pe] = A.n_machines;
       }
     } else {
       // Equal keys mean identical tuples (same first completion after the cut,
@@ -795,12 +810,12 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
           tu.c = cnt[c];
           tu.b = b_off[c];
           tu.pad = 0;
-          A.tuples[pe * A.slots + d] = tu;
+          *A.ts.at(e, p, d) = tu;
           ++d;
         }
       }
-      A.nmap[pe] = d;
-      A.nslots[pe] = d;
+      A.ts.nmap[pe] = d;
+      A.ts.nslots[pe] = d;
     }
   }
 }
@@ -1120,17 +1135,17 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   }
 
   if (active) {
-    const int64_t pe = p * A.S + e;
+    const int64_t pe = A.ts.idx(e, p);
     if (MCH == 1) {
       Tuple tu;
       tu.a = a_off[0];
       tu.c = cnt[0];
       tu.b = b_off[0];
       tu.pad = 0;
-      A.tuples[pe * A.slots + k_lane] = tu;
+      *A.ts.at(e, p, k_lane) = tu;
       if (k_lane == 0) {
-        A.nmap[pe] = A.n_machines;
-        A.nslots[pe] = A.n_machines;
+        A.ts.nmap[pe] = A.n_machines;
+        A.ts.nslots[pe] = A.n_machines;
       }
     } else {
       int d = 0;
@@ -1145,12 +1160,12 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
           tu.c = cnt[c];
           tu.b = b_off[c];
           tu.pad = 0;
-          A.tuples[pe * A.slots + d] = tu;
+          *A.ts.at(e, p, d) = tu;
           ++d;
         }
       }
-      A.nmap[pe] = d;
-      A.nslots[pe] = d;
+      A.ts.nmap[pe] = d;
+      A.ts.nslots[pe] = d;
     }
   }
 }
@@ -1215,14 +1230,11 @@ struct ClosureArgs {
   const int64_t* tau;
   const int32_t* seg_beg;
   const int32_t* seg_end;
-  Tuple* tuples;
-  const int32_t* nmap;
-  int32_t* nslots;
+  TupleStore ts;
   int32_t* flags;               // [S] non-zero: recount this episode with the fallback
   unsigned long long* repairs;  // repair-tuple counter
   int64_t S;
   int32_t P;
-  int32_t slots;
 };
 
 // The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
@@ -1252,32 +1264,32 @@ __device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params&
 
 template <int N>
 __device__ bool has_map_key(const ClosureArgs& A, int64_t q, int64_t e, int32_t key) {
-  const Tuple* T = A.tuples + (q * A.S + e) * A.slots;
-  const int nm = A.nmap[q * A.S + e];
+  const int nm = A.ts.nmap[A.ts.idx(e, q)];
   bool hit = false;
-#pragma unroll
-  for (int m = 0; m < N; ++m) hit |= (m < nm) && (T[m].a == key);
+  for (int m = 0; m < nm && m < N; ++m) hit |= A.ts.at(e, q, m)->a == key;
   return hit;
 }
 
 template <int N, class Mach>
 __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
+  // items episode-major: consecutive lanes take consecutive boundaries of one
+  // episode, so their first tuples are contiguous
   const int64_t n_items = (int64_t)(A.P - 1) * A.S;
   const int64_t item = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   uint32_t missing = 0;
   if (item < n_items) {
-    const int64_t p = item / A.S;
-    const int64_t e = item - p * A.S;
-    const Tuple* L = A.tuples + (p * A.S + e) * A.slots;
-    const Tuple* R = A.tuples + ((p + 1) * A.S + e) * A.slots;
-    const int nl = A.nmap[p * A.S + e];
-    const int nr = A.nmap[(p + 1) * A.S + e];
+    const int64_t e = item / (A.P - 1);
+    const int64_t p = item - e * (A.P - 1);
+    const int nl = A.ts.nmap[A.ts.idx(e, p)];
+    const int nr = A.ts.nmap[A.ts.idx(e, p + 1)];
     int32_t keys[N];
+    keys[0] = A.ts.T0[A.ts.idx(e, p + 1)].a;
 #pragma unroll
-    for (int m = 0; m < N; ++m) keys[m] = m < nr ? R[m].a : -1;
+    for (int m = 1; m < N; ++m) keys[m] = m < nr ? A.ts.at(e, p + 1, m)->a : -1;
     int32_t exits[N];
+    exits[0] = A.ts.T0[A.ts.idx(e, p)].b;
 #pragma unroll
-    for (int k = 0; k < N; ++k) exits[k] = k < nl ? L[k].b : -1;
+    for (int k = 1; k < N; ++k) exits[k] = k < nl ? A.ts.at(e, p, k)->b : -1;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       bool hit = false, dup = false;
@@ -1295,14 +1307,14 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
     wmask &= wmask - 1;
     const int64_t it = (int64_t)__shfl((long long)item, src);
     uint32_t miss = (uint32_t)__shfl((int)missing, src);
-    const int64_t p = it / A.S;
-    const int64_t e = it - p * A.S;
+    const int64_t e = it / (A.P - 1);
+    const int64_t p = it - e * (A.P - 1);
     typename Mach::Params prm;
     prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
     while (miss != 0u) {
       const int k = __ffs((int)miss) - 1;
       miss &= miss - 1;
-      int32_t x_off = A.tuples[(p * A.S + e) * A.slots + k].b;
+      int32_t x_off = A.ts.at(e, p, k)->b;
       int64_t q = p + 1;
       for (;;) {
         if (x_off <= 0) {  // a sentinel exit always has a sentinel key; never repair it
@@ -1311,14 +1323,14 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
         }
         const Tuple tu = repair_tuple<Mach>(A, prm, q, A.tau[q] + x_off);
         int slot = 0;
-        if (lane == 0) slot = atomicAdd(&A.nslots[q * A.S + e], 1);
+        if (lane == 0) slot = atomicAdd(&A.ts.nslots[A.ts.idx(e, q)], 1);
         slot = __shfl(slot, 0);
-        if (slot >= A.slots) {
+        if (slot >= A.ts.slots) {
           if (lane == 0) atomicOr(&A.flags[e], 1);
           break;
         }
         if (lane == 0) {
-          A.tuples[(q * A.S + e) * A.slots + slot] = tu;
+          *A.ts.at(e, q, slot) = tu;
           atomicAdd(A.repairs, 1ull);
         }
         if (q + 1 >= A.P) break;
@@ -1340,8 +1352,8 @@ struct FallbackArgs {
   const int32_t* ep_hi;
   const int32_t* ep_span;
   const int32_t* flags;
-  const Tuple* tuples;  // segment 0's first tuple holds the answer
-  int32_t slots;
+  const Tuple* T0;      // segment 0's first tuple of episode e (at e * P) holds the answer
+  int64_t P;
   unsigned long long* fallbacks;
   int64_t* out;
   int64_t n;
@@ -1360,7 +1372,7 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(FallbackArgs A) {
   if (e >= A.S) return;
   const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
   if (A.flags[e] == 0) {
-    if (lane0) A.out[e] = A.tuples[e * A.slots].c;
+    if (lane0) A.out[e] = A.T0[e * A.P].c;
     return;
   }
   typename Mach::Params prm;
