@@ -219,6 +219,10 @@ inline unsigned grid_for(int64_t items) { return (unsigned)((items + kBlock - 1)
 struct DeviceInfo {
   bool ok = false;
   int cu_count = 0;
+  // resident tick-kernel workgroups per CU, by [N][one lane holds all machines],
+  // for the LDS size tick_lds (queried once: the query is slow)
+  int tick_per_cu[EP_MAX_NODES + 1][2] = {};
+  size_t tick_lds[EP_MAX_NODES + 1][2] = {};
 };
 
 std::mutex g_info_mu;
@@ -555,6 +559,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
 
   int64_t max_span = 0, max_hi = 0;
   int K = 1;
+  int dil_k = 0;  // doubling steps of the tick kernel's dilation (windows up to 63 ticks)
   for (int64_t e = 0; e < S; ++e) {
     int64_t span = 0;
     for (int j = 0; j < N - 1; ++j) {
@@ -563,6 +568,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       if (lo < 0 || lo >= hi) return EP_ERR_INTERVAL;
       span += hi;
       max_hi = std::max(max_hi, hi);
+      if (hi <= 63) dil_k = std::max(dil_k, dil_steps((uint32_t)lo, (uint32_t)hi));
       // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1
       const int64_t runs = hi / (hi - lo + 1) + 1;
       while (K < runs && K <= EP_MAX_RUNS) K <<= 1;
@@ -799,10 +805,31 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ma.ts = ts;
     ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH;
     ma.U = U; ma.n_machines = L.n_machines;
-    ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split;
+    ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split; ma.dil_steps = dil_k;
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;
     dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));
+    // tick kernel: where a segment group fits one chunk, as few workgroups per
+    // group as still fill every CU loop over its episode groups, building the
+    // bitmaps once each (the kernel decides per group; the grid is mgrid)
+    const int64_t seg_groups = (P + L.R - 1) / L.R;
+    ma.eg_blocks = ma.n_egroups;
+    if (L.bits && L.split != 2) {
+      int per_cu = 0;
+      {
+        std::lock_guard<std::mutex> lock(g_info_mu);
+        int& cached = info->tick_per_cu[N][L.all_mach ? 1 : 0];
+        size_t& cached_lds = info->tick_lds[N][L.all_mach ? 1 : 0];
+        if (cached == 0 || cached_lds != L.lds_ticks) {
+          if (Lr->occupancy_ticks(L.all_mach, L.block, L.lds_ticks, &cached) != hipSuccess || cached < 1)
+            cached = 1;
+          cached_lds = L.lds_ticks;
+        }
+        per_cu = cached;
+      }
+      const int64_t want = (int64_t)info->cu_count * per_cu;
+      ma.eg_blocks = std::min<int64_t>(ma.n_egroups, std::max<int64_t>(1, (want + seg_groups - 1) / seg_groups));
+    }
     if (prof) hipEventRecord(rec.ev[1], stream);
     hipError_t le = hipSuccess;
     if (!L.bits) {

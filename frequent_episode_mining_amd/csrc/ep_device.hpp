@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace epk {
 
 constexpr int kWave = 64;
@@ -370,6 +372,9 @@ struct MapArgs {
   int32_t CW;          // tick kernel: 64-tick words per segment per chunk
   int32_t split;       // 0: each segment to the kernel segment_uses_ticks picks; 1: all to
                        // the tick kernel; 2: all to the position kernel
+  int32_t dil_steps;   // tick kernel: doubling steps of the widest interval of the call
+  int64_t eg_blocks;   // tick kernel: workgroups that loop over a segment group's episode
+                       // groups when its segments fit one chunk each
 };
 
 // Which Map kernel counts a segment: the tick kernel costs ~(N-1) bit
@@ -823,54 +828,96 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
 
 // ------------------------------------------------------- tick Map kernel
 
+// Dilation program of one interval (lo, hi], hi <= 63: the first shift lo + 1
+// and the amounts of the doubling steps, 5 bits per step, whose subset sums
+// are exactly 0 .. hi-lo-1 (amounts 1, 2, 4, ... then the remainder; steps
+// past the last have amount 0 and change nothing).
+struct DilProg {
+  uint32_t a;   // lo + 1
+  uint32_t pk;  // step i amount at bits 5i .. 5i+4
+};
+
+// Doubling steps an interval (lo, hi] needs; the kernel runs the largest count
+// of the call for every episode.
+__host__ __device__ inline int dil_steps(uint32_t lo, uint32_t hi) {
+  const uint32_t W = hi - lo;
+  int k = 0;
+  while ((2u << k) <= W) ++k;  // 2^k <= W < 2^(k+1)
+  return k + (W != (1u << k) ? 1 : 0);
+}
+
+__device__ inline DilProg dil_prog(uint32_t lo, uint32_t hi) {
+  const uint32_t W = hi - lo;  // 1 .. 63
+  const int k = 31 - __clz((int)W);
+  uint32_t pk = 0;
+  for (int i = 0; i < k; ++i) pk |= (1u << i) << (5 * i);
+  pk |= (W - (1u << k)) << (5 * k);
+  return {lo + 1, pk};
+}
+
 // Candidates of node j+1 in one 64-tick word from node j's candidates in the
 // previous word (prev) and this word (cur): bit i is set iff some node-j
-// candidate lies d ticks earlier with lo < d <= hi (hi <= 63).  The 128-bit
-// stream prev:cur is shifted by lo + 1 and then smeared over hi - lo shifts
-// by doubling.
-__device__ inline uint64_t dilate(uint64_t prev, uint64_t cur, uint32_t lo, uint32_t hi) {
-  const uint32_t a = lo + 1;                   // 1..63
-  uint64_t y = (cur << a) | (prev >> (64 - a));
-  uint64_t z = prev << a;                      // only its top hi - lo bits are used
-  const uint32_t W = hi - lo;                  // shifts 0..W-1 are ORed
-  uint32_t width = 1;
+// candidate lies d ticks earlier with lo < d <= hi.  The 128-bit stream
+// prev:cur is shifted by lo + 1, then ORed with its own shifts by the doubling
+// amounts.  The high word takes the top s bits of the low word at each step as
+// ((hi32(z) << s) >> 32), which is 0 for s = 0, so padding steps are exact
+// no-ops and the code has no per-lane branches.  K is uniform over the launch.
+__device__ inline uint64_t dilate(uint64_t prev, uint64_t cur, DilProg d, int K) {
+  uint64_t y = (cur << d.a) | (prev >> (64 - d.a));
+  uint64_t z = prev << d.a;
 #pragma unroll
-  for (int it = 0; it < 6; ++it) {
-    if (width * 2 <= W) {
-      y |= (y << width) | (z >> (64 - width));
-      z |= z << width;
-      width *= 2;
-    }
+  for (int i = 0; i < 6; ++i) {
+    if (i >= K) break;
+    const uint32_t s = (d.pk >> (5 * i)) & 31u;
+    const uint64_t spill = ((uint64_t)(uint32_t)(z >> 32) << s) >> 32;
+    y |= (y << s) | spill;
+    if (i + 1 < K) z |= z << s;
   }
-  const uint32_t rest = W - width;             // 0 <= rest < width
-  if (rest) y |= (y << rest) | (z >> (64 - rest));
   return y;
 }
 
-// Bits i of a word starting at tick t0 with lo_tick <= t0 + i <= hi_tick.
-__device__ inline uint64_t tick_range_mask(int64_t t0, int64_t lo_tick, int64_t hi_tick) {
-  int64_t a = lo_tick - t0;
-  int64_t b = hi_tick - t0;
-  if (a > 63 || b < 0 || a > b) return 0;
-  if (a < 0) a = 0;
-  if (b > 63) b = 63;
-  const uint64_t upto_b = (~0ull) >> (63 - b);
-  const uint64_t below_a = a == 0 ? 0ull : ((~0ull) >> (64 - a));
-  return upto_b & ~below_a;
+// dilate() with the step count fixed at compile time (KC >= the launch's K;
+// the extra steps have amount 0).
+template <int KC>
+__device__ inline uint64_t dilate_k(uint64_t prev, uint64_t cur, DilProg d) {
+  uint64_t y = (cur << d.a) | (prev >> (64 - d.a));
+  uint64_t z = prev << d.a;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const uint32_t s = (d.pk >> (5 * i)) & 31u;
+    const uint64_t spill = ((uint64_t)(uint32_t)(z >> 32) << s) >> 32;
+    y |= (y << s) | spill;
+    if (i + 1 < KC) z |= z << s;
+  }
+  return y;
 }
 
 // The candidate chain of one word: node 0 candidates are its events within
-// `keep`; node j+1 candidates are its events within `keep` that a node-j
-// candidate can precede.  Writes nodes 0..N-2 to cur, returns node N-1
+// keep_lo (ticks after the machine's last reset); node j+1 candidates are its
+// events that a node-j candidate can precede.  Later nodes need no mask:
+// every candidate descends from a node-0 candidate after the reset, and the
+// window only moves forward.  Writes nodes 0..N-2 to cur and returns node N-1
 // (completions).
 template <int N>
-__device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep, const uint64_t* prev,
-                                      uint64_t* cur, const uint32_t* lo, const uint32_t* hi) {
-  uint64_t c = E[0] & keep;
+__device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep_lo, const uint64_t* prev,
+                                      uint64_t* cur, const DilProg* dp, int K) {
+  uint64_t c = E[0] & keep_lo;
 #pragma unroll
   for (int j = 1; j < N; ++j) {
     cur[j - 1] = c;
-    c = E[j] & keep & dilate(prev[j - 1], c, lo[j - 1], hi[j - 1]);
+    c = E[j] & dilate(prev[j - 1], c, dp[j - 1], K);
+  }
+  return c;
+}
+
+template <int N, int KC>
+__device__ inline uint64_t word_chain_k(const uint64_t* E, uint64_t keep_lo, const uint64_t* prev,
+                                        uint64_t* cur, const DilProg* dp) {
+  uint64_t c = E[0] & keep_lo;
+#pragma unroll
+  for (int j = 1; j < N; ++j) {
+    cur[j - 1] = c;
+    c = E[j] & dilate_k<KC>(prev[j - 1], c, dp[j - 1]);
   }
   return c;
 }
@@ -883,7 +930,15 @@ __device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep, const ui
 // per node, the candidate bitmap of the previous word; one word advances all
 // 64 ticks at once with shifts and ANDs (word_chain).  A completion (rare)
 // resets the machine: the rest of the word is recomputed from an empty state.
-// Lanes, machine classes and tuples are as in the position kernel.
+// Times inside the word loop are int32 offsets from the current chunk's first
+// tick.  Lanes, machine classes and tuples are as in the position kernel.
+//
+// The grid holds one workgroup per (episode group, group of R segments).  When
+// every segment of the group fits one chunk, workgroups 0 .. eg_blocks-1 of
+// the group each loop over its episode groups (eg, eg + eg_blocks, ...) and
+// build the bitmaps once, reusing them for every later episode group; the
+// other workgroups of the group exit at once.  Otherwise each workgroup counts
+// its own episode group.
 template <int N, int MCH>
 __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -891,282 +946,434 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   __shared__ int32_t s_nw[kBlock];      // words of segment r in the current chunk (0: none)
   __shared__ int32_t s_skip[kBlock];    // the chunk starts >= 64 ticks after the last word
   __shared__ int32_t s_ev[kBlock];      // next event index of segment r
-  __shared__ int32_t s_ev_end[kBlock];  // end of this chunk's events of segment r
-  __shared__ int32_t s_more;
+  __shared__ int32_t s_end[kBlock];     // first event past the chunk (lowered by the fill)
+  __shared__ int32_t s_maxw[kBlock];    // last word of the chunk holding an event
+  __shared__ int32_t s_seg_end[kBlock]; // segment r's event range end; 0 for a segment not counted here
+  __shared__ int32_t s_built[kBlock];   // first event of the chunk the bitmaps hold (-1: none)
+  __shared__ int32_t s_more, s_reuse, s_fit;
   uint64_t* s_tb = (uint64_t*)smem;     // [R*CW words][U], word-major
 
+  constexpr int NI = N > 1 ? N - 1 : 1;
+  constexpr int kPer = 8;               // events per thread per fill batch
+  constexpr int32_t kFar = 1 << 30;     // offsets are clamped to +-kFar
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int per_seg = A.G * A.M;
   const int r_idx = tid / per_seg;
   const int g = (tid / A.M) % A.G;
   const int k_lane = tid % A.M;
-  const int64_t seg_group = (int64_t)blockIdx.x / A.n_egroups;
-  const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
+  // segment group fastest: the workgroups that loop (eg_id < eg_blocks) are
+  // the first ones, spread over every XCD by the round-robin dispatch
+  const int64_t seg_groups = (A.P + A.R - 1) / A.R;
+  const int64_t eg_id = (int64_t)blockIdx.x / seg_groups;
+  const int64_t seg_group = (int64_t)blockIdx.x - eg_id * seg_groups;
   const int64_t p = seg_group * A.R + r_idx;
-  const int64_t e = ep_group * A.G + g;
-  const bool active = tid < A.R * per_seg && p < A.P && e < A.S && segment_uses_ticks(A, p, N);
+  const bool seg_here = tid < A.R * per_seg && p < A.P && segment_uses_ticks(A, p, N);
   const int CW = A.CW;
+  const int K = A.dil_steps;
+  const int CE = kPer * nthr;
+  const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
 
+  if (tid == 0) s_fit = 1;
+  __syncthreads();
   if (tid < A.R) {
     const int64_t pp = seg_group * A.R + tid;
-    int32_t ev = 0, ev_end = 0;
+    int32_t end = 0;
     if (pp < A.P && segment_uses_ticks(A, pp, N)) {
-      ev = A.seg_beg[pp];
-      ev_end = A.seg_end[pp];
+      end = A.seg_end[pp];
+      const int32_t beg = A.seg_beg[pp];
+      if (beg < end && (((int64_t)A.times[end - 1] - A.times[beg]) >> 6) >= CW) s_fit = 0;
     }
-    s_ev[tid] = ev;
-    s_ev_end[tid] = ev_end;                      // segment end until the first chunk
-    s_cur[tid] = INT64_MIN / 2;                  // no word processed yet
-    s_nw[tid] = 0;
+    s_seg_end[tid] = end;
+    s_built[tid] = -1;
   }
-
-  // ---- lane state
-  uint32_t slot[N];
-  uint32_t lo[N > 1 ? N - 1 : 1], hi[N > 1 ? N - 1 : 1];
-  int32_t span = 0;
-  uint64_t prv[MCH][N > 1 ? N - 1 : 1];  // per class: node candidates of the previous word
-  int64_t r[MCH];
-  uint32_t mem[MCH];
-  int32_t cnt[MCH], a_off[MCH], b_off[MCH];
-  uint32_t found = 0, fin = 0;
-  const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
-  int64_t tau_lo = 0, tau_hi = 0, stop = 0;
-  bool single = MCH == 1;
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
-#pragma unroll
-    for (int j = 0; j < N - 1; ++j) {
-      lo[j] = (uint32_t)A.ep_lo[e * (N - 1) + j];
-      hi[j] = (uint32_t)A.ep_hi[e * (N - 1) + j];
-    }
-    span = A.ep_span[e];
+  int64_t tau_lo = 0, tau_hi = 0;
+  if (seg_here) {
     tau_lo = A.tau[p];
     tau_hi = A.tau[p + 1];
-    stop = tau_hi + span;
-#pragma unroll
-    for (int c = 0; c < MCH; ++c) {
-      const int k = (MCH == 1) ? k_lane : c;
-      r[c] = tau_lo - prefix_hi<N>(A.ep_hi, e, k);
-      mem[c] = 1u << c;
-      cnt[c] = 0;
-      a_off[c] = 0;
-      b_off[c] = 0;
-#pragma unroll
-      for (int j = 0; j < N - 1; ++j) prv[c][j] = 0;
-    }
-  } else {
-    fin = all;
   }
+  __syncthreads();
+  const bool fit = s_fit != 0;
+  if (fit && eg_id >= A.eg_blocks) return;  // the group's looping workgroups cover it
+  const int64_t eg_step = fit ? A.eg_blocks : A.n_egroups;
 
-  // completion of the machines of class c at tick t
-  auto complete_members = [&](uint32_t members, int64_t t) {
-    const uint32_t live = members & ~fin;
-#pragma unroll
-    for (int k = 0; k < MCH; ++k) {
-      if ((live >> k) & 1u) {
-        if (t > tau_lo) {
-          if (!((found >> k) & 1u)) {
-            found |= 1u << k;
-            const int64_t dd = t - tau_lo;
-            a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
-          }
-          if (t <= tau_hi) {
-            ++cnt[k];
-          } else {
-            b_off[k] = (int32_t)(t - tau_hi);
-            fin |= 1u << k;
-          }
-        }
-      }
-    }
-  };
-
-  // Chunks are event-driven: a segment's next chunk starts right after its
-  // last processed word, or at its next event when that lies 64 or more ticks
-  // later (no event in between, and every candidate is then older than any
-  // t_high <= 63, so the windows are simply emptied).  A chunk ends at the word
-  // of its last event, so the work is bounded by the events, not the ticks.
-  for (;;) {
-    __syncthreads();  // previous chunk fully consumed; segment cursors final
-    if (tid == 0) s_more = 0;
-    __syncthreads();
+  for (int64_t eg = eg_id; eg < A.n_egroups; eg += eg_step) {
+    const int64_t e = eg * A.G + g;
+    const bool active = seg_here && e < A.S;
     if (tid < A.R) {
       const int64_t pp = seg_group * A.R + tid;
-      const int32_t ev = s_ev[tid];
-      int32_t nw = 0;
-      if (pp < A.P && ev < A.seg_end[pp] && segment_uses_ticks(A, pp, N)) {
-        const int64_t next_t = A.times[ev];
-        const int64_t contiguous = s_cur[tid] + (int64_t)s_nw[tid] * 64;
-        const bool skip = next_t >= contiguous + 64;
-        const int64_t start = skip ? next_t : contiguous;
-        const int64_t last_tick = start + (int64_t)CW * 64 - 1;
-        const int32_t end = (int32_t)upper_bound_time(A.times, ev, A.seg_end[pp], last_tick);
-        const int64_t last_t = A.times[end - 1];
-        nw = (int32_t)((last_t - start) / 64 + 1);
-        s_cur[tid] = start;
-        s_skip[tid] = skip ? 1 : 0;
-        s_ev_end[tid] = end;
-        s_more = 1;
-      } else {
-        s_ev_end[tid] = ev;
-        s_skip[tid] = 0;
-      }
-      s_nw[tid] = nw;
+      s_ev[tid] = s_seg_end[tid] ? A.seg_beg[pp] : 0;
+      s_cur[tid] = INT64_MIN / 2;                // no word processed yet
+      s_nw[tid] = 0;
     }
-    for (int i = tid; i < A.R * CW * A.U; i += nthr) s_tb[i] = 0;
-    __syncthreads();
-    if (!s_more) break;
-    for (int rr = 0; rr < A.R; ++rr) {
-      const int32_t b0 = s_ev[rr];
-      const int32_t cnt_ev = s_ev_end[rr] - b0;
-      const int64_t chunk_t0 = s_cur[rr];
-      for (int i = tid; i < cnt_ev; i += nthr) {
-        const uint32_t u = A.remap[A.types[b0 + i]];
-        if (u) {
-          const int64_t o = (int64_t)A.times[b0 + i] - chunk_t0;  // 0 <= o < CW*64
-          atomicOr((unsigned long long*)&s_tb[((int64_t)rr * CW + (o >> 6)) * A.U + (u - 1)],
-                   1ull << (o & 63));
-        }
-      }
-    }
-    __syncthreads();
-    if (tid < A.R) s_ev[tid] = s_ev_end[tid];
-    if (fin == all) continue;
-    const int nw = s_nw[r_idx];
-    if (nw == 0) continue;
-    const int64_t chunk_t0 = s_cur[r_idx];
-    if (s_skip[r_idx]) {
+
+    // ---- lane state
+    int32_t lds_slot[N];     // this lane's node-type bitmaps in word 0 of its segment
+    DilProg dp[NI];
+    int32_t span = 0;
+    uint64_t prv[MCH][NI];   // per class: node candidates of the previous word
+    int32_t r[MCH];          // per class: last reset, as an offset from org
+    uint32_t mem[MCH];
+    int32_t cnt[MCH], a_off[MCH], b_off[MCH];
+    uint32_t found = 0, fin = 0;
+    int64_t stop = 0, org = 0;
+    bool single = MCH == 1;
+    if (active) {
 #pragma unroll
-      for (int c = 0; c < MCH; ++c)
+      for (int j = 0; j < N; ++j)
+        lds_slot[j] = r_idx * CW * A.U + (A.ep_slot[e * N + j] - 1);
 #pragma unroll
-        for (int j = 0; j < N - 1; ++j) prv[c][j] = 0;
-    }
-    for (int wi = 0; wi < nw; ++wi) {
-      const int64_t t0 = chunk_t0 + (int64_t)wi * 64;
-      if (t0 > stop) {
-        fin = all;
-        break;
-      }
-      const uint64_t* row = s_tb + ((int64_t)r_idx * CW + wi) * A.U;
-      uint64_t E[N];
-#pragma unroll
-      for (int j = 0; j < N; ++j) E[j] = row[slot[j] - 1];
-      if (!single) {
-        // classes whose last reset lies more than Span before this word are
-        // identical for the rest of the stream: merge them
-        uint32_t stale = 0, acc = 0;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if (mem[c] && r[c] + span < t0) {
-            stale |= 1u << c;
-            acc |= mem[c];
-          }
-        if (__popc(stale) >= 2) {
-          const int lowest = __ffs((int)stale) - 1;
-#pragma unroll
-          for (int c = 0; c < MCH; ++c)
-            if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
-        }
-      }
-      uint32_t done = 0;  // classes that completed in this word (for merging)
-      int64_t done_at[MCH];
+      for (int j = 0; j < N - 1; ++j)
+        dp[j] = dil_prog((uint32_t)A.ep_lo[e * (N - 1) + j], (uint32_t)A.ep_hi[e * (N - 1) + j]);
+      span = A.ep_span[e];
+      stop = tau_hi + span;
+      org = tau_lo;
 #pragma unroll
       for (int c = 0; c < MCH; ++c) {
-        done_at[c] = -1;
-        if (c > 0 && single) continue;
-        if (!mem[c]) continue;
-        uint64_t keep = tick_range_mask(t0, r[c] + 1, stop);
-        uint64_t cur[N > 1 ? N - 1 : 1];
-        uint64_t last = word_chain<N>(E, keep, prv[c], cur, lo, hi);
-        while (last != 0) {
-          const int bit = __ffsll((unsigned long long)last) - 1;
-          const int64_t t = t0 + bit;
-          complete_members(mem[c], t);
-          r[c] = t;
-          done |= 1u << c;
-          done_at[c] = t;
-          keep = bit == 63 ? 0ull : (keep & ~((~0ull) >> (63 - bit)));
-          uint64_t zero[N > 1 ? N - 1 : 1];
+        const int k = (MCH == 1) ? k_lane : c;
+        r[c] = -(int32_t)prefix_hi<N>(A.ep_hi, e, k);
+        mem[c] = 1u << c;
+        cnt[c] = 0;
+        a_off[c] = 0;
+        b_off[c] = 0;
 #pragma unroll
-          for (int j = 0; j < N - 1; ++j) zero[j] = 0;
-          last = word_chain<N>(E, keep, zero, cur, lo, hi);
-        }
-#pragma unroll
-        for (int j = 0; j < N - 1; ++j) prv[c][j] = cur[j];
+        for (int j = 0; j < NI; ++j) prv[c][j] = 0;
       }
-      if (done) {
-        if (!single) {
-          // classes that last reset on the same tick are identical
+    } else {
+      fin = all;
+      single = true;
 #pragma unroll
+      for (int j = 0; j < N; ++j) lds_slot[j] = 0;
+#pragma unroll
+      for (int j = 0; j < NI; ++j) dp[j] = {1u, 0u};
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        r[c] = 0;
+        mem[c] = 0;
+        cnt[c] = a_off[c] = b_off[c] = 0;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) prv[c][j] = 0;
+      }
+    }
+
+    // completion of the machines of class c at tick t
+    auto complete_members = [&](uint32_t members, int64_t t) {
+      const uint32_t live = members & ~fin;
+  #pragma unroll
+      for (int k = 0; k < MCH; ++k) {
+        if ((live >> k) & 1u) {
+          if (t > tau_lo) {
+            if (!((found >> k) & 1u)) {
+              found |= 1u << k;
+              const int64_t dd = t - tau_lo;
+              a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+            }
+            if (t <= tau_hi) {
+              ++cnt[k];
+            } else {
+              b_off[k] = (int32_t)(t - tau_hi);
+              fin |= 1u << k;
+            }
+          }
+        }
+      }
+    };
+
+    // Chunks are event-driven: a segment's next chunk starts right after its
+    // last processed word, or at its next event when that lies 64 or more
+    // ticks later (no event in between, and every candidate is then older
+    // than any t_high <= 63, so the windows are simply emptied).  A chunk is at
+    // most CW words and ends at the word of its last event, so the work is
+    // bounded by the events, not the ticks.  The fill reads the events in
+    // batches of kPer per thread until a batch reaches past the chunk; the
+    // first event past it and the chunk's last word come out of LDS atomics.
+    for (;;) {
+      __syncthreads();  // previous chunk fully consumed; segment cursors final
+      if (tid == 0) {
+        s_more = 0;
+        s_reuse = 1;
+      }
+      __syncthreads();
+      if (tid < A.R) {
+        const int32_t ev = s_ev[tid];
+        const int32_t seg_end = s_seg_end[tid];
+        if (ev < seg_end) {
+          const int64_t next_t = A.times[ev];
+          const int64_t contiguous = s_cur[tid] + (int64_t)s_nw[tid] * 64;
+          const bool skip = next_t >= contiguous + 64;
+          s_cur[tid] = skip ? next_t : contiguous;
+          s_skip[tid] = skip ? 1 : 0;
+          s_more = 1;
+          if (s_built[tid] != ev) s_reuse = 0;
+        } else {
+          s_skip[tid] = 0;
+          s_nw[tid] = 0;
+        }
+      }
+      __syncthreads();
+      if (!s_more) break;
+      if (!s_reuse) {
+        for (int i = tid; i < A.R * CW * A.U; i += nthr) s_tb[i] = 0;
+        if (tid < A.R) {
+          s_end[tid] = s_seg_end[tid];
+          s_maxw[tid] = -1;
+        }
+        __syncthreads();
+        for (int rr = 0; rr < A.R; ++rr) {
+          const int32_t b0 = s_ev[rr];
+          const int32_t seg_end = s_seg_end[rr];
+          if (b0 >= seg_end) continue;
+          const int64_t chunk_t0 = s_cur[rr];
+          int32_t my_min = INT32_MAX, my_maxw = -1;
+          for (int32_t base = b0;; base += CE) {
+            // all loads of a batch are issued before any is used
+            int32_t tt[kPer];
+            uint32_t ty[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+              const int32_t i = base + k * nthr + tid;
+              tt[k] = i < seg_end ? A.times[i] : 0;
+              ty[k] = i < seg_end ? A.types[i] : 0u;
+            }
+            const int64_t batch_last = (int64_t)base + CE < seg_end ? (int64_t)base + CE - 1 : seg_end - 1;
+            const int64_t last_t = A.times[batch_last];
+            uint32_t u[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) u[k] = A.remap[ty[k]];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+              const int32_t i = base + k * nthr + tid;
+              if (i < seg_end) {
+                const int64_t w = ((int64_t)tt[k] - chunk_t0) >> 6;  // >= 0
+                if (w < CW) {
+                  my_maxw = (int32_t)w;  // events are sorted: the last one wins
+                  if (u[k])
+                    atomicOr((unsigned long long*)&s_tb[((int64_t)rr * CW + w) * A.U + (u[k] - 1)],
+                             1ull << ((tt[k] - chunk_t0) & 63));
+                } else if (i < my_min) {
+                  my_min = i;
+                }
+              }
+            }
+            if (batch_last == seg_end - 1 || ((last_t - chunk_t0) >> 6) >= CW) break;
+          }
+          if (my_min != INT32_MAX) atomicMin(&s_end[rr], my_min);
+          if (my_maxw >= 0) atomicMax(&s_maxw[rr], my_maxw);
+        }
+        __syncthreads();
+        if (tid < A.R) {
+          // the bitmaps now hold this chunk; a later episode group reuses them
+          s_built[tid] = s_ev[tid] < s_seg_end[tid] ? s_ev[tid] : -1;
+        }
+      }
+      if (tid < A.R && s_ev[tid] < s_seg_end[tid]) {
+        // a reused chunk has the same extent as when it was built
+        s_nw[tid] = s_maxw[tid] + 1;
+        s_ev[tid] = s_end[tid];
+      }
+      __syncthreads();
+      const int nw = fin == all ? 0 : s_nw[r_idx];
+      int32_t stop_rel = -1;
+      if (nw > 0) {
+        // move the time origin to this chunk's first tick
+        const int64_t chunk_t0 = s_cur[r_idx];
+        const int64_t delta = chunk_t0 - org;
+  #pragma unroll
+        for (int c = 0; c < MCH; ++c) {
+          const int64_t v = (int64_t)r[c] - delta;
+          r[c] = (int32_t)(v < -kFar ? -kFar : v);
+        }
+        org = chunk_t0;
+        const int64_t stop_d = stop - org;
+        stop_rel = (int32_t)(stop_d > kFar ? kFar : (stop_d < -1 ? -1 : stop_d));
+        if (s_skip[r_idx]) {
+  #pragma unroll
           for (int c = 0; c < MCH; ++c)
-#pragma unroll
+  #pragma unroll
+            for (int j = 0; j < NI; ++j) prv[c][j] = 0;
+        }
+      }
+      int wi = 0;
+      // Words of a lane that still has several machine classes (the first words
+      // of a segment, and after a completion while classes differ).
+      for (; MCH > 1 && wi < nw && !single; ++wi) {
+        const int32_t wb = wi * 64;
+        if (wb > stop_rel) {
+          fin = all;
+          break;
+        }
+        const int32_t row = wi * A.U;
+        uint64_t E[N];
+  #pragma unroll
+        for (int j = 0; j < N; ++j) E[j] = s_tb[lds_slot[j] + row];
+        const int32_t to = stop_rel - wb;  // >= 0
+        const uint64_t keep_hi = to >= 63 ? ~0ull : ((~0ull) >> (63 - to));
+        {
+          // classes whose last reset lies more than Span before this word are
+          // identical for the rest of the stream: merge them
+          uint32_t stale = 0, acc = 0;
+  #pragma unroll
+          for (int c = 0; c < MCH; ++c)
+            if (mem[c] && r[c] + span < wb) {
+              stale |= 1u << c;
+              acc |= mem[c];
+            }
+          if (__popc(stale) >= 2) {
+            const int lowest = __ffs((int)stale) - 1;
+  #pragma unroll
+            for (int c = 0; c < MCH; ++c)
+              if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+          }
+        }
+        uint32_t done = 0;  // classes that completed in this word (for merging)
+  #pragma unroll
+        for (int c = 0; c < MCH; ++c) {
+          if (!mem[c]) continue;
+          const int32_t from = r[c] + 1 - wb;
+          const uint64_t keep_lo = from <= 0 ? ~0ull : (from >= 64 ? 0ull : ((~0ull) << from));
+          uint64_t cur[NI];
+          uint64_t last = word_chain<N>(E, keep_lo, prv[c], cur, dp, K) & keep_hi;
+          while (last != 0) {
+            const int bit = __ffsll((unsigned long long)last) - 1;
+            complete_members(mem[c], org + wb + bit);
+            r[c] = wb + bit;
+            done |= 1u << c;
+            const uint64_t after = bit == 63 ? 0ull : ((~0ull) << (bit + 1));
+            uint64_t zero[NI];
+  #pragma unroll
+            for (int j = 0; j < NI; ++j) zero[j] = 0;
+            last = word_chain<N>(E, after, zero, cur, dp, K) & keep_hi;
+          }
+  #pragma unroll
+          for (int j = 0; j < NI; ++j) prv[c][j] = cur[j];
+        }
+        if (done) {
+          // classes that last reset on the same tick are identical
+  #pragma unroll
+          for (int c = 0; c < MCH; ++c)
+  #pragma unroll
             for (int c2 = 0; c2 < c; ++c2)
-              if (mem[c] && mem[c2] && ((done >> c) & 1u) && ((done >> c2) & 1u) &&
-                  done_at[c] == done_at[c2]) {
+              if (mem[c] && mem[c2] && ((done >> c) & 1u) && ((done >> c2) & 1u) && r[c] == r[c2]) {
                 mem[c2] |= mem[c];
                 mem[c] = 0u;
               }
+  #pragma unroll
+          for (int c = 0; c < MCH; ++c)
+            if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
+          if (fin == all) break;
         }
-#pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
-        if (fin == all) break;
-      }
-      if (!single) {
         uint32_t alive = 0;
-#pragma unroll
+  #pragma unroll
         for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
         if (__popc(alive) == 1) {
-#pragma unroll
+  #pragma unroll
           for (int c = 1; c < MCH; ++c)
             if ((alive >> c) & 1u) {
-#pragma unroll
-              for (int j = 0; j < N - 1; ++j) prv[0][j] = prv[c][j];
+  #pragma unroll
+              for (int j = 0; j < NI; ++j) prv[0][j] = prv[c][j];
               r[0] = r[c];
               mem[0] = mem[c];
-              mem[c] = 0u;
             }
+          // the other classes are empty from here on
+  #pragma unroll
+          for (int c = 1; c < MCH; ++c) {
+            mem[c] = 0u;
+            r[c] = 0;
+  #pragma unroll
+            for (int j = 0; j < NI; ++j) prv[c][j] = 0;
+          }
           single = true;
         }
       }
-    }
-  }
-
-  if (active) {
-    const int64_t pe = A.ts.idx(e, p);
-    if (MCH == 1) {
-      Tuple tu;
-      tu.a = a_off[0];
-      tu.c = cnt[0];
-      tu.b = b_off[0];
-      tu.pad = 0;
-      *A.ts.at(e, p, k_lane) = tu;
-      if (k_lane == 0) {
-        A.ts.nmap[pe] = A.n_machines;
-        A.ts.nslots[pe] = A.n_machines;
-      }
-    } else {
-      int d = 0;
-#pragma unroll
-      for (int c = 0; c < MCH; ++c) {
-        bool dup = false;
-#pragma unroll
-        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
-        if (!dup) {
-          Tuple tu;
-          tu.a = a_off[c];
-          tu.c = cnt[c];
-          tu.b = b_off[c];
-          tu.pad = 0;
-          *A.ts.at(e, p, d) = tu;
-          ++d;
+      // Words of a lane with one class: the lean loop.  Ticks past stop are
+      // masked out of the completions (keep_hi), so the loop needs no exit test;
+      // a lane whose machines have all finished steps on without effect.
+      auto single_words = [&](auto kc) {
+        constexpr int KC = decltype(kc)::value;
+        uint64_t pv[NI];
+  #pragma unroll
+        for (int j = 0; j < NI; ++j) pv[j] = prv[0][j];
+        int32_t r0 = r[0];
+        const uint32_t m0 = mem[0];
+        for (; wi < nw; ++wi) {
+          const int32_t wb = wi * 64;
+          const int32_t row = wi * A.U;
+          uint64_t E[N];
+  #pragma unroll
+          for (int j = 0; j < N; ++j) E[j] = s_tb[lds_slot[j] + row];
+          const int32_t from = r0 + 1 - wb;
+          const uint64_t keep_lo = from <= 0 ? ~0ull : (from >= 64 ? 0ull : ((~0ull) << from));
+          const int32_t to = stop_rel - wb;
+          const uint64_t keep_hi = to >= 63 ? ~0ull : (to < 0 ? 0ull : ((~0ull) >> (63 - to)));
+          uint64_t cur[NI];
+          uint64_t last = word_chain_k<N, KC>(E, keep_lo, pv, cur, dp) & keep_hi;
+          while (last != 0) {
+            const int bit = __ffsll((unsigned long long)last) - 1;
+            complete_members(m0, org + wb + bit);
+            r0 = wb + bit;
+            const uint64_t after = bit == 63 ? 0ull : ((~0ull) << (bit + 1));
+            uint64_t zero[NI];
+  #pragma unroll
+            for (int j = 0; j < NI; ++j) zero[j] = 0;
+            last = word_chain_k<N, KC>(E, after, zero, cur, dp) & keep_hi;
+          }
+  #pragma unroll
+          for (int j = 0; j < NI; ++j) pv[j] = cur[j];
         }
+  #pragma unroll
+        for (int j = 0; j < NI; ++j) prv[0][j] = pv[j];
+        r[0] = r0;
+      };
+      if (wi < nw && fin != all) {
+        if (K <= 1)
+          single_words(std::integral_constant<int, 1>());
+        else if (K == 2)
+          single_words(std::integral_constant<int, 2>());
+        else if (K == 3)
+          single_words(std::integral_constant<int, 3>());
+        else if (K == 4)
+          single_words(std::integral_constant<int, 4>());
+        else
+          single_words(std::integral_constant<int, 6>());
       }
-      A.ts.nmap[pe] = d;
-      A.ts.nslots[pe] = d;
+      if (nw > 0 && stop_rel < nw * 64) fin = all;  // the lane passed its stop tick
     }
+
+    if (active) {
+      const int64_t pe = A.ts.idx(e, p);
+      if (MCH == 1) {
+        Tuple tu;
+        tu.a = a_off[0];
+        tu.c = cnt[0];
+        tu.b = b_off[0];
+        tu.pad = 0;
+        *A.ts.at(e, p, k_lane) = tu;
+        if (k_lane == 0) {
+          A.ts.nmap[pe] = A.n_machines;
+          A.ts.nslots[pe] = A.n_machines;
+        }
+      } else {
+        int d = 0;
+  #pragma unroll
+        for (int c = 0; c < MCH; ++c) {
+          bool dup = false;
+  #pragma unroll
+          for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
+          if (!dup) {
+            Tuple tu;
+            tu.a = a_off[c];
+            tu.c = cnt[c];
+            tu.b = b_off[c];
+            tu.pad = 0;
+            *A.ts.at(e, p, d) = tu;
+            ++d;
+          }
+        }
+        A.ts.nmap[pe] = d;
+        A.ts.nslots[pe] = d;
+      }
+    }
+
   }
 }
 
@@ -1406,6 +1613,8 @@ struct Launchers {
   hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
   // resident workgroups per CU of a Map kernel for a block size and LDS size
   hipError_t (*occupancy)(int win, bool all_machines, int block, size_t lds, int* blocks_per_cu);
+  // the same for the tick Map kernel
+  hipError_t (*occupancy_ticks)(bool all_machines, int block, size_t lds, int* blocks_per_cu);
 };
 
 }  // namespace epk

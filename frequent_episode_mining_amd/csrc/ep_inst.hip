@@ -114,7 +114,14 @@ hipError_t occupancy(int win, bool all_machines, int block, size_t lds, int* out
   }
 }
 
-const Launchers kLaunchers = {launch_scan, launch_bits, launch_ticks, launch_closure, launch_finish, occupancy};
+hipError_t occupancy_ticks(bool all_machines, int block, size_t lds, int* out) {
+  if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
+  return all_machines ? occ(map_ticks_kernel<EP_N, kClassMch>, block, lds, out)
+                      : occ(map_ticks_kernel<EP_N, 1>, block, lds, out);
+}
+
+const Launchers kLaunchers = {launch_scan,   launch_bits, launch_ticks, launch_closure,
+                              launch_finish, occupancy,   occupancy_ticks};
 
 }  // namespace
 
