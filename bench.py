@@ -58,10 +58,10 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per Map launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "map_kernel_%s_traffic.md" % workload)
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the kernel from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -73,7 +73,9 @@ def stored_traffic(workload: str):
 
 
 def cpu_baseline(wl, gpu_counts, target_s: float):
-    """The oracle, as it stands, on a bounded sample of the workload's episodes."""
+    """The oracle, as it stands, on a bounded sample of the workload's episodes:
+    as many episodes (evenly spaced) as fit the time budget, and when all of
+    them fit, the whole workload repeated until the budget is spent."""
     import oracle
     threads = min(os.cpu_count() or 1, 16)
     S = wl.n_episodes
@@ -82,15 +84,20 @@ def cpu_baseline(wl, gpu_counts, target_s: float):
                                   wl.t_high[:probe], n_threads=threads)
     per_ep = dt / probe
     m = int(min(S, max(probe, target_s / max(per_ep, 1e-9))))
-    # spread the sample over the whole episode list
     idx = np.unique(np.linspace(0, S - 1, m).astype(np.int64))
-    want, dt, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
-                                        wl.t_high[idx], n_threads=threads)
-    ok = bool(np.array_equal(gpu_counts[idx], want))
-    value = wl.n_events * idx.size / dt
+    reps, total, used, ok = 0, 0.0, threads, True
+    while True:
+        want, dt, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
+                                            wl.t_high[idx], n_threads=threads)
+        ok = ok and bool(np.array_equal(gpu_counts[idx], want))
+        reps += 1
+        total += dt
+        if total >= 0.9 * target_s or reps >= 1000:
+            break
+    value = wl.n_events * idx.size * reps / total
     return {"value": value, "unit": "episode-events/s", "cores": int(used), "kind": "oracle",
-            "sample": "%d of %d episodes (evenly spaced) over all %d events, %.2f s"
-                      % (idx.size, S, wl.n_events, dt)}, ok, idx.size
+            "sample": "%d of %d episodes (evenly spaced) over all %d events, %d pass(es), %.2f s"
+                      % (idx.size, S, wl.n_events, reps, total)}, ok, idx.size
 
 
 def calibrate_copy(nbytes: int, reps: int):
@@ -178,24 +185,49 @@ def main():
     ms_per_step = max(gpu_ms, wall_ms)
     counts = out.cpu().numpy()
     log("host enqueue %.4f ms per call" % ((we - w0) * 1000.0 / args.steps))
-    log("step %.4f ms (gpu events %.4f, wall %.4f); phases per call: map %.4f closure %.4f "
-        "concat %.4f other %.4f ms" % (ms_per_step, gpu_ms, wall_ms, prof["map_ms"] / prof["calls"],
-                                       prof["closure_ms"] / prof["calls"],
-                                       prof["concat_ms"] / prof["calls"], prof["other_ms"] / prof["calls"]))
+    log("step %.4f ms (gpu events %.4f, wall %.4f); phases per call: map %.4f (filter %.4f, "
+        "ticks %.4f, positions %.4f) closure %.4f concat %.4f other %.4f ms"
+        % (ms_per_step, gpu_ms, wall_ms, prof["map_ms"] / prof["calls"],
+           prof["map_filter_ms"] / prof["calls"], prof["map_ticks_ms"] / prof["calls"],
+           prof["map_positions_ms"] / prof["calls"],
+           prof["closure_ms"] / prof["calls"], prof["concat_ms"] / prof["calls"],
+           prof["other_ms"] / prof["calls"]))
 
     n, S = wl.n_events, wl.n_episodes
     value = n * S / (ms_per_step / 1000.0)
 
-    map_s = prof["map_ms"] / prof["calls"] / 1000.0
+    # the dominant Map-step kernel of this workload, timed alone by the
+    # library's events on the stream it runs on
+    per = {k: prof[k] / prof["calls"] for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
+    if st["kernels"] & 1:
+        pos_name = "map_list_kernel" if st["kernels"] & 4 else "map_bits_kernel"
+    else:
+        pos_name = "map_scan_kernel"
+    names = {"map_filter_ms": "filter_kernel", "map_ticks_ms": "map_ticks_kernel",
+             "map_positions_ms": pos_name}
+    top = max(per, key=per.get)
+    kernel, kernel_ms = names[top], per[top]
+    map_s = kernel_ms / 1000.0
     rel = relevant_pairs(wl)
-    achieved = OPS_PER_RELEVANT_PAIR * rel / map_s / 1e12
-    traffic = stored_traffic(wl.name)
-    roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
-                "frac": achieved / ALU_PEAK_TOPS, "traffic": traffic,
-                "kernel": "map_kernel", "kernel_ms": map_s * 1000.0,
-                "work": "%d int32 ops x %d (episode, relevant event) pairs"
-                        % (OPS_PER_RELEVANT_PAIR, rel),
-                "hbm_one_pass_frac": 6.0 * n / map_s / 1e9 / HBM_PEAK_GBS}
+    traffic = stored_traffic(wl.name, kernel)
+    if kernel == "filter_kernel":
+        # one read of the stream, one {time, levels} entry written per
+        # (episode, relevant event) pair
+        moved = 6.0 * n + 8.0 * rel
+        achieved = moved / map_s / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                    "work": "6 B x %d events read + 8 B x %d entries written" % (n, rel)}
+    else:
+        achieved = OPS_PER_RELEVANT_PAIR * rel / map_s / 1e12
+        roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
+                    "frac": achieved / ALU_PEAK_TOPS, "traffic": traffic,
+                    "work": "%d int32 ops x %d (episode, relevant event) pairs"
+                            % (OPS_PER_RELEVANT_PAIR, rel)}
+    roofline.update({"kernel": kernel, "kernel_ms": kernel_ms,
+                     "map_kernels_ms": {names[k]: v for k, v in per.items()},
+                     "hbm_one_pass_frac": 6.0 * n / (prof["map_ms"] / prof["calls"] / 1000.0)
+                                          / 1e9 / HBM_PEAK_GBS})
 
     cpu = None
     parity = None

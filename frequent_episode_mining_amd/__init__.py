@@ -36,7 +36,7 @@ class EpEpisodes(ctypes.Structure):
 
 class EpStats(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
-                ("max_runs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_runs", ctypes.c_int32), ("kernels", ctypes.c_int32),
                 ("repairs", ctypes.c_int64), ("fallbacks", ctypes.c_int64)]
 
 
@@ -49,7 +49,8 @@ class EpOptions(ctypes.Structure):
 class EpProfile(ctypes.Structure):
     _fields_ = [("map_ms", ctypes.c_double), ("closure_ms", ctypes.c_double),
                 ("concat_ms", ctypes.c_double), ("other_ms", ctypes.c_double),
-                ("calls", ctypes.c_int64)]
+                ("calls", ctypes.c_int64), ("map_ticks_ms", ctypes.c_double),
+                ("map_positions_ms", ctypes.c_double), ("map_filter_ms", ctypes.c_double)]
 
 
 class EpError(RuntimeError):
@@ -176,7 +177,8 @@ def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str
     _check(status)
     if stats:
         return out, {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,
-                     "max_runs": st.max_runs, "repairs": st.repairs, "fallbacks": st.fallbacks}
+                     "max_runs": st.max_runs, "kernels": st.kernels, "repairs": st.repairs,
+                     "fallbacks": st.fallbacks}
     return out
 
 
@@ -201,7 +203,8 @@ def profile_end() -> dict:
     p = EpProfile()
     _check(load_library().ep_profile_end(ctypes.byref(p)))
     return {"map_ms": p.map_ms, "closure_ms": p.closure_ms, "concat_ms": p.concat_ms,
-            "other_ms": p.other_ms, "calls": p.calls}
+            "other_ms": p.other_ms, "calls": p.calls, "map_ticks_ms": p.map_ticks_ms,
+            "map_positions_ms": p.map_positions_ms, "map_filter_ms": p.map_filter_ms}
 
 
 def segment_cut(t_min: int, t_max: int, n_segments: int, p: int) -> int:

@@ -62,15 +62,17 @@ const Launchers* launchers_for(int N) {
 
 // ------------------------------------------------------------ small kernels
 
-// Per-call set-up in one launch: the type -> node-slot map, the equal-time
-// cuts with each segment's event range, and the flag and counter words.
-//   remap  : slot of event type y = 1 + its rank among the sorted distinct node
-//            types, 0 for a type on no node (binary search of `distinct`).
+// Per-call set-up in one launch: the equal-time cuts with each segment's event
+// range, and the flag and counter words.
 //   cuts   : tau_p = t_min - 1 + floor(p (t_max - t_min + 1) / P) for p = 0..P
 //            ("Design of MapConcatenate": segment p holds (tau_p, tau_{p+1}]);
 //            segment p needs the events in (tau_p - maxSpan, tau_{p+1} + maxSpan]
 //            since its machines start up to maxSpan before the left cut and
 //            look up to maxSpan past the right cut for the exit b.
+// With few segments each range end is one wave's 64-ary search of the sorted
+// times (a handful of dependent loads instead of a binary search's log2 n);
+// with many, the searches alone fill the GPU and each is one thread's binary
+// search (fewer loads in all).
 struct SetupArgs {
   const int32_t* times;
   int64_t n;
@@ -79,43 +81,83 @@ struct SetupArgs {
   int64_t* tau;
   int32_t* beg;
   int32_t* end;
-  const uint16_t* distinct;
-  int32_t U;
-  uint8_t* remap;  // null: not needed
   int32_t* flags;  // [S + 1]
   int64_t S;
   unsigned long long* counters;  // [4]
+  int32_t wave_search;  // range ends by one wave each (small P) or one thread each
 };
+
+__device__ inline int64_t cut_of(int64_t t_min, int64_t t_max, int64_t p, int64_t P) {
+  return t_min - 1 + (p * (t_max - t_min + 1)) / P;
+}
+
+// First index i in [0, n) with times[i] > v, n if none; every lane of the wave
+// calls it with the same arguments and gets the answer.  Invariant: the
+// answer lies in [lo, hi], times[lo-1] <= v and times[hi] > v (or hi = n).
+__device__ int64_t wave_upper_bound(const int32_t* times, int64_t n, int64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t lo = 0, hi = n;
+  while (hi - lo > kWave) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    int64_t idx = lo + (int64_t)(lane + 1) * step - 1;
+    idx = idx < hi - 1 ? idx : hi - 1;
+    const uint64_t gt = __ballot((int64_t)times[idx] > v);
+    if (gt == 0) {
+      lo = hi;  // lane 63 probed hi - 1
+    } else {
+      const int f = __ffsll((unsigned long long)gt) - 1;
+      const int64_t idx_f = lo + (int64_t)(f + 1) * step - 1;
+      const int64_t new_lo = f == 0 ? lo : lo + (int64_t)f * step;
+      hi = idx_f < hi - 1 ? idx_f : hi - 1;
+      lo = new_lo;
+    }
+  }
+  const int64_t idx = lo + lane;
+  const bool in = idx < hi;  // lanes past the range read times[0] (n >= 1) and ignore it
+  const uint64_t gt = __ballot(in && (int64_t)times[in ? idx : 0] > v);
+  return gt ? lo + (__ffsll((unsigned long long)gt) - 1) : hi;
+}
+
+constexpr int32_t kWaveSearchMaxP = 4096;
+
+__host__ __device__ inline int64_t setup_search_threads(int32_t P, bool wave) {
+  return (int64_t)2 * P * (wave ? kWave : 1);
+}
 
 __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
   int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  const int64_t n_remap = A.remap ? 65536 : 0;
-  if (i < n_remap) {
-    const int32_t y = (int32_t)i;
-    int32_t lo = 0, hi = A.U;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi) >> 1;
-      if ((int32_t)A.distinct[mid] < y)
-        lo = mid + 1;
-      else
-        hi = mid;
-    }
-    A.remap[y] = (lo < A.U && (int32_t)A.distinct[lo] == y) ? (uint8_t)(lo + 1) : (uint8_t)0;
-    return;
-  }
-  i -= n_remap;
-  if (i <= A.P) {
-    const int64_t p = i;
+  const int64_t n_search = setup_search_threads(A.P, A.wave_search != 0);
+  if (i < n_search && !A.wave_search) {
+    const int64_t p = i >> 1;
     const int64_t t_min = A.times[0];
     const int64_t t_max = A.times[A.n - 1];
-    const int64_t width = t_max - t_min + 1;
-    const int64_t cut = t_min - 1 + (p * width) / A.P;
-    A.tau[p] = cut;
-    if (p < A.P) {
-      const int64_t next = t_min - 1 + ((p + 1) * width) / A.P;
-      A.beg[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut - A.max_span);
-      A.end[p] = (int32_t)upper_bound_time(A.times, 0, A.n, next + A.max_span);
+    if (i & 1)
+      A.end[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p + 1, A.P) + A.max_span);
+    else
+      A.beg[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p, A.P) - A.max_span);
+    return;
+  }
+  if (i < n_search) {
+    // wave w: w even -> beg[w / 2], w odd -> end[w / 2] (whole waves: n_search is a
+    // multiple of the wave size)
+    const int64_t w = i / kWave;
+    const int64_t p = w >> 1;
+    const int64_t t_min = A.times[0];
+    const int64_t t_max = A.times[A.n - 1];
+    const int64_t v = (w & 1) ? cut_of(t_min, t_max, p + 1, A.P) + A.max_span
+                              : cut_of(t_min, t_max, p, A.P) - A.max_span;
+    const int64_t r = wave_upper_bound(A.times, A.n, v);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      if (w & 1)
+        A.end[p] = (int32_t)r;
+      else
+        A.beg[p] = (int32_t)r;
     }
+    return;
+  }
+  i -= n_search;
+  if (i <= A.P) {
+    A.tau[i] = cut_of(A.times[0], A.times[A.n - 1], i, A.P);
     return;
   }
   i -= (int64_t)A.P + 1;
@@ -125,6 +167,181 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
   }
   i -= A.S + 1;
   if (i < 4) A.counters[i] = 0ull;
+}
+
+// ------------------------------------------------------------- event filter
+
+// One pass over the stream for the list Map kernel.  Block b holds events
+// [b * kListBlock, (b + 1) * kListBlock); each event gets its node-type slot
+// and the set of episodes with that type, and for each episode its events are
+// written in order to the block's region as {time, node levels}: episode e's
+// entries start at list_off[b][e] and number list_cnt[b][e].  The region holds
+// kListBlock * max_share entries (max_share: most episodes one type is on), so
+// blocks need nothing from each other.  A thread takes 16 consecutive events;
+// its per-episode counts are packed two to a 32-bit word (16-bit fields; a
+// block holds at most 4096), so one scan serves two episodes.
+constexpr int kFilterPer = kListBlock / kBlock;  // 16
+constexpr int kMaxListEpisodes = 32;
+constexpr double kMaxListBytes = 32.0 * (1ull << 30);  // list scratch bound of the list path
+
+struct FilterArgs {
+  const int32_t* times;
+  const uint16_t* types;
+  int64_t n;
+  const uint64_t* type_seen;     // [1024] the call's node types as a 65,536-bit set
+  const uint8_t* type_rank;      // [1024] set bits before each 64-bit word
+  const uint32_t* slot_eps;      // [256] episodes with slot u's type (bit e); slot 0: none
+  const uint16_t* slot_levels;   // [256 * S] node levels of episode e with slot u's type
+  int32_t S;                     // <= kMaxListEpisodes
+  int32_t max_share;
+  int2* lists;
+  int32_t* list_off;             // [blocks * S]
+  int32_t* list_cnt;             // [blocks * S]
+};
+
+// One workgroup loops over blocks b = blockIdx.x, + gridDim.x, ...: the LDS
+// tables are loaded once, and the next block's events are loaded before the
+// current block is classified and written.  G packed count words serve up to
+// 4 G episodes.
+template <int G>
+__global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
+  constexpr int kE = 4 * G;  // episodes this instance serves at most
+  __shared__ uint64_t s_seen[1024];
+  __shared__ uint8_t s_rank[1024];
+  __shared__ uint32_t s_eps[256];
+  __shared__ uint16_t s_lv[256 * kE];
+  __shared__ uint16_t s_pre[kE][kBlock];  // thread's next rank per episode
+  __shared__ uint32_t s_wsum[kBlock / kWave][2 * G];
+  __shared__ int32_t s_off[kE];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int S = A.S;
+  for (int i = tid; i < 1024; i += kBlock) {
+    s_seen[i] = A.type_seen[i];
+    s_rank[i] = A.type_rank[i];
+  }
+  for (int i = tid; i < 256; i += kBlock) s_eps[i] = A.slot_eps[i];
+  for (int i = tid; i < 256 * S; i += kBlock) s_lv[(i / S) * kE + i % S] = A.slot_levels[i];
+  const bool vec = ((uintptr_t)A.times & 15) == 0 && ((uintptr_t)A.types & 15) == 0;
+  const int64_t n_blocks = (A.n + kListBlock - 1) / kListBlock;
+
+  int32_t t[kFilterPer], tn[kFilterPer];
+  uint32_t y[kFilterPer], yn[kFilterPer];
+  auto load = [&](int64_t b, int32_t* tt, uint32_t* yy) {
+    const int64_t first = b * kListBlock + (int64_t)tid * kFilterPer;
+    if (vec && first + kFilterPer <= A.n) {
+      const int4* tv = (const int4*)(A.times + first);
+      const uint4* yv = (const uint4*)(A.types + first);
+#pragma unroll
+      for (int q = 0; q < kFilterPer / 4; ++q) {
+        const int4 v = tv[q];
+        tt[4 * q] = v.x;
+        tt[4 * q + 1] = v.y;
+        tt[4 * q + 2] = v.z;
+        tt[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int q = 0; q < kFilterPer / 8; ++q) {
+        const uint4 v = yv[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          yy[8 * q + 2 * h] = w[h] & 0xffffu;
+          yy[8 * q + 2 * h + 1] = w[h] >> 16;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFilterPer; ++k) {
+        const bool in = first + k < A.n;
+        tt[k] = in ? A.times[first + k] : 0;
+        yy[k] = in ? A.types[first + k] : 0u;
+      }
+    }
+  };
+  int64_t b = blockIdx.x;
+  if (b < n_blocks) load(b, tn, yn);
+  __syncthreads();  // tables in LDS
+
+  for (; b < n_blocks; b += gridDim.x) {
+    const int64_t first = b * kListBlock + (int64_t)tid * kFilterPer;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      t[k] = tn[k];
+      y[k] = yn[k];
+    }
+    if (b + gridDim.x < n_blocks) load(b + gridDim.x, tn, yn);  // in flight meanwhile
+
+    uint32_t sl[kFilterPer], ep[kFilterPer];
+    uint32_t c[2 * G];  // packed counts, two 16-bit fields per word
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) c[g] = 0;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      sl[k] = first + k < A.n ? type_slot(s_seen, s_rank, y[k]) : 0u;
+      ep[k] = s_eps[sl[k]];
+#pragma unroll
+      for (int g = 0; g < 2 * G; ++g) c[g] += ((ep[k] >> (2 * g)) & 1u) | (((ep[k] >> (2 * g + 1)) & 1u) << 16);
+    }
+    // block-wide exclusive scan of the packed counts: wave scan, then waves
+    uint32_t incl[2 * G];
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) {
+      uint32_t v = c[g];
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
+      }
+      incl[g] = v;
+      if (lane == kWave - 1) s_wsum[wave][g] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) {
+      uint32_t before = 0;
+#pragma unroll
+      for (int w = 0; w < kBlock / kWave; ++w) before += w < wave ? s_wsum[w][g] : 0u;
+      const uint32_t excl = before + incl[g] - c[g];
+      if (2 * g < S) s_pre[2 * g][tid] = (uint16_t)(excl & 0xffffu);
+      if (2 * g + 1 < S) s_pre[2 * g + 1][tid] = (uint16_t)(excl >> 16);
+    }
+    if (tid == 0) {
+      int32_t off = 0;
+#pragma unroll
+      for (int g = 0; g < 2 * G; ++g) {
+        uint32_t all = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / kWave; ++w) all += s_wsum[w][g];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * g + h;
+          if (e < S) {
+            const int32_t cnt = (int32_t)((all >> (16 * h)) & 0xffffu);
+            s_off[e] = off;
+            A.list_off[b * S + e] = off;
+            A.list_cnt[b * S + e] = cnt;
+            off += cnt;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      uint32_t m = ep[k];
+      while (m) {
+        const int e = __ffs((int)m) - 1;
+        m &= m - 1;
+        const uint16_t r = s_pre[e][tid];
+        s_pre[e][tid] = (uint16_t)(r + 1);
+        region[s_off[e] + r] = make_int2(t[k], (int32_t)s_lv[sl[k] * kE + e]);
+      }
+    }
+    __syncthreads();  // s_wsum, s_pre and s_off are rewritten by the next block
+  }
 }
 
 // ------------------------------------------------------------- Concatenate
@@ -198,7 +415,7 @@ __global__ __launch_bounds__(kBlock) void concat_tree_kernel(TupleStore ts, int3
 }
 
 inline int64_t setup_items(const SetupArgs& A) {
-  return (A.remap ? 65536 : 0) + (int64_t)A.P + 1 + A.S + 1 + 4;
+  return setup_search_threads(A.P, A.wave_search != 0) + (int64_t)A.P + 1 + A.S + 1 + 4;
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n, int64_t v) {
@@ -326,8 +543,11 @@ int scratch_release(int dev, ScratchBlock* b, hipStream_t stream) {
 // Profiling session: per counting call, events around its phases.  Events
 // come from a pool that lives as long as the process, so recording adds no
 // event creation to the timed calls once the pool is warm.
+constexpr int kProfEvents = 7;
 struct ProfRecord {
-  hipEvent_t ev[5];  // start, before Map, after Map, after closure, after Concatenate
+  // start, before Map (the filter), before the tick Map kernel, after it,
+  // after Map, after closure, after Concatenate
+  hipEvent_t ev[kProfEvents];
   hipEvent_t end;
 };
 std::mutex g_prof_mu;
@@ -350,7 +570,7 @@ hipEvent_t pooled_event() {
 int prof_record_start(ProfRecord* r, hipStream_t s) {
   {
     std::lock_guard<std::mutex> lock(g_prof_mu);
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < kProfEvents; ++i)
       if (!(r->ev[i] = pooled_event())) return EP_ERR_HIP;
     if (!(r->end = pooled_event())) return EP_ERR_HIP;
   }
@@ -528,6 +748,7 @@ struct Launch {
   int CW;          // tick kernel: 64-tick words per segment per chunk
   size_t lds_ticks;
   int split;       // 0: per-segment choice between tick and position kernels; 1: ticks; 2: positions
+  bool list;       // sparse segments through the filter + list Map kernels (else the position kernel)
   int slots;
   int n_machines;
 };
@@ -603,6 +824,26 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     return rank_base[y >> 6] + (uint32_t)__builtin_popcountll(below) + 1;
   };
 
+  // the list path's tables: per node-type slot, the episodes with that type
+  // (bit e) and, per (slot, episode), the node levels with it; max_share is
+  // the most episodes one type is on (the filter's per-block region size)
+  uint32_t slot_eps[256];
+  uint16_t slot_levels[256 * kMaxListEpisodes];
+  int max_share = 1;
+  if (S <= kMaxListEpisodes && U <= 255) {
+    memset(slot_eps, 0, sizeof(slot_eps));
+    memset(slot_levels, 0, sizeof(uint16_t) * 256 * S);
+    for (int64_t e = 0; e < S; ++e)
+      for (int j = 0; j < N; ++j) {
+        const uint32_t u = slot_of(episodes.types[e * N + j]);
+        slot_eps[u] |= 1u << e;
+        slot_levels[u * S + e] |= (uint16_t)(1u << j);
+      }
+    for (int u = 0; u < 256; ++u) max_share = std::max(max_share, __builtin_popcount(slot_eps[u]));
+  }
+  const int64_t n_lblocks = (n_events + kListBlock - 1) / kListBlock;
+  const double list_bytes = (double)n_lblocks * kListBlock * max_share * sizeof(int2);
+
   int dev = 0;
   EP_HIP(hipGetDevice(&dev));
   if (n_events == 0) {
@@ -645,7 +886,16 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     // one lane per (segment, episode) holding every machine, unless that
     // leaves the GPU with too few lanes for a fixed segment count
     const int64_t target = (int64_t)info->cu_count * lanes_per_cu_est;
-    L.all_mach = L.n_machines > 1 && N <= kMaxClassNodes && S * (int64_t)P * 4 >= target;
+    L.split = 0;
+    if (const char* sp = getenv("EP_SPLIT")) {
+      if (!strcmp(sp, "ticks")) L.split = 1;
+      if (!strcmp(sp, "positions")) L.split = 2;
+    }
+    // few episodes: sparse segments read the filter kernel's per-episode lists
+    // (one lane per (segment, episode) walks only its episode's events)
+    L.list = S <= kMaxListEpisodes && L.split != 1 && list_bytes <= kMaxListBytes &&
+             !getenv("EP_NO_LIST");
+    L.all_mach = L.n_machines > 1 && N <= kMaxClassNodes && (L.list || S * (int64_t)P * 4 >= target);
     const char* lanes_env = getenv("EP_LANES");
     if (lanes_env && N <= kMaxClassNodes && L.n_machines > 1)
       L.all_mach = strcmp(lanes_env, "machine") != 0;
@@ -654,26 +904,25 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     L.R = (L.G == S) ? std::max(1, L.block / (L.G * L.M)) : 1;
     L.R = (int)std::min<int64_t>(L.R, P);
     // LDS per workgroup: U presence bitmaps + times + slots of one chunk, <= 64 KiB
-    for (;;) {
+    // (the list kernel stages nothing)
+    for (; !L.list;) {
+      // events per segment per chunk: about 2,048 events per tile, a multiple of
+      // 64 (whole presence-bitmap words)
       L.CH = std::max((2048 / L.R) & ~63, 64);
       const int tile = L.R * L.CH;
       L.lds = (size_t)U * (tile / 64) * 8 + (size_t)tile * 5;
       if (L.lds <= 65536 || L.R == 1) break;
       L.R = (L.R + 1) / 2;
     }
-    if (L.lds > 65536) {
+    if (L.lds > 65536 || L.list) {
       L.CH = 64;
       L.lds = (size_t)U * 8 + 64 * 5;
     }
     // tick kernel: per chunk, R segments x CW words x U slot bitmaps, <= 32 KiB
     L.CW = (int)std::max<int64_t>(1, std::min<int64_t>(64, 32768 / ((int64_t)L.R * U * 8)));
     L.lds_ticks = (size_t)L.R * L.CW * U * 8;
-    L.split = 0;
-    if (const char* sp = getenv("EP_SPLIT")) {
-      if (!strcmp(sp, "ticks")) L.split = 1;
-      if (!strcmp(sp, "positions")) L.split = 2;
-    }
   } else {
+    L.list = false;
     L.all_mach = false;
     L.M = L.n_machines;
     L.G = (int)std::min<int64_t>(S, L.block / L.M);
@@ -696,9 +945,16 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_lohi = align_up(sizeof(int32_t) * S * std::max(N - 1, 1), 256);
   const size_t sz_span = align_up(sizeof(int32_t) * S, 256);
   const size_t sz_slot = align_up((size_t)S * N, 256);
-  const size_t sz_dist = align_up(sizeof(uint16_t) * U, 256);
-  const size_t host_bytes = sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_dist;
-  const size_t sz_remap = 65536;
+  const size_t sz_seen = sizeof(uint64_t) * 1024;  // node types as a 65,536-bit set
+  const size_t sz_rank = 1024;                       // set bits before each 64-bit word
+  const size_t sz_seps = L.list ? sizeof(uint32_t) * 256 : 0;
+  const size_t sz_slv = L.list ? align_up(sizeof(uint16_t) * 256 * S, 256) : 0;
+  const size_t host_bytes =
+      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv;
+  // (+ slack: the list kernel's aligned batches may read two entries past the
+  // last block's region)
+  const size_t sz_lists = L.list ? align_up((size_t)list_bytes + 4 * sizeof(int2), 256) : 0;
+  const size_t sz_lidx = L.list ? align_up(sizeof(int32_t) * (size_t)n_lblocks * S, 256) : 0;
   const size_t sz_tau = align_up(sizeof(int64_t) * (P + 1), 256);
   const size_t sz_seg = align_up(sizeof(int32_t) * P, 256);
   const size_t sz_t0 = align_up(sizeof(Tuple) * (size_t)P * S, 256);
@@ -708,7 +964,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
   const size_t total =
-      host_bytes + sz_remap + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt;
+      host_bytes + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt + sz_lists +
+      2 * sz_lidx;
 
   mark();  // plan
   ScratchBlock* block = nullptr;
@@ -723,8 +980,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     int32_t* d_hi = (int32_t*)(ws + off); off += sz_lohi;
     int32_t* d_span = (int32_t*)(ws + off); off += sz_span;
     uint8_t* d_slot = (uint8_t*)(ws + off); off += sz_slot;
-    uint16_t* d_dist = (uint16_t*)(ws + off); off += sz_dist;
-    uint8_t* d_remap = (uint8_t*)(ws + off); off += sz_remap;
+    uint64_t* d_seen = (uint64_t*)(ws + off); off += sz_seen;
+    uint8_t* d_rank = (uint8_t*)(ws + off); off += sz_rank;
+    uint32_t* d_seps = (uint32_t*)(ws + off); off += sz_seps;
+    uint16_t* d_slv = (uint16_t*)(ws + off); off += sz_slv;
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
@@ -736,8 +995,11 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ts.T0 = d_t0; ts.TX = d_tx; ts.nmap = d_nmap; ts.nslots = d_nslots; ts.P = P; ts.slots = L.slots;
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
+    int2* d_lists = (int2*)(ws + off); off += sz_lists;
+    int32_t* d_loff = (int32_t*)(ws + off); off += sz_lidx;
+    int32_t* d_lcnt = (int32_t*)(ws + off); off += sz_lidx;
 
-    // episode table, spans, node slots and the distinct types, written
+    // episode table, spans, node slots and the node-type set, written
     // straight into pinned staging: one upload
     {
       char* host = nullptr;
@@ -756,10 +1018,14 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         for (int j = 0; j < N; ++j)
           slots[e * N + j] = (uint8_t)(U <= 255 ? slot_of(episodes.types[e * N + j]) : 0);
       }
-      uint16_t* dist = (uint16_t*)(host + sz_types + 2 * sz_lohi + sz_span + sz_slot);
-      int k = 0;
-      for (int w = 0; w < 1024; ++w)
-        for (uint64_t m = seen[w]; m; m &= m - 1) dist[k++] = (uint16_t)(w * 64 + __builtin_ctzll(m));
+      memcpy(host + sz_types + 2 * sz_lohi + sz_span + sz_slot, seen, sz_seen);
+      uint8_t* rank = (uint8_t*)(host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen);
+      for (int w = 0; w < 1024; ++w) rank[w] = (uint8_t)(U <= 255 ? rank_base[w] : 0);
+      if (L.list) {
+        char* at = host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank;
+        memcpy(at, slot_eps, sz_seps);
+        memcpy(at + sz_seps, slot_levels, sizeof(uint16_t) * 256 * S);
+      }
       if ((status = staging_commit(dev, ws, host_bytes, stream))) break;
     }
 
@@ -791,8 +1057,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     SetupArgs sa;
     sa.times = times; sa.n = n_events; sa.P = P; sa.max_span = max_span;
     sa.tau = d_tau; sa.beg = d_beg; sa.end = d_end;
-    sa.distinct = d_dist; sa.U = U; sa.remap = L.bits ? d_remap : nullptr;
     sa.flags = d_flags; sa.S = S; sa.counters = d_cnt;
+    sa.wave_search = P <= kWaveSearchMaxP ? 1 : 0;
     hipLaunchKernelGGL(setup_kernel, dim3(grid_for(setup_items(sa))), dim3(kBlock), 0, stream, sa);
     if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
 
@@ -800,12 +1066,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     MapArgs ma;
     ma.times = times; ma.types = types;
     ma.ep_types = d_types; ma.ep_lo = d_lo; ma.ep_hi = d_hi; ma.ep_span = d_span;
-    ma.ep_slot = d_slot; ma.remap = d_remap;
+    ma.ep_slot = d_slot; ma.type_seen = d_seen; ma.type_rank = d_rank;
     ma.tau = d_tau; ma.seg_beg = d_beg; ma.seg_end = d_end;
     ma.ts = ts;
     ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH;
     ma.U = U; ma.n_machines = L.n_machines;
     ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split; ma.dil_steps = dil_k;
+    ma.lists = d_lists; ma.list_off = d_loff; ma.list_cnt = d_lcnt; ma.max_share = max_share;
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;
     dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));
@@ -832,16 +1099,40 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
     if (prof) hipEventRecord(rec.ev[1], stream);
     hipError_t le = hipSuccess;
-    if (!L.bits) {
+    if (L.list) {
+      FilterArgs fa;
+      fa.times = times; fa.types = types; fa.n = n_events;
+      fa.type_seen = d_seen; fa.type_rank = d_rank; fa.slot_eps = d_seps; fa.slot_levels = d_slv;
+      fa.S = (int32_t)S; fa.max_share = max_share;
+      fa.lists = d_lists; fa.list_off = d_loff; fa.list_cnt = d_lcnt;
+      // persistent workgroups: a few per CU, each looping over blocks
+      const int64_t fgrid = std::min<int64_t>(n_lblocks, (int64_t)info->cu_count * 4);
+      const dim3 fg((unsigned)fgrid), fb(kBlock);
+      if (S <= 4)
+        hipLaunchKernelGGL(filter_kernel<1>, fg, fb, 0, stream, fa);
+      else if (S <= 8)
+        hipLaunchKernelGGL(filter_kernel<2>, fg, fb, 0, stream, fa);
+      else if (S <= 16)
+        hipLaunchKernelGGL(filter_kernel<4>, fg, fb, 0, stream, fa);
+      else
+        hipLaunchKernelGGL(filter_kernel<8>, fg, fb, 0, stream, fa);
+      le = hipGetLastError();
+    }
+    if (prof) hipEventRecord(rec.ev[2], stream);
+    if (le == hipSuccess && !L.bits) {
+      if (prof) hipEventRecord(rec.ev[3], stream);  // no tick kernel: an empty interval
       le = Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
-    } else {
-      // each segment goes to the tick or the position kernel (segment_uses_ticks)
+    } else if (le == hipSuccess) {
+      // each segment goes to the tick kernel or, by segment_uses_ticks, to the
+      // list or the position kernel
       if (L.split != 2) le = Lr->map_ticks(ma, L.all_mach, mgrid, dim3(L.block), L.lds_ticks, stream);
+      if (prof) hipEventRecord(rec.ev[3], stream);
       if (le == hipSuccess && L.split != 1)
-        le = Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream);
+        le = L.list ? Lr->map_list(ma, L.win, L.all_mach, mgrid, dim3(L.block), stream)
+                    : Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream);
     }
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
-    if (prof) hipEventRecord(rec.ev[2], stream);
+    if (prof) hipEventRecord(rec.ev[4], stream);
 
     mark();  // map launches
     if (P > 1) {
@@ -855,7 +1146,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         status = EP_ERR_HIP;
         break;
       }
-      if (prof) hipEventRecord(rec.ev[3], stream);
+      if (prof) hipEventRecord(rec.ev[5], stream);
       // Concatenate tree: each launch joins groups of `members` blocks in LDS
       int members = kConcatMembers;
       while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
@@ -869,8 +1160,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       if (status != EP_OK) break;
     }
     if (prof) {
-      if (P <= 1) hipEventRecord(rec.ev[3], stream);
-      hipEventRecord(rec.ev[4], stream);
+      if (P <= 1) hipEventRecord(rec.ev[5], stream);
+      hipEventRecord(rec.ev[6], stream);
     }
     mark();  // closure + tree launches
     FallbackArgs fa;
@@ -899,7 +1190,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       opt->stats->mode = pmode;
       opt->stats->n_segments = P;
       opt->stats->max_runs = L.win >= kBits32 ? (L.win == kBits32 ? 32 : 64) : K;
-      opt->stats->reserved = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0);
+      opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0);
       opt->stats->repairs = (int64_t)cnt[0];
       opt->stats->fallbacks = (int64_t)cnt[1];
     }
@@ -931,18 +1222,23 @@ extern "C" int ep_profile_end(ep_profile* out) {
   ep_profile acc{};
   int status = EP_OK;
   for (ProfRecord& r : recs) {
-    float ms[5] = {0, 0, 0, 0, 0};
+    float ms[kProfEvents] = {};
     if (hipEventSynchronize(r.end) != hipSuccess) status = EP_ERR_HIP;
-    hipEvent_t seq[6] = {r.ev[0], r.ev[1], r.ev[2], r.ev[3], r.ev[4], r.end};
-    for (int i = 0; i < 5 && status == EP_OK; ++i)
+    hipEvent_t seq[kProfEvents + 1];
+    for (int i = 0; i < kProfEvents; ++i) seq[i] = r.ev[i];
+    seq[kProfEvents] = r.end;
+    for (int i = 0; i < kProfEvents && status == EP_OK; ++i)
       if (hipEventElapsedTime(&ms[i], seq[i], seq[i + 1]) != hipSuccess) status = EP_ERR_HIP;
-    acc.other_ms += ms[0] + ms[4];
-    acc.map_ms += ms[1];
-    acc.closure_ms += ms[2];
-    acc.concat_ms += ms[3];
+    acc.other_ms += ms[0] + ms[6];
+    acc.map_filter_ms += ms[1];
+    acc.map_ticks_ms += ms[2];
+    acc.map_positions_ms += ms[3];
+    acc.map_ms += ms[1] + ms[2] + ms[3];
+    acc.closure_ms += ms[4];
+    acc.concat_ms += ms[5];
     acc.calls += 1;
     std::lock_guard<std::mutex> lock(g_prof_mu);
-    for (int i = 0; i < 5; ++i) g_event_pool.push_back(r.ev[i]);
+    for (int i = 0; i < kProfEvents; ++i) g_event_pool.push_back(r.ev[i]);
     g_event_pool.push_back(r.end);
   }
   if (out) *out = acc;

@@ -35,6 +35,7 @@ namespace epk {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;  // largest workgroup of every kernel here
 constexpr int kTile = 2048;  // events staged in LDS per chunk by the scan Map kernel
+constexpr int kListBlock = 4096;  // events per block of the filter kernel (256 threads x 16)
 
 // One (a, count, b) tuple of the Map step (Map rules 1-4, Fig. 5), with a and b
 // stored as offsets from the segment's left and right cut; 0 is the sentinel
@@ -354,7 +355,8 @@ struct MapArgs {
   const int32_t* ep_hi;      // [S*(N-1)]
   const int32_t* ep_span;    // [S]
   const uint8_t* ep_slot;    // [S*N] node type -> 1..U (bit kernels)
-  const uint8_t* remap;      // [65536] event type -> slot, 0 = on no node (bit kernels)
+  const uint64_t* type_seen; // [1024] the call's node types as a 65,536-bit set (bit kernels)
+  const uint8_t* type_rank;  // [1024] set bits of type_seen before each 64-bit word
   const int64_t* tau;        // [P+1] cuts
   const int32_t* seg_beg;    // [P] first event index with time > tau_p - maxSpan
   const int32_t* seg_end;    // [P] first event index with time > tau_{p+1} + maxSpan
@@ -373,9 +375,29 @@ struct MapArgs {
   int32_t split;       // 0: each segment to the kernel segment_uses_ticks picks; 1: all to
                        // the tick kernel; 2: all to the position kernel
   int32_t dil_steps;   // tick kernel: doubling steps of the widest interval of the call
+  const int2* lists;        // list kernel: per event block, each episode's entries {time, levels}
+  const int32_t* list_off;  // [blocks * S] start of episode e's entries in block b's region
+  const int32_t* list_cnt;  // [blocks * S] their number
+  int32_t max_share;        // most episodes one node type belongs to (region = kListBlock * this)
   int64_t eg_blocks;   // tick kernel: workgroups that loop over a segment group's episode
                        // groups when its segments fit one chunk each
 };
+
+// Node-type slot of event type y: 1 + the rank of y among the call's node
+// types, 0 for a type on no node.  seen/rank are the MapArgs tables, copied to
+// LDS by each workgroup (two independent LDS reads per event).
+__device__ inline uint32_t type_slot(const uint64_t* seen, const uint8_t* rank, uint32_t y) {
+  const uint64_t w = seen[y >> 6];
+  const uint64_t bit = 1ull << (y & 63);
+  return (w & bit) ? (uint32_t)rank[y >> 6] + (uint32_t)__popcll(w & (bit - 1)) + 1u : 0u;
+}
+
+__device__ inline void load_type_tables(const MapArgs& A, uint64_t* seen, uint8_t* rank) {
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) {
+    seen[i] = A.type_seen[i];
+    rank[i] = A.type_rank[i];
+  }
+}
 
 // Which Map kernel counts a segment: the tick kernel costs ~(N-1) bit
 // operations per 64 ticks of the segment, the position kernel ~1 step per
@@ -473,28 +495,287 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   }
 }
 
-// Bit Map kernel (bit windows, relevant events only).
+// The Map machines of one (segment, episode) held by one lane (MCH = N) as
+// equivalence classes, or one Map machine per lane (MCH = 1), on bit windows.
+// Machines that reset at the same time are identical from then on, and so
+// are machines whose last reset lies more than Span before the current event
+// (every occurrence that can still complete starts after both resets), so the
+// lane advances one window state per class; after the boundary halo a lane
+// usually carries a single class.  Events are fed in time order as (t, lm),
+// lm = the node levels whose type the event has.
+template <int N, int W, int MCH>
+struct ClassLane {
+  using Bits = typename BitsOf<W>::type;
+  static constexpr int NI = N > 1 ? N - 1 : 1;
+  static constexpr uint32_t kAll = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
+  uint32_t slot[N];
+  Bits win[NI];
+  int32_t span;
+  Bits m[MCH][NI];
+  int64_t r[MCH];
+  uint32_t mem[MCH];  // machines in class c (bit k); a class lives while mem != 0
+  int32_t cnt[MCH], a_off[MCH], b_off[MCH];
+  uint32_t found, fin;
+  int64_t tau_lo, tau_hi, stop, check_at;
+  int32_t B;
+  bool single;  // exactly one class left, held in slot 0
+
+  __device__ void init(const MapArgs& A, int64_t e, int64_t p, int k_lane, bool active) {
+    found = 0;
+    fin = 0;
+    span = 0;
+    tau_lo = tau_hi = stop = 0;
+    check_at = INT64_MAX;
+    B = INT32_MIN;
+    single = MCH == 1;
+    if (!active) {
+      fin = kAll;
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      win[j] = window_bits<W>((uint32_t)A.ep_lo[e * (N - 1) + j], (uint32_t)A.ep_hi[e * (N - 1) + j]);
+    span = A.ep_span[e];
+    tau_lo = A.tau[p];
+    tau_hi = A.tau[p + 1];
+    stop = tau_hi + span;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int k = (MCH == 1) ? k_lane : c;
+      r[c] = tau_lo - prefix_hi<N>(A.ep_hi, e, k);
+      mem[c] = 1u << c;
+      cnt[c] = 0;
+      a_off[c] = 0;
+      b_off[c] = 0;
+#pragma unroll
+      for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
+      if (MCH > 1) check_at = min(check_at, r[c] + span + 1);
+    }
+  }
+
+  __device__ bool finished() const { return fin == kAll; }
+
+  __device__ uint32_t level_mask(uint32_t u) const {
+    uint32_t lm = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
+    return lm;
+  }
+
+  // completion of the classes in `done` at t: every member machine completes
+  // and resets; returns the members
+  __device__ uint32_t complete_class(uint32_t done, int32_t t) {
+    uint32_t members = 0;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c)
+      if ((done >> c) & 1u) {
+        members |= mem[c];
+        r[c] = t;
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
+      }
+    const uint32_t live = members & ~fin;  // machines still recording their tuple
+#pragma unroll
+    for (int k = 0; k < MCH; ++k) {
+      if ((live >> k) & 1u) {
+        if ((int64_t)t > tau_lo) {
+          if (!((found >> k) & 1u)) {
+            found |= 1u << k;
+            const int64_t dd = (int64_t)t - tau_lo;
+            a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+          }
+          if ((int64_t)t <= tau_hi) {
+            ++cnt[k];
+          } else {
+            b_off[k] = (int32_t)((int64_t)t - tau_hi);
+            fin |= 1u << k;
+          }
+        }
+      }
+    }
+    return members;
+  }
+
+  // One event while several classes live (MCH > 1).  Returns false once the
+  // lane has finished; `single` is set when one class is left.
+  __device__ bool step_many(int32_t t, uint32_t lm) {
+    if ((int64_t)t > stop) {
+      fin = kAll;
+      return false;
+    }
+    const uint32_t d = (uint32_t)t - (uint32_t)B;
+    B = t;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c)
+      if (mem[c]) {
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
+      }
+    if ((int64_t)t >= check_at) {
+      // classes whose last reset lies more than Span back are identical: merge
+      uint32_t stale = 0, acc = 0;
+      int64_t next = INT64_MAX;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c)
+        if (mem[c]) {
+          if (r[c] + span < (int64_t)t) {
+            stale |= 1u << c;
+            acc |= mem[c];
+          } else {
+            next = min(next, r[c] + span + 1);
+          }
+        }
+      if (__popc(stale) >= 2) {
+        const int lowest = __ffs((int)stale) - 1;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+      }
+      check_at = next;
+    }
+    uint32_t done = 0;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      if (mem[c] && (int64_t)t > r[c]) {
+        bool hit[NI];
+#pragma unroll
+        for (int j = 0; j < N - 1; ++j) hit[j] = (m[c][j] & win[j]) != 0;
+        bool complete = (lm >> (N - 1)) & 1u;
+        if constexpr (N > 1) complete = complete && hit[N - 2];
+        if (complete) {
+          done |= 1u << c;
+        } else {
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j)
+            if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[c][j] |= (Bits)1;
+        }
+      }
+    }
+    if (done) {
+      const uint32_t members = complete_class(done, t);
+      // classes that completed together are identical from now on
+      if (__popc(done) >= 2) {
+        const int lowest = __ffs((int)done) - 1;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((done >> c) & 1u) mem[c] = (c == lowest) ? members : 0u;
+      }
+      check_at = min(check_at, (int64_t)t + span + 1);
+#pragma unroll
+      for (int c = 0; c < MCH; ++c)
+        if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
+      if (fin == kAll) return false;
+    }
+    // classes never split; once one is left, move it to slot 0
+    uint32_t alive = 0;
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
+    if (__popc(alive) == 1) {
+#pragma unroll
+      for (int c = 1; c < MCH; ++c)
+        if ((alive >> c) & 1u) {
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) m[0][j] = m[c][j];
+          r[0] = r[c];
+          mem[0] = mem[c];
+          mem[c] = 0u;
+        }
+      single = true;
+    }
+    return true;
+  }
+
+  // One event with a single class left (slot 0).  Returns false once the lane
+  // has finished.  Branch-free but for the rare completion: an event at or
+  // before the last reset only ages the windows.
+  __device__ bool step_one(int32_t t, uint32_t lm) {
+    if ((int64_t)t > stop) {
+      fin = kAll;
+      return false;
+    }
+    const uint32_t d = (uint32_t)t - (uint32_t)B;
+    B = t;
+    const uint32_t live = (int64_t)t > r[0] ? 1u : 0u;
+    uint32_t hit[NI];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      m[0][j] = age<W>(m[0][j], d);
+      hit[j] = (m[0][j] & win[j]) != 0 ? 1u : 0u;
+    }
+    uint32_t complete = live & (lm >> (N - 1)) & 1u;
+    if constexpr (N > 1) complete &= hit[N - 2];
+    if (complete) {
+      complete_class(1u, t);
+      if ((mem[0] & ~fin) == 0u) mem[0] = 0u;
+      return fin != kAll;
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      m[0][j] |= (Bits)(live & (lm >> j) & (j == 0 ? 1u : hit[j > 0 ? j - 1 : 0]));
+    return true;
+  }
+
+  __device__ bool step(int32_t t, uint32_t lm) { return single ? step_one(t, lm) : step_many(t, lm); }
+
+  // The tuples of the (segment, episode): one per machine lane (MCH = 1), or
+  // the distinct ones of the classes (equal keys mean identical tuples: same
+  // first completion after the cut, or none within Span); machine 0's tuple
+  // stays first.
+  __device__ void write(const MapArgs& A, int64_t e, int64_t p, int k_lane) const {
+    const int64_t pe = A.ts.idx(e, p);
+    if (MCH == 1) {
+      Tuple tu;
+      tu.a = a_off[0];
+      tu.c = cnt[0];
+      tu.b = b_off[0];
+      tu.pad = 0;
+      *A.ts.at(e, p, k_lane) = tu;
+      if (k_lane == 0) {
+        A.ts.nmap[pe] = A.n_machines;
+        A.ts.nslots[pe] = A.n_machines;
+      }
+    } else {
+      int d = 0;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c) {
+        bool dup = false;
+#pragma unroll
+        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
+        if (!dup) {
+          Tuple tu;
+          tu.a = a_off[c];
+          tu.c = cnt[c];
+          tu.b = b_off[c];
+          tu.pad = 0;
+          *A.ts.at(e, p, d) = tu;
+          ++d;
+        }
+      }
+      A.ts.nmap[pe] = d;
+      A.ts.nslots[pe] = d;
+    }
+  }
+};
+
+// Position Map kernel (bit windows, relevant events only).
 //
 // Each chunk of events is staged in LDS with, for every node type slot u, a
 // presence bitmap over the chunk's positions (bit i of word w: event 64w+i has
 // a type on slot u).  A lane ORs the bitmaps of its episode's node types and
 // visits only the set bits, in order (the machines ignore every other event
-// anyway).  Lanes of one workgroup share the staged chunk.
-//
-// MCH = N: one lane holds all N machines of a (segment, episode).  Machines
-// that reset at the same time are identical from then on, and so are machines
-// whose last reset lies more than Span before the current event (every
-// occurrence that can still complete starts after both resets), so the lane
-// keeps machines in equivalence classes and advances one window state per
-// class; after the boundary halo a lane usually carries a single class.
-// MCH = 1: one lane per machine (M lanes per (segment, episode)).
+// anyway).  Lanes of one workgroup share the staged chunk.  The lane's
+// machines are a ClassLane: MCH = N, all N machines of a (segment, episode) as
+// classes; MCH = 1, one machine per lane (M lanes per (segment, episode)).
 template <int N, int W, int MCH>
 __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
-  using Bits = typename BitsOf<W>::type;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int32_t s_beg[kBlock];
   __shared__ int32_t s_len[kBlock];
   __shared__ int32_t s_chunks;
+  __shared__ uint64_t s_seen[1024];  // node-type set and ranks (type_slot)
+  __shared__ uint8_t s_rank[1024];
 
   const int tile = A.R * A.CH;
   const int words = tile >> 6;
@@ -527,68 +808,62 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
     s_len[tid] = len;
     atomicMax(&s_chunks, (len + A.CH - 1) / A.CH);
   }
-
-  // ---- lane state
-  uint32_t slot[N];
-  Bits win[N > 1 ? N - 1 : 1];
-  int32_t span = 0;
-  Bits m[MCH][N > 1 ? N - 1 : 1];
-  int64_t r[MCH];
-  uint32_t mem[MCH];  // machines in class c (bit k); a class lives while mem != 0
-  int32_t cnt[MCH], a_off[MCH], b_off[MCH];
-  uint32_t found = 0, fin = 0;
-  const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
-  int64_t tau_lo = 0, tau_hi = 0, stop = 0, check_at = INT64_MAX;
-  int32_t B = INT32_MIN;
-  bool single = MCH == 1;  // exactly one class left, held in slot 0
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) slot[j] = A.ep_slot[e * N + j];
-#pragma unroll
-    for (int j = 0; j < N - 1; ++j)
-      win[j] = window_bits<W>((uint32_t)A.ep_lo[e * (N - 1) + j], (uint32_t)A.ep_hi[e * (N - 1) + j]);
-    span = A.ep_span[e];
-    tau_lo = A.tau[p];
-    tau_hi = A.tau[p + 1];
-    stop = tau_hi + span;
-#pragma unroll
-    for (int c = 0; c < MCH; ++c) {
-      const int k = (MCH == 1) ? k_lane : c;
-      r[c] = tau_lo - prefix_hi<N>(A.ep_hi, e, k);
-      mem[c] = 1u << c;
-      cnt[c] = 0;
-      a_off[c] = 0;
-      b_off[c] = 0;
-#pragma unroll
-      for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
-      if (MCH > 1) check_at = min(check_at, r[c] + span + 1);
-    }
-  } else {
-    fin = all;
-  }
+  ClassLane<N, W, MCH> lane;
+  lane.init(A, e, p, k_lane, active);
   __syncthreads();
   const int n_chunks = s_chunks;
+  if (n_chunks > 0) {
+    load_type_tables(A, s_seen, s_rank);
+    __syncthreads();
+  }
+
+  // The fill: the tile (R segments x CH events, CH a multiple of 64) is read in
+  // batches of kPer events per thread with every load of a batch in flight,
+  // position pos = segment * CH + offset.
+  constexpr int kPer = 4;
+  const int CE = kPer * nthr;
+  // pos / CH through a float reciprocal: pos + 0.5 is at least 0.5 / CH from a
+  // multiple of CH and pos < 2^16, far inside float precision; the two
+  // corrections keep it exact regardless
+  const float inv_ch = 1.0f / (float)A.CH;
+  auto in_tile = [&](int ch, int pos, int32_t* src) -> bool {
+    if (pos >= tile) return false;
+    int rr = (int)(((float)pos + 0.5f) * inv_ch);
+    rr -= rr * A.CH > pos ? 1 : 0;
+    rr += (rr + 1) * A.CH <= pos ? 1 : 0;
+    const int32_t i = pos - rr * A.CH;
+    *src = s_beg[rr] + ch * A.CH + i;
+    return i < s_len[rr] - ch * A.CH;
+  };
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     if (ch > 0) __syncthreads();  // previous chunk fully consumed
     for (int i = tid; i < A.U * words; i += nthr) s_bits[i] = 0;
     __syncthreads();
-    for (int rr = 0; rr < A.R; ++rr) {
-      const int32_t base = s_beg[rr] + ch * A.CH;
-      const int32_t avail = s_len[rr] - ch * A.CH;
-      for (int i = tid; i < A.CH; i += nthr) {
-        if (i < avail) {
-          const int pos = rr * A.CH + i;
-          const uint32_t u = A.remap[A.types[base + i]];
-          s_t[pos] = A.times[base + i];
+    for (int i0 = 0; i0 < tile; i0 += CE) {
+      int32_t tt[kPer];
+      uint32_t ty[kPer];
+      bool ok[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        int32_t src = 0;
+        ok[k] = in_tile(ch, i0 + k * nthr + tid, &src);
+        tt[k] = ok[k] ? A.times[src] : 0;
+        ty[k] = ok[k] ? A.types[src] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int pos = i0 + k * nthr + tid;
+        const uint32_t u = ok[k] ? type_slot(s_seen, s_rank, ty[k]) : 0u;
+        if (u) {
+          s_t[pos] = tt[k];
           s_s[pos] = (uint8_t)u;
-          if (u) atomicOr((unsigned long long*)&s_bits[(pos >> 6) * A.U + (u - 1)],
-                          1ull << (pos & 63));
+          atomicOr((unsigned long long*)&s_bits[(pos >> 6) * A.U + (u - 1)], 1ull << (pos & 63));
         }
       }
     }
     __syncthreads();
-    if (fin == all) continue;
+    if (lane.finished()) continue;
     int32_t len = s_len[r_idx] - ch * A.CH;
     len = len < A.CH ? len : A.CH;
     if (len <= 0) continue;
@@ -599,151 +874,30 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
     int w = w0;
     uint64_t word = 0;
 #pragma unroll
-    for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
+    for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (lane.slot[j] - 1)];
     // next relevant position, or -1 when the chunk is exhausted
     auto next_pos = [&]() -> int {
       while (word == 0) {
         if (++w >= w1) return -1;
 #pragma unroll
-        for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (slot[j] - 1)];
+        for (int j = 0; j < N; ++j) word |= s_bits[w * A.U + (lane.slot[j] - 1)];
       }
       const int pos = (w << 6) + (__ffsll((unsigned long long)word) - 1);
       word &= word - 1;
       return pos;
     };
-    // completion of class c at t: every member machine completes and resets
-    auto complete_class = [&](uint32_t done, int32_t t) {
-      uint32_t members = 0;
-#pragma unroll
-      for (int c = 0; c < MCH; ++c)
-        if ((done >> c) & 1u) {
-          members |= mem[c];
-          r[c] = t;
-#pragma unroll
-          for (int j = 0; j < N - 1; ++j) m[c][j] = 0;
-        }
-      const uint32_t live = members & ~fin;  // machines still recording their tuple
-#pragma unroll
-      for (int k = 0; k < MCH; ++k) {
-        if ((live >> k) & 1u) {
-          if ((int64_t)t > tau_lo) {
-            if (!((found >> k) & 1u)) {
-              found |= 1u << k;
-              const int64_t dd = (int64_t)t - tau_lo;
-              a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
-            }
-            if ((int64_t)t <= tau_hi) {
-              ++cnt[k];
-            } else {
-              b_off[k] = (int32_t)((int64_t)t - tau_hi);
-              fin |= 1u << k;
-            }
-          }
-        }
-      }
-      return members;
-    };
-
-    // ---- loop A: several classes (boundary halo only; MCH > 1)
-    if (MCH > 1 && !single) {
+    // several classes (boundary halo only; MCH > 1)
+    if (MCH > 1 && !lane.single) {
       for (;;) {
         const int pos = next_pos();
         if (pos < 0) break;
-        const int32_t t = s_t[pos];
-        const uint32_t u = s_s[pos];
-        uint32_t lm = 0;
-#pragma unroll
-        for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
-        if ((int64_t)t > stop) {
-          fin = all;
-          break;
-        }
-        const uint32_t d = (uint32_t)t - (uint32_t)B;
-        B = t;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c)
-          if (mem[c]) {
-#pragma unroll
-            for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
-          }
-        if ((int64_t)t >= check_at) {
-          // classes whose last reset lies more than Span back are identical: merge
-          uint32_t stale = 0, acc = 0;
-          int64_t next = INT64_MAX;
-#pragma unroll
-          for (int c = 0; c < MCH; ++c)
-            if (mem[c]) {
-              if (r[c] + span < (int64_t)t) {
-                stale |= 1u << c;
-                acc |= mem[c];
-              } else {
-                next = min(next, r[c] + span + 1);
-              }
-            }
-          if (__popc(stale) >= 2) {
-            const int lowest = __ffs((int)stale) - 1;
-#pragma unroll
-            for (int c = 0; c < MCH; ++c)
-              if ((stale >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
-          }
-          check_at = next;
-        }
-        uint32_t done = 0;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c) {
-          if (mem[c] && (int64_t)t > r[c]) {
-            bool hit[N > 1 ? N - 1 : 1];
-#pragma unroll
-            for (int j = 0; j < N - 1; ++j) hit[j] = (m[c][j] & win[j]) != 0;
-            bool complete = (lm >> (N - 1)) & 1u;
-            if constexpr (N > 1) complete = complete && hit[N - 2];
-            if (complete) {
-              done |= 1u << c;
-            } else {
-#pragma unroll
-              for (int j = 0; j < N - 1; ++j)
-                if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[c][j] |= (Bits)1;
-            }
-          }
-        }
-        if (done) {
-          const uint32_t members = complete_class(done, t);
-          // classes that completed together are identical from now on
-          if (__popc(done) >= 2) {
-            const int lowest = __ffs((int)done) - 1;
-#pragma unroll
-            for (int c = 0; c < MCH; ++c)
-              if ((done >> c) & 1u) mem[c] = (c == lowest) ? members : 0u;
-          }
-          check_at = min(check_at, (int64_t)t + span + 1);
-#pragma unroll
-          for (int c = 0; c < MCH; ++c)
-            if ((mem[c] & ~fin) == 0u) mem[c] = 0u;
-          if (fin == all) break;
-        }
-        // classes never split; once one is left, move it to slot 0
-        uint32_t alive = 0;
-#pragma unroll
-        for (int c = 0; c < MCH; ++c) alive |= (mem[c] != 0u ? 1u : 0u) << c;
-        if (__popc(alive) == 1) {
-#pragma unroll
-          for (int c = 1; c < MCH; ++c)
-            if ((alive >> c) & 1u) {
-#pragma unroll
-              for (int j = 0; j < N - 1; ++j) m[0][j] = m[c][j];
-              r[0] = r[c];
-              mem[0] = mem[c];
-              mem[c] = 0u;
-            }
-          single = true;
-          break;
-        }
+        if (!lane.step_many(s_t[pos], lane.level_mask(s_s[pos]))) break;
+        if (lane.single) break;
       }
     }
-
-    // ---- loop B: one class, in slot 0; the next event's LDS reads are issued
-    // before the current event is processed
-    if (single && fin != all) {
+    // one class, in slot 0; the next event's LDS reads are issued before the
+    // current event is processed
+    if (lane.single && !lane.finished()) {
       int pos = next_pos();
       int32_t t_next = pos >= 0 ? s_t[pos] : 0;
       uint32_t u_next = pos >= 0 ? s_s[pos] : 0u;
@@ -755,76 +909,132 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
           t_next = s_t[pos];
           u_next = s_s[pos];
         }
-        uint32_t lm = 0;
-#pragma unroll
-        for (int j = 0; j < N; ++j) lm |= (uint32_t)(slot[j] == u) << j;
-        if ((int64_t)t > stop) {
-          fin = all;
-          break;
-        }
-        const uint32_t d = (uint32_t)t - (uint32_t)B;
-        B = t;
-#pragma unroll
-        for (int j = 0; j < N - 1; ++j) m[0][j] = age<W>(m[0][j], d);
-        if ((int64_t)t > r[0]) {
-          bool hit[N > 1 ? N - 1 : 1];
-#pragma unroll
-          for (int j = 0; j < N - 1; ++j) hit[j] = (m[0][j] & win[j]) != 0;
-          bool complete = (lm >> (N - 1)) & 1u;
-          if constexpr (N > 1) complete = complete && hit[N - 2];
-          if (complete) {
-            complete_class(1u, t);
-            if ((mem[0] & ~fin) == 0u) mem[0] = 0u;
-            if (fin == all) break;
-          } else {
-#pragma unroll
-            for (int j = 0; j < N - 1; ++j)
-              if (((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0])) m[0][j] |= (Bits)1;
-          }
-        }
+        if (!lane.step_one(t, lane.level_mask(u))) break;
       }
     }
   }
 
-  if (active) {
-    const int64_t pe = A.ts.idx(e, p);
-    if (MCH == 1) {
-      Tuple tu;
-      tu.a = a_off[0];
-      tu.c = cnt[0];
-      tu.b = b_off[0];
-      tu.pad = 0;
-      *A.ts.at(e, p, k_lane) = tu;
-      if (k_lane == 0) {
-        A.ts.nmap[pe] = A.n_machines;
-        A.ts.nslots[pe] = A.n_machines;
-      }
-    } else {
-      // Equal keys mean identical tuples (same first completion after the cut,
-      // or none within Span), so only distinct keys are kept; machine 0's
-      // tuple stays first.
-      int d = 0;
-#pragma unroll
-      for (int c = 0; c < MCH; ++c) {
-        bool dup = false;
-#pragma unroll
-        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
-        if (!dup) {
-          Tuple tu;
-          tu.a = a_off[c];
-          tu.c = cnt[c];
-          tu.b = b_off[c];
-          tu.pad = 0;
-          *A.ts.at(e, p, d) = tu;
-          ++d;
-        }
-      }
-      A.ts.nmap[pe] = d;
-      A.ts.nslots[pe] = d;
-    }
-  }
+  if (active) lane.write(A, e, p, k_lane);
 }
 
+// List Map kernel (bit windows): the ClassLane machines fed from the filter
+// kernel's per-episode event lists instead of a staged chunk.  The lane of
+// (segment, episode) reads, in time order, its episode's entries of the event
+// blocks its segment's range (tau_p - maxSpan, tau_{p+1} + maxSpan] covers;
+// no LDS and no barriers.  Entries are taken in batches of kD: the loads of
+// the next batch are issued before the current one is stepped through, and
+// the next block's list bounds before the current block's entries.
+template <int N, int W, int MCH>
+__global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
+  constexpr int kD = 8;
+  const int tid = threadIdx.x;
+  const int per_seg = A.G * A.M;
+  const int r_idx = tid / per_seg;
+  const int g = (tid / A.M) % A.G;
+  const int k_lane = tid % A.M;
+  const int64_t seg_group = (int64_t)blockIdx.x / A.n_egroups;
+  const int64_t ep_group = (int64_t)blockIdx.x - seg_group * A.n_egroups;
+  const int64_t p = seg_group * A.R + r_idx;
+  const int64_t e = ep_group * A.G + g;
+  const bool active = tid < A.R * per_seg && p < A.P && e < A.S && !segment_uses_ticks(A, p, N);
+  if (!active) return;
+  ClassLane<N, W, MCH> lane;
+  lane.init(A, e, p, k_lane, true);
+  const int32_t beg = A.seg_beg[p];
+  const int32_t end = A.seg_end[p];
+  // the range holds times in (lo_t, tau_{p+1} + maxSpan]; the machines stop
+  // by themselves at tau_{p+1} + Span
+  const int64_t lo_t = lane.tau_lo - A.max_span;
+  if (beg < end) {
+    const int64_t b_last = (end - 1) / kListBlock;
+    int64_t b = beg / kListBlock;
+    const int2* list = nullptr;
+    int32_t n_here = 0, i = 0;
+    // block b's list; the next block's bounds are loaded meanwhile
+    int32_t off_next = A.list_off[b * A.S + e];
+    int32_t cnt_next = A.list_cnt[b * A.S + e];
+    auto open = [&]() {
+      list = A.lists + b * (int64_t)kListBlock * A.max_share + off_next;
+      n_here = cnt_next;
+      i = 0;
+      if (b < b_last) {
+        off_next = A.list_off[(b + 1) * A.S + e];
+        cnt_next = A.list_cnt[(b + 1) * A.S + e];
+      }
+    };
+    open();
+    // the first block also holds the episode's events before the range: skip
+    // them by a binary search for the first entry after lo_t
+    {
+      int32_t lo = 0, hi = n_here;
+      while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if ((int64_t)list[mid].x <= lo_t)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      i = lo;
+    }
+    bool go = true;
+    // several classes (the segment's first events): one entry at a time, the
+    // next entry's load issued before the current one is stepped
+    if (MCH > 1) {
+      int2 en = i < n_here ? list[i] : make_int2(0, 0);
+      while (go && !lane.single) {
+        while (i >= n_here && b < b_last) {
+          ++b;
+          open();
+          if (i < n_here) en = list[i];
+        }
+        if (i >= n_here) break;
+        const int2 cur = en;
+        ++i;
+        if (i < n_here) en = list[i];
+        go = lane.step_many(cur.x, (uint32_t)cur.y);
+      }
+    }
+    // one class: batches of kD entries read as kD / 2 aligned 16-byte loads
+    // (a lane reads its list in whole lines, which stay useful even when the
+    // L1 cannot hold every lane's line), the next batch's loads in flight.
+    // A batch starts at an even entry of the region (region starts are
+    // 16-byte aligned); entries before i or past the list are read (they lie
+    // in the region, or in the buffer's slack) and skipped.  The loads are
+    // unconditional so that the compiler can count them and wait only for the
+    // batch about to be stepped through.
+    while (go && lane.single) {
+      const int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
+      const int32_t rel = (int32_t)(list - region);   // the list's first entry in the region
+      const int32_t first = i;                         // entries before it are done
+      const int32_t n_end = n_here;
+      int32_t j0 = (rel + i) & ~1;                     // even region index of the first batch
+      const int32_t j_last = (rel + n_end + 1) & ~1;   // clamp for the loads
+      const int4* v = (const int4*)region;
+      int4 cur[kD / 2];
+#pragma unroll
+      for (int q = 0; q < kD / 2; ++q) cur[q] = v[min(j0 + 2 * q, j_last) >> 1];
+      for (; go && j0 < rel + n_end; j0 += kD) {
+        int4 nxt[kD / 2];
+#pragma unroll
+        for (int q = 0; q < kD / 2; ++q) nxt[q] = v[min(j0 + kD + 2 * q, j_last) >> 1];
+#pragma unroll
+        for (int k = 0; k < kD; ++k) {
+          const int32_t idx = j0 + k - rel;  // index within this episode's list
+          const int4 w = cur[k >> 1];
+          const int32_t t = (k & 1) ? w.z : w.x;
+          const uint32_t lm = (uint32_t)((k & 1) ? w.w : w.y);
+          if (go && idx >= first && idx < n_end && (int64_t)t > lo_t) go = lane.step_one(t, lm);
+        }
+#pragma unroll
+        for (int q = 0; q < kD / 2; ++q) cur[q] = nxt[q];
+      }
+      if (!go || b >= b_last) break;
+      ++b;
+      open();
+    }
+  }
+  lane.write(A, e, p, k_lane);
+}
 
 // ------------------------------------------------------- tick Map kernel
 
@@ -951,6 +1161,8 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   __shared__ int32_t s_seg_end[kBlock]; // segment r's event range end; 0 for a segment not counted here
   __shared__ int32_t s_built[kBlock];   // first event of the chunk the bitmaps hold (-1: none)
   __shared__ int32_t s_more, s_reuse, s_fit;
+  __shared__ uint64_t s_seen[1024];     // node-type set and ranks (type_slot)
+  __shared__ uint8_t s_rank[1024];
   uint64_t* s_tb = (uint64_t*)smem;     // [R*CW words][U], word-major
 
   constexpr int NI = N > 1 ? N - 1 : 1;
@@ -995,6 +1207,7 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   __syncthreads();
   const bool fit = s_fit != 0;
   if (fit && eg_id >= A.eg_blocks) return;  // the group's looping workgroups cover it
+  load_type_tables(A, s_seen, s_rank);  // first read after the chunk loop's barrier
   const int64_t eg_step = fit ? A.eg_blocks : A.n_egroups;
 
   for (int64_t eg = eg_id; eg < A.n_egroups; eg += eg_step) {
@@ -1139,7 +1352,7 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
             const int64_t last_t = A.times[batch_last];
             uint32_t u[kPer];
 #pragma unroll
-            for (int k = 0; k < kPer; ++k) u[k] = A.remap[ty[k]];
+            for (int k = 0; k < kPer; ++k) u[k] = type_slot(s_seen, s_rank, ty[k]);
 #pragma unroll
             for (int k = 0; k < kPer; ++k) {
               const int32_t i = base + k * nthr + tid;
@@ -1609,6 +1822,9 @@ struct Launchers {
   // tick Map kernel (bit windows up to 63 ticks)
   hipError_t (*map_ticks)(const MapArgs&, bool all_machines, dim3 grid, dim3 block, size_t lds,
                           hipStream_t);
+  // list Map kernel (win must be a bit kind); reads the filter kernel's lists
+  hipError_t (*map_list)(const MapArgs&, int win, bool all_machines, dim3 grid, dim3 block,
+                         hipStream_t);
   hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
   hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
   // resident workgroups per CU of a Map kernel for a block size and LDS size

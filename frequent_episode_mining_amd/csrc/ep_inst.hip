@@ -49,6 +49,24 @@ hipError_t launch_bits(const MapArgs& a, int win, bool all_machines, dim3 grid, 
   return hipErrorInvalidValue;
 }
 
+template <int W, int MCH>
+hipError_t launch_list_wm(const MapArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((map_list_kernel<EP_N, W, MCH>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_list(const MapArgs& a, int win, bool all_machines, dim3 grid, dim3 block,
+                       hipStream_t s) {
+  if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
+  if (win == kBits32)
+    return all_machines ? launch_list_wm<32, kClassMch>(a, grid, block, s)
+                        : launch_list_wm<32, 1>(a, grid, block, s);
+  if (win == kBits64)
+    return all_machines ? launch_list_wm<64, kClassMch>(a, grid, block, s)
+                        : launch_list_wm<64, 1>(a, grid, block, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_ticks(const MapArgs& a, bool all_machines, dim3 grid, dim3 block, size_t lds,
                         hipStream_t s) {
   if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
@@ -120,8 +138,8 @@ hipError_t occupancy_ticks(bool all_machines, int block, size_t lds, int* out) {
                       : occ(map_ticks_kernel<EP_N, 1>, block, lds, out);
 }
 
-const Launchers kLaunchers = {launch_scan,   launch_bits, launch_ticks, launch_closure,
-                              launch_finish, occupancy,   occupancy_ticks};
+const Launchers kLaunchers = {launch_scan,    launch_bits,   launch_ticks, launch_list,
+                              launch_closure, launch_finish, occupancy,    occupancy_ticks};
 
 }  // namespace
 

@@ -126,7 +126,10 @@ typedef struct {
   int32_t mode;         /* scheme that ran: EP_MODE_PTPE or EP_MODE_MAPCONCAT */
   int32_t n_segments;   /* P (1 for PTPE) */
   int32_t max_runs;     /* run capacity per node window the kernels were built with */
-  int32_t reserved;
+  int32_t kernels;      /* bit 0: bit-window Map kernels (tick/list/position), else the
+                           scan kernel; bit 1: one lane holds every machine of a
+                           (segment, episode); bit 2: sparse segments through the event
+                           filter and the list Map kernel (else the position kernel) */
   int64_t repairs;      /* repair tuples made for unmatched segment exits */
   int64_t fallbacks;    /* episodes recounted by the whole-stream fallback */
 } ep_stats;
@@ -189,11 +192,16 @@ int64_t ep_segment_cut(int32_t t_min, int32_t t_max, int32_t n_segments, int32_t
  * waits for the recorded events and returns the summed durations.  Calls made
  * outside a session record nothing.  Sessions are process-wide (one at a
  * time); ep_profile_end() returns EP_ERR_ARG if none is open.
- *   map_ms      Map kernel (PTPE: the whole count)
- *   closure_ms  boundary match + repair
- *   concat_ms   all Concatenate tree levels
- *   other_ms    cuts, fills, extraction, fallback
- *   calls       counting calls recorded
+ *   map_ms            Map step, both kernels (PTPE: the whole count)
+ *   closure_ms        boundary match + repair
+ *   concat_ms         all Concatenate tree levels
+ *   other_ms          cuts, fills, extraction, fallback
+ *   calls             counting calls recorded
+ *   map_ticks_ms      the tick Map kernel alone (part of map_ms)
+ *   map_positions_ms  the list or position Map kernel, or the scan Map kernel
+ *                     when windows are runs (part of map_ms)
+ *   map_filter_ms     the event filter feeding the list Map kernel (part of
+ *                     map_ms; 0 when the call does not use it)
  */
 typedef struct {
   double map_ms;
@@ -201,6 +209,9 @@ typedef struct {
   double concat_ms;
   double other_ms;
   int64_t calls;
+  double map_ticks_ms;
+  double map_positions_ms;
+  double map_filter_ms;
 } ep_profile;
 
 int ep_profile_begin(void);

@@ -53,11 +53,24 @@ MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 1), ("mapconcat", 2), ("mapconc
          ("mapconcat", 4), ("mapconcat", 7), ("mapconcat", 16), ("mapconcat", 64)]
 
 
-@pytest.mark.parametrize("split", ["auto", "ticks", "positions"])
+def _split_env(monkeypatch, split):
+    """Route segments: 'ticks' / 'positions' force one kernel for every segment
+    ('positions' means the list kernel where the call qualifies for it);
+    'position-kernel' forces the position kernel itself."""
+    if split == "position-kernel":
+        monkeypatch.setenv("EP_SPLIT", "positions")
+        monkeypatch.setenv("EP_NO_LIST", "1")
+    elif split != "auto":
+        monkeypatch.setenv("EP_SPLIT", split)
+
+
+SPLITS = ["auto", "ticks", "positions", "position-kernel"]
+
+
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("case", all_cases(), ids=lambda c: c["name"])
 def test_golden(fem, case, split, monkeypatch):
-    if split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
+    _split_env(monkeypatch, split)
     _log("golden %s %s" % (case["name"], split))
     want = np.array(case["expect"]["count"], np.int64)
     for mode, P in MODES:
@@ -74,10 +87,9 @@ def test_boundary_miss_is_repaired(fem):
     assert st["repairs"] >= 1 and st["fallbacks"] == 0 and st["n_segments"] == 2
 
 
-@pytest.mark.parametrize("split", ["auto", "ticks", "positions"])
+@pytest.mark.parametrize("split", SPLITS)
 def test_fuzz_small_streams(fem, split, monkeypatch):
-    if split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
+    _split_env(monkeypatch, split)
     rng = np.random.default_rng(31)
     checked = 0
     for trial in range(60):
@@ -118,10 +130,9 @@ def test_validate_rejects_unsorted(fem):
     assert ei.value.status == -4
 
 
-@pytest.mark.parametrize("split", ["auto", "ticks", "positions"])
+@pytest.mark.parametrize("split", SPLITS)
 def test_extreme_times(fem, split, monkeypatch):
-    if split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
+    _split_env(monkeypatch, split)
     # times at both ends of the int32 range: cut and window arithmetic must not overflow
     lo32, hi32 = -2 ** 31, 2 ** 31 - 1
     times = np.array([lo32, lo32, lo32 + 1, lo32 + 3, 0, 1, 2, hi32 - 3, hi32 - 1, hi32, hi32], np.int32)
@@ -151,19 +162,25 @@ def test_config_small(fem, name):
         assert st["fallbacks"] == 0
 
 
-@pytest.mark.parametrize("layout", ["scan", "machine-lanes", "ticks", "positions", "ticks-machine-lanes"])
+@pytest.mark.parametrize("layout", ["scan", "machine-lanes", "ticks", "positions", "ticks-machine-lanes",
+                                    "position-kernel", "position-kernel-machine-lanes",
+                                    "positions-machine-lanes"])
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "longchain"])
 def test_config_small_other_kernels(fem, name, layout, monkeypatch):
-    # the same counts from the scan Map kernel (run windows, every event) and
-    # from the bit kernel with one machine per lane
+    # the same counts from the scan Map kernel (run windows, every event), the
+    # tick kernel, the list kernel ('positions' where the call has few
+    # episodes), the position kernel, each with one machine per lane too
     if layout == "scan":
         monkeypatch.setenv("EP_FORCE_SCAN", "1")
     if "machine-lanes" in layout:
         monkeypatch.setenv("EP_LANES", "machine")
     if layout.startswith("ticks"):
         monkeypatch.setenv("EP_SPLIT", "ticks")
-    if layout == "positions":
+    if layout.startswith("positions"):
         monkeypatch.setenv("EP_SPLIT", "positions")
+    if layout.startswith("position-kernel"):
+        monkeypatch.setenv("EP_SPLIT", "positions")
+        monkeypatch.setenv("EP_NO_LIST", "1")
     wl = W.make_small(name)
     want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
     for mode, P in [("auto", 0), ("mapconcat", 64), ("mapconcat", 1000)]:
@@ -171,10 +188,9 @@ def test_config_small_other_kernels(fem, name, layout, monkeypatch):
         _check(got, want, "%s %s %s P=%d" % (name, layout, mode, P))
 
 
-@pytest.mark.parametrize("split", ["auto", "ticks"])
+@pytest.mark.parametrize("split", ["auto", "ticks", "position-kernel"])
 def test_fuzz_wide_windows(fem, split, monkeypatch):
-    if split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
+    _split_env(monkeypatch, split)
     # t_high up to 60 (64-bit windows) and beyond 63 (run windows), t_low near t_high
     rng = np.random.default_rng(41)
     for trial in range(30):
