@@ -84,6 +84,8 @@ def load_library(path: str | None = None):
     lib.ep_segment_cut.argtypes = [i32, i32, i32, i32]
     lib.ep_profile_begin.restype = ctypes.c_int
     lib.ep_profile_begin.argtypes = []
+    lib.ep_profile_begin_kernel.restype = ctypes.c_int
+    lib.ep_profile_begin_kernel.argtypes = [i32, i32]
     lib.ep_profile_end.restype = ctypes.c_int
     lib.ep_profile_end.argtypes = [ctypes.POINTER(EpProfile)]
     lib.ep_status_string.restype = ctypes.c_char_p
@@ -196,6 +198,15 @@ def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_
 def profile_begin():
     """Start recording per-phase GPU durations (HIP events) of later calls."""
     _check(load_library().ep_profile_begin())
+
+
+PROFILE_KERNELS = {"filter": 0, "ticks": 1, "positions": 2}
+
+
+def profile_begin_kernel(which: str, every: int = 1) -> None:
+    """Time one Map kernel ('filter', 'ticks' or 'positions') on one call in
+    `every`, recording nothing else."""
+    _check(load_library().ep_profile_begin_kernel(PROFILE_KERNELS[which], every))
 
 
 def profile_end() -> dict:

@@ -273,16 +273,34 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
     }
     if (b + gridDim.x < n_blocks) load(b + gridDim.x, tn, yn);  // in flight meanwhile
 
+    // events of this thread that exist (the last block may be partial)
+    const int64_t left = A.n - first;
+    const int n_valid = left >= kFilterPer ? kFilterPer : (left > 0 ? (int)left : 0);
     uint32_t sl[kFilterPer], ep[kFilterPer];
-    uint32_t c[2 * G];  // packed counts, two 16-bit fields per word
+    // per-thread counts in 8-bit fields, four episodes to a word (at most 16
+    // each): x * 0x204081 puts bit i of a 4-bit x at bit 8i with no carries
+    uint32_t c8[G];
 #pragma unroll
-    for (int g = 0; g < 2 * G; ++g) c[g] = 0;
+    for (int g = 0; g < G; ++g) c8[g] = 0;
 #pragma unroll
     for (int k = 0; k < kFilterPer; ++k) {
-      sl[k] = first + k < A.n ? type_slot(s_seen, s_rank, y[k]) : 0u;
+      const uint32_t yk = y[k];
+      const uint64_t w = s_seen[yk >> 6];
+      const uint32_t sh = yk & 63u;
+      const bool on = k < n_valid && ((w >> sh) & 1ull);
+      const uint32_t below = (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
+      sl[k] = on ? (uint32_t)s_rank[yk >> 6] + below + 1u : 0u;
       ep[k] = s_eps[sl[k]];
 #pragma unroll
-      for (int g = 0; g < 2 * G; ++g) c[g] += ((ep[k] >> (2 * g)) & 1u) | (((ep[k] >> (2 * g + 1)) & 1u) << 16);
+      for (int g = 0; g < G; ++g) c8[g] += __umul24((ep[k] >> (4 * g)) & 15u, 0x204081u) & 0x01010101u;
+    }
+    // widen to two 16-bit fields per word: word 2g + h holds episodes 4g + 2h
+    // and 4g + 2h + 1
+    uint32_t c[2 * G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      c[2 * g] = (c8[g] & 0xffu) | ((c8[g] & 0xff00u) << 8);
+      c[2 * g + 1] = ((c8[g] >> 16) & 0xffu) | ((c8[g] >> 24) << 16);
     }
     // block-wide exclusive scan of the packed counts: wave scan, then waves
     uint32_t incl[2 * G];
@@ -549,9 +567,13 @@ struct ProfRecord {
   // after Map, after closure, after Concatenate
   hipEvent_t ev[kProfEvents];
   hipEvent_t end;
+  int which;  // -1: every phase; else the one Map kernel timed (EP_PROFILE_*)
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+int g_prof_which = -1;   // -1: every phase of every call
+int g_prof_every = 1;    // one call in this many is recorded
+int64_t g_prof_calls = 0;
 std::vector<ProfRecord> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -567,13 +589,15 @@ hipEvent_t pooled_event() {
   return e;
 }
 
-int prof_record_start(ProfRecord* r, hipStream_t s) {
+int prof_record_start(ProfRecord* r, int which, hipStream_t s) {
+  r->which = which;
   {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (int i = 0; i < kProfEvents; ++i)
       if (!(r->ev[i] = pooled_event())) return EP_ERR_HIP;
     if (!(r->end = pooled_event())) return EP_ERR_HIP;
   }
+  if (which >= 0) return EP_OK;
   return hipEventRecord(r->ev[0], s) == hipSuccess ? EP_OK : EP_ERR_HIP;
 }
 
@@ -1048,12 +1072,22 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
 
     mark();  // upload
     bool prof = false;
+    int prof_which = -1;
     ProfRecord rec{};
     {
       std::lock_guard<std::mutex> lock(g_prof_mu);
-      prof = g_prof_on;
+      if (g_prof_on) {
+        prof_which = g_prof_which;
+        prof = (g_prof_calls++ % g_prof_every) == 0;
+      }
     }
-    if (prof && (status = prof_record_start(&rec, stream))) break;
+    if (prof && (status = prof_record_start(&rec, prof_which, stream))) break;
+    // records boundary i when the session times it (every boundary, or the
+    // two around the one Map kernel it times)
+    auto rec_at = [&](int i) {
+      if (prof && (prof_which < 0 || i == prof_which + 1 || i == prof_which + 2))
+        (void)hipEventRecord(rec.ev[i], stream);
+    };
     SetupArgs sa;
     sa.times = times; sa.n = n_events; sa.P = P; sa.max_span = max_span;
     sa.tau = d_tau; sa.beg = d_beg; sa.end = d_end;
@@ -1097,7 +1131,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       const int64_t want = (int64_t)info->cu_count * per_cu;
       ma.eg_blocks = std::min<int64_t>(ma.n_egroups, std::max<int64_t>(1, (want + seg_groups - 1) / seg_groups));
     }
-    if (prof) hipEventRecord(rec.ev[1], stream);
+    rec_at(1);
     hipError_t le = hipSuccess;
     if (L.list) {
       FilterArgs fa;
@@ -1118,21 +1152,21 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         hipLaunchKernelGGL(filter_kernel<8>, fg, fb, 0, stream, fa);
       le = hipGetLastError();
     }
-    if (prof) hipEventRecord(rec.ev[2], stream);
+    rec_at(2);
     if (le == hipSuccess && !L.bits) {
-      if (prof) hipEventRecord(rec.ev[3], stream);  // no tick kernel: an empty interval
+      rec_at(3);  // no tick kernel: an empty interval
       le = Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
     } else if (le == hipSuccess) {
       // each segment goes to the tick kernel or, by segment_uses_ticks, to the
       // list or the position kernel
       if (L.split != 2) le = Lr->map_ticks(ma, L.all_mach, mgrid, dim3(L.block), L.lds_ticks, stream);
-      if (prof) hipEventRecord(rec.ev[3], stream);
+      rec_at(3);
       if (le == hipSuccess && L.split != 1)
         le = L.list ? Lr->map_list(ma, L.win, L.all_mach, mgrid, dim3(L.block), stream)
                     : Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream);
     }
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
-    if (prof) hipEventRecord(rec.ev[4], stream);
+    rec_at(4);
 
     mark();  // map launches
     if (P > 1) {
@@ -1146,7 +1180,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         status = EP_ERR_HIP;
         break;
       }
-      if (prof) hipEventRecord(rec.ev[5], stream);
+      rec_at(5);
       // Concatenate tree: each launch joins groups of `members` blocks in LDS
       int members = kConcatMembers;
       while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
@@ -1159,10 +1193,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       if (status != EP_OK) break;
     }
-    if (prof) {
-      if (P <= 1) hipEventRecord(rec.ev[5], stream);
-      hipEventRecord(rec.ev[6], stream);
-    }
+    if (P <= 1) rec_at(5);
+    rec_at(6);
     mark();  // closure + tree launches
     FallbackArgs fa;
     fa.times = times; fa.types = types;
@@ -1175,7 +1207,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       break;
     }
     if (prof) {
-      hipEventRecord(rec.end, stream);
+      if (prof_which < 0) (void)hipEventRecord(rec.end, stream);
       std::lock_guard<std::mutex> lock(g_prof_mu);
       g_prof.push_back(rec);
     }
@@ -1208,6 +1240,20 @@ extern "C" int ep_profile_begin(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
   g_prof.clear();
   g_prof_on = true;
+  g_prof_which = -1;
+  g_prof_every = 1;
+  g_prof_calls = 0;
+  return EP_OK;
+}
+
+extern "C" int ep_profile_begin_kernel(int32_t which, int32_t every) {
+  if (which < EP_PROFILE_FILTER || which > EP_PROFILE_POSITIONS || every < 1) return EP_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  g_prof.clear();
+  g_prof_on = true;
+  g_prof_which = which;
+  g_prof_every = every;
+  g_prof_calls = 0;
   return EP_OK;
 }
 
@@ -1222,6 +1268,23 @@ extern "C" int ep_profile_end(ep_profile* out) {
   ep_profile acc{};
   int status = EP_OK;
   for (ProfRecord& r : recs) {
+    if (r.which >= 0) {
+      // one Map kernel: the interval between its two boundaries
+      float k_ms = 0.f;
+      if (hipEventSynchronize(r.ev[r.which + 2]) != hipSuccess ||
+          hipEventElapsedTime(&k_ms, r.ev[r.which + 1], r.ev[r.which + 2]) != hipSuccess)
+        status = EP_ERR_HIP;
+      double* field = r.which == EP_PROFILE_FILTER
+                          ? &acc.map_filter_ms
+                          : (r.which == EP_PROFILE_TICKS ? &acc.map_ticks_ms : &acc.map_positions_ms);
+      *field += k_ms;
+      acc.map_ms += k_ms;
+      acc.calls += 1;
+      std::lock_guard<std::mutex> lock(g_prof_mu);
+      for (int i = 0; i < kProfEvents; ++i) g_event_pool.push_back(r.ev[i]);
+      g_event_pool.push_back(r.end);
+      continue;
+    }
     float ms[kProfEvents] = {};
     if (hipEventSynchronize(r.end) != hipSuccess) status = EP_ERR_HIP;
     hipEvent_t seq[kProfEvents + 1];

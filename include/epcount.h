@@ -217,6 +217,17 @@ typedef struct {
 int ep_profile_begin(void);
 int ep_profile_end(ep_profile* out);
 
+/*
+ * A lighter session for timing one Map kernel while the calls themselves are
+ * being timed: only the two events around that kernel are recorded, on one
+ * call in `every` (every >= 1), so the calls' own duration is barely
+ * disturbed (each recorded event costs the stream a few microseconds).
+ * ep_profile_end() then fills map_ms, the chosen kernel's field and calls
+ * (= calls recorded).  Returns EP_ERR_ARG for an unknown kernel or every < 1.
+ */
+enum { EP_PROFILE_FILTER = 0, EP_PROFILE_TICKS = 1, EP_PROFILE_POSITIONS = 2 };
+int ep_profile_begin_kernel(int32_t which, int32_t every);
+
 /* Static text for a status code. */
 const char* ep_status_string(int status);
 
