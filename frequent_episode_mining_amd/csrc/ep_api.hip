@@ -371,9 +371,9 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
 // right block R maps each (a, c, b) of L to (a, c + c', b') for the tuple of R
 // whose key a' equals b.  Launched with stride 1, then `members`, then
 // members^2, ..., until one member is left.
-constexpr int kConcatMembers = 256;
+constexpr int kConcatMembers = 512;  // threads of a tree workgroup at most
 
-__global__ __launch_bounds__(kBlock) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
+__global__ __launch_bounds__(kConcatMembers) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
                                                              int32_t P, int64_t stride, int32_t members,
                                                              int64_t groups) {
   extern __shared__ __align__(16) unsigned char smem[];
