@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # node-type test, the window check and the window update, ~10 int32 ops.
 OPS_PER_RELEVANT_PAIR = 10
 KERNEL_SOURCES = ["frequent_episode_mining_amd/csrc/ep_device.hpp",
-                  "frequent_episode_mining_amd/csrc/ep_inst.hip"]
+                  "frequent_episode_mining_amd/csrc/ep_inst.hip",
+                  "frequent_episode_mining_amd/csrc/ep_api.hip"]
 
 
 def log(msg):
