@@ -7,8 +7,10 @@ it shares no code with the HIP path.
 The arithmetic lives in ``alpha0.c`` (the reference serial state machine
 alpha_0 of the page "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
 Episodes Using Graphics Processors", Fig. 3 text and the opening section's
-Algorithm 1, restated from its description).  This module only compiles it with
-gcc and marshals numpy arrays through ctypes.
+Algorithm 1, restated from its description; and the upper-bound-only machine of
+Algorithm A2).  This module compiles it with gcc and marshals numpy arrays
+through ctypes; :func:`two_pass` strings the two machines together in the order
+of the two-pass elimination section (A2+A1).
 """
 from __future__ import annotations
 
@@ -51,6 +53,15 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_count_batch_mode.restype = ctypes.c_int
+        lib.oracle_count_batch_mode.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_count_one_upper.restype = ctypes.c_int64
+        lib.oracle_count_one_upper.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -93,6 +104,57 @@ def count(times, types, ep_types, t_low, t_high, n_threads: int | None = None):
     if np.any(out < 0):
         raise MemoryError("oracle ran out of memory")
     return out
+
+
+def count_upper(times, types, ep_types, t_high, n_threads: int | None = None):
+    """Counts of the relaxed episodes alpha' (Algorithm A2: every lower bound 0,
+    upper bounds kept), as int64[S].  ``ep_types``: [S, N]; ``t_high``: [S, N-1].
+    """
+    ep_types = np.ascontiguousarray(ep_types, dtype=np.uint16)
+    if ep_types.ndim == 1:
+        ep_types = ep_types[None, :]
+    S, N = ep_types.shape
+    t_high = np.ascontiguousarray(t_high, dtype=np.int32).reshape(S, max(N - 1, 0))
+    t_low = np.zeros_like(t_high)
+    times, types, ep_types, t_low, t_high = _prep(times, types, ep_types, t_low, t_high)
+    out = np.zeros(S, dtype=np.int64)
+    if S == 0:
+        return out
+    if n_threads is None:
+        n_threads = os.cpu_count() or 1
+    lib = _load()
+    lib.oracle_count_batch_mode(times.ctypes.data, types.ctypes.data, times.size, N,
+                                ep_types.ctypes.data, t_low.ctypes.data, t_high.ctypes.data,
+                                S, out.ctypes.data, int(n_threads), 1)
+    if np.any(out < 0):
+        raise MemoryError("oracle ran out of memory")
+    return out
+
+
+def two_pass(times, types, ep_types, t_low, t_high, threshold: int,
+             n_threads: int | None = None):
+    """Algorithm A2+A1 (two-pass elimination section) for a support threshold.
+
+    First pass: count every relaxed episode alpha' (:func:`count_upper`) and
+    drop the episodes whose relaxed count is below ``threshold``.  Second
+    pass: count the remaining episodes alpha exactly (:func:`count`).
+    Returns ``(counts, upper)``: ``upper`` = the first pass's counts;
+    ``counts[e]`` = count(alpha_e) for the episodes kept, -1 for the dropped
+    ones.  The frequent episodes are those with ``counts >= threshold``.
+    """
+    ep_types = np.ascontiguousarray(ep_types, dtype=np.uint16)
+    if ep_types.ndim == 1:
+        ep_types = ep_types[None, :]
+    S, N = ep_types.shape
+    t_low = np.ascontiguousarray(t_low, dtype=np.int32).reshape(S, max(N - 1, 0))
+    t_high = np.ascontiguousarray(t_high, dtype=np.int32).reshape(S, max(N - 1, 0))
+    _prep(times, types, ep_types, t_low, t_high)  # validates the full table
+    upper = count_upper(times, types, ep_types, t_high, n_threads)
+    keep = np.flatnonzero(upper >= threshold)
+    counts = np.full(S, -1, dtype=np.int64)
+    if keep.size:
+        counts[keep] = count(times, types, ep_types[keep], t_low[keep], t_high[keep], n_threads)
+    return counts, upper
 
 
 def count_timed(times, types, ep_types, t_low, t_high, n_threads: int | None = None):

@@ -122,6 +122,68 @@ int64_t oracle_count_one(const int32_t* times, const uint16_t* types, int64_t n,
   return failed ? -1 : count;
 }
 
+/*
+ * Algorithm A2 (section on the constrained problem with upper limits only):
+ * the episode alpha' keeps the event types and upper bounds of alpha and
+ * relaxes every lower bound to 0, so a predecessor qualifies when
+ * 0 < t - t' <= hi.  Among the entries of the node list that are earlier
+ * than t, the latest one is then the best candidate, so the constraint check
+ * needs only that entry instead of a scan of the list (the O(1) check the
+ * two-pass elimination section contrasts with the list scan).  A list is
+ * therefore kept as its latest time and the latest time strictly before
+ * that one (an entry on the tick of t itself is never a predecessor).
+ * Counting, resets and non-overlap are those of oracle_count_one.
+ */
+typedef struct {
+  int64_t last;   /* latest appended time, or NONE */
+  int64_t before; /* latest appended time < last, or NONE */
+} tlast;
+
+#define TLAST_NONE INT64_MIN
+
+static void tlast_push(tlast* L, int64_t t) {
+  if (L->last == TLAST_NONE || t > L->last) {
+    L->before = L->last;
+    L->last = t;
+  }
+}
+
+/* Is there an appended t' with 0 < t - t' <= hi?  Only the latest t' < t matters. */
+static int tlast_has_predecessor(const tlast* L, int64_t t, int64_t hi) {
+  int64_t p = (L->last != TLAST_NONE && L->last < t) ? L->last : L->before;
+  return p != TLAST_NONE && p < t && t - p <= hi;
+}
+
+int64_t oracle_count_one_upper(const int32_t* times, const uint16_t* types, int64_t n,
+                               int32_t N, const uint16_t* ep_types, const int32_t* hi) {
+  if (N < 1) return -1;
+  tlast* L = (tlast*)malloc(sizeof(tlast) * (size_t)(N > 1 ? N - 1 : 1));
+  if (!L) return -1;
+  for (int k = 0; k < N - 1; ++k) L[k].last = L[k].before = TLAST_NONE;
+  int64_t r = INT64_MIN;
+  int64_t count = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = times[i];
+    uint16_t y = types[i];
+    if (t <= r) continue;
+    if (ep_types[N - 1] == y) {
+      int done = (N == 1) || tlast_has_predecessor(&L[N - 2], t, hi[N - 2]);
+      if (done) {
+        count += 1;
+        r = t;
+        for (int k = 0; k < N - 1; ++k) L[k].last = L[k].before = TLAST_NONE;
+        continue;
+      }
+    }
+    for (int k = 0; k < N - 1; ++k) {
+      if (ep_types[k] != y) continue;
+      if (k == 0 || tlast_has_predecessor(&L[k - 1], t, hi[k - 1])) tlast_push(&L[k], t);
+    }
+  }
+  free(L);
+  return count;
+}
+
 /* ---- episodes are independent (opening section): count them on a thread pool ---- */
 
 typedef struct {
@@ -134,7 +196,8 @@ typedef struct {
   const int32_t* hi;        /* [S*(N-1)] */
   int64_t S;
   int64_t* out;
-  int64_t next; /* shared work counter */
+  int upper_only; /* count alpha' (Algorithm A2) instead of alpha */
+  int64_t next;   /* shared work counter */
   pthread_mutex_t mu;
 } batch_job;
 
@@ -146,19 +209,23 @@ static void* batch_worker(void* arg) {
     pthread_mutex_unlock(&J->mu);
     if (e >= J->S) break;
     int64_t m = J->N > 1 ? J->N - 1 : 0;
-    J->out[e] = oracle_count_one(J->times, J->types, J->n, J->N, J->ep_types + e * J->N,
-                                 J->lo + e * m, J->hi + e * m);
+    J->out[e] = J->upper_only
+                    ? oracle_count_one_upper(J->times, J->types, J->n, J->N,
+                                             J->ep_types + e * J->N, J->hi + e * m)
+                    : oracle_count_one(J->times, J->types, J->n, J->N, J->ep_types + e * J->N,
+                                       J->lo + e * m, J->hi + e * m);
   }
   return NULL;
 }
 
 /*
- * Count S episodes of N nodes each.  n_threads <= 0 means one thread.
- * Returns the number of threads used.
+ * Count S episodes of N nodes each (upper_only: their relaxed versions alpha',
+ * lo unused).  n_threads <= 0 means one thread.  Returns the number of threads
+ * used.
  */
-int oracle_count_batch(const int32_t* times, const uint16_t* types, int64_t n, int32_t N,
-                       const uint16_t* ep_types, const int32_t* lo, const int32_t* hi,
-                       int64_t S, int64_t* out, int n_threads) {
+int oracle_count_batch_mode(const int32_t* times, const uint16_t* types, int64_t n, int32_t N,
+                            const uint16_t* ep_types, const int32_t* lo, const int32_t* hi,
+                            int64_t S, int64_t* out, int n_threads, int upper_only) {
   if (n_threads < 1) n_threads = 1;
   if ((int64_t)n_threads > S) n_threads = S > 0 ? (int)S : 1;
   batch_job J;
@@ -171,6 +238,7 @@ int oracle_count_batch(const int32_t* times, const uint16_t* types, int64_t n, i
   J.hi = hi;
   J.S = S;
   J.out = out;
+  J.upper_only = upper_only;
   J.next = 0;
   pthread_mutex_init(&J.mu, NULL);
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)n_threads);
@@ -182,4 +250,10 @@ int oracle_count_batch(const int32_t* times, const uint16_t* types, int64_t n, i
   free(th);
   pthread_mutex_destroy(&J.mu);
   return started > 0 ? started : 1;
+}
+
+int oracle_count_batch(const int32_t* times, const uint16_t* types, int64_t n, int32_t N,
+                       const uint16_t* ep_types, const int32_t* lo, const int32_t* hi,
+                       int64_t S, int64_t* out, int n_threads) {
+  return oracle_count_batch_mode(times, types, n, N, ep_types, lo, hi, S, out, n_threads, 0);
 }

@@ -31,6 +31,18 @@ def test_golden_fixtures(case):
     # the brute force agrees with the hand derivation too
     assert brute_count(case["times"], case["types"], case["ep_types"], case["t_low"],
                        case["t_high"]) == case["expect"]["count"][0]
+    if "upper" in case["expect"]:
+        # Algorithm A2: the relaxed episode (lower bounds 0), by hand and by brute force
+        got_u = oracle.count_upper(case["times"], case["types"], case["ep_types"], case["t_high"])
+        assert got_u[0] == case["expect"]["upper"][0]
+        assert brute_count(case["times"], case["types"], case["ep_types"],
+                           np.zeros_like(case["t_low"]), case["t_high"]) == case["expect"]["upper"][0]
+    if "two_pass" in case["expect"]:
+        tp = case["expect"]["two_pass"]
+        for theta, want in zip(tp[0::2], tp[1::2]):
+            counts, upper = oracle.two_pass(case["times"], case["types"], case["ep_types"],
+                                            case["t_low"], case["t_high"], theta)
+            assert counts[0] == want and upper[0] == case["expect"]["upper"][0]
     if "segments" in case["expect"]:
         cut = case["cut"]
         left = case["times"] <= cut
@@ -143,6 +155,62 @@ def test_invariants():
             assert base[e] <= cap
 
 
+# ---- Algorithm A2 (upper bounds only) and the two-pass elimination A2+A1 ----
+
+
+def test_upper_only_matches_bruteforce_on_tiny_streams():
+    # the relaxed episode's count is the most disjoint occurrences with 0 < dt <= hi
+    nonzero = 0
+    for times, types, ep, lo, hi in _random_cases(11, 1500):
+        want = brute_count(times, types, ep, np.zeros_like(lo), hi)
+        got = oracle.count_upper(times, types, ep[None], hi[None])[0]
+        assert got == want, (times.tolist(), types.tolist(), ep.tolist(), hi.tolist())
+        nonzero += want > 0
+    assert nonzero > 300
+
+
+def test_upper_only_agrees_with_list_machine():
+    # two machines for the same relaxed episode: the O(1) latest-entry check and
+    # alpha_0's list scan run with every lower bound set to 0
+    rng = np.random.default_rng(17)
+    for _ in range(40):
+        times, types = W.random_stream(rng, int(rng.integers(100, 3000)), 5, max_gap=3)
+        ep, lo, hi = W.random_episodes(rng, 12, int(rng.integers(1, 6)), 5, max_hi=12)
+        assert np.array_equal(oracle.count_upper(times, types, ep, hi),
+                              oracle.count(times, types, ep, np.zeros_like(lo), hi))
+
+
+def test_upper_only_bounds_the_count():
+    # every occurrence of alpha is one of alpha', so count(alpha') >= count(alpha)
+    rng = np.random.default_rng(19)
+    strictly = 0
+    for _ in range(40):
+        times, types = W.random_stream(rng, int(rng.integers(100, 2000)), 4, max_gap=3)
+        ep, lo, hi = W.random_episodes(rng, 12, int(rng.integers(2, 5)), 4, max_hi=10)
+        up = oracle.count_upper(times, types, ep, hi)
+        ex = oracle.count(times, types, ep, lo, hi)
+        assert np.all(up >= ex)
+        strictly += int(np.sum(up > ex))
+    assert strictly > 50
+
+
+def test_two_pass_keeps_exactly_the_frequent_episodes():
+    # A2+A1 returns the exact count of every episode whose relaxed count reaches
+    # the threshold, and drops only episodes whose exact count is below it
+    rng = np.random.default_rng(23)
+    for _ in range(20):
+        times, types = W.random_stream(rng, int(rng.integers(200, 3000)), 4, max_gap=3)
+        ep, lo, hi = W.random_episodes(rng, 24, int(rng.integers(2, 5)), 4, max_hi=10)
+        exact = oracle.count(times, types, ep, lo, hi)
+        theta = int(np.quantile(exact, rng.uniform(0.2, 0.9))) if exact.size else 0
+        counts, upper = oracle.two_pass(times, types, ep, lo, hi, theta)
+        kept = counts >= 0
+        assert np.array_equal(kept, upper >= theta)
+        assert np.array_equal(counts[kept], exact[kept])
+        assert np.all(exact[~kept] < theta)
+        assert np.array_equal(np.flatnonzero(counts >= theta), np.flatnonzero(exact >= theta))
+
+
 def test_tiny_workload_planted_floor():
     # the tiny workload plants 20 A->B->C chains with gaps <= 4 inside (0,5]
     wl = W.make("tiny")
@@ -176,6 +244,21 @@ MUTANTS = {
 }
 
 
+MUTANTS_UPPER = {
+    "upper_forgets_earlier_entry": ("? L->last : L->before;", "? L->last : TLAST_NONE;"),
+    "upper_same_tick_chains": ("int64_t p = (L->last != TLAST_NONE && L->last < t) ? L->last : L->before;\n"
+                               "  return p != TLAST_NONE && p < t && t - p <= hi;",
+                               "int64_t p = L->last;\n  return p != TLAST_NONE && p <= t && t - p <= hi;"),
+    "upper_bound_exclusive_a2": ("return p != TLAST_NONE && p < t && t - p <= hi;",
+                                 "return p != TLAST_NONE && p < t && t - p < hi;"),
+    "upper_no_reset": ("        count += 1;\n        r = t;\n        for (int k = 0; k < N - 1; ++k) L[k].last",
+                       "        count += 1;\n        r = t;\n        if (0) for (int k = 0; k < N - 1; ++k) L[k].last"),
+    "upper_keeps_first_time": ("if (L->last == TLAST_NONE || t > L->last) {", "if (L->last == TLAST_NONE) {"),
+    "upper_wrong_interval_index": ("tlast_has_predecessor(&L[k - 1], t, hi[k - 1])",
+                                   "tlast_has_predecessor(&L[k - 1], t, hi[0])"),
+}
+
+
 def _build_mutant(tmp_path, name, old, new):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "alpha0.c")).read()
     assert old in src, name
@@ -187,6 +270,8 @@ def _build_mutant(tmp_path, name, old, new):
     lib = ctypes.CDLL(str(so))
     lib.oracle_count_one.restype = ctypes.c_int64
     lib.oracle_count_one.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 3
+    lib.oracle_count_one_upper.restype = ctypes.c_int64
+    lib.oracle_count_one_upper.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 2
     return lib
 
 
@@ -213,6 +298,33 @@ def test_pins_catch_mutants(tmp_path, name):
     if not caught:
         for times, types, ep, lo, hi in _random_cases(7, 1500):
             if _mutant_count(lib, times, types, ep, lo, hi) != brute_count(times, types, ep, lo, hi):
+                caught = True
+                break
+    assert caught, "mutant %s survived the pins" % name
+
+
+def _mutant_count_upper(lib, times, types, ep, hi):
+    times = np.ascontiguousarray(times, np.int32)
+    types = np.ascontiguousarray(types, np.uint16)
+    ep = np.ascontiguousarray(ep, np.uint16)
+    hi = np.ascontiguousarray(hi, np.int32)
+    return lib.oracle_count_one_upper(times.ctypes.data, types.ctypes.data, times.size, ep.size,
+                                      ep.ctypes.data, hi.ctypes.data)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_UPPER))
+def test_pins_catch_upper_only_mutants(tmp_path, name):
+    old, new = MUTANTS_UPPER[name]
+    lib = _build_mutant(tmp_path, name, old, new)
+    caught = False
+    for case in CASES:
+        if "upper" in case["expect"] and _mutant_count_upper(
+                lib, case["times"], case["types"], case["ep_types"], case["t_high"]) != case["expect"]["upper"][0]:
+            caught = True
+            break
+    if not caught:
+        for times, types, ep, lo, hi in _random_cases(11, 1500):
+            if _mutant_count_upper(lib, times, types, ep, hi) != brute_count(times, types, ep, np.zeros_like(lo), hi):
                 caught = True
                 break
     assert caught, "mutant %s survived the pins" % name
