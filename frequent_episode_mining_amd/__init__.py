@@ -42,7 +42,7 @@ class EpStats(ctypes.Structure):
 
 class EpOptions(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
-                ("validate", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("validate", ctypes.c_int32), ("upper_only", ctypes.c_int32),
                 ("stats", ctypes.POINTER(EpStats))]
 
 
@@ -77,6 +77,9 @@ def load_library(path: str | None = None):
     lib.ep_count_episodes_ex.restype = ctypes.c_int
     lib.ep_count_episodes_ex.argtypes = [vp, vp, i64, EpEpisodes, i64, vp, vp,
                                          ctypes.POINTER(EpOptions)]
+    lib.ep_count_two_pass.restype = ctypes.c_int
+    lib.ep_count_two_pass.argtypes = [vp, vp, i64, EpEpisodes, i64, i64, vp, vp,
+                                      ctypes.POINTER(ctypes.c_int64), vp, ctypes.POINTER(EpOptions)]
     lib.ep_plan.restype = ctypes.c_int
     lib.ep_plan.argtypes = [i64, i32, i64, i32, i32, i32, i32,
                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -141,47 +144,104 @@ def _device_ptr(t, dtype_ok, name):
     return t.data_ptr() if t.numel() else None
 
 
+def _stream_args(times, types):
+    import torch
+    tp = _device_ptr(times, (torch.int32,), "times")
+    yp = _device_ptr(types, (torch.int16, getattr(torch, "uint16", torch.int16)), "types")
+    if types.numel() != times.numel():
+        raise ValueError("times and types differ in length")
+    return tp, yp, times.numel()
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _on_device(device, fn):
+    import torch
+    if torch.cuda.current_device() == device.index:
+        return fn()
+    with torch.cuda.device(device):
+        return fn()
+
+
+def _stats_dict(st):
+    return {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,
+            "max_runs": st.max_runs, "kernels": st.kernels, "repairs": st.repairs,
+            "fallbacks": st.fallbacks}
+
+
 def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str = "auto",
                    n_segments: int = 0, validate: bool = False, stats: bool = False,
-                   out=None, stream=None):
+                   upper_only: bool = False, out=None, stream=None):
     """Counts of S episodes over one GPU-resident event stream.
 
     times: int32 [n] GPU tensor, non-decreasing.  types: uint16 (or int16, same
     bits) [n] GPU tensor.  ep_types: [S, N] host array (or an EpisodeTable);
-    t_low/t_high: [S, N-1] host arrays.  Returns an int64 [S] GPU tensor (and
-    the ep_stats dict if ``stats``).  Enqueued on ``stream`` (default: torch's
-    current stream); ``validate``/``stats`` synchronise that stream.
+    t_low/t_high: [S, N-1] host arrays.  ``upper_only`` counts the relaxed
+    episodes (every lower bound taken as 0; ``t_low`` may be None).  Returns an
+    int64 [S] GPU tensor (and the ep_stats dict if ``stats``).  Enqueued on
+    ``stream`` (default: torch's current stream); ``validate``/``stats``
+    synchronise that stream.
     """
     import torch
+    if upper_only and t_low is None and not isinstance(ep_types, EpisodeTable):
+        t_low = np.zeros_like(np.asarray(t_high, dtype=np.int32))
     table = ep_types if isinstance(ep_types, EpisodeTable) else EpisodeTable(ep_types, t_low, t_high)
-    tp = _device_ptr(times, (torch.int32,), "times")
-    yp = _device_ptr(types, (torch.int16, getattr(torch, "uint16", torch.int16)), "types")
-    n = times.numel()
-    if types.numel() != n:
-        raise ValueError("times and types differ in length")
+    tp, yp, n = _stream_args(times, types)
     S = table.n_episodes
     if out is None:
         out = torch.empty(S, dtype=torch.int64, device=times.device)
     op = _device_ptr(out, (torch.int64,), "out") if S else None
-    if stream is None:
-        stream = torch.cuda.current_stream(times.device)
-    sp = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    sp = _stream_handle(stream, times.device)
+    lib = load_library()
+    st = EpStats()
+    opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), int(bool(upper_only)),
+                    ctypes.pointer(st) if stats else None)
+    status = _on_device(times.device, lambda: lib.ep_count_episodes_ex(
+        tp, yp, n, table.as_struct(), S, op, sp, ctypes.byref(opt)))
+    _check(status)
+    if stats:
+        return out, _stats_dict(st)
+    return out
+
+
+def count_two_pass(times, types, ep_types, t_low=None, t_high=None, *, threshold: int,
+                   mode: str = "auto", n_segments: int = 0, validate: bool = False,
+                   stats: bool = False, stream=None):
+    """Two-pass elimination (A2 then A1) for a support threshold.
+
+    Returns ``(counts, upper, n_kept)`` (plus the second pass's ep_stats dict
+    if ``stats``): ``upper`` = int64 [S] GPU tensor of the relaxed counts,
+    ``counts`` = int64 [S] GPU tensor with the exact count of every episode
+    whose relaxed count reaches ``threshold`` and -1 for the others, ``n_kept``
+    = how many were counted exactly.  Synchronises ``stream`` once between the
+    passes.
+    """
+    import torch
+    table = ep_types if isinstance(ep_types, EpisodeTable) else EpisodeTable(ep_types, t_low, t_high)
+    tp, yp, n = _stream_args(times, types)
+    S = table.n_episodes
+    counts = torch.empty(S, dtype=torch.int64, device=times.device)
+    upper = torch.empty(S, dtype=torch.int64, device=times.device)
+    cp = _device_ptr(counts, (torch.int64,), "counts") if S else None
+    up = _device_ptr(upper, (torch.int64,), "upper") if S else None
+    sp = _stream_handle(stream, times.device)
     lib = load_library()
     st = EpStats()
     opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), 0,
                     ctypes.pointer(st) if stats else None)
-    if torch.cuda.current_device() == times.device.index:
-        status = lib.ep_count_episodes_ex(tp, yp, n, table.as_struct(), S, op, sp, ctypes.byref(opt))
-    else:
-        with torch.cuda.device(times.device):
-            status = lib.ep_count_episodes_ex(tp, yp, n, table.as_struct(), S, op, sp,
-                                              ctypes.byref(opt))
+    kept = ctypes.c_int64(0)
+    status = _on_device(times.device, lambda: lib.ep_count_two_pass(
+        tp, yp, n, table.as_struct(), S, int(threshold), cp, up, ctypes.byref(kept), sp,
+        ctypes.byref(opt)))
     _check(status)
     if stats:
-        return out, {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,
-                     "max_runs": st.max_runs, "kernels": st.kernels, "repairs": st.repairs,
-                     "fallbacks": st.fallbacks}
-    return out
+        return counts, upper, kept.value, _stats_dict(st)
+    return counts, upper, kept.value
 
 
 def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_segments: int = 0,

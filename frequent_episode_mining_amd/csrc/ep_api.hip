@@ -441,6 +441,56 @@ __global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n,
   if (i < n) p[i] = v;
 }
 
+// Two-pass elimination, last step: the second pass wrote the kept episodes'
+// exact counts, in episode order, to out[0 .. kept); spread them to their
+// episodes in place and mark the dropped ones -1.  Episode e is kept when
+// upper[e] >= theta; its compact index is the number of kept episodes before
+// it, which is <= e.  One workgroup walks 1,024-episode chunks from the last
+// one down: every thread reads its value, the workgroup waits, then writes.
+// A chunk writes only its own indices, which no lower chunk reads (their
+// compact indices are below the chunk), and reads happen before the barrier
+// that precedes the chunk's writes.
+constexpr int kMergeBlock = 1024;
+__global__ __launch_bounds__(kMergeBlock) void two_pass_merge_kernel(const int64_t* upper, int64_t S,
+                                                                     int64_t theta, int64_t* out) {
+  constexpr int kWaves = kMergeBlock / kWave;
+  __shared__ int32_t s_wave[kWaves];
+  __shared__ int64_t s_part[kWaves];
+  __shared__ int64_t s_val[kMergeBlock];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  // kept episodes in all
+  int64_t local = 0;
+  for (int64_t e = tid; e < S; e += kMergeBlock) local += upper[e] >= theta;
+  for (int off = kWave / 2; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  if (lane == 0) s_part[wave] = local;
+  __syncthreads();
+  int64_t total = 0;
+  for (int w = 0; w < kWaves; ++w) total += s_part[w];
+  int64_t after = 0;  // kept episodes at indices above the current chunk
+  for (int64_t c = (S + kMergeBlock - 1) / kMergeBlock - 1; c >= 0; --c) {
+    const int64_t e = c * kMergeBlock + tid;
+    const bool keep = e < S && upper[e] >= theta;
+    const uint64_t ballot = __ballot(keep);
+    const int below = __popcll(ballot & ((1ull << lane) - 1));
+    __syncthreads();  // the previous chunk is done with s_wave
+    if (lane == 0) s_wave[wave] = __popcll(ballot);
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      chunk += s_wave[w];
+    }
+    const int64_t rank = total - after - chunk + before + below;
+    // the value goes through LDS, so the read has landed before the barrier
+    s_val[tid] = keep ? out[rank] : -1;
+    __syncthreads();
+    if (e < S) out[e] = s_val[tid];
+    after += chunk;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* times, int64_t n,
                                                               int32_t* bad) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -795,6 +845,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const int64_t S = n_episodes;
   if (n_events < 0 || S < 0 || n_events > INT32_MAX) return EP_ERR_ARG;
   if (N < 1 || N > EP_MAX_NODES) return EP_ERR_NODES;
+  // Algorithm A2: the relaxed episodes, every lower bound taken as 0
+  std::vector<int32_t> zero_low;
+  if (opt && opt->upper_only && S > 0 && N > 1) {
+    zero_low.assign((size_t)(S * (N - 1)), 0);
+    episodes.t_low = zero_low.data();
+  }
   if (S > 0 && (!out_counts || !episodes.types)) return EP_ERR_ARG;
   if (S > 0 && N > 1 && (!episodes.t_low || !episodes.t_high)) return EP_ERR_ARG;
   if (n_events > 0 && S > 0 && (!times || !types)) return EP_ERR_ARG;
@@ -1326,6 +1382,72 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   }
   fprintf(stderr, "\n");
   return st;
+}
+
+extern "C" int ep_count_two_pass(const int32_t* times, const uint16_t* types, int64_t n_events,
+                                 ep_episodes episodes, int64_t n_episodes, int64_t threshold,
+                                 int64_t* out_counts, int64_t* out_upper, int64_t* n_kept,
+                                 hipStream_t stream, const ep_options* opt) {
+  using namespace epk;
+  const int32_t N = episodes.n_nodes;
+  const int64_t S = n_episodes;
+  if (n_kept) *n_kept = 0;
+  if (S < 0 || n_events < 0 || n_events > INT32_MAX) return EP_ERR_ARG;
+  if (N < 1 || N > EP_MAX_NODES) return EP_ERR_NODES;
+  if (opt && opt->upper_only) return EP_ERR_ARG;
+  if (S == 0) return EP_OK;
+  if (!out_counts || !out_upper || !episodes.types) return EP_ERR_ARG;
+  if (N > 1 && (!episodes.t_low || !episodes.t_high)) return EP_ERR_ARG;
+  // the whole table is checked here: the second pass sees only the kept rows
+  for (int64_t e = 0; e < S; ++e) {
+    int64_t span = 0;
+    for (int j = 0; j < N - 1; ++j) {
+      const int64_t lo = episodes.t_low[e * (N - 1) + j];
+      const int64_t hi = episodes.t_high[e * (N - 1) + j];
+      if (lo < 0 || lo >= hi) return EP_ERR_INTERVAL;
+      span += hi;
+    }
+    if (span > INT32_MAX) return EP_ERR_INTERVAL;
+  }
+  // first pass (A2): every relaxed episode
+  ep_options o1{};
+  if (opt) o1 = *opt;
+  o1.upper_only = 1;
+  o1.stats = nullptr;
+  if (int st = count_episodes_impl(times, types, n_events, episodes, S, out_upper, stream, &o1))
+    return st;
+  std::vector<int64_t> upper((size_t)S);
+  EP_HIP(hipMemcpyAsync(upper.data(), out_upper, (size_t)S * sizeof(int64_t), hipMemcpyDeviceToHost,
+                        stream));
+  EP_HIP(hipStreamSynchronize(stream));
+  // second pass (A1): the kept episodes, exact, written compactly to out_counts
+  std::vector<uint16_t> k_types;
+  std::vector<int32_t> k_low, k_high;
+  int64_t kept = 0;
+  for (int64_t e = 0; e < S; ++e) {
+    if (upper[(size_t)e] < threshold) continue;
+    k_types.insert(k_types.end(), episodes.types + e * N, episodes.types + (e + 1) * N);
+    if (N > 1) {
+      k_low.insert(k_low.end(), episodes.t_low + e * (N - 1), episodes.t_low + (e + 1) * (N - 1));
+      k_high.insert(k_high.end(), episodes.t_high + e * (N - 1), episodes.t_high + (e + 1) * (N - 1));
+    }
+    ++kept;
+  }
+  if (kept > 0) {
+    ep_episodes sub{N, k_types.data(), N > 1 ? k_low.data() : nullptr,
+                    N > 1 ? k_high.data() : nullptr};
+    ep_options o2{};
+    if (opt) o2 = *opt;
+    o2.upper_only = 0;
+    o2.validate = 0;  // the first pass checked the stream
+    if (int st = count_episodes_impl(times, types, n_events, sub, kept, out_counts, stream, &o2))
+      return st;
+  }
+  hipLaunchKernelGGL(two_pass_merge_kernel, dim3(1), dim3(kMergeBlock), 0, stream, out_upper, S,
+                     threshold, out_counts);
+  EP_HIP(hipGetLastError());
+  if (n_kept) *n_kept = kept;
+  return EP_OK;
 }
 
 extern "C" int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_events,

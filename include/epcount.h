@@ -141,6 +141,15 @@ typedef struct {
  *               valid; the planner picks powers of two (Concatenate section).
  *   validate    non-zero: check on the device that times are non-decreasing
  *               and return EP_ERR_UNSORTED if not.  Synchronises `stream`.
+ *   upper_only  non-zero: count the relaxed episodes alpha' of Algorithm A2
+ *               (section on the constrained problem with upper limits only):
+ *               the same event types and upper bounds with every lower bound
+ *               taken as 0, so an occurrence needs 0 < t_{i+1} - t_i <= t_high_i.
+ *               `episodes.t_low` is then not read (it may be NULL); every
+ *               t_high must be > 0.  Every occurrence of an episode is one of
+ *               its relaxed version, so count(alpha') >= count(alpha).  The
+ *               relaxed windows never need more than one candidate run, so
+ *               this mode never returns EP_ERR_UNSUPPORTED.
  *   stats       if non-NULL, filled after the work completes.  Synchronises
  *               `stream`.
  */
@@ -148,7 +157,7 @@ typedef struct {
   int32_t mode;
   int32_t n_segments;
   int32_t validate;
-  int32_t reserved;
+  int32_t upper_only;
   ep_stats* stats;
 } ep_options;
 
@@ -156,6 +165,37 @@ typedef struct {
 int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
                          ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
                          hipStream_t stream, const ep_options* opt);
+
+/*
+ * Two-pass elimination A2+A1 for a support threshold (two-pass elimination
+ * section): the first pass counts every relaxed episode alpha' (upper_only
+ * above); episodes whose relaxed count is below `threshold` cannot be frequent
+ * (count(alpha) <= count(alpha') < threshold) and are dropped; the second pass
+ * counts the remaining episodes exactly.
+ *   times, types, n_events, episodes, n_episodes  as in ep_count_episodes
+ *               (the full table, t_low included, is checked before any work).
+ *   threshold   support threshold; episodes with relaxed count >= threshold
+ *               go to the second pass (threshold <= 0 keeps every episode).
+ *   out_counts  DEVICE, int64[n_episodes]: count(alpha_e) for the episodes
+ *               kept, -1 for the dropped ones.  The frequent episodes are
+ *               those with out_counts[e] >= threshold.
+ *   out_upper   DEVICE, int64[n_episodes]: the first pass's counts
+ *               count(alpha'_e) of every episode.
+ *   n_kept      HOST, may be NULL: receives the number of episodes counted in
+ *               the second pass.
+ *   stream      as in ep_count_episodes.
+ *   opt         may be NULL; mode, n_segments and validate apply to both
+ *               passes, stats to the second pass (left untouched when no
+ *               episode is kept); upper_only must be 0 (else EP_ERR_ARG).
+ * The host needs the first pass's counts to build the second pass's table, so
+ * the call synchronises `stream` once between the passes; the second pass and
+ * the final scatter are enqueued asynchronously as usual.  Returns EP_OK or an
+ * ep_status error (as in ep_count_episodes_ex).
+ */
+int ep_count_two_pass(const int32_t* times, const uint16_t* types, int64_t n_events,
+                      ep_episodes episodes, int64_t n_episodes, int64_t threshold,
+                      int64_t* out_counts, int64_t* out_upper, int64_t* n_kept,
+                      hipStream_t stream, const ep_options* opt);
 
 /*
  * The planner alone, on a described device (no GPU needed): which scheme and

@@ -70,6 +70,44 @@ def test_host_argument_errors():
     assert _call(S=0, out=0) == 0
 
 
+def _call_two_pass(n_events=10, S=1, N=2, lo=(0,), hi=(5,), out=1, upper=1, opt=None):
+    lib = fem.load_library()
+    ep_t = np.zeros(max(S, 1) * N, np.uint16)
+    lo_a = np.array(list(lo) * max(S, 1), np.int32)
+    hi_a = np.array(list(hi) * max(S, 1), np.int32)
+    eps = fem.EpEpisodes(N, ep_t.ctypes.data, lo_a.ctypes.data if lo_a.size else None,
+                         hi_a.ctypes.data if hi_a.size else None)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case here fails on the host
+    kept = ctypes.c_int64(-5)
+    st = lib.ep_count_two_pass(fake, fake, n_events, eps, S, 1, fake if out else None,
+                               fake if upper else None, ctypes.byref(kept), None, opt)
+    return st, kept.value
+
+
+def test_upper_only_host_checks():
+    # the relaxed count reads no lower bounds: a NULL t_low is accepted up to the
+    # device work, so only host-side failures are exercised here
+    relaxed = fem.EpOptions(0, 0, 0, 1, None)
+    assert _call(lo=(0,), hi=(0,), opt=ctypes.byref(relaxed)) == -3  # t_high must be > 0
+    assert _call(lo=(0,), hi=(-4,), opt=ctypes.byref(relaxed)) == -3
+    assert _call(n_events=-1, opt=ctypes.byref(relaxed)) == -1
+    assert _call(S=0, out=0, opt=ctypes.byref(relaxed)) == 0
+
+
+def test_two_pass_host_errors():
+    assert _call_two_pass(n_events=-1) == (-1, 0)
+    assert _call_two_pass(S=-1) == (-1, 0)
+    assert _call_two_pass(N=0, lo=(), hi=()) == (-2, 0)
+    assert _call_two_pass(out=0) == (-1, 0)
+    assert _call_two_pass(upper=0) == (-1, 0)
+    # the full table is checked before the first pass, lower bounds included
+    assert _call_two_pass(lo=(5,), hi=(5,)) == (-3, 0)
+    assert _call_two_pass(lo=(-1,), hi=(5,)) == (-3, 0)
+    relaxed = fem.EpOptions(0, 0, 0, 1, None)
+    assert _call_two_pass(opt=ctypes.byref(relaxed)) == (-1, 0)
+    assert _call_two_pass(S=0, out=0, upper=0) == (0, 0)
+
+
 def test_planner_rule():
     # episodes alone fill 256 CUs x 2048 lanes -> PTPE
     assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
