@@ -10,6 +10,11 @@ candidate episodes with (2,8] delays.
 Prints ONE JSON line: episode-events/s (events x episodes / step time), the
 roofline of the dominant kernel (Map) measured live with HIP events, and the
 CPU oracle timed on a bounded sample of the same workload on the host cores.
+
+--scheme upper counts the relaxed episodes (every lower delay bound 0);
+--scheme two-pass runs the two-pass elimination for a support threshold (the
+relaxed count of every episode, then the exact count of those reaching the
+threshold): one step is then one ep_count_two_pass call.
 """
 from __future__ import annotations
 
@@ -33,9 +38,11 @@ HBM_PEAK_GBS = 8000.0
 # Algorithmic work of the counting machine per (episode, relevant event): the
 # node-type test, the window check and the window update, ~10 int32 ops.
 OPS_PER_RELEVANT_PAIR = 10
+# Device code of every kernel (host code is not hashed: a change there leaves
+# the kernels and their traffic as they were).
 KERNEL_SOURCES = ["frequent_episode_mining_amd/csrc/ep_device.hpp",
                   "frequent_episode_mining_amd/csrc/ep_inst.hip",
-                  "frequent_episode_mining_amd/csrc/ep_api.hip"]
+                  "frequent_episode_mining_amd/csrc/ep_kernels.hpp"]
 
 
 def log(msg):
@@ -49,6 +56,11 @@ def relevant_pairs(wl) -> int:
     for row in wl.ep_types:
         total += int(cnt[np.unique(row)].sum())
     return total
+
+
+def relevant_pairs_rows(wl, rows) -> int:
+    cnt = np.bincount(wl.types, minlength=65536).astype(np.int64)
+    return int(sum(int(cnt[np.unique(wl.ep_types[r])].sum()) for r in rows))
 
 
 def kernel_source_sha() -> str:
@@ -73,24 +85,40 @@ def stored_traffic(workload: str, kernel: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(wl, gpu_counts, target_s: float):
+def oracle_timed(wl, idx, scheme: str, threshold: int, threads: int):
+    """The oracle on episodes ``idx``: (results, seconds, threads used).  The
+    results are the counts, the relaxed counts, or both stacked (two-pass)."""
+    import oracle
+    t0 = time.perf_counter()
+    if scheme == "alpha":
+        want, _, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
+                                           wl.t_high[idx], n_threads=threads)
+    elif scheme == "upper":
+        want = oracle.count_upper(wl.times, wl.types, wl.ep_types[idx], wl.t_high[idx],
+                                  n_threads=threads)
+    else:
+        want = np.stack(oracle.two_pass(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
+                                        wl.t_high[idx], threshold, n_threads=threads))
+    dt = time.perf_counter() - t0
+    return want, dt, min(threads, len(idx))
+
+
+def cpu_baseline(wl, gpu_result, target_s: float, scheme: str = "alpha", threshold: int = 0):
     """The oracle, as it stands, on a bounded sample of the workload's episodes:
     as many episodes (evenly spaced) as fit the time budget, and when all of
-    them fit, the whole workload repeated until the budget is spent."""
-    import oracle
+    them fit, the whole workload repeated until the budget is spent.
+    ``gpu_result`` is indexed by episode along its last axis."""
     threads = min(os.cpu_count() or 1, 16)
     S = wl.n_episodes
     probe = min(S, max(threads, 8))
-    _, dt, _ = oracle.count_timed(wl.times, wl.types, wl.ep_types[:probe], wl.t_low[:probe],
-                                  wl.t_high[:probe], n_threads=threads)
+    _, dt, _ = oracle_timed(wl, np.arange(probe), scheme, threshold, threads)
     per_ep = dt / probe
     m = int(min(S, max(probe, target_s / max(per_ep, 1e-9))))
     idx = np.unique(np.linspace(0, S - 1, m).astype(np.int64))
     reps, total, used, ok = 0, 0.0, threads, True
     while True:
-        want, dt, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
-                                            wl.t_high[idx], n_threads=threads)
-        ok = ok and bool(np.array_equal(gpu_counts[idx], want))
+        want, dt, used = oracle_timed(wl, idx, scheme, threshold, threads)
+        ok = ok and bool(np.array_equal(gpu_result[..., idx], want))
         reps += 1
         total += dt
         if total >= 0.9 * target_s or reps >= 1000:
@@ -126,6 +154,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scheme", default="alpha", choices=["alpha", "upper", "two-pass"],
+                    help="alpha: exact counts; upper: relaxed episodes (lower bounds 0); "
+                         "two-pass: relaxed counts, then exact counts of those >= --threshold")
+    ap.add_argument("--threshold", type=int, default=30000,
+                    help="support threshold of --scheme two-pass")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -162,10 +195,27 @@ def main():
     out = torch.empty(wl.n_episodes, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    _, st = fem.count_episodes(times, types, table, mode=mode, n_segments=seg, stats=True, out=out)
+    scheme = args.scheme
+    kept_box = [0]
+
+    def step():
+        if scheme == "two-pass":
+            c, u, kept_box[0] = fem.count_two_pass(times, types, table, threshold=args.threshold,
+                                                   mode=mode, n_segments=seg, stream=stream)
+            return c, u
+        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream,
+                           upper_only=(scheme == "upper"))
+        return out, None
+
+    if scheme == "two-pass":
+        _, _, _, st = fem.count_two_pass(times, types, table, threshold=args.threshold, mode=mode,
+                                         n_segments=seg, stats=True, stream=stream)
+    else:
+        _, st = fem.count_episodes(times, types, table, mode=mode, n_segments=seg, stats=True,
+                                   out=out, upper_only=(scheme == "upper"))
     log("plan: %s" % st)
     for _ in range(args.warmup):
-        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
+        step()
     torch.cuda.synchronize(dev)
 
     # An untimed pass with every phase timed (events around each phase cost
@@ -173,21 +223,22 @@ def main():
     # Map-step kernel dominates.
     fem.profile_begin()
     for _ in range(args.steps):
-        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
+        step()
     prof = fem.profile_end()
-    per = {k: prof[k] / prof["calls"] for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
+    per = {k: prof[k] / args.steps for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
     if not st["kernels"] & 4:
         per["map_filter_ms"] = 0.0  # no filter launched: the interval is two bare events
     top = max(per, key=per.get)
     which = {"map_filter_ms": "filter", "map_ticks_ms": "ticks", "map_positions_ms": "positions"}[top]
-    log("phases per call: map %.4f (filter %.4f, ticks %.4f, positions %.4f) closure %.4f "
+    log("phases per step: map %.4f (filter %.4f, ticks %.4f, positions %.4f) closure %.4f "
         "concat %.4f other %.4f ms"
-        % (prof["map_ms"] / prof["calls"], per["map_filter_ms"], per["map_ticks_ms"],
-           per["map_positions_ms"], prof["closure_ms"] / prof["calls"],
-           prof["concat_ms"] / prof["calls"], prof["other_ms"] / prof["calls"]))
+        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_ticks_ms"],
+           per["map_positions_ms"], prof["closure_ms"] / args.steps,
+           prof["concat_ms"] / args.steps, prof["other_ms"] / args.steps))
 
-    # The timed region: only the dominant kernel's two events, on one call in four.
-    every = 4
+    # The timed region: only the dominant kernel's two events, on one call in
+    # four (every call for the two-pass scheme: its steps alternate passes).
+    every = 1 if scheme == "two-pass" else 4
     fem.profile_begin_kernel(which, every)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -195,7 +246,7 @@ def main():
     w0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream)
+        res, res_upper = step()
     ev1.record(stream)
     we = time.perf_counter()
     torch.cuda.synchronize(dev)
@@ -204,7 +255,12 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     wall_ms = (w1 - w0) * 1000.0 / args.steps
     ms_per_step = max(gpu_ms, wall_ms)
-    counts = out.cpu().numpy()
+    counts = res.cpu().numpy()
+    if scheme == "two-pass":
+        upper = res_upper.cpu().numpy()
+        counts = np.stack([counts, upper])
+        log("two-pass: threshold %d, %d of %d episodes counted exactly, %d frequent"
+            % (args.threshold, kept_box[0], wl.n_episodes, int((counts[0] >= args.threshold).sum())))
     log("host enqueue %.4f ms per call" % ((we - w0) * 1000.0 / args.steps))
     log("step %.4f ms (gpu events %.4f, wall %.4f); %s kernel %.4f ms per launch (%d launches timed)"
         % (ms_per_step, gpu_ms, wall_ms, which, kprof[top] / max(kprof["calls"], 1), kprof["calls"]))
@@ -223,7 +279,15 @@ def main():
     kernel, kernel_ms = names[top], kprof[top] / max(kprof["calls"], 1)
     map_s = kernel_ms / 1000.0
     rel = relevant_pairs(wl)
-    traffic = stored_traffic(wl.name, kernel)
+    if scheme == "two-pass":
+        # both passes' launches per step: all episodes, then the kept ones
+        kept_rows = np.flatnonzero(counts[1] >= args.threshold)
+        rel = rel + relevant_pairs_rows(wl, kept_rows)
+        kernel_ms = kprof[top] / args.steps
+        map_s = kernel_ms / 1000.0
+    traffic = stored_traffic(wl.name if scheme == "alpha" else "%s-%s" % (wl.name, scheme), kernel)
+    if traffic is not None and scheme == "two-pass":
+        traffic *= 2  # the stored figure is per dispatch; a step launches the kernel twice
     if kernel == "filter_kernel":
         # one read of the stream, one {time, levels} entry written per
         # (episode, relevant event) pair
@@ -239,15 +303,16 @@ def main():
                     "work": "%d int32 ops x %d (episode, relevant event) pairs"
                             % (OPS_PER_RELEVANT_PAIR, rel)}
     roofline.update({"kernel": kernel, "kernel_ms": kernel_ms,
+                     "launches_per_step": 2 if scheme == "two-pass" else 1,
                      "timed_launches": kprof["calls"],
                      "map_kernels_ms": {names[k]: v for k, v in per.items()},
-                     "hbm_one_pass_frac": 6.0 * n / (prof["map_ms"] / prof["calls"] / 1000.0)
+                     "hbm_one_pass_frac": 6.0 * n / (prof["map_ms"] / args.steps / 1000.0)
                                           / 1e9 / HBM_PEAK_GBS})
 
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu, ok, m = cpu_baseline(wl, counts, args.cpu_seconds)
+        cpu, ok, m = cpu_baseline(wl, counts, args.cpu_seconds, scheme, args.threshold)
         parity = "bit-exact on %d sampled episodes" % m if ok else "MISMATCH"
         log("cpu oracle: %s; parity %s" % (cpu["sample"], parity))
         if not ok:
@@ -270,6 +335,10 @@ def main():
                    "n_episodes": S, "n_nodes": wl.n_nodes, "mode": st["mode"],
                    "segments": st["n_segments"], "window_runs": st["max_runs"],
                    "repairs": st["repairs"], "fallbacks": st["fallbacks"],
+                   "scheme": {"alpha": "exact counts",
+                              "upper": "relaxed episodes (lower bounds 0)",
+                              "two-pass": "two-pass elimination, threshold %d, %d kept"
+                                          % (args.threshold, kept_box[0])}[scheme],
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

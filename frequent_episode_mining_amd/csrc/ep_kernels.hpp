@@ -1,0 +1,458 @@
+// Device kernels of the library that are not specialised per episode size:
+// the per-call set-up (cuts and segment ranges), the event filter of the list
+// path, the Concatenate tree, and small helpers (fill, the two-pass scatter,
+// the sortedness check).  Included once, by the host unit ep_api.hip.
+//
+// Source page: "Towards Chip-on-Chip Neuroscience: Fast Mining of Frequent
+// Episodes Using Graphics Processors".
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ep_device.hpp"
+
+namespace epk {
+namespace {
+// ------------------------------------------------------------ small kernels
+
+// Per-call set-up in one launch: the equal-time cuts with each segment's event
+// range, and the flag and counter words.
+//   cuts   : tau_p = t_min - 1 + floor(p (t_max - t_min + 1) / P) for p = 0..P
+//            ("Design of MapConcatenate": segment p holds (tau_p, tau_{p+1}]);
+//            segment p needs the events in (tau_p - maxSpan, tau_{p+1} + maxSpan]
+//            since its machines start up to maxSpan before the left cut and
+//            look up to maxSpan past the right cut for the exit b.
+// With few segments each range end is one wave's 64-ary search of the sorted
+// times (a handful of dependent loads instead of a binary search's log2 n);
+// with many, the searches alone fill the GPU and each is one thread's binary
+// search (fewer loads in all).
+struct SetupArgs {
+  const int32_t* times;
+  int64_t n;
+  int32_t P;
+  int64_t max_span;
+  int64_t* tau;
+  int32_t* beg;
+  int32_t* end;
+  int32_t* flags;  // [S + 1]
+  int64_t S;
+  unsigned long long* counters;  // [4]
+  int32_t wave_search;  // range ends by one wave each (small P) or one thread each
+};
+
+__device__ inline int64_t cut_of(int64_t t_min, int64_t t_max, int64_t p, int64_t P) {
+  return t_min - 1 + (p * (t_max - t_min + 1)) / P;
+}
+
+// First index i in [0, n) with times[i] > v, n if none; every lane of the wave
+// calls it with the same arguments and gets the answer.  Invariant: the
+// answer lies in [lo, hi], times[lo-1] <= v and times[hi] > v (or hi = n).
+__device__ int64_t wave_upper_bound(const int32_t* times, int64_t n, int64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t lo = 0, hi = n;
+  while (hi - lo > kWave) {
+    const int64_t step = (hi - lo + kWave - 1) / kWave;
+    int64_t idx = lo + (int64_t)(lane + 1) * step - 1;
+    idx = idx < hi - 1 ? idx : hi - 1;
+    const uint64_t gt = __ballot((int64_t)times[idx] > v);
+    if (gt == 0) {
+      lo = hi;  // lane 63 probed hi - 1
+    } else {
+      const int f = __ffsll((unsigned long long)gt) - 1;
+      const int64_t idx_f = lo + (int64_t)(f + 1) * step - 1;
+      const int64_t new_lo = f == 0 ? lo : lo + (int64_t)f * step;
+      hi = idx_f < hi - 1 ? idx_f : hi - 1;
+      lo = new_lo;
+    }
+  }
+  const int64_t idx = lo + lane;
+  const bool in = idx < hi;  // lanes past the range read times[0] (n >= 1) and ignore it
+  const uint64_t gt = __ballot(in && (int64_t)times[in ? idx : 0] > v);
+  return gt ? lo + (__ffsll((unsigned long long)gt) - 1) : hi;
+}
+
+constexpr int32_t kWaveSearchMaxP = 4096;
+
+__host__ __device__ inline int64_t setup_search_threads(int32_t P, bool wave) {
+  return (int64_t)2 * P * (wave ? kWave : 1);
+}
+
+__global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
+  int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t n_search = setup_search_threads(A.P, A.wave_search != 0);
+  if (i < n_search && !A.wave_search) {
+    const int64_t p = i >> 1;
+    const int64_t t_min = A.times[0];
+    const int64_t t_max = A.times[A.n - 1];
+    if (i & 1)
+      A.end[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p + 1, A.P) + A.max_span);
+    else
+      A.beg[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p, A.P) - A.max_span);
+    return;
+  }
+  if (i < n_search) {
+    // wave w: w even -> beg[w / 2], w odd -> end[w / 2] (whole waves: n_search is a
+    // multiple of the wave size)
+    const int64_t w = i / kWave;
+    const int64_t p = w >> 1;
+    const int64_t t_min = A.times[0];
+    const int64_t t_max = A.times[A.n - 1];
+    const int64_t v = (w & 1) ? cut_of(t_min, t_max, p + 1, A.P) + A.max_span
+                              : cut_of(t_min, t_max, p, A.P) - A.max_span;
+    const int64_t r = wave_upper_bound(A.times, A.n, v);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      if (w & 1)
+        A.end[p] = (int32_t)r;
+      else
+        A.beg[p] = (int32_t)r;
+    }
+    return;
+  }
+  i -= n_search;
+  if (i <= A.P) {
+    A.tau[i] = cut_of(A.times[0], A.times[A.n - 1], i, A.P);
+    return;
+  }
+  i -= (int64_t)A.P + 1;
+  if (i <= A.S) {
+    A.flags[i] = 0;
+    return;
+  }
+  i -= A.S + 1;
+  if (i < 4) A.counters[i] = 0ull;
+}
+
+// ------------------------------------------------------------- event filter
+
+// One pass over the stream for the list Map kernel.  Block b holds events
+// [b * kListBlock, (b + 1) * kListBlock); each event gets its node-type slot
+// and the set of episodes with that type, and for each episode its events are
+// written in order to the block's region as {time, node levels}: episode e's
+// entries start at list_off[b][e] and number list_cnt[b][e].  The region holds
+// kListBlock * max_share entries (max_share: most episodes one type is on), so
+// blocks need nothing from each other.  A thread takes 16 consecutive events;
+// its per-episode counts are packed two to a 32-bit word (16-bit fields; a
+// block holds at most 4096), so one scan serves two episodes.
+constexpr int kFilterPer = kListBlock / kBlock;  // 16
+constexpr int kMaxListEpisodes = 32;
+constexpr double kMaxListBytes = 32.0 * (1ull << 30);  // list scratch bound of the list path
+
+struct FilterArgs {
+  const int32_t* times;
+  const uint16_t* types;
+  int64_t n;
+  const uint64_t* type_seen;     // [1024] the call's node types as a 65,536-bit set
+  const uint8_t* type_rank;      // [1024] set bits before each 64-bit word
+  const uint32_t* slot_eps;      // [256] episodes with slot u's type (bit e); slot 0: none
+  const uint16_t* slot_levels;   // [256 * S] node levels of episode e with slot u's type
+  int32_t S;                     // <= kMaxListEpisodes
+  int32_t max_share;
+  int2* lists;
+  int32_t* list_off;             // [blocks * S]
+  int32_t* list_cnt;             // [blocks * S]
+};
+
+// One workgroup loops over blocks b = blockIdx.x, + gridDim.x, ...: the LDS
+// tables are loaded once, and the next block's events are loaded before the
+// current block is classified and written.  G packed count words serve up to
+// 4 G episodes.
+template <int G>
+__global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
+  constexpr int kE = 4 * G;  // episodes this instance serves at most
+  __shared__ uint64_t s_seen[1024];
+  __shared__ uint8_t s_rank[1024];
+  __shared__ uint32_t s_eps[256];
+  __shared__ uint16_t s_lv[256 * kE];
+  __shared__ uint16_t s_pre[kE][kBlock];  // thread's next rank per episode
+  __shared__ uint32_t s_wsum[kBlock / kWave][2 * G];
+  __shared__ int32_t s_off[kE];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int S = A.S;
+  for (int i = tid; i < 1024; i += kBlock) {
+    s_seen[i] = A.type_seen[i];
+    s_rank[i] = A.type_rank[i];
+  }
+  for (int i = tid; i < 256; i += kBlock) s_eps[i] = A.slot_eps[i];
+  for (int i = tid; i < 256 * S; i += kBlock) s_lv[(i / S) * kE + i % S] = A.slot_levels[i];
+  const bool vec = ((uintptr_t)A.times & 15) == 0 && ((uintptr_t)A.types & 15) == 0;
+  const int64_t n_blocks = (A.n + kListBlock - 1) / kListBlock;
+
+  int32_t t[kFilterPer], tn[kFilterPer];
+  uint32_t y[kFilterPer], yn[kFilterPer];
+  auto load = [&](int64_t b, int32_t* tt, uint32_t* yy) {
+    const int64_t first = b * kListBlock + (int64_t)tid * kFilterPer;
+    if (vec && first + kFilterPer <= A.n) {
+      const int4* tv = (const int4*)(A.times + first);
+      const uint4* yv = (const uint4*)(A.types + first);
+#pragma unroll
+      for (int q = 0; q < kFilterPer / 4; ++q) {
+        const int4 v = tv[q];
+        tt[4 * q] = v.x;
+        tt[4 * q + 1] = v.y;
+        tt[4 * q + 2] = v.z;
+        tt[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int q = 0; q < kFilterPer / 8; ++q) {
+        const uint4 v = yv[q];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          yy[8 * q + 2 * h] = w[h] & 0xffffu;
+          yy[8 * q + 2 * h + 1] = w[h] >> 16;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kFilterPer; ++k) {
+        const bool in = first + k < A.n;
+        tt[k] = in ? A.times[first + k] : 0;
+        yy[k] = in ? A.types[first + k] : 0u;
+      }
+    }
+  };
+  int64_t b = blockIdx.x;
+  if (b < n_blocks) load(b, tn, yn);
+  __syncthreads();  // tables in LDS
+
+  for (; b < n_blocks; b += gridDim.x) {
+    const int64_t first = b * kListBlock + (int64_t)tid * kFilterPer;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      t[k] = tn[k];
+      y[k] = yn[k];
+    }
+    if (b + gridDim.x < n_blocks) load(b + gridDim.x, tn, yn);  // in flight meanwhile
+
+    // events of this thread that exist (the last block may be partial)
+    const int64_t left = A.n - first;
+    const int n_valid = left >= kFilterPer ? kFilterPer : (left > 0 ? (int)left : 0);
+    uint32_t sl[kFilterPer], ep[kFilterPer];
+    // per-thread counts in 8-bit fields, four episodes to a word (at most 16
+    // each): x * 0x204081 puts bit i of a 4-bit x at bit 8i with no carries
+    uint32_t c8[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) c8[g] = 0;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      const uint32_t yk = y[k];
+      const uint64_t w = s_seen[yk >> 6];
+      const uint32_t sh = yk & 63u;
+      const bool on = k < n_valid && ((w >> sh) & 1ull);
+      const uint32_t below = (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
+      sl[k] = on ? (uint32_t)s_rank[yk >> 6] + below + 1u : 0u;
+      ep[k] = s_eps[sl[k]];
+#pragma unroll
+      for (int g = 0; g < G; ++g) c8[g] += __umul24((ep[k] >> (4 * g)) & 15u, 0x204081u) & 0x01010101u;
+    }
+    // widen to two 16-bit fields per word: word 2g + h holds episodes 4g + 2h
+    // and 4g + 2h + 1
+    uint32_t c[2 * G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      c[2 * g] = (c8[g] & 0xffu) | ((c8[g] & 0xff00u) << 8);
+      c[2 * g + 1] = ((c8[g] >> 16) & 0xffu) | ((c8[g] >> 24) << 16);
+    }
+    // block-wide exclusive scan of the packed counts: wave scan, then waves
+    uint32_t incl[2 * G];
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) {
+      uint32_t v = c[g];
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
+      }
+      incl[g] = v;
+      if (lane == kWave - 1) s_wsum[wave][g] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < 2 * G; ++g) {
+      uint32_t before = 0;
+#pragma unroll
+      for (int w = 0; w < kBlock / kWave; ++w) before += w < wave ? s_wsum[w][g] : 0u;
+      const uint32_t excl = before + incl[g] - c[g];
+      if (2 * g < S) s_pre[2 * g][tid] = (uint16_t)(excl & 0xffffu);
+      if (2 * g + 1 < S) s_pre[2 * g + 1][tid] = (uint16_t)(excl >> 16);
+    }
+    if (tid == 0) {
+      int32_t off = 0;
+#pragma unroll
+      for (int g = 0; g < 2 * G; ++g) {
+        uint32_t all = 0;
+#pragma unroll
+        for (int w = 0; w < kBlock / kWave; ++w) all += s_wsum[w][g];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * g + h;
+          if (e < S) {
+            const int32_t cnt = (int32_t)((all >> (16 * h)) & 0xffffu);
+            s_off[e] = off;
+            A.list_off[b * S + e] = off;
+            A.list_cnt[b * S + e] = cnt;
+            off += cnt;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
+#pragma unroll
+    for (int k = 0; k < kFilterPer; ++k) {
+      uint32_t m = ep[k];
+      while (m) {
+        const int e = __ffs((int)m) - 1;
+        m &= m - 1;
+        const uint16_t r = s_pre[e][tid];
+        s_pre[e][tid] = (uint16_t)(r + 1);
+        region[s_off[e] + r] = make_int2(t[k], (int32_t)s_lv[sl[k] * kE + e]);
+      }
+    }
+    __syncthreads();  // s_wsum, s_pre and s_off are rewritten by the next block
+  }
+}
+
+// ------------------------------------------------------------- Concatenate
+
+// One workgroup joins G consecutive members (segments p0, p0 + stride, ...)
+// of one episode in LDS, level by level (Concatenate rules 1-3, Fig. 6), and
+// writes the merged tuples back to the first member.  Members hold their
+// tuple list keyed by their first segment's keys; joining left block L with
+// right block R maps each (a, c, b) of L to (a, c + c', b') for the tuple of R
+// whose key a' equals b.  Launched with stride 1, then `members`, then
+// members^2, ..., until one member is left.
+constexpr int kConcatMembers = 512;  // threads of a tree workgroup at most
+
+__global__ __launch_bounds__(kConcatMembers) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
+                                                             int32_t P, int64_t stride, int32_t members,
+                                                             int64_t groups) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int slots = ts.slots;
+  int32_t* s_a = (int32_t*)smem;                      // [members][slots]
+  int32_t* s_c = s_a + members * slots;
+  int32_t* s_b = s_c + members * slots;
+  int32_t* s_n = s_b + members * slots;               // [members]
+  __shared__ int32_t s_miss;
+  const int64_t e = (int64_t)blockIdx.x / groups;
+  const int64_t p0 = ((int64_t)blockIdx.x - e * groups) * stride * members;
+  const int i = threadIdx.x;
+  const int64_t p = p0 + (int64_t)i * stride;
+  if (i == 0) s_miss = 0;
+  int n = 0;
+  if (p < P) {
+    n = min(ts.nslots[ts.idx(e, p)], slots);
+    for (int k = 0; k < n; ++k) {
+      const Tuple tu = *ts.at(e, p, k);
+      s_a[i * slots + k] = tu.a;
+      s_c[i * slots + k] = tu.c;
+      s_b[i * slots + k] = tu.b;
+    }
+  }
+  s_n[i] = n;
+  __syncthreads();
+  for (int h = 1; h < members; h <<= 1) {
+    if ((i & (2 * h - 1)) == 0 && i + h < members && p + (int64_t)h * stride < P) {
+      const int nl = s_n[i];
+      const int nr = s_n[i + h];
+      for (int k = 0; k < nl; ++k) {
+        const int32_t b = s_b[i * slots + k];
+        int hit = -1;
+        for (int m = 0; m < nr; ++m)
+          if (hit < 0 && s_a[(i + h) * slots + m] == b) hit = m;
+        if (hit >= 0) {
+          s_c[i * slots + k] += s_c[(i + h) * slots + hit];
+          s_b[i * slots + k] = s_b[(i + h) * slots + hit];
+        } else {
+          s_miss = 1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (i == 0 && p < P) {
+    for (int k = 0; k < s_n[0]; ++k) {
+      Tuple tu;
+      tu.a = s_a[k];
+      tu.c = s_c[k];
+      tu.b = s_b[k];
+      tu.pad = 0;
+      *ts.at(e, p, k) = tu;
+    }
+    if (s_miss) atomicOr(&flags[e], 2);
+  }
+}
+
+inline int64_t setup_items(const SetupArgs& A) {
+  return setup_search_threads(A.P, A.wave_search != 0) + (int64_t)A.P + 1 + A.S + 1 + 4;
+}
+
+__global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n, int64_t v) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Two-pass elimination, last step: the second pass wrote the kept episodes'
+// exact counts, in episode order, to out[0 .. kept); spread them to their
+// episodes in place and mark the dropped ones -1.  Episode e is kept when
+// upper[e] >= theta; its compact index is the number of kept episodes before
+// it, which is <= e.  One workgroup walks 1,024-episode chunks from the last
+// one down: every thread reads its value, the workgroup waits, then writes.
+// A chunk writes only its own indices, which no lower chunk reads (their
+// compact indices are below the chunk), and reads happen before the barrier
+// that precedes the chunk's writes.
+constexpr int kMergeBlock = 1024;
+__global__ __launch_bounds__(kMergeBlock) void two_pass_merge_kernel(const int64_t* upper, int64_t S,
+                                                                     int64_t theta, int64_t* out) {
+  constexpr int kWaves = kMergeBlock / kWave;
+  __shared__ int32_t s_wave[kWaves];
+  __shared__ int64_t s_part[kWaves];
+  __shared__ int64_t s_val[kMergeBlock];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  // kept episodes in all
+  int64_t local = 0;
+  for (int64_t e = tid; e < S; e += kMergeBlock) local += upper[e] >= theta;
+  for (int off = kWave / 2; off > 0; off >>= 1) local += __shfl_xor(local, off);
+  if (lane == 0) s_part[wave] = local;
+  __syncthreads();
+  int64_t total = 0;
+  for (int w = 0; w < kWaves; ++w) total += s_part[w];
+  int64_t after = 0;  // kept episodes at indices above the current chunk
+  for (int64_t c = (S + kMergeBlock - 1) / kMergeBlock - 1; c >= 0; --c) {
+    const int64_t e = c * kMergeBlock + tid;
+    const bool keep = e < S && upper[e] >= theta;
+    const uint64_t ballot = __ballot(keep);
+    const int below = __popcll(ballot & ((1ull << lane) - 1));
+    __syncthreads();  // the previous chunk is done with s_wave
+    if (lane == 0) s_wave[wave] = __popcll(ballot);
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      chunk += s_wave[w];
+    }
+    const int64_t rank = total - after - chunk + before + below;
+    // the value goes through LDS, so the read has landed before the barrier
+    s_val[tid] = keep ? out[rank] : -1;
+    __syncthreads();
+    if (e < S) out[e] = s_val[tid];
+    after += chunk;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* times, int64_t n,
+                                                              int32_t* bad) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i + 1 < n && times[i] > times[i + 1]) atomicOr(bad, 1);
+}
+
+inline unsigned grid_for(int64_t items) { return (unsigned)((items + kBlock - 1) / kBlock); }
+
+}  // namespace
+}  // namespace epk
