@@ -1038,12 +1038,14 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
 
 // ------------------------------------------------------- tick Map kernel
 
-// Dilation program of one interval (lo, hi], hi <= 63: the first shift lo + 1
-// and the amounts of the doubling steps, 5 bits per step, whose subset sums
-// are exactly 0 .. hi-lo-1 (amounts 1, 2, 4, ... then the remainder; steps
-// past the last have amount 0 and change nothing).
+// Dilation program of one interval (lo, hi], hi <= 63: the first shifts lo + 1
+// (this word) and 64 - hi (the previous word) and the amounts of the doubling
+// steps, 5 bits per step, whose subset sums are exactly 0 .. hi-lo-1 (amounts
+// 1, 2, 4, ... then the remainder; steps past the last have amount 0 and
+// change nothing).
 struct DilProg {
   uint32_t a;   // lo + 1
+  uint32_t h;   // 64 - hi
   uint32_t pk;  // step i amount at bits 5i .. 5i+4
 };
 
@@ -1062,56 +1064,75 @@ __device__ inline DilProg dil_prog(uint32_t lo, uint32_t hi) {
   uint32_t pk = 0;
   for (int i = 0; i < k; ++i) pk |= (1u << i) << (5 * i);
   pk |= (W - (1u << k)) << (5 * k);
-  return {lo + 1, pk};
+  return {lo + 1, 64 - hi, pk};
 }
 
 // Candidates of node j+1 in one 64-tick word from node j's candidates in the
 // previous word (prev) and this word (cur): bit i is set iff some node-j
-// candidate lies d ticks earlier with lo < d <= hi.  The 128-bit stream
-// prev:cur is shifted by lo + 1, then ORed with its own shifts by the doubling
-// amounts.  The high word takes the top s bits of the low word at each step as
-// ((hi32(z) << s) >> 32), which is 0 for s = 0, so padding steps are exact
-// no-ops and the code has no per-lane branches.  K is uniform over the launch.
+// candidate lies d ticks earlier with lo < d <= hi.  With W = hi - lo that is
+// the OR over m in [0, W) of (cur << (lo+1)) << m, from this word, and of
+// (prev >> (64-hi)) >> m, from the previous one (hi <= 63, so no candidate
+// older than the previous word can reach this one).  Each part is one 64-bit
+// doubling chain over the program's amounts; the two chains are independent,
+// and amount-0 padding steps are exact no-ops, so the code has no per-lane
+// branches.  K is uniform over the launch.
 __device__ inline uint64_t dilate(uint64_t prev, uint64_t cur, DilProg d, int K) {
-  uint64_t y = (cur << d.a) | (prev >> (64 - d.a));
-  uint64_t z = prev << d.a;
+  uint64_t y = cur << d.a;
+  uint64_t x = prev >> d.h;
 #pragma unroll
   for (int i = 0; i < 6; ++i) {
     if (i >= K) break;
     const uint32_t s = (d.pk >> (5 * i)) & 31u;
-    const uint64_t spill = ((uint64_t)(uint32_t)(z >> 32) << s) >> 32;
-    y |= (y << s) | spill;
-    if (i + 1 < K) z |= z << s;
+    y |= y << s;
+    x |= x >> s;
+  }
+  return y | x;
+}
+
+// dilate() with an empty previous word (right after a reset).
+__device__ inline uint64_t dilate_noprev(uint64_t cur, DilProg d, int K) {
+  uint64_t y = cur << d.a;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    if (i >= K) break;
+    y |= y << ((d.pk >> (5 * i)) & 31u);
   }
   return y;
 }
 
-// dilate() with the step count fixed at compile time (KC >= the launch's K;
-// the extra steps have amount 0).
+// The same two with the step count fixed at compile time (KC >= the launch's
+// K; the extra steps have amount 0).
 template <int KC>
 __device__ inline uint64_t dilate_k(uint64_t prev, uint64_t cur, DilProg d) {
-  uint64_t y = (cur << d.a) | (prev >> (64 - d.a));
-  uint64_t z = prev << d.a;
+  uint64_t y = cur << d.a;
+  uint64_t x = prev >> d.h;
 #pragma unroll
   for (int i = 0; i < KC; ++i) {
     const uint32_t s = (d.pk >> (5 * i)) & 31u;
-    const uint64_t spill = ((uint64_t)(uint32_t)(z >> 32) << s) >> 32;
-    y |= (y << s) | spill;
-    if (i + 1 < KC) z |= z << s;
+    y |= y << s;
+    x |= x >> s;
   }
+  return y | x;
+}
+
+template <int KC>
+__device__ inline uint64_t dilate_k_noprev(uint64_t cur, DilProg d) {
+  uint64_t y = cur << d.a;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) y |= y << ((d.pk >> (5 * i)) & 31u);
   return y;
 }
 
-// The candidate chain of one word: node 0 candidates are its events within
-// keep_lo (ticks after the machine's last reset); node j+1 candidates are its
-// events that a node-j candidate can precede.  Later nodes need no mask:
-// every candidate descends from a node-0 candidate after the reset, and the
-// window only moves forward.  Writes nodes 0..N-2 to cur and returns node N-1
-// (completions).
+// The candidate chain of one word: node 0 candidates are e0 (its events after
+// the machine's last reset); node j+1 candidates are its events that a node-j
+// candidate can precede.  Later nodes need no mask: every candidate descends
+// from a node-0 candidate after the reset, and the window only moves forward.
+// Writes nodes 0..N-2 to cur and returns node N-1 (completions).  The _noprev
+// forms take an empty previous word (the machine reset inside this word).
 template <int N>
-__device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep_lo, const uint64_t* prev,
+__device__ inline uint64_t word_chain(const uint64_t* E, uint64_t e0, const uint64_t* prev,
                                       uint64_t* cur, const DilProg* dp, int K) {
-  uint64_t c = E[0] & keep_lo;
+  uint64_t c = e0;
 #pragma unroll
   for (int j = 1; j < N; ++j) {
     cur[j - 1] = c;
@@ -1120,14 +1141,38 @@ __device__ inline uint64_t word_chain(const uint64_t* E, uint64_t keep_lo, const
   return c;
 }
 
+template <int N>
+__device__ inline uint64_t word_chain_noprev(const uint64_t* E, uint64_t e0, uint64_t* cur,
+                                             const DilProg* dp, int K) {
+  uint64_t c = e0;
+#pragma unroll
+  for (int j = 1; j < N; ++j) {
+    cur[j - 1] = c;
+    c = E[j] & dilate_noprev(c, dp[j - 1], K);
+  }
+  return c;
+}
+
 template <int N, int KC>
-__device__ inline uint64_t word_chain_k(const uint64_t* E, uint64_t keep_lo, const uint64_t* prev,
+__device__ inline uint64_t word_chain_k(const uint64_t* E, uint64_t e0, const uint64_t* prev,
                                         uint64_t* cur, const DilProg* dp) {
-  uint64_t c = E[0] & keep_lo;
+  uint64_t c = e0;
 #pragma unroll
   for (int j = 1; j < N; ++j) {
     cur[j - 1] = c;
     c = E[j] & dilate_k<KC>(prev[j - 1], c, dp[j - 1]);
+  }
+  return c;
+}
+
+template <int N, int KC>
+__device__ inline uint64_t word_chain_k_noprev(const uint64_t* E, uint64_t e0, uint64_t* cur,
+                                               const DilProg* dp) {
+  uint64_t c = e0;
+#pragma unroll
+  for (int j = 1; j < N; ++j) {
+    cur[j - 1] = c;
+    c = E[j] & dilate_k_noprev<KC>(c, dp[j - 1]);
   }
   return c;
 }
@@ -1445,17 +1490,14 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
           const int32_t from = r[c] + 1 - wb;
           const uint64_t keep_lo = from <= 0 ? ~0ull : (from >= 64 ? 0ull : ((~0ull) << from));
           uint64_t cur[NI];
-          uint64_t last = word_chain<N>(E, keep_lo, prv[c], cur, dp, K) & keep_hi;
+          uint64_t last = word_chain<N>(E, E[0] & keep_lo, prv[c], cur, dp, K) & keep_hi;
           while (last != 0) {
             const int bit = __ffsll((unsigned long long)last) - 1;
             complete_members(mem[c], org + wb + bit);
             r[c] = wb + bit;
             done |= 1u << c;
-            const uint64_t after = bit == 63 ? 0ull : ((~0ull) << (bit + 1));
-            uint64_t zero[NI];
-  #pragma unroll
-            for (int j = 0; j < NI; ++j) zero[j] = 0;
-            last = word_chain<N>(E, after, zero, cur, dp, K) & keep_hi;
+            const uint64_t after = (~1ull) << bit;  // ticks after the completion (0 for bit 63)
+            last = word_chain_noprev<N>(E, E[0] & after, cur, dp, K) & keep_hi;
           }
   #pragma unroll
           for (int j = 0; j < NI; ++j) prv[c][j] = cur[j];
@@ -1499,36 +1541,64 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
         }
       }
       // Words of a lane with one class: the lean loop.  Ticks past stop are
-      // masked out of the completions (keep_hi), so the loop needs no exit test;
-      // a lane whose machines have all finished steps on without effect.
+      // masked out of the completions, so the loop needs no exit test; a lane
+      // whose machines have all finished steps on without effect.  The masks
+      // for the last reset and for stop are needed only in a segment's first
+      // and last words, so each sits behind a branch that the wave takes only
+      // when one of its lanes needs it.  The class's completions are recorded
+      // as tick offsets from org (the first after tau_p, the count in
+      // (tau_p, tau_{p+1}], the first after tau_{p+1}) and credited to its
+      // member machines once, after the loop.
       auto single_words = [&](auto kc) {
         constexpr int KC = decltype(kc)::value;
+        constexpr int32_t kNone = INT32_MIN;
         uint64_t pv[NI];
   #pragma unroll
         for (int j = 0; j < NI; ++j) pv[j] = prv[0][j];
         int32_t r0 = r[0];
         const uint32_t m0 = mem[0];
+        const int64_t tlo_d = tau_lo - org, thi_d = tau_hi - org;
+        const int32_t tlo = (int32_t)(tlo_d < -kFar ? -kFar : (tlo_d > kFar ? kFar : tlo_d));
+        const int32_t thi = (int32_t)(thi_d < -kFar ? -kFar : (thi_d > kFar ? kFar : thi_d));
+        int32_t c_first = kNone, c_b = kNone, c_cnt = 0;
+        int32_t ew[N];  // index of this lane's bitmap word of node j in word wi
+  #pragma unroll
+        for (int j = 0; j < N; ++j) ew[j] = lds_slot[j] + wi * A.U;
+        const int32_t stride = A.U;
         for (; wi < nw; ++wi) {
           const int32_t wb = wi * 64;
-          const int32_t row = wi * A.U;
           uint64_t E[N];
   #pragma unroll
-          for (int j = 0; j < N; ++j) E[j] = s_tb[lds_slot[j] + row];
-          const int32_t from = r0 + 1 - wb;
-          const uint64_t keep_lo = from <= 0 ? ~0ull : (from >= 64 ? 0ull : ((~0ull) << from));
-          const int32_t to = stop_rel - wb;
-          const uint64_t keep_hi = to >= 63 ? ~0ull : (to < 0 ? 0ull : ((~0ull) >> (63 - to)));
+          for (int j = 0; j < N; ++j) {
+            E[j] = s_tb[ew[j]];
+            ew[j] += stride;
+          }
+          uint64_t e0 = E[0];
+          if (__ballot(r0 >= wb)) {
+            const int32_t from = r0 + 1 - wb;
+            e0 &= from <= 0 ? ~0ull : (from >= 64 ? 0ull : ((~0ull) << from));
+          }
           uint64_t cur[NI];
-          uint64_t last = word_chain_k<N, KC>(E, keep_lo, pv, cur, dp) & keep_hi;
+          uint64_t last = word_chain_k<N, KC>(E, e0, pv, cur, dp);
+          uint64_t kh = ~0ull;
+          const int32_t to = stop_rel - wb;
+          if (__ballot(to < 63)) {
+            kh = to >= 63 ? ~0ull : (to < 0 ? 0ull : ((~0ull) >> (63 - to)));
+            last &= kh;
+          }
           while (last != 0) {
             const int bit = __ffsll((unsigned long long)last) - 1;
-            complete_members(m0, org + wb + bit);
-            r0 = wb + bit;
-            const uint64_t after = bit == 63 ? 0ull : ((~0ull) << (bit + 1));
-            uint64_t zero[NI];
-  #pragma unroll
-            for (int j = 0; j < NI; ++j) zero[j] = 0;
-            last = word_chain_k<N, KC>(E, after, zero, cur, dp) & keep_hi;
+            const int32_t t = wb + bit;
+            if (t > tlo) {
+              if (c_first == kNone) c_first = t;
+              if (t <= thi)
+                ++c_cnt;
+              else if (c_b == kNone)
+                c_b = t;
+            }
+            r0 = t;
+            const uint64_t after = (~1ull) << bit;
+            last = word_chain_k_noprev<N, KC>(E, E[0] & after, cur, dp) & kh;
           }
   #pragma unroll
           for (int j = 0; j < NI; ++j) pv[j] = cur[j];
@@ -1536,6 +1606,27 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
   #pragma unroll
         for (int j = 0; j < NI; ++j) prv[0][j] = pv[j];
         r[0] = r0;
+        // every live member completed at the class's completions: the first
+        // after tau_p sets a (if the member has none yet), the ones up to
+        // tau_{p+1} count, the first after tau_{p+1} sets b and ends the member
+        const uint32_t live = m0 & ~fin;
+        if (live && c_first != kNone) {
+  #pragma unroll
+          for (int k = 0; k < MCH; ++k) {
+            if ((live >> k) & 1u) {
+              if (!((found >> k) & 1u)) {
+                found |= 1u << k;
+                const int64_t dd = org + c_first - tau_lo;
+                a_off[k] = dd <= (int64_t)span ? (int32_t)dd : 0;
+              }
+              cnt[k] += c_cnt;
+              if (c_b != kNone) {
+                b_off[k] = (int32_t)(org + c_b - tau_hi);
+                fin |= 1u << k;
+              }
+            }
+          }
+        }
       };
       if (wi < nw && fin != all) {
         if (K <= 1)
@@ -1546,6 +1637,8 @@ __global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
           single_words(std::integral_constant<int, 3>());
         else if (K == 4)
           single_words(std::integral_constant<int, 4>());
+        else if (K == 5)
+          single_words(std::integral_constant<int, 5>());
         else
           single_words(std::integral_constant<int, 6>());
       }
