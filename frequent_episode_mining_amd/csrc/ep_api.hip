@@ -71,6 +71,9 @@ struct DeviceInfo {
   // for the LDS size tick_lds (queried once: the query is slow)
   int tick_per_cu[EP_MAX_NODES + 1][2] = {};
   size_t tick_lds[EP_MAX_NODES + 1][2] = {};
+  // resident lanes per CU of the tick kernel with one lane per (segment,
+  // episode), as its registers allow (the planner's T_B * B_MP), by N
+  int plan_lanes[EP_MAX_NODES + 1] = {};
 };
 
 std::mutex g_info_mu;
@@ -517,7 +520,21 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     if (K > EP_MAX_RUNS) return EP_ERR_UNSUPPORTED;
     L.win = K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4);
   }
-  const int lanes_per_cu_est = 2048;  // 8 waves on each of 4 SIMDs
+  // lanes one CU holds for the counting kernel (the hybrid rule's T_B * B_MP):
+  // the tick kernel's workgroups per CU as its registers allow, times its
+  // threads, for bit windows; 8 waves on each of 4 SIMDs otherwise
+  int lanes_per_cu_est = 2048;
+  if (L.bits) {
+    std::lock_guard<std::mutex> lock(g_info_mu);
+    int& lanes = info->plan_lanes[N];
+    if (lanes == 0) {
+      int per_cu = 0;
+      if (Lr->occupancy_ticks(N <= kMaxClassNodes, kBlock, 0, &per_cu) != hipSuccess || per_cu < 1)
+        per_cu = 2048 / kBlock;
+      lanes = std::min(per_cu * kBlock, 2048);
+    }
+    lanes_per_cu_est = lanes;
+  }
   int32_t pmode = 0, P = 1;
   plan_rule(S, N, n_events, mode, opt ? opt->n_segments : 0, info->cu_count, lanes_per_cu_est,
             &pmode, &P);
