@@ -1194,8 +1194,11 @@ __device__ inline uint64_t word_chain_k_noprev(const uint64_t* E, uint64_t e0, u
 // build the bitmaps once, reusing them for every later episode group; the
 // other workgroups of the group exit at once.  Otherwise each workgroup counts
 // its own episode group.
+// Up to four nodes the kernel is held to three waves per SIMD (168 VGPRs):
+// the few registers it then spills are used outside the word loops.
 template <int N, int MCH>
-__global__ __launch_bounds__(kBlock) void map_ticks_kernel(MapArgs A) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(N <= 4 ? 3 : 1)))
+void map_ticks_kernel(MapArgs A) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int64_t s_cur[kBlock];     // first tick of segment r's current chunk
   __shared__ int32_t s_nw[kBlock];      // words of segment r in the current chunk (0: none)
