@@ -157,6 +157,65 @@ def two_pass(times, types, ep_types, t_low, t_high, threshold: int,
     return counts, upper
 
 
+def mine(times, types, alphabet, bins, max_nodes: int, threshold: int,
+         n_threads: int | None = None):
+    """Level-wise mining of frequent serial episodes (the mining loop the page
+    counts candidates for: episodes of one size are counted together, and the
+    frequent ones of size k give the candidates of size k+1).
+
+    ``alphabet``: event types to mine over; ``bins``: list of (lo, hi) delay
+    intervals a candidate may use between consecutive nodes.  An episode is
+    frequent when its count reaches ``threshold``.  Candidates:
+      size 1: every alphabet type;
+      size 2: every ordered pair (a, c) of frequent types, once per bin;
+      size k+1: alpha joined with beta when beta without its last node equals
+        alpha without its first node (types and bins): alpha's nodes followed
+        by beta's last bin and type.
+    A node dropped from either end of an occurrence leaves an occurrence of
+    the shorter episode, and non-overlapped occurrences stay non-overlapped,
+    so every sub-episode obtained that way is at least as frequent: the join
+    reaches every frequent episode.
+
+    Returns {k: (ep_types [S,k], t_low [S,k-1], t_high [S,k-1], counts [S])}
+    for every k with a frequent episode, rows in increasing order of
+    (type 1, bin 1, type 2, bin 2, ..., type k) with bins by their index.
+    """
+    bins = [(int(lo), int(hi)) for lo, hi in bins]
+    out = {}
+    # an episode is (types tuple, bin-index tuple)
+    level = [((int(a),), ()) for a in sorted(set(int(a) for a in alphabet))]
+    k = 1
+    while level and k <= max_nodes:
+        ep = np.array([t for t, _ in level], dtype=np.uint16).reshape(len(level), k)
+        lo = np.array([[bins[b][0] for b in bs] for _, bs in level], dtype=np.int32).reshape(len(level), k - 1)
+        hi = np.array([[bins[b][1] for b in bs] for _, bs in level], dtype=np.int32).reshape(len(level), k - 1)
+        cnt = count(times, types, ep, lo, hi, n_threads)
+        keep = cnt >= threshold
+        if not keep.any():
+            break
+        out[k] = (ep[keep], lo[keep], hi[keep], cnt[keep])
+        frequent = [level[i] for i in np.flatnonzero(keep)]
+        if k == max_nodes:
+            break
+        nxt = []
+        if k == 1:
+            for (a,), _ in frequent:
+                for b in range(len(bins)):
+                    for (c,), _ in frequent:
+                        nxt.append(((a, c), (b,)))
+        else:
+            by_prefix = {}
+            for t, bs in frequent:
+                by_prefix.setdefault((t[:-1], bs[:-1]), []).append((t, bs))
+            for t, bs in frequent:
+                for t2, bs2 in by_prefix.get((t[1:], bs[1:]), []):
+                    nxt.append((t + (t2[-1],), bs + (bs2[-1],)))
+        nxt.sort(key=lambda e: [v for pair in zip(e[0], e[1] + (-1,)) for v in pair])
+        level = nxt
+        k += 1
+    return out
+
+
 def count_timed(times, types, ep_types, t_low, t_high, n_threads: int | None = None):
     """Like :func:`count`, also returning (seconds, threads used)."""
     times, types, ep_types, t_low, t_high = _prep(times, types, ep_types, t_low, t_high)
