@@ -46,6 +46,13 @@ class EpOptions(ctypes.Structure):
                 ("stats", ctypes.POINTER(EpStats))]
 
 
+class EpMineOptions(ctypes.Structure):
+    _fields_ = [("n_bins", ctypes.c_int32), ("bin_lo", ctypes.c_void_p), ("bin_hi", ctypes.c_void_p),
+                ("max_nodes", ctypes.c_int32), ("threshold", ctypes.c_int64),
+                ("two_pass", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("max_candidates", ctypes.c_int64)]
+
+
 class EpProfile(ctypes.Structure):
     _fields_ = [("map_ms", ctypes.c_double), ("closure_ms", ctypes.c_double),
                 ("concat_ms", ctypes.c_double), ("other_ms", ctypes.c_double),
@@ -80,6 +87,19 @@ def load_library(path: str | None = None):
     lib.ep_count_two_pass.restype = ctypes.c_int
     lib.ep_count_two_pass.argtypes = [vp, vp, i64, EpEpisodes, i64, i64, vp, vp,
                                       ctypes.POINTER(ctypes.c_int64), vp, ctypes.POINTER(EpOptions)]
+    lib.ep_mine.restype = ctypes.c_int
+    lib.ep_mine.argtypes = [vp, vp, i64, vp, i32, ctypes.POINTER(EpMineOptions), vp,
+                            ctypes.POINTER(ctypes.c_void_p)]
+    lib.ep_mined_max_nodes.restype = i32
+    lib.ep_mined_max_nodes.argtypes = [vp]
+    lib.ep_mined_count.restype = i64
+    lib.ep_mined_count.argtypes = [vp, i32]
+    lib.ep_mined_candidates.restype = i64
+    lib.ep_mined_candidates.argtypes = [vp, i32]
+    lib.ep_mined_get.restype = ctypes.c_int
+    lib.ep_mined_get.argtypes = [vp, i32, vp, vp, vp, vp]
+    lib.ep_mined_free.restype = None
+    lib.ep_mined_free.argtypes = [vp]
     lib.ep_plan.restype = ctypes.c_int
     lib.ep_plan.argtypes = [i64, i32, i64, i32, i32, i32, i32,
                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -242,6 +262,47 @@ def count_two_pass(times, types, ep_types, t_low=None, t_high=None, *, threshold
     if stats:
         return counts, upper, kept.value, _stats_dict(st)
     return counts, upper, kept.value
+
+
+def mine(times, types, alphabet, bins, *, max_nodes: int, threshold: int, two_pass: bool = False,
+         mode: str = "auto", max_candidates: int = 0, stream=None, candidates: bool = False):
+    """Level-wise mining of frequent episodes over a GPU-resident stream.
+
+    ``alphabet``: event types to mine over; ``bins``: list of (lo, hi) delay
+    intervals candidates may use.  Returns {k: (ep_types [S,k], t_low [S,k-1],
+    t_high [S,k-1], counts [S])} (host arrays, rows in increasing order of
+    (type 1, bin 1, ..., type k)), and also {k: candidates counted} if
+    ``candidates``.  Synchronises ``stream`` once per episode size.
+    """
+    tp, yp, n = _stream_args(times, types)
+    alpha = np.ascontiguousarray(np.asarray(list(alphabet), dtype=np.uint16))
+    lo = np.ascontiguousarray(np.array([b[0] for b in bins], dtype=np.int32))
+    hi = np.ascontiguousarray(np.array([b[1] for b in bins], dtype=np.int32))
+    opt = EpMineOptions(len(bins), lo.ctypes.data if lo.size else None,
+                        hi.ctypes.data if hi.size else None, int(max_nodes), int(threshold),
+                        int(bool(two_pass)), MODES[mode], int(max_candidates))
+    sp = _stream_handle(stream, times.device)
+    lib = load_library()
+    handle = ctypes.c_void_p()
+    status = _on_device(times.device, lambda: lib.ep_mine(
+        tp, yp, n, alpha.ctypes.data if alpha.size else None, alpha.size, ctypes.byref(opt), sp,
+        ctypes.byref(handle)))
+    _check(status)
+    try:
+        out, cands = {}, {}
+        for k in range(1, lib.ep_mined_max_nodes(handle) + 1):
+            S = lib.ep_mined_count(handle, k)
+            cands[k] = lib.ep_mined_candidates(handle, k)
+            ep = np.zeros((S, k), np.uint16)
+            tl = np.zeros((S, k - 1), np.int32)
+            th = np.zeros((S, k - 1), np.int32)
+            cnt = np.zeros(S, np.int64)
+            _check(lib.ep_mined_get(handle, k, ep.ctypes.data, tl.ctypes.data if tl.size else None,
+                                    th.ctypes.data if th.size else None, cnt.ctypes.data))
+            out[k] = (ep, tl, th, cnt)
+    finally:
+        lib.ep_mined_free(handle)
+    return (out, cands) if candidates else out
 
 
 def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_segments: int = 0,

@@ -49,12 +49,13 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every HIP unit for gfx950 and link libepcount.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(16, os.cpu_count() or 4)
-    units = [(os.path.join(CSRC, "ep_api.hip"), os.path.join(BUILD, "ep_api.o"), [])]
+    units = [(os.path.join(CSRC, "ep_api.hip"), os.path.join(BUILD, "ep_api.o"), []),
+             (os.path.join(CSRC, "ep_mine.hip"), os.path.join(BUILD, "ep_mine.o"), [])]
     for n in range(1, MAX_NODES + 1):
         units.append((os.path.join(CSRC, "ep_inst.hip"), os.path.join(BUILD, "ep_inst_n%d.o" % n),
                       ["-DEP_N=%d" % n]))
     # largest episode sizes first: they take longest
-    units = [units[0]] + units[1:][::-1]
+    units = units[:2] + units[2:][::-1]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, units))
     tmp = LIB + ".tmp%d" % os.getpid()

@@ -302,6 +302,75 @@ def longchain(n: int = 500_000_000, seed: int = BASE_SEED + 4, n_types: int = 25
                     % (n, n_types, S, N, per_episode, P))
 
 
+@dataclasses.dataclass
+class MiningWorkload:
+    name: str
+    times: np.ndarray        # int32[n], non-decreasing
+    types: np.ndarray        # uint16[n]
+    alphabet: np.ndarray     # uint16[], the types mined over
+    bins: list               # [(lo, hi)] delay intervals candidates may use
+    max_nodes: int
+    threshold: int
+    description: str
+
+    @property
+    def n_events(self) -> int:
+        return int(self.times.shape[0])
+
+
+SYM26_SHORT = [0, 1, 2, 3]
+SYM26_LONG = [10, 11, 12, 13, 14, 15, 16, 17]
+
+
+def sym26(seconds: float = 60.0, seed: int = BASE_SEED + 6, rate_hz: float = 34.0,
+          link_p: float = 0.9, threshold: int = 300) -> MiningWorkload:
+    """The shape of the page's Sym26 model data: 26 neurons firing as Poisson
+    processes at 20 Hz on a 1 ms tick, with one short (4-node) and one long
+    (8-node) causal chain embedded.  Each chain starts as a Poisson process at
+    ``rate_hz``; each link fires with probability ``link_p`` after U{2..6} ms.
+    Mined over all 26 types with delay bins (0,5], (5,10], (10,20] up to 8
+    nodes; about 50,000 events in 60 s."""
+    rng = np.random.default_rng(seed)
+    n_types = 26
+    T = int(round(seconds * 1000))
+    n_bg = int(rng.binomial(n_types * T, 0.02))
+    t_bg = np.sort(rng.integers(1, T + 1, size=n_bg)).astype(np.int64)
+    y_bg = rng.integers(0, n_types, size=n_bg).astype(np.uint16)
+    pt, py = [t_bg], [y_bg]
+    for chain in (SYM26_SHORT, SYM26_LONG):
+        n_start = int(rng.poisson(rate_hz * seconds))
+        starts = rng.integers(1, T + 1, size=n_start)
+        for s0 in starts:
+            t = int(s0)
+            ts, ys = [t], [chain[0]]
+            for node in chain[1:]:
+                if rng.random() >= link_p:
+                    break
+                t += int(rng.integers(2, 7))
+                ts.append(t)
+                ys.append(node)
+            pt.append(np.array(ts, np.int64))
+            py.append(np.array(ys, np.uint16))
+    times = np.concatenate(pt)
+    types = np.concatenate(py)
+    key = rng.random(times.size)
+    o = np.lexsort((key, times))
+    times = times[o].astype(np.int32)
+    types = types[o]
+    bins = [(0, 5), (5, 10), (10, 20)]
+    return MiningWorkload("sym26", times, types, np.arange(n_types, dtype=np.uint16), bins, 8,
+                          threshold, "%d events over %.0f s, 26 types @20Hz/1ms, a 4-node and an "
+                          "8-node chain at %.0f Hz (links p=%.1f, U{2..6} ms), bins %s, threshold %d"
+                          % (times.size, seconds, rate_hz, link_p, bins, threshold))
+
+
+MINING = {"sym26": sym26}
+
+
+def make_mining(name: str, **overrides) -> MiningWorkload:
+    return MINING[name](**overrides)
+
+
 CONFIGS = {
     "tiny": tiny,
     "ptpe": ptpe,

@@ -198,6 +198,74 @@ int ep_count_two_pass(const int32_t* times, const uint16_t* types, int64_t n_eve
                       hipStream_t stream, const ep_options* opt);
 
 /*
+ * Level-wise mining of frequent serial episodes: the mining loop whose
+ * counting step the schemes above serve (opening section: the counting of
+ * candidate episodes is the costly part of mining; two-pass elimination
+ * section: candidates counted level by level).  Episodes of one size are
+ * counted together on the GPU; the frequent ones (count >= threshold) of size
+ * k give the candidates of size k+1:
+ *   size 1    every alphabet type;
+ *   size 2    every ordered pair (a, c) of frequent types, once per bin;
+ *   size k+1  alpha followed by beta's last bin and type, for every frequent
+ *             alpha and beta where beta without its last node equals alpha
+ *             without its first node (types and bins).
+ * Removing the first or last node of an occurrence leaves an occurrence of
+ * the shorter episode and keeps occurrences non-overlapped, so these joins
+ * reach every frequent episode up to max_nodes.
+ */
+typedef struct {
+  int32_t n_bins;          /* delay intervals a candidate may use between consecutive nodes */
+  const int32_t* bin_lo;   /* HOST [n_bins], distinct bins with 0 <= bin_lo[i] < bin_hi[i] */
+  const int32_t* bin_hi;   /* HOST [n_bins] */
+  int32_t max_nodes;       /* largest episode size mined, 1 .. EP_MAX_NODES */
+  int64_t threshold;       /* an episode is frequent when its count >= threshold (>= 1) */
+  int32_t two_pass;        /* non-zero: count sizes >= 2 with ep_count_two_pass */
+  int32_t mode;            /* scheme of the counting calls: EP_MODE_AUTO / PTPE / MAPCONCAT */
+  int64_t max_candidates;  /* > 0: return EP_ERR_UNSUPPORTED when a size has more candidates */
+} ep_mine_options;
+
+/* Opaque result of ep_mine: the frequent episodes of each size, in host
+ * memory owned by the library until ep_mined_free. */
+typedef struct ep_mined ep_mined;
+
+/*
+ * Mine the frequent episodes of one event stream.
+ *   times, types, n_events  DEVICE event stream as in ep_count_episodes.
+ *   alphabet    HOST uint16[n_alphabet], the event types to mine over
+ *               (duplicates are ignored).
+ *   opt         options above (required).
+ *   stream      HIP stream the counting work is enqueued on; the call
+ *               synchronises it once per size (the next candidates depend on
+ *               the counts).
+ *   out         receives the result (NULL on error); free with ep_mined_free.
+ * Returns EP_OK, EP_ERR_ARG (null or negative arguments, threshold < 1,
+ * n_bins < 1 with max_nodes > 1, duplicate bins), EP_ERR_NODES (max_nodes out
+ * of range), EP_ERR_INTERVAL (a bad bin), EP_ERR_UNSUPPORTED (too many
+ * candidates, or a bin the counting kernels cannot hold), or an error of the
+ * counting calls.  Rows of every size are in increasing order of
+ * (type 1, bin 1, type 2, bin 2, ..., type k), bins by their index in opt.
+ */
+int ep_mine(const int32_t* times, const uint16_t* types, int64_t n_events,
+            const uint16_t* alphabet, int32_t n_alphabet, const ep_mine_options* opt,
+            hipStream_t stream, ep_mined** out);
+
+/* Largest episode size with a frequent episode (0 if none). */
+int32_t ep_mined_max_nodes(const ep_mined* m);
+/* Frequent episodes of size n_nodes (0 outside 1..ep_mined_max_nodes). */
+int64_t ep_mined_count(const ep_mined* m, int32_t n_nodes);
+/* Candidates counted at size n_nodes (0 if that size was not reached). */
+int64_t ep_mined_candidates(const ep_mined* m, int32_t n_nodes);
+/*
+ * Copy the frequent episodes of size k = n_nodes into HOST arrays sized by
+ * ep_mined_count: types [count * k], t_low / t_high [count * (k-1)] (may be
+ * NULL when k == 1), counts [count].  Returns EP_OK or EP_ERR_ARG.
+ */
+int ep_mined_get(const ep_mined* m, int32_t n_nodes, uint16_t* types, int32_t* t_low,
+                 int32_t* t_high, int64_t* counts);
+/* Release a result (NULL is a no-op). */
+void ep_mined_free(ep_mined* m);
+
+/*
  * The planner alone, on a described device (no GPU needed): which scheme and
  * segment count a call would use.
  *   n_episodes, n_nodes, n_events  sizes of the call.

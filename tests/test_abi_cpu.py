@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|int64_t|const char\*)\s+(ep_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|int32_t|int64_t|void|const char\*)\s+(ep_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
@@ -106,6 +106,41 @@ def test_two_pass_host_errors():
     relaxed = fem.EpOptions(0, 0, 0, 1, None)
     assert _call_two_pass(opt=ctypes.byref(relaxed)) == (-1, 0)
     assert _call_two_pass(S=0, out=0, upper=0) == (0, 0)
+
+
+def _mine_call(max_nodes=2, threshold=1, bins=((0, 5),), n_events=10, alphabet=(1, 2), out=True,
+               mode=0):
+    lib = fem.load_library()
+    lo = np.array([b[0] for b in bins], np.int32)
+    hi = np.array([b[1] for b in bins], np.int32)
+    al = np.array(alphabet, np.uint16)
+    opt = fem.EpMineOptions(len(bins), lo.ctypes.data if lo.size else None,
+                            hi.ctypes.data if hi.size else None, max_nodes, threshold, 0, mode, 0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case here fails on the host
+    handle = ctypes.c_void_p(0x77)
+    st = lib.ep_mine(fake, fake, n_events, al.ctypes.data if al.size else None, al.size,
+                     ctypes.byref(opt), None, ctypes.byref(handle) if out else None)
+    return st, handle.value
+
+
+def test_mine_host_errors():
+    assert _mine_call(out=False)[0] == -1
+    assert _mine_call(max_nodes=0) == (-2, None)
+    assert _mine_call(max_nodes=17) == (-2, None)
+    assert _mine_call(threshold=0) == (-1, None)
+    assert _mine_call(n_events=-1) == (-1, None)
+    assert _mine_call(mode=5) == (-1, None)
+    assert _mine_call(bins=()) == (-1, None)
+    assert _mine_call(bins=((3, 3),)) == (-3, None)
+    assert _mine_call(bins=((-1, 3),)) == (-3, None)
+    assert _mine_call(bins=((0, 3), (0, 3))) == (-1, None)
+    lib = fem.load_library()
+    # accessors on no result
+    assert lib.ep_mined_max_nodes(None) == 0
+    assert lib.ep_mined_count(None, 1) == 0
+    assert lib.ep_mined_candidates(None, 1) == 0
+    assert lib.ep_mined_get(None, 1, None, None, None, None) == -1
+    lib.ep_mined_free(None)
 
 
 def test_planner_rule():
