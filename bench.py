@@ -141,13 +141,164 @@ def calibrate_copy(nbytes: int, reps: int):
                       "launches": reps}))
 
 
+def mining_candidates(mined, bins):
+    """The candidate lists ep_mine counted, rebuilt from its frequent sets with
+    the same rule (for the work figure of the roofline): {k: [types tuple]}."""
+    index = {b: i for i, b in enumerate(bins)}
+    out = {}
+    ks = sorted(mined)
+    for k in ks:
+        if k == 1:
+            continue
+        prev = mined.get(k - 1)
+        if prev is None:
+            break
+        ep, lo, hi, _ = prev
+        rows = [(tuple(int(x) for x in ep[i]),
+                 tuple(index[(int(lo[i, j]), int(hi[i, j]))] for j in range(k - 2)))
+                for i in range(ep.shape[0])]
+        cands = []
+        if k == 2:
+            for (a,), _ in rows:
+                for b in range(len(bins)):
+                    for (c,), _ in rows:
+                        cands.append((a, c))
+        else:
+            by_prefix = {}
+            for t, bs in rows:
+                by_prefix.setdefault((t[:-1], bs[:-1]), []).append(t)
+            for t, bs in rows:
+                for t2 in by_prefix.get((t[1:], bs[1:]), []):
+                    cands.append(t + (t2[-1],))
+        out[k] = cands
+    return out
+
+
+def main_mine(args):
+    """Level-wise mining benchmark: one step = one ep_mine call."""
+    import torch
+    import frequent_episode_mining_amd as fem
+    from frequent_episode_mining_amd import workloads as W
+
+    t0 = time.time()
+    wl = W.make_mining(args.config)
+    threshold = wl.threshold if args.threshold is None else args.threshold
+    log("workload %s: %s (%.1fs to generate)" % (wl.name, wl.description, time.time() - t0))
+    dev = torch.device("cuda:0")
+    times, types = fem.to_device(wl.times, wl.types, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return fem.mine(times, types, wl.alphabet, wl.bins, max_nodes=wl.max_nodes,
+                        threshold=threshold, two_pass=args.two_pass_mining, mode=args.mode,
+                        stream=stream, candidates=True)
+
+    mined, cands = step()
+    log("levels: frequent %s, candidates %s" % ({k: len(v[3]) for k, v in mined.items()}, cands))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    fem.profile_begin()
+    for _ in range(args.steps):
+        step()
+    prof = fem.profile_end()
+    per = {k: prof[k] / args.steps for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
+    top = max(per, key=per.get)
+    which = {"map_filter_ms": "filter", "map_ticks_ms": "ticks", "map_positions_ms": "positions"}[top]
+    log("phases per step: map %.4f (filter %.4f, ticks %.4f, positions %.4f) closure %.4f "
+        "concat %.4f other %.4f ms; %.1f counting calls per step"
+        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_ticks_ms"],
+           per["map_positions_ms"], prof["closure_ms"] / args.steps, prof["concat_ms"] / args.steps,
+           prof["other_ms"] / args.steps, prof["calls"] / args.steps))
+    fem.profile_begin_kernel(which, 1)
+    torch.cuda.synchronize(dev)
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        mined, cands = step()
+    torch.cuda.synchronize(dev)
+    w1 = time.perf_counter()
+    kprof = fem.profile_end()
+    ms_per_step = (w1 - w0) * 1000.0 / args.steps
+    n = wl.n_events
+    total_cands = sum(cands.values())
+    value = n * total_cands / (ms_per_step / 1000.0)
+    kernel_ms = kprof[top] / args.steps
+    # work of the dominant kernel: 10 int32 ops per (candidate, relevant event)
+    cnt = np.bincount(wl.types, minlength=65536).astype(np.int64)
+    rel = int(cnt[np.unique(wl.alphabet)].sum())  # size 1: each type's own events
+    for k, lst in mining_candidates(mined, wl.bins).items():
+        rel += sum(int(cnt[np.unique(np.array(t))].sum()) for t in lst)
+    names = {"map_filter_ms": "filter_kernel", "map_ticks_ms": "map_ticks_kernel",
+             "map_positions_ms": "map_bits_kernel"}
+    achieved = OPS_PER_RELEVANT_PAIR * rel / (kernel_ms / 1000.0) / 1e12 if kernel_ms > 0 else 0.0
+    roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
+                "frac": achieved / ALU_PEAK_TOPS, "traffic": None,
+                "work": "%d int32 ops x %d (candidate, relevant event) pairs over all sizes"
+                        % (OPS_PER_RELEVANT_PAIR, rel),
+                "kernel": names[top], "kernel_ms": kernel_ms,
+                "launches_per_step": kprof["calls"] / args.steps, "timed_launches": kprof["calls"]}
+    log("step %.4f ms; %s kernel %.4f ms per step" % (ms_per_step, which, kernel_ms))
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(os.cpu_count() or 1, 16)
+        reps, total, ok = 0, 0.0, True
+        while True:
+            t0 = time.perf_counter()
+            want = oracle.mine(wl.times, wl.types, wl.alphabet, wl.bins, wl.max_nodes, threshold,
+                               n_threads=threads)
+            total += time.perf_counter() - t0
+            reps += 1
+            ok = ok and sorted(want) == sorted(mined) and all(
+                all(np.array_equal(a, b) for a, b in zip(mined[k], want[k])) for k in want)
+            if total >= 0.9 * args.cpu_seconds or reps >= 100:
+                break
+        cpu = {"value": n * total_cands * reps / total, "unit": "episode-events/s",
+               "cores": threads, "kind": "oracle",
+               "sample": "the whole mining job (%d sizes, %d candidates), %d pass(es), %.2f s"
+                         % (len(cands), total_cands, reps, total)}
+        parity = "identical frequent sets and counts" if ok else "MISMATCH"
+        log("cpu oracle: %s; parity %s" % (cpu["sample"], parity))
+
+    line = {
+        "metric": "episode-events/sec (events x candidate episodes counted)",
+        "value": value,
+        "unit": "episode-events/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "n_events": n,
+                   "scheme": "level-wise mining%s, threshold %d, up to %d nodes"
+                             % (" (two-pass counting)" if args.two_pass_mining else "", threshold,
+                                wl.max_nodes),
+                   "frequent": {str(k): int(len(v[3])) for k, v in mined.items()},
+                   "candidates": {str(k): int(v) for k, v in cands.items()},
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line))
+    if parity == "MISMATCH":
+        sys.exit(1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="ptpe",
-                    choices=["tiny", "ptpe", "mapconcat", "level2", "longchain"])
+                    choices=["tiny", "ptpe", "mapconcat", "level2", "longchain", "sym26"],
+                    help="a counting workload, or sym26: level-wise mining of a Sym26-shaped stream")
     ap.add_argument("--mode", default="auto", choices=["auto", "ptpe", "mapconcat"])
     ap.add_argument("--segments", type=int, default=-1,
                     help="MapConcatenate segment count (-1: the workload's own, 0: planner)")
@@ -157,8 +308,11 @@ def main():
     ap.add_argument("--scheme", default="alpha", choices=["alpha", "upper", "two-pass"],
                     help="alpha: exact counts; upper: relaxed episodes (lower bounds 0); "
                          "two-pass: relaxed counts, then exact counts of those >= --threshold")
-    ap.add_argument("--threshold", type=int, default=30000,
-                    help="support threshold of --scheme two-pass")
+    ap.add_argument("--threshold", type=int, default=None,
+                    help="support threshold of --scheme two-pass (default 30000) or of mining "
+                         "(default: the workload's)")
+    ap.add_argument("--two-pass-mining", action="store_true",
+                    help="sym26: count every size from 2 on with the two-pass elimination")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -177,6 +331,10 @@ def main():
     from frequent_episode_mining_amd import workloads as W
 
     fem.load_library()
+    if args.config in W.MINING:
+        return main_mine(args)
+    if args.threshold is None:
+        args.threshold = 30000
     t0 = time.time()
     wl = W.make(args.config)
     log("workload %s: %s (%.1fs to generate)" % (wl.name, wl.description, time.time() - t0))
