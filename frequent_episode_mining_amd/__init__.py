@@ -100,6 +100,17 @@ def load_library(path: str | None = None):
     lib.ep_mined_get.argtypes = [vp, i32, vp, vp, vp, vp]
     lib.ep_mined_free.restype = None
     lib.ep_mined_free.argtypes = [vp]
+    lib.ep_stream_create.restype = ctypes.c_int
+    lib.ep_stream_create.argtypes = [EpEpisodes, i64, ctypes.POINTER(EpOptions), vp,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+    lib.ep_stream_push.restype = ctypes.c_int
+    lib.ep_stream_push.argtypes = [vp, vp, vp, i64, vp]
+    lib.ep_stream_counts.restype = ctypes.c_int
+    lib.ep_stream_counts.argtypes = [vp, vp, vp]
+    lib.ep_stream_events.restype = i64
+    lib.ep_stream_events.argtypes = [vp]
+    lib.ep_stream_destroy.restype = None
+    lib.ep_stream_destroy.argtypes = [vp]
     lib.ep_plan.restype = ctypes.c_int
     lib.ep_plan.argtypes = [i64, i32, i64, i32, i32, i32, i32,
                             ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -303,6 +314,61 @@ def mine(times, types, alphabet, bins, *, max_nodes: int, threshold: int, two_pa
     finally:
         lib.ep_mined_free(handle)
     return (out, cands) if candidates else out
+
+
+class EpisodeStream:
+    """Counts of a fixed episode table over a stream that arrives in batches.
+
+    ``push(times, types)`` adds one batch (GPU tensors; its first time not
+    before the previous batch's last); ``counts()`` returns the counts over
+    every event pushed so far (int64 [S] GPU tensor).  Each push synchronises
+    its stream.
+    """
+
+    def __init__(self, ep_types, t_low=None, t_high=None, *, mode: str = "auto", n_segments: int = 0,
+                 validate: bool = False, upper_only: bool = False, device="cuda", stream=None):
+        import torch
+        if upper_only and t_low is None and not isinstance(ep_types, EpisodeTable):
+            t_low = np.zeros_like(np.asarray(t_high, dtype=np.int32))
+        self.table = ep_types if isinstance(ep_types, EpisodeTable) else EpisodeTable(ep_types, t_low, t_high)
+        self.device = torch.device(device)
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self._lib = load_library()
+        self._handle = ctypes.c_void_p()
+        opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), int(bool(upper_only)), None)
+        sp = _stream_handle(stream, self.device)
+        status = _on_device(self.device, lambda: self._lib.ep_stream_create(
+            self.table.as_struct(), self.table.n_episodes, ctypes.byref(opt), sp, ctypes.byref(self._handle)))
+        _check(status)
+
+    def push(self, times, types, stream=None):
+        tp, yp, n = _stream_args(times, types)
+        sp = _stream_handle(stream, times.device)
+        _check(_on_device(times.device, lambda: self._lib.ep_stream_push(self._handle, tp, yp, n, sp)))
+
+    def counts(self, stream=None):
+        import torch
+        out = torch.empty(self.table.n_episodes, dtype=torch.int64, device=self.device)
+        op = _device_ptr(out, (torch.int64,), "out") if out.numel() else None
+        sp = _stream_handle(stream, self.device)
+        _check(_on_device(self.device, lambda: self._lib.ep_stream_counts(self._handle, op, sp)))
+        return out
+
+    @property
+    def events(self) -> int:
+        return int(self._lib.ep_stream_events(self._handle))
+
+    def close(self):
+        if self._handle:
+            self._lib.ep_stream_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def plan(n_episodes: int, n_nodes: int, n_events: int, *, mode: str = "auto", n_segments: int = 0,

@@ -403,9 +403,20 @@ inline void mark() {
   if (g_ntp < 16) g_tp[g_ntp++] = std::chrono::steady_clock::now();
 }
 
+// A counting call made for one batch of an ep_stream (see stream_entry_kernel):
+// the carried reset times, the running counts, where to write the new reset
+// times, and the first and last event times of the call's events.
+struct StreamHook {
+  const int64_t* entry;
+  int64_t* total;
+  int64_t* reset_out;
+  int64_t t_first;
+  int64_t t_end;
+};
+
 int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
-                        hipStream_t stream, const ep_options* opt) {
+                        hipStream_t stream, const ep_options* opt, const StreamHook* sh = nullptr) {
   // ---- host-side argument checks (nothing is enqueued before they pass)
   const int32_t N = episodes.n_nodes;
   const int64_t S = n_episodes;
@@ -536,8 +547,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     lanes_per_cu_est = lanes;
   }
   int32_t pmode = 0, P = 1;
-  plan_rule(S, N, n_events, mode, opt ? opt->n_segments : 0, info->cu_count, lanes_per_cu_est,
-            &pmode, &P);
+  plan_rule(S, N, n_events, sh ? EP_MODE_MAPCONCAT : mode, opt ? opt->n_segments : 0,
+            info->cu_count, lanes_per_cu_est, &pmode, &P);
+  if (sh) {
+    // a batch of a stream: segments longer than maxSpan ticks (see the tail)
+    const int64_t cap = std::max<int64_t>(1, (sh->t_end - sh->t_first + 1) / (max_span + 1));
+    P = (int32_t)std::min<int64_t>(P, cap);
+  }
   L.mode = pmode;
   L.P = P;
   L.n_machines = (pmode == EP_MODE_PTPE) ? 1 : N;
@@ -769,7 +785,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
     rec_at(1);
     hipError_t le = hipSuccess;
-    if (L.list) {
+    const bool skip_map = sh && P == 1;  // one segment of a stream: the tail counts it
+    if (L.list && !skip_map) {
       FilterArgs fa;
       fa.times = times; fa.types = types; fa.n = n_events;
       fa.type_seen = d_seen; fa.type_rank = d_rank; fa.slot_eps = d_seps; fa.slot_levels = d_slv;
@@ -789,7 +806,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       le = hipGetLastError();
     }
     rec_at(2);
-    if (le == hipSuccess && !L.bits) {
+    if (skip_map) {
+      rec_at(3);
+    } else if (le == hipSuccess && !L.bits) {
       rec_at(3);  // no tick kernel: an empty interval
       le = Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
     } else if (le == hipSuccess) {
@@ -803,6 +822,21 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
     rec_at(4);
+    StreamArgs stra{};
+    if (sh) {
+      ClosureArgs& c = stra.c;
+      c.times = times; c.types = types;
+      c.ep_types = d_types; c.ep_lo = d_lo; c.ep_hi = d_hi; c.ep_span = d_span;
+      c.tau = d_tau; c.seg_beg = d_beg; c.seg_end = d_end;
+      c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
+      c.S = S; c.P = P;
+      stra.entry = sh->entry; stra.total = sh->total; stra.reset_out = sh->reset_out;
+      stra.n = n_events; stra.t_end = sh->t_end; stra.max_span = max_span;
+      if (P > 1 && Lr->stream_entry(stra, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+    }
 
     mark();  // map launches
     if (P > 1) {
@@ -821,10 +855,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       int members = kConcatMembers;
       while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
       const size_t lds = (size_t)members * (12 * L.slots + 4);
-      for (int64_t stride = 1; stride < P; stride *= members) {
-        const int64_t groups = (P + stride * members - 1) / (stride * members);
+      // a stream's batch joins all but the last segment (the tail runs that one)
+      const int32_t Pt = sh ? P - 1 : P;
+      for (int64_t stride = 1; stride < Pt; stride *= members) {
+        const int64_t groups = (Pt + stride * members - 1) / (stride * members);
         hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(members), lds,
-                           stream, ts, d_flags, S, P, stride, members, groups);
+                           stream, ts, d_flags, S, Pt, stride, members, groups);
         if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
       }
       if (status != EP_OK) break;
@@ -832,15 +868,22 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     if (P <= 1) rec_at(5);
     rec_at(6);
     mark();  // closure + tree launches
-    FallbackArgs fa;
-    fa.times = times; fa.types = types;
-    fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
-    fa.flags = d_flags; fa.T0 = d_t0; fa.P = P;
-    fa.fallbacks = d_cnt + 1; fa.out = out_counts;
-    fa.n = n_events; fa.S = S;
-    if (Lr->finish(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
-      status = EP_ERR_HIP;
-      break;
+    if (sh) {
+      if (Lr->stream_tail(stra, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+    } else {
+      FallbackArgs fa;
+      fa.times = times; fa.types = types;
+      fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
+      fa.flags = d_flags; fa.T0 = d_t0; fa.P = P;
+      fa.fallbacks = d_cnt + 1; fa.out = out_counts;
+      fa.n = n_events; fa.S = S;
+      if (Lr->finish(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
     }
     if (prof) {
       if (prof_which < 0) (void)hipEventRecord(rec.end, stream);
@@ -1028,6 +1071,200 @@ extern "C" int ep_count_two_pass(const int32_t* times, const uint16_t* types, in
   EP_HIP(hipGetLastError());
   if (n_kept) *n_kept = kept;
   return EP_OK;
+}
+
+// ------------------------------------------------------------- streaming
+
+struct ep_stream {
+  int dev = 0;
+  int32_t N = 0;
+  int64_t S = 0;
+  std::vector<uint16_t> types;      // the episode table (host copy)
+  std::vector<int32_t> lo, hi;
+  ep_options opt{};
+  int64_t max_span = 0;
+  int64_t t_last = INT64_MIN;       // last event time pushed so far
+  int64_t events = 0;               // events pushed so far
+  int64_t* total = nullptr;         // device [S] running counts
+  int64_t* reset[2] = {nullptr, nullptr};  // device [S] carried reset times (ping-pong)
+  int cur = 0;                      // reset[cur] holds the times to carry into the next push
+  int64_t* scalar = nullptr;        // device scratch word
+  int32_t* halo_t = nullptr;        // device halo: events within maxSpan of t_last
+  uint16_t* halo_y = nullptr;
+  int64_t halo_n = 0, halo_cap = 0;
+  int32_t* comb_t = nullptr;        // device: halo followed by the batch
+  uint16_t* comb_y = nullptr;
+  int64_t comb_cap = 0;
+};
+
+namespace {
+
+int grow(int32_t** t, uint16_t** y, int64_t* cap, int64_t need) {
+  if (need <= *cap) return EP_OK;
+  const int64_t c = std::max<int64_t>(need + need / 4, 1 << 16);
+  int32_t* nt = nullptr;
+  uint16_t* ny = nullptr;
+  if (hipMalloc((void**)&nt, (size_t)c * sizeof(int32_t)) != hipSuccess) return EP_ERR_WORKSPACE;
+  if (hipMalloc((void**)&ny, (size_t)c * sizeof(uint16_t)) != hipSuccess) {
+    (void)hipFree(nt);
+    return EP_ERR_WORKSPACE;
+  }
+  // the old buffers may still be read by queued work: wait for the device first
+  if (*t && (hipDeviceSynchronize() != hipSuccess || hipFree(*t) != hipSuccess || hipFree(*y) != hipSuccess)) {
+    (void)hipFree(nt);
+    (void)hipFree(ny);
+    return EP_ERR_HIP;
+  }
+  *t = nt;
+  *y = ny;
+  *cap = c;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" int ep_stream_create(ep_episodes episodes, int64_t n_episodes, const ep_options* opt,
+                                hipStream_t stream, ep_stream** out) {
+  using namespace epk;
+  if (!out) return EP_ERR_ARG;
+  *out = nullptr;
+  const int32_t N = episodes.n_nodes;
+  const int64_t S = n_episodes;
+  if (S < 0) return EP_ERR_ARG;
+  if (N < 1 || N > EP_MAX_NODES) return EP_ERR_NODES;
+  const bool upper_only = opt && opt->upper_only;
+  if (S > 0 && (!episodes.types || (N > 1 && (!episodes.t_high || (!upper_only && !episodes.t_low)))))
+    return EP_ERR_ARG;
+  if (opt && (opt->mode < EP_MODE_AUTO || opt->mode > EP_MODE_MAPCONCAT || opt->n_segments < 0))
+    return EP_ERR_ARG;
+  ep_stream* st = new ep_stream();
+  st->N = N;
+  st->S = S;
+  st->types.assign(episodes.types, episodes.types + S * N);
+  if (N > 1) {
+    st->hi.assign(episodes.t_high, episodes.t_high + S * (N - 1));
+    if (upper_only)
+      st->lo.assign((size_t)(S * (N - 1)), 0);
+    else
+      st->lo.assign(episodes.t_low, episodes.t_low + S * (N - 1));
+  }
+  for (int64_t e = 0; e < S; ++e) {
+    int64_t span = 0;
+    for (int j = 0; j < N - 1; ++j) {
+      const int64_t l = st->lo[(size_t)(e * (N - 1) + j)], h = st->hi[(size_t)(e * (N - 1) + j)];
+      if (l < 0 || l >= h) {
+        delete st;
+        return EP_ERR_INTERVAL;
+      }
+      span += h;
+    }
+    if (span > INT32_MAX) {
+      delete st;
+      return EP_ERR_INTERVAL;
+    }
+    st->max_span = std::max(st->max_span, span);
+  }
+  if (opt) st->opt = *opt;
+  st->opt.upper_only = 0;  // the table copy already holds the relaxed bounds
+  st->opt.stats = nullptr;
+  int status = EP_OK;
+  do {
+    if (hipGetDevice(&st->dev) != hipSuccess) { status = EP_ERR_HIP; break; }
+    const size_t b = (size_t)std::max<int64_t>(S, 1) * sizeof(int64_t);
+    if (hipMalloc((void**)&st->total, b) != hipSuccess || hipMalloc((void**)&st->reset[0], b) != hipSuccess ||
+        hipMalloc((void**)&st->reset[1], b) != hipSuccess ||
+        hipMalloc((void**)&st->scalar, sizeof(int64_t)) != hipSuccess) {
+      status = EP_ERR_WORKSPACE;
+      break;
+    }
+    if (S > 0) {
+      hipLaunchKernelGGL(fill_i64_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, st->total, S, (int64_t)0);
+      hipLaunchKernelGGL(fill_i64_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, st->reset[0], S, kNoReset);
+      if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
+    }
+  } while (0);
+  if (status != EP_OK) {
+    ep_stream_destroy(st);
+    return status;
+  }
+  *out = st;
+  return EP_OK;
+}
+
+extern "C" int ep_stream_push(ep_stream* st, const int32_t* times, const uint16_t* types, int64_t n_events,
+                              hipStream_t stream) {
+  using namespace epk;
+  if (!st || n_events < 0 || n_events > INT32_MAX) return EP_ERR_ARG;
+  if (n_events == 0 || st->S == 0) {
+    if (n_events > 0) st->events += n_events;
+    return EP_OK;
+  }
+  if (!times || !types) return EP_ERR_ARG;
+  int dev = 0;
+  EP_HIP(hipGetDevice(&dev));
+  if (dev != st->dev) return EP_ERR_ARG;
+  // the batch's first and last times
+  int32_t ends[2] = {0, 0};
+  EP_HIP(hipMemcpyAsync(&ends[0], times, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  EP_HIP(hipMemcpyAsync(&ends[1], times + n_events - 1, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  EP_HIP(hipStreamSynchronize(stream));
+  if (st->t_last != INT64_MIN && (int64_t)ends[0] < st->t_last) return EP_ERR_UNSORTED;
+  const int64_t n = st->halo_n + n_events;
+  if (n > INT32_MAX) return EP_ERR_ARG;
+  if (int s = grow(&st->comb_t, &st->comb_y, &st->comb_cap, n)) return s;
+  int32_t halo_first = 0;
+  if (st->halo_n > 0) {
+    EP_HIP(hipMemcpyAsync(st->comb_t, st->halo_t, (size_t)st->halo_n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
+    EP_HIP(hipMemcpyAsync(st->comb_y, st->halo_y, (size_t)st->halo_n * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
+    EP_HIP(hipMemcpyAsync(&halo_first, st->halo_t, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  }
+  EP_HIP(hipMemcpyAsync(st->comb_t + st->halo_n, times, (size_t)n_events * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
+  EP_HIP(hipMemcpyAsync(st->comb_y + st->halo_n, types, (size_t)n_events * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
+  StreamHook hook;
+  hook.entry = st->reset[st->cur];
+  hook.total = st->total;
+  hook.reset_out = st->reset[1 - st->cur];
+  if (st->halo_n > 0) EP_HIP(hipStreamSynchronize(stream));
+  hook.t_first = st->halo_n > 0 ? (int64_t)halo_first : (int64_t)ends[0];
+  hook.t_end = ends[1];
+  ep_episodes eps{st->N, st->types.data(), st->N > 1 ? st->lo.data() : nullptr,
+                  st->N > 1 ? st->hi.data() : nullptr};
+  if (int s = count_episodes_impl(st->comb_t, st->comb_y, n, eps, st->S, st->total, stream, &st->opt, &hook))
+    return s;
+  st->cur = 1 - st->cur;
+  // the new halo: events within maxSpan of the last one
+  hipLaunchKernelGGL(lower_bound_kernel, dim3(1), dim3(64), 0, stream, st->comb_t, n, hook.t_end - st->max_span,
+                     st->scalar);
+  EP_HIP(hipGetLastError());
+  int64_t h0 = 0;
+  EP_HIP(hipMemcpyAsync(&h0, st->scalar, sizeof(int64_t), hipMemcpyDeviceToHost, stream));
+  EP_HIP(hipStreamSynchronize(stream));
+  const int64_t hn = n - h0;
+  if (int s = grow(&st->halo_t, &st->halo_y, &st->halo_cap, hn)) return s;
+  EP_HIP(hipMemcpyAsync(st->halo_t, st->comb_t + h0, (size_t)hn * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
+  EP_HIP(hipMemcpyAsync(st->halo_y, st->comb_y + h0, (size_t)hn * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
+  st->halo_n = hn;
+  st->t_last = hook.t_end;
+  st->events += n_events;
+  return EP_OK;
+}
+
+extern "C" int ep_stream_counts(const ep_stream* st, int64_t* out_counts, hipStream_t stream) {
+  if (!st || (st->S > 0 && !out_counts)) return EP_ERR_ARG;
+  if (st->S == 0) return EP_OK;
+  EP_HIP(hipMemcpyAsync(out_counts, st->total, (size_t)st->S * sizeof(int64_t), hipMemcpyDeviceToDevice, stream));
+  return EP_OK;
+}
+
+extern "C" int64_t ep_stream_events(const ep_stream* st) { return st ? st->events : 0; }
+
+extern "C" void ep_stream_destroy(ep_stream* st) {
+  if (!st) return;
+  if (st->total || st->comb_t || st->halo_t) (void)hipDeviceSynchronize();
+  for (void* p : {(void*)st->total, (void*)st->reset[0], (void*)st->reset[1], (void*)st->scalar,
+                  (void*)st->halo_t, (void*)st->halo_y, (void*)st->comb_t, (void*)st->comb_y})
+    if (p) (void)hipFree(p);
+  delete st;
 }
 
 extern "C" int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_events,

@@ -310,6 +310,7 @@ struct SegMachine {
   int32_t b_off;
   bool first_found;
   bool finished;
+  int64_t last;  // the last completion in (tau_lo, tau_hi] (INT64_MIN: none)
 
   __device__ void init(int64_t reset_at, int64_t lo_cut, int64_t hi_cut, int32_t span) {
     m.reset(reset_at);
@@ -321,6 +322,7 @@ struct SegMachine {
     b_off = 0;
     first_found = false;
     finished = false;
+    last = INT64_MIN;
   }
 
   __device__ void feed(int32_t t, uint32_t lm, const typename Mach::Params& P) {
@@ -337,6 +339,7 @@ struct SegMachine {
       }
       if ((int64_t)t <= tau_hi) {
         ++count;
+        last = t;
       } else {
         b_off = (int32_t)((int64_t)t - tau_hi);
         finished = true;
@@ -1802,12 +1805,13 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
     keys[0] = A.ts.T0[A.ts.idx(e, p + 1)].a;
 #pragma unroll
     for (int m = 1; m < N; ++m) keys[m] = m < nr ? A.ts.at(e, p + 1, m)->a : -1;
-    int32_t exits[N];
+    // segment 0 of a stream's batch may hold one tuple more (the carried reset's)
+    int32_t exits[N + 1];
     exits[0] = A.ts.T0[A.ts.idx(e, p)].b;
 #pragma unroll
-    for (int k = 1; k < N; ++k) exits[k] = k < nl ? A.ts.at(e, p, k)->b : -1;
+    for (int k = 1; k <= N; ++k) exits[k] = k < nl ? A.ts.at(e, p, k)->b : -1;
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
+    for (int k = 0; k <= N; ++k) {
       bool hit = false, dup = false;
 #pragma unroll
       for (int m = 0; m < N; ++m) hit |= keys[m] == exits[k];
@@ -1909,6 +1913,134 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(FallbackArgs A) {
 enum WinKind { kRuns1 = 0, kRuns2 = 1, kRuns4 = 2, kBits32 = 3, kBits64 = 4, kNumWin = 5 };
 
 // Per-N entry points, defined in ep_inst.hip (one translation unit per N).
+// ------------------------------------------------------------- streaming
+
+// Counting a stream that arrives in batches.  Between calls the stream
+// carries the events within maxSpan (the table's largest Span) of the last
+// event seen so far, time T (the halo: times >= T - maxSpan), which the next
+// call counts again in front of its new events, and each episode carries the
+// time r of the last completion of its reference machine alpha_0 when r lies
+// in the halo (kNoReset otherwise).  An occurrence completing after T starts
+// no earlier than T - Span, so alpha_0 after T behaves like a machine reset
+// at r fed the halo and the new events.  With no r in the halo, alpha_0's
+// last reset is older than every halo event, so a fresh machine fed the halo
+// sees a subset of alpha_0's events and completes nowhere in it (alpha_0
+// would have completed too), and after T it completes where alpha_0 does.
+// (An r older than Span but inside the halo must be carried: a fresh machine
+// could complete at r again.)  Over the combined events:
+//   - stream_entry_kernel adds to segment 0 the tuple of a machine reset at r
+//     (a repair-style tuple: its count includes the completion at r, counted
+//     by the earlier call, which the tail takes off again);
+//   - the tree joins segments 0 .. P-2 only;
+//   - stream_tail_kernel follows the chain from segment 0 to the last segment
+//     and runs it there with one wave to the last event, which gives the
+//     count of this call and the new r.  Segments are planned more than
+//     maxSpan ticks long, so every completion in the next halo lies in the
+//     last segment.
+constexpr int64_t kNoReset = INT64_MIN;
+
+struct StreamArgs {
+  ClosureArgs c;          // the call's events (halo + batch), table, cuts, tuples, flags
+  const int64_t* entry;   // [S] carried reset times (kNoReset: none)
+  int64_t* total;         // [S] running counts; this call's completions are added
+  int64_t* reset_out;     // [S] reset time to carry into the next call
+  int64_t n;              // events of the call
+  int64_t t_end;          // time of its last event
+  int64_t max_span;       // the table's largest Span (the halo width)
+};
+
+// One wave per episode: the tuple of a machine reset at the carried r, added
+// to segment 0 after the Map tuples (before the closure checks its exit).
+template <int N, class Mach>
+__global__ __launch_bounds__(kBlock) void stream_entry_kernel(StreamArgs A) {
+  const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (e >= A.c.S) return;
+  const int64_t x = A.entry[e];
+  if (x == kNoReset) return;
+  const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
+  typename Mach::Params prm;
+  prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
+  const Tuple tu = repair_tuple<Mach>(A.c, prm, 0, x);
+  if (!lane0) return;
+  const TupleStore& ts = A.c.ts;
+  const int64_t pe = ts.idx(e, 0);
+  const int nm = ts.nmap[pe];
+  for (int m = 0; m < nm; ++m)
+    if (ts.at(e, 0, m)->a == tu.a) return;  // an equal key: the same chain
+  if (nm >= ts.slots) {
+    atomicOr(&A.c.flags[e], 1);
+    return;
+  }
+  *ts.at(e, 0, nm) = tu;
+  ts.nmap[pe] = nm + 1;
+  ts.nslots[pe] = nm + 1;
+}
+
+// One wave per episode: this call's count and the reset time to carry.
+template <int N, class Mach>
+__global__ __launch_bounds__(kBlock) void stream_tail_kernel(StreamArgs A) {
+  const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
+  if (e >= A.c.S) return;
+  const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
+  const TupleStore& ts = A.c.ts;
+  const int64_t x = A.entry[e];
+  const int64_t P = A.c.P;
+  const int64_t tau0 = A.c.tau[0];
+  typename Mach::Params prm;
+  prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
+  // the chain through segments 0 .. P-2 (joined by the tree)
+  bool whole = A.c.flags[e] != 0 || P == 1;
+  int64_t cnt = 0, reset_t = 0, last = kNoReset, i0 = 0;
+  if (!whole) {
+    const int ns = min(ts.nslots[ts.idx(e, 0)], ts.slots);
+    int hit = -1;
+    if (x == kNoReset) {
+      hit = 0;  // machine 0 of segment 0: alpha_0 from the first event
+    } else {
+      const int32_t key = (int32_t)(x - tau0);
+      for (int m = 0; m < ns; ++m)
+        if (hit < 0 && ts.at(e, 0, m)->a == key) hit = m;
+    }
+    if (hit < 0) {
+      whole = true;
+    } else {
+      const Tuple tu = *ts.at(e, 0, hit);
+      const int64_t cut = A.c.tau[P - 1];
+      cnt = (int64_t)tu.c - (x == kNoReset ? 0 : 1);
+      if (tu.b > 0) {
+        reset_t = cut + tu.b;  // the chain's first completion in the last segment
+        cnt += 1;
+        last = reset_t;
+      } else {
+        reset_t = cut;  // no completion within Span of the cut: a fresh machine there
+      }
+      i0 = upper_bound_time(A.c.times, A.c.seg_beg[P - 1], A.n, reset_t);
+    }
+  }
+  if (whole) {
+    // one segment, or an episode the tree could not join: the whole call
+    reset_t = x == kNoReset ? tau0 : x;
+    cnt = 0;
+    last = kNoReset;
+    i0 = upper_bound_time(A.c.times, 0, A.n, reset_t);
+  }
+  SegMachine<Mach> sm;
+  sm.init(reset_t, reset_t, A.t_end, prm.span);
+  wave_feed_range<Mach>(A.c.times, A.c.types, i0, A.n, sm, prm);
+  if (!lane0) return;
+  cnt += sm.count;
+  if (sm.count > 0) last = sm.last;
+  // the reset to carry if it lies in the next halo (times >= t_end - maxSpan)
+  int64_t carry = kNoReset;
+  if (last != kNoReset) {
+    if (last >= A.t_end - A.max_span) carry = last;
+  } else if (cnt == 0 && x != kNoReset && x >= A.t_end - A.max_span) {
+    carry = x;  // no completion in this call: the carried reset still holds
+  }
+  A.total[e] += cnt;
+  A.reset_out[e] = carry;
+}
+
 struct Launchers {
   // scan Map kernel (run windows; win must be a run kind)
   hipError_t (*map_scan)(const MapArgs&, int win, dim3 grid, dim3 block, hipStream_t);
@@ -1923,6 +2055,9 @@ struct Launchers {
                          hipStream_t);
   hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
   hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
+  // streaming: the carried reset's tuple in segment 0, and the chain's tail
+  hipError_t (*stream_entry)(const StreamArgs&, int win, dim3 grid, hipStream_t);
+  hipError_t (*stream_tail)(const StreamArgs&, int win, dim3 grid, hipStream_t);
   // resident workgroups per CU of a Map kernel for a block size and LDS size
   hipError_t (*occupancy)(int win, bool all_machines, int block, size_t lds, int* blocks_per_cu);
   // the same for the tick Map kernel

@@ -111,6 +111,34 @@ hipError_t launch_finish(const FallbackArgs& a, int win, dim3 grid, hipStream_t 
   }
 }
 
+template <class Mach>
+hipError_t launch_stream_m(const StreamArgs& a, bool tail, dim3 grid, hipStream_t s) {
+  if (tail)
+    hipLaunchKernelGGL((stream_tail_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((stream_entry_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream(const StreamArgs& a, int win, bool tail, dim3 grid, hipStream_t s) {
+  switch (win) {
+    case kRuns1: return launch_stream_m<RunMachine<EP_N, 1>>(a, tail, grid, s);
+    case kRuns2: return launch_stream_m<RunMachine<EP_N, 2>>(a, tail, grid, s);
+    case kRuns4: return launch_stream_m<RunMachine<EP_N, 4>>(a, tail, grid, s);
+    case kBits32: return launch_stream_m<BitMachine<EP_N, 32>>(a, tail, grid, s);
+    case kBits64: return launch_stream_m<BitMachine<EP_N, 64>>(a, tail, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stream_entry(const StreamArgs& a, int win, dim3 grid, hipStream_t s) {
+  return launch_stream(a, win, false, grid, s);
+}
+
+hipError_t launch_stream_tail(const StreamArgs& a, int win, dim3 grid, hipStream_t s) {
+  return launch_stream(a, win, true, grid, s);
+}
+
 template <class F>
 hipError_t occ(F f, int block, size_t lds, int* out) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, f, block, lds);
@@ -138,8 +166,10 @@ hipError_t occupancy_ticks(bool all_machines, int block, size_t lds, int* out) {
                       : occ(map_ticks_kernel<EP_N, 1>, block, lds, out);
 }
 
-const Launchers kLaunchers = {launch_scan,    launch_bits,   launch_ticks, launch_list,
-                              launch_closure, launch_finish, occupancy,    occupancy_ticks};
+const Launchers kLaunchers = {launch_scan,         launch_bits,        launch_ticks,
+                              launch_list,         launch_closure,     launch_finish,
+                              launch_stream_entry, launch_stream_tail, occupancy,
+                              occupancy_ticks};
 
 }  // namespace
 

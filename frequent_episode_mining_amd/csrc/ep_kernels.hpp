@@ -446,6 +446,20 @@ __global__ __launch_bounds__(kMergeBlock) void two_pass_merge_kernel(const int64
   }
 }
 
+// First index with times[i] >= bound (one thread: a binary search).
+__global__ void lower_bound_kernel(const int32_t* times, int64_t n, int64_t bound, int64_t* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = lo + ((hi - lo) >> 1);
+    if ((int64_t)times[mid] < bound)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  *out = lo;
+}
+
 __global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* times, int64_t n,
                                                               int32_t* bad) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;

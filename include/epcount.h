@@ -266,6 +266,55 @@ int ep_mined_get(const ep_mined* m, int32_t n_nodes, uint16_t* types, int32_t* t
 void ep_mined_free(ep_mined* m);
 
 /*
+ * Streaming counts: the stream arrives in batches and the counts after each
+ * batch are those of all events pushed so far (the tuple carry of the
+ * Concatenate section, across calls).  Between batches each episode keeps
+ * the time of the last completion of its reference machine alpha_0 when it
+ * lies within Span of the last event pushed, and the stream keeps the events
+ * within maxSpan (the largest Span of the table) of that last event: an
+ * occurrence completing later starts no earlier than Span before it, so
+ * these fix every later count exactly.  Each push counts those kept events
+ * again in front of the new ones (device memory: the kept events plus one
+ * copy of the batch).  A stream object is used by one host thread at a time.
+ */
+typedef struct ep_stream ep_stream;
+
+/*
+ * Create a stream for a fixed episode table (HOST, copied; as in
+ * ep_count_episodes).  opt may be NULL; its mode and n_segments guide the
+ * per-batch plans (batches are counted with MAPCONCAT, P capped so that every
+ * segment spans at least maxSpan ticks), validate checks each batch's order,
+ * upper_only counts the relaxed episodes; stats is ignored.  The running
+ * counts start at 0 on the current device, set on `stream`.  Returns EP_OK,
+ * EP_ERR_ARG, EP_ERR_NODES, EP_ERR_INTERVAL, EP_ERR_WORKSPACE or EP_ERR_HIP;
+ * *out is NULL on error.
+ */
+int ep_stream_create(ep_episodes episodes, int64_t n_episodes, const ep_options* opt,
+                     hipStream_t stream, ep_stream** out);
+
+/*
+ * Count one batch: DEVICE times/types [n_events], non-decreasing, the first
+ * time not before the last time of the previous batch (equal times are
+ * allowed: a tick may span two batches).  Synchronises `stream` (the next
+ * batch's plan depends on this one's last events).  Returns EP_OK,
+ * EP_ERR_ARG (bad arguments, or another device than the stream's),
+ * EP_ERR_UNSORTED (the batch starts before the previous one ended, or with
+ * validate, is unsorted), or an error of the counting path.  On an error the
+ * stream's counts are unspecified.
+ */
+int ep_stream_push(ep_stream* st, const int32_t* times, const uint16_t* types, int64_t n_events,
+                   hipStream_t stream);
+
+/* Copy the running counts (DEVICE int64[n_episodes]) on `stream`. */
+int ep_stream_counts(const ep_stream* st, int64_t* out_counts, hipStream_t stream);
+
+/* Events pushed so far. */
+int64_t ep_stream_events(const ep_stream* st);
+
+/* Release a stream (NULL is a no-op); waits for the device. */
+void ep_stream_destroy(ep_stream* st);
+
+/*
  * The planner alone, on a described device (no GPU needed): which scheme and
  * segment count a call would use.
  *   n_episodes, n_nodes, n_events  sizes of the call.

@@ -143,6 +143,35 @@ def test_mine_host_errors():
     lib.ep_mined_free(None)
 
 
+def test_stream_host_errors():
+    lib = fem.load_library()
+    ep_t = np.zeros(2, np.uint16)
+    lo = np.array([0], np.int32)
+    hi = np.array([5], np.int32)
+    bad = np.array([5], np.int32)
+    h = ctypes.c_void_p(0x55)
+    ok_eps = fem.EpEpisodes(2, ep_t.ctypes.data, lo.ctypes.data, hi.ctypes.data)
+    assert lib.ep_stream_create(ok_eps, 1, None, None, None) == -1
+    assert lib.ep_stream_create(ok_eps, -1, None, None, ctypes.byref(h)) == -1 and h.value is None
+    assert lib.ep_stream_create(fem.EpEpisodes(0, ep_t.ctypes.data, None, None), 1, None, None,
+                                ctypes.byref(h)) == -2
+    assert lib.ep_stream_create(fem.EpEpisodes(2, None, lo.ctypes.data, hi.ctypes.data), 1, None, None,
+                                ctypes.byref(h)) == -1
+    assert lib.ep_stream_create(fem.EpEpisodes(2, ep_t.ctypes.data, bad.ctypes.data, hi.ctypes.data), 1,
+                                None, None, ctypes.byref(h)) == -3
+    bad_mode = fem.EpOptions(9, 0, 0, 0, None)
+    assert lib.ep_stream_create(ok_eps, 1, ctypes.byref(bad_mode), None, ctypes.byref(h)) == -1
+    # a relaxed table needs no lower bounds
+    relaxed = fem.EpOptions(0, 0, 0, 1, None)
+    zero_hi = np.array([0], np.int32)
+    assert lib.ep_stream_create(fem.EpEpisodes(2, ep_t.ctypes.data, None, zero_hi.ctypes.data), 1,
+                                ctypes.byref(relaxed), None, ctypes.byref(h)) == -3
+    assert lib.ep_stream_push(None, None, None, 0, None) == -1
+    assert lib.ep_stream_counts(None, None, None) == -1
+    assert lib.ep_stream_events(None) == 0
+    lib.ep_stream_destroy(None)
+
+
 def test_planner_rule():
     # episodes alone fill 256 CUs x 2048 lanes -> PTPE
     assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
