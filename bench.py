@@ -90,7 +90,7 @@ def oracle_timed(wl, idx, scheme: str, threshold: int, threads: int):
     results are the counts, the relaxed counts, or both stacked (two-pass)."""
     import oracle
     t0 = time.perf_counter()
-    if scheme == "alpha":
+    if scheme in ("alpha", "stream"):
         want, _, used = oracle.count_timed(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
                                            wl.t_high[idx], n_threads=threads)
     elif scheme == "upper":
@@ -305,9 +305,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--scheme", default="alpha", choices=["alpha", "upper", "two-pass"],
+    ap.add_argument("--scheme", default="alpha", choices=["alpha", "upper", "two-pass", "stream"],
                     help="alpha: exact counts; upper: relaxed episodes (lower bounds 0); "
-                         "two-pass: relaxed counts, then exact counts of those >= --threshold")
+                         "two-pass: relaxed counts, then exact counts of those >= --threshold; "
+                         "stream: the stream pushed in --batches batches to an EpisodeStream")
+    ap.add_argument("--batches", type=int, default=10, help="batches of --scheme stream")
     ap.add_argument("--threshold", type=int, default=None,
                     help="support threshold of --scheme two-pass (default 30000) or of mining "
                          "(default: the workload's)")
@@ -356,7 +358,16 @@ def main():
     scheme = args.scheme
     kept_box = [0]
 
+    cuts = np.linspace(0, wl.n_events, max(1, args.batches) + 1).astype(np.int64)
+
     def step():
+        if scheme == "stream":
+            st = fem.EpisodeStream(table, mode=mode, n_segments=seg, stream=stream)
+            for i in range(cuts.size - 1):
+                st.push(times[cuts[i]:cuts[i + 1]], types[cuts[i]:cuts[i + 1]], stream=stream)
+            c = st.counts(stream=stream)
+            st.close()
+            return c, None
         if scheme == "two-pass":
             c, u, kept_box[0] = fem.count_two_pass(times, types, table, threshold=args.threshold,
                                                    mode=mode, n_segments=seg, stream=stream)
@@ -365,7 +376,10 @@ def main():
                            upper_only=(scheme == "upper"))
         return out, None
 
-    if scheme == "two-pass":
+    if scheme == "stream":
+        st = {"mode": "mapconcat per batch", "n_segments": 0, "max_runs": 0, "kernels": 1 | 2,
+              "repairs": 0, "fallbacks": 0}
+    elif scheme == "two-pass":
         _, _, _, st = fem.count_two_pass(times, types, table, threshold=args.threshold, mode=mode,
                                          n_segments=seg, stats=True, stream=stream)
     else:
@@ -396,7 +410,7 @@ def main():
 
     # The timed region: only the dominant kernel's two events, on one call in
     # four (every call for the two-pass scheme: its steps alternate passes).
-    every = 1 if scheme == "two-pass" else 4
+    every = 1 if scheme in ("two-pass", "stream") else 4
     fem.profile_begin_kernel(which, every)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -443,6 +457,10 @@ def main():
         rel = rel + relevant_pairs_rows(wl, kept_rows)
         kernel_ms = kprof[top] / args.steps
         map_s = kernel_ms / 1000.0
+    elif scheme == "stream":
+        # every batch's launch: the whole stream once (the halo re-counts are extra work)
+        kernel_ms = kprof[top] / args.steps
+        map_s = kernel_ms / 1000.0
     traffic = stored_traffic(wl.name if scheme == "alpha" else "%s-%s" % (wl.name, scheme), kernel)
     if traffic is not None and scheme == "two-pass":
         traffic *= 2  # the stored figure is per dispatch; a step launches the kernel twice
@@ -461,7 +479,7 @@ def main():
                     "work": "%d int32 ops x %d (episode, relevant event) pairs"
                             % (OPS_PER_RELEVANT_PAIR, rel)}
     roofline.update({"kernel": kernel, "kernel_ms": kernel_ms,
-                     "launches_per_step": 2 if scheme == "two-pass" else 1,
+                     "launches_per_step": kprof["calls"] / args.steps,
                      "timed_launches": kprof["calls"],
                      "map_kernels_ms": {names[k]: v for k, v in per.items()},
                      "hbm_one_pass_frac": 6.0 * n / (prof["map_ms"] / args.steps / 1000.0)
@@ -496,7 +514,8 @@ def main():
                    "scheme": {"alpha": "exact counts",
                               "upper": "relaxed episodes (lower bounds 0)",
                               "two-pass": "two-pass elimination, threshold %d, %d kept"
-                                          % (args.threshold, kept_box[0])}[scheme],
+                                          % (args.threshold, kept_box[0]),
+                              "stream": "streaming counts, %d batches" % args.batches}[scheme],
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
