@@ -839,7 +839,35 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
 
     mark();  // map launches
-    if (P > 1) {
+    // up to kReduceMembers segments: closure, tree and result in one launch
+    // (a full wave at least: repairs and recounts are wave-cooperative)
+    int red_members = kWave;
+    while (red_members < P) red_members <<= 1;
+    const size_t red_lds = (size_t)red_members * (12 * L.slots + 8);
+    // fused when the post-Map work is small enough for its launches to matter
+    // (S x P <= 2^20 tuples); beyond, the closure kernel spreads each
+    // episode's repairs over the whole grid and wins
+    const bool fused = !sh && P <= kReduceMembers && red_lds <= 65536 && S * (int64_t)P <= (1 << 20) &&
+                       !getenv("EP_NO_REDUCE");
+    if (fused) {
+      const int members = red_members;
+      const size_t lds = red_lds;
+      ReduceArgs ra;
+      ClosureArgs& c = ra.c;
+      c.times = times; c.types = types;
+      c.ep_types = d_types; c.ep_lo = d_lo; c.ep_hi = d_hi; c.ep_span = d_span;
+      c.tau = d_tau; c.seg_beg = d_beg; c.seg_end = d_end;
+      c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
+      c.S = S; c.P = P;
+      ra.fallbacks = d_cnt + 1; ra.out = out_counts; ra.n = n_events;
+      if (Lr->reduce(ra, L.win, dim3((unsigned)S), dim3((unsigned)members), lds, stream) !=
+          hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
+      rec_at(5);
+    }
+    if (P > 1 && !fused) {
       ClosureArgs ca;
       ca.times = times; ca.types = types;
       ca.ep_types = d_types; ca.ep_lo = d_lo; ca.ep_hi = d_hi; ca.ep_span = d_span;
@@ -852,11 +880,14 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       rec_at(5);
       // Concatenate tree: each launch joins groups of `members` blocks in LDS
-      int members = kConcatMembers;
-      while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
-      const size_t lds = (size_t)members * (12 * L.slots + 4);
       // a stream's batch joins all but the last segment (the tail runs that one)
       const int32_t Pt = sh ? P - 1 : P;
+      // members per workgroup: the fewest powers of two covering Pt (less LDS,
+      // more resident workgroups), within 64 KiB of LDS
+      int members = kConcatMembers;
+      while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
+      while (members > 1 && members / 2 >= Pt) members >>= 1;
+      const size_t lds = (size_t)members * (12 * L.slots + 4);
       for (int64_t stride = 1; stride < Pt; stride *= members) {
         const int64_t groups = (Pt + stride * members - 1) / (stride * members);
         hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(members), lds,
@@ -865,7 +896,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       if (status != EP_OK) break;
     }
-    if (P <= 1) rec_at(5);
+    if (P <= 1 && !fused) rec_at(5);
     rec_at(6);
     mark();  // closure + tree launches
     if (sh) {
@@ -873,7 +904,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         status = EP_ERR_HIP;
         break;
       }
-    } else {
+    } else if (!fused) {
       FallbackArgs fa;
       fa.times = times; fa.types = types;
       fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;

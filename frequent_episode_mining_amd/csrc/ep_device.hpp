@@ -1907,6 +1907,195 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(FallbackArgs A) {
   }
 }
 
+// ------------------------------------------------ closure + tree + result
+
+// For P <= 512 segments one workgroup per episode does the closure, the
+// Concatenate tree and the result extraction in LDS, in one launch:
+//   1. thread p loads segment p's tuples;
+//   2. thread p checks the exits of segment p's Map tuples against the keys
+//      of segment p+1 and queues the misses;
+//   3. the waves repair the queued misses: each wave takes its share of the
+//      queue and follows each chain at once (a machine reset at the exit
+//      over the next segment, again while the new exit finds no key); lane 0
+//      reads and appends a segment's LDS list under that segment's LDS lock
+//      (one lock held at a time), so the waves of an episode repair in
+//      parallel;
+//   4. the tree joins the members level by level (Concatenate rules 1-3);
+//   5. member 0's first tuple (machine 0 of segment 0, i.e. alpha_0) holds
+//      the count.
+// An episode flagged by a Map kernel, a repair-list overflow or a tree miss
+// is recounted over the whole stream by wave 0, as in finish_kernel.
+constexpr int kReduceMembers = 512;
+constexpr int kReduceQueue = 256;
+
+struct ReduceArgs {
+  ClosureArgs c;
+  unsigned long long* fallbacks;
+  int64_t* out;
+  int64_t n;
+};
+
+template <int N, class Mach>
+__global__ __launch_bounds__(kReduceMembers) void reduce_kernel(ReduceArgs A) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const TupleStore& ts = A.c.ts;
+  const int slots = ts.slots;
+  const int members = blockDim.x;
+  int32_t* s_a = (int32_t*)smem;  // [members][slots]
+  int32_t* s_c = s_a + members * slots;
+  int32_t* s_b = s_c + members * slots;
+  int32_t* s_n = s_b + members * slots;  // [members] tuples held
+  int32_t* s_lock = s_n + members;        // [members] 1 while a wave edits segment p's list
+  __shared__ int32_t s_q[kReduceQueue];   // misses, as p * slots + k
+  __shared__ int32_t s_nq, s_bad;
+  const int64_t e = blockIdx.x;
+  const int i = threadIdx.x;
+  const int lane = i & (kWave - 1);
+  const int wave = i / kWave;
+  const int n_waves = members / kWave;
+  const int64_t P = A.c.P;
+  if (i == 0) {
+    s_nq = 0;
+    s_bad = A.c.flags[e] != 0 ? 1 : 0;
+  }
+  int n = 0, nm = 0;
+  if (i < P) {
+    const int64_t pe = ts.idx(e, i);
+    n = min(ts.nslots[pe], slots);
+    nm = min(ts.nmap[pe], n);
+    for (int k = 0; k < n; ++k) {
+      const Tuple tu = *ts.at(e, i, k);
+      s_a[i * slots + k] = tu.a;
+      s_c[i * slots + k] = tu.c;
+      s_b[i * slots + k] = tu.b;
+    }
+  }
+  s_n[i] = n;
+  s_lock[i] = 0;
+  __syncthreads();
+  // closure check: every distinct exit of segment i needs a key in segment i+1
+  if (i + 1 < P) {
+    const int nr = s_n[i + 1];
+    for (int k = 0; k < nm; ++k) {
+      const int32_t b = s_b[i * slots + k];
+      bool dup = false, hit = false;
+      for (int k2 = 0; k2 < k; ++k2) dup |= s_b[i * slots + k2] == b;
+      for (int m = 0; m < nr; ++m) hit |= s_a[(i + 1) * slots + m] == b;
+      if (!dup && !hit) {
+        const int q = atomicAdd(&s_nq, 1);
+        if (q < kReduceQueue)
+          s_q[q] = i * slots + k;
+        else
+          s_bad = 1;
+      }
+    }
+  }
+  __syncthreads();
+  const int nq = min(s_nq, kReduceQueue);
+  if (nq > 0 && s_bad == 0) {
+    typename Mach::Params prm;
+    prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
+    auto lock = [&](int64_t q) {
+      while (atomicCAS(&s_lock[q], 0, 1) != 0) {
+      }
+      __threadfence_block();
+    };
+    auto unlock = [&](int64_t q) {
+      __threadfence_block();
+      atomicExch(&s_lock[q], 0);
+    };
+    auto has_key = [&](int64_t q, int32_t key) {
+      bool hit = false;
+      for (int m = 0; m < s_n[q]; ++m) hit |= s_a[q * slots + m] == key;
+      return hit;
+    };
+    for (int j = wave; j < nq; j += n_waves) {
+      const int item = s_q[j];
+      int64_t q = item / slots + 1;
+      int32_t x_off = s_b[item];
+      for (;;) {
+        int go = 0;
+        if (lane == 0) {
+          if (x_off <= 0) {
+            s_bad = 1;  // a sentinel exit always has a sentinel key
+          } else {
+            lock(q);
+            go = has_key(q, x_off) ? 0 : 1;  // another chain may have repaired it
+            unlock(q);
+          }
+        }
+        go = __shfl(go, 0);
+        if (!go) break;
+        const Tuple tu = repair_tuple<Mach>(A.c, prm, q, A.c.tau[q] + x_off);
+        int next = 0;
+        if (lane == 0) {
+          lock(q);
+          bool added = false;
+          if (!has_key(q, tu.a)) {
+            const int h = s_n[q];
+            if (h >= slots) {
+              s_bad = 1;
+            } else {
+              s_a[q * slots + h] = tu.a;
+              s_c[q * slots + h] = tu.c;
+              s_b[q * slots + h] = tu.b;
+              s_n[q] = h + 1;
+              added = true;
+              atomicAdd(A.c.repairs, 1ull);
+            }
+          }
+          unlock(q);
+          if (added && q + 1 < P) {
+            lock(q + 1);
+            next = has_key(q + 1, tu.b) ? 0 : 1;
+            unlock(q + 1);
+          }
+        }
+        next = __shfl(next, 0);
+        if (!next) break;
+        x_off = tu.b;
+        ++q;
+      }
+    }
+  }
+  __syncthreads();
+  // the tree
+  for (int h = 1; h < members; h <<= 1) {
+    if ((i & (2 * h - 1)) == 0 && i + h < P) {
+      const int nl = s_n[i];
+      const int nr = s_n[i + h];
+      for (int k = 0; k < nl; ++k) {
+        const int32_t b = s_b[i * slots + k];
+        int hit = -1;
+        for (int m = 0; m < nr; ++m)
+          if (hit < 0 && s_a[(i + h) * slots + m] == b) hit = m;
+        if (hit >= 0) {
+          s_c[i * slots + k] += s_c[(i + h) * slots + hit];
+          s_b[i * slots + k] = s_b[(i + h) * slots + hit];
+        } else {
+          s_bad = 1;  // a chain the answer may pass through lost its way: recount
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (s_bad == 0) {
+    if (i == 0) A.out[e] = s_c[0];
+    return;
+  }
+  if (i >= kWave) return;
+  typename Mach::Params prm;
+  prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
+  const int64_t before = (int64_t)A.c.times[0] - 1;
+  SegMachine<Mach> sm;
+  sm.init(before, before, INT64_MAX / 4, prm.span);
+  wave_feed_range<Mach>(A.c.times, A.c.types, 0, A.n, sm, prm);
+  if (lane == 0) {
+    A.out[e] = sm.count;
+    atomicAdd(A.fallbacks, 1ull);
+  }
+}
+
 // ----------------------------------------------------------- launchers
 
 // Window kinds: run windows with K = 1, 2, 4 runs, or bit windows of 32 / 64 bits.
@@ -2055,6 +2244,8 @@ struct Launchers {
                          hipStream_t);
   hipError_t (*closure)(const ClosureArgs&, int win, dim3 grid, hipStream_t);
   hipError_t (*finish)(const FallbackArgs&, int win, dim3 grid, hipStream_t);
+  // closure + tree + result in one launch for P <= kReduceMembers
+  hipError_t (*reduce)(const ReduceArgs&, int win, dim3 grid, dim3 block, size_t lds, hipStream_t);
   // streaming: the carried reset's tuple in segment 0, and the chain's tail
   hipError_t (*stream_entry)(const StreamArgs&, int win, dim3 grid, hipStream_t);
   hipError_t (*stream_tail)(const StreamArgs&, int win, dim3 grid, hipStream_t);

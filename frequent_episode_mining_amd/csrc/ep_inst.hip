@@ -112,6 +112,23 @@ hipError_t launch_finish(const FallbackArgs& a, int win, dim3 grid, hipStream_t 
 }
 
 template <class Mach>
+hipError_t launch_reduce_m(const ReduceArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((reduce_kernel<EP_N, Mach>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int win, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  switch (win) {
+    case kRuns1: return launch_reduce_m<RunMachine<EP_N, 1>>(a, grid, block, lds, s);
+    case kRuns2: return launch_reduce_m<RunMachine<EP_N, 2>>(a, grid, block, lds, s);
+    case kRuns4: return launch_reduce_m<RunMachine<EP_N, 4>>(a, grid, block, lds, s);
+    case kBits32: return launch_reduce_m<BitMachine<EP_N, 32>>(a, grid, block, lds, s);
+    case kBits64: return launch_reduce_m<BitMachine<EP_N, 64>>(a, grid, block, lds, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class Mach>
 hipError_t launch_stream_m(const StreamArgs& a, bool tail, dim3 grid, hipStream_t s) {
   if (tail)
     hipLaunchKernelGGL((stream_tail_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
@@ -168,8 +185,8 @@ hipError_t occupancy_ticks(bool all_machines, int block, size_t lds, int* out) {
 
 const Launchers kLaunchers = {launch_scan,         launch_bits,        launch_ticks,
                               launch_list,         launch_closure,     launch_finish,
-                              launch_stream_entry, launch_stream_tail, occupancy,
-                              occupancy_ticks};
+                              launch_reduce,       launch_stream_entry, launch_stream_tail,
+                              occupancy,           occupancy_ticks};
 
 }  // namespace
 

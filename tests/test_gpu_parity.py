@@ -228,3 +228,35 @@ def test_ptpe_config_full_size(fem):
     _log("gpu plan %s" % st)
     _check(got, want, "ptpe full auto")
     assert want[0] >= 200  # the planted chains
+
+
+@pytest.mark.parametrize("name", ["tiny", "ptpe", "level2", "longchain"])
+def test_config_small_separate_closure_and_tree(fem, name, monkeypatch):
+    # the three-launch path (closure kernel, tree launches, finish kernel) that
+    # calls with more than 512 segments take, forced for every segment count
+    monkeypatch.setenv("EP_NO_REDUCE", "1")
+    wl = W.make_small(name)
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    for mode, P in [("auto", 0), ("mapconcat", 2), ("mapconcat", 64), ("mapconcat", 300)]:
+        got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, stats=True)
+        _check(got, want, "%s separate %s P=%d" % (name, mode, P))
+        assert st["fallbacks"] == 0
+
+
+def test_fuzz_separate_closure_and_tree(fem, monkeypatch):
+    monkeypatch.setenv("EP_NO_REDUCE", "1")
+    rng = np.random.default_rng(37)
+    for trial in range(30):
+        n = int(rng.integers(1, 400))
+        n_types = int(rng.integers(1, 6))
+        N = int(rng.integers(1, 6))
+        times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 4)))
+        ep, lo, hi = W.random_episodes(rng, int(rng.integers(1, 60)), N, n_types, max_hi=6)
+        ok = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1) if N > 1 else np.ones(ep.shape[0], bool)
+        ep, lo, hi = ep[ok], lo[ok], hi[ok]
+        if ep.shape[0] == 0:
+            continue
+        want = oracle.count(times, types, ep, lo, hi)
+        for mode, P in [("mapconcat", 3), ("mapconcat", 16), ("mapconcat", max(1, n))]:
+            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
+                   "separate fuzz %d n=%d %s P=%d" % (trial, n, mode, P))
