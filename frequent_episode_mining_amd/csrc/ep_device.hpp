@@ -1217,7 +1217,7 @@ void map_ticks_kernel(MapArgs A) {
   uint64_t* s_tb = (uint64_t*)smem;     // [R*CW words][U], word-major
 
   constexpr int NI = N > 1 ? N - 1 : 1;
-  constexpr int kPer = 8;               // events per thread per fill batch
+  constexpr int kPer = N >= 3 ? 4 : 8;  // events per thread per fill batch (fewer registers as N grows)
   constexpr int32_t kFar = 1 << 30;     // offsets are clamped to +-kFar
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
