@@ -84,7 +84,8 @@ DeviceInfo g_info[64];
 // a few calls ahead of the GPU.
 constexpr int kStagingSlots = 4;
 struct StagingSlot {
-  void* buf = nullptr;
+  void* buf = nullptr;   // coherent pinned host memory
+  void* dbuf = nullptr;  // the same memory as the device addresses it
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
@@ -314,10 +315,13 @@ int device_info(int dev, DeviceInfo** out) {
 }
 
 // Pinned staging in two steps: staging_acquire() locks the device's ring,
-// waits until its next slot's previous copy has finished and hands out the
-// slot; staging_commit() enqueues the copy to `dst`, records the slot's event
-// and unlocks.  Every acquire is followed by exactly one commit or abort.
-int staging_acquire(int dev, size_t bytes, char** out) {
+// waits until its next slot's previous reader has finished and hands out the
+// slot (host and device addresses); staging_release() records the slot's
+// event after the work that reads it (the set-up kernel copies it to the
+// device) and unlocks.  Every acquire is followed by exactly one release.
+// The slots are coherent host memory, so a kernel reads what the host wrote
+// even when a slot comes round again.
+int staging_acquire(int dev, size_t bytes, char** out, const void** dout) {
   Staging& st = g_staging[dev];
   st.mu.lock();
   StagingSlot& s = st.slot[st.next];
@@ -329,10 +333,16 @@ int staging_acquire(int dev, size_t bytes, char** out) {
   if (status == EP_OK && s.cap < bytes) {
     if (s.buf) hipHostFree(s.buf);
     s.buf = nullptr;
+    s.dbuf = nullptr;
     s.cap = 0;
     const size_t cap = std::max<size_t>(bytes, 1 << 16);
-    if (hipHostMalloc(&s.buf, cap, hipHostMallocDefault) != hipSuccess) {
+    if (hipHostMalloc(&s.buf, cap, hipHostMallocCoherent) != hipSuccess) {
       s.buf = nullptr;
+      status = EP_ERR_HIP;
+    } else if (hipHostGetDevicePointer(&s.dbuf, s.buf, 0) != hipSuccess || !s.dbuf) {
+      hipHostFree(s.buf);
+      s.buf = nullptr;
+      s.dbuf = nullptr;
       status = EP_ERR_HIP;
     } else {
       s.cap = cap;
@@ -345,18 +355,20 @@ int staging_acquire(int dev, size_t bytes, char** out) {
     return status;
   }
   *out = (char*)s.buf;
+  *dout = s.dbuf;
   return EP_OK;
 }
 
-int staging_commit(int dev, void* dst, size_t bytes, hipStream_t stream) {
+// `used`: work reading the slot was enqueued on `stream` (record its event).
+int staging_release(int dev, bool used, hipStream_t stream) {
   Staging& st = g_staging[dev];
   StagingSlot& s = st.slot[st.next];
   int status = EP_OK;
-  if (hipMemcpyAsync(dst, s.buf, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
-      hipEventRecord(s.ev, stream) != hipSuccess) {
-    status = EP_ERR_HIP;
-  } else {
-    s.pending = true;
+  if (used) {
+    if (hipEventRecord(s.ev, stream) != hipSuccess)
+      status = EP_ERR_HIP;
+    else
+      s.pending = true;
   }
   st.next = (st.next + 1) % kStagingSlots;
   st.mu.unlock();
@@ -676,10 +688,11 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     int32_t* d_lcnt = (int32_t*)(ws + off); off += sz_lidx;
 
     // episode table, spans, node slots and the node-type set, written
-    // straight into pinned staging: one upload
+    // straight into pinned staging; the set-up kernel copies it to the device
+    const void* tab_dev = nullptr;
     {
       char* host = nullptr;
-      if ((status = staging_acquire(dev, host_bytes, &host))) break;
+      if ((status = staging_acquire(dev, host_bytes, &host, &tab_dev))) break;
       memcpy(host, episodes.types, sizeof(uint16_t) * S * N);
       if (N > 1) {
         memcpy(host + sz_types, episodes.t_low, sizeof(int32_t) * S * (N - 1));
@@ -702,7 +715,6 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         memcpy(at, slot_eps, sz_seps);
         memcpy(at + sz_seps, slot_levels, sizeof(uint16_t) * 256 * S);
       }
-      if ((status = staging_commit(dev, ws, host_bytes, stream))) break;
     }
 
     if (opt && opt->validate) {
@@ -714,10 +726,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       if (hipMemcpyAsync(&bad, d_cnt, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
           hipStreamSynchronize(stream) != hipSuccess) {
         status = EP_ERR_HIP;
+        staging_release(dev, false, stream);
         break;
       }
       if (bad) {
         status = EP_ERR_UNSORTED;
+        staging_release(dev, false, stream);
         break;
       }
     }
@@ -733,7 +747,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         prof = (g_prof_calls++ % g_prof_every) == 0;
       }
     }
-    if (prof && (status = prof_record_start(&rec, prof_which, stream))) break;
+    if (prof && (status = prof_record_start(&rec, prof_which, stream))) {
+      staging_release(dev, false, stream);
+      break;
+    }
     // records boundary i when the session times it (every boundary, or the
     // two around the one Map kernel it times)
     auto rec_at = [&](int i) {
@@ -745,8 +762,14 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     sa.tau = d_tau; sa.beg = d_beg; sa.end = d_end;
     sa.flags = d_flags; sa.S = S; sa.counters = d_cnt;
     sa.wave_search = P <= kWaveSearchMaxP ? 1 : 0;
+    sa.tab_src = (const uint4*)tab_dev;
+    sa.tab_dst = (uint4*)ws;
+    sa.tab_words = (int64_t)(host_bytes / sizeof(uint4));
     hipLaunchKernelGGL(setup_kernel, dim3(grid_for(setup_items(sa))), dim3(kBlock), 0, stream, sa);
-    if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
+    const bool launched = hipGetLastError() == hipSuccess;
+    if (int st = staging_release(dev, launched, stream)) status = st;
+    if (!launched) status = EP_ERR_HIP;
+    if (status != EP_OK) break;
 
     mark();  // setup launch
     MapArgs ma;

@@ -40,6 +40,9 @@ struct SetupArgs {
   int64_t S;
   unsigned long long* counters;  // [4]
   int32_t wave_search;  // range ends by one wave each (small P) or one thread each
+  const uint4* tab_src;  // the episode table in pinned host memory (device-visible)
+  uint4* tab_dst;        // its device copy
+  int64_t tab_words;     // 16-byte words
 };
 
 __device__ inline int64_t cut_of(int64_t t_min, int64_t t_max, int64_t p, int64_t P) {
@@ -121,7 +124,14 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
     return;
   }
   i -= A.S + 1;
-  if (i < 4) A.counters[i] = 0ull;
+  if (i < 4) {
+    A.counters[i] = 0ull;
+    return;
+  }
+  i -= 4;
+  // the episode table: read from pinned host memory over the bus, so no copy
+  // engine sits between the host and this launch
+  if (i < A.tab_words) A.tab_dst[i] = A.tab_src[i];
 }
 
 // ------------------------------------------------------------- event filter
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(kConcatMembers) void concat_tree_kernel(TupleStore 
 }
 
 inline int64_t setup_items(const SetupArgs& A) {
-  return setup_search_threads(A.P, A.wave_search != 0) + (int64_t)A.P + 1 + A.S + 1 + 4;
+  return setup_search_threads(A.P, A.wave_search != 0) + (int64_t)A.P + 1 + A.S + 1 + 4 + A.tab_words;
 }
 
 __global__ __launch_bounds__(kBlock) void fill_i64_kernel(int64_t* p, int64_t n, int64_t v) {
