@@ -816,16 +816,26 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       fa.S = (int32_t)S; fa.max_share = max_share;
       fa.lists = d_lists; fa.list_off = d_loff; fa.list_cnt = d_lcnt;
       // persistent workgroups: a few per CU, each looping over blocks
-      const int64_t fgrid = std::min<int64_t>(n_lblocks, (int64_t)info->cu_count * 4);
+      // (as many as fit a CU: the LDS per workgroup grows with S)
+      const int64_t fgrid =
+          std::min<int64_t>(n_lblocks, (int64_t)info->cu_count * (S <= 8 ? 4 : (S <= 16 ? 3 : 2)));
       const dim3 fg((unsigned)fgrid), fb(kBlock);
-      if (S <= 4)
-        hipLaunchKernelGGL(filter_kernel<1>, fg, fb, 0, stream, fa);
-      else if (S <= 8)
-        hipLaunchKernelGGL(filter_kernel<2>, fg, fb, 0, stream, fa);
-      else if (S <= 16)
-        hipLaunchKernelGGL(filter_kernel<4>, fg, fb, 0, stream, fa);
-      else
-        hipLaunchKernelGGL(filter_kernel<8>, fg, fb, 0, stream, fa);
+      // node types small enough for a direct type -> slot table in LDS
+      int32_t type_cap = 0;
+      for (int64_t i = 0; i < S * N; ++i) type_cap = std::max<int32_t>(type_cap, (int32_t)episodes.types[i] + 1);
+      fa.type_cap = type_cap;
+      const bool direct = type_cap <= kFilterTab;
+      const int fgw = S <= 4 ? 1 : (S <= 8 ? 2 : (S <= 16 ? 4 : 8));
+      switch (fgw * 2 + (direct ? 1 : 0)) {
+        case 3: hipLaunchKernelGGL((filter_kernel<1, true>), fg, fb, 0, stream, fa); break;
+        case 2: hipLaunchKernelGGL((filter_kernel<1, false>), fg, fb, 0, stream, fa); break;
+        case 5: hipLaunchKernelGGL((filter_kernel<2, true>), fg, fb, 0, stream, fa); break;
+        case 4: hipLaunchKernelGGL((filter_kernel<2, false>), fg, fb, 0, stream, fa); break;
+        case 9: hipLaunchKernelGGL((filter_kernel<4, true>), fg, fb, 0, stream, fa); break;
+        case 8: hipLaunchKernelGGL((filter_kernel<4, false>), fg, fb, 0, stream, fa); break;
+        case 17: hipLaunchKernelGGL((filter_kernel<8, true>), fg, fb, 0, stream, fa); break;
+        default: hipLaunchKernelGGL((filter_kernel<8, false>), fg, fb, 0, stream, fa); break;
+      }
       le = hipGetLastError();
     }
     rec_at(2);

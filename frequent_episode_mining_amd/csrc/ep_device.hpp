@@ -386,6 +386,19 @@ struct MapArgs {
                        // groups when its segments fit one chunk each
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active): the
+// shifts 1, 2, 4 and 8 within each row of 16 lanes, then the last lane of
+// rows 0 and 2 added to rows 1 and 3, then lane 31 to rows 2 and 3.
+__device__ inline uint32_t wave_incl_scan(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Node-type slot of event type y: 1 + the rank of y among the call's node
 // types, 0 for a type on no node.  seen/rank are the MapArgs tables, copied to
 // LDS by each workgroup (two independent LDS reads per event).
@@ -720,6 +733,35 @@ struct ClassLane {
     return true;
   }
 
+  // step_one for the lanes where `use` holds, as predicated arithmetic (the
+  // others keep their state): no branch but for the rare completion.
+  // Returns false once the lane has finished.
+  __device__ bool step_one_if(bool use, int32_t t, uint32_t lm) {
+    const bool over = use && (int64_t)t > stop;
+    const bool on = use && !over;
+    const uint32_t d = on ? (uint32_t)t - (uint32_t)B : 0u;
+    B = on ? t : B;
+    const uint32_t live = (on && (int64_t)t > r[0]) ? 1u : 0u;
+    uint32_t hit[NI];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      m[0][j] = age<W>(m[0][j], d);
+      hit[j] = (m[0][j] & win[j]) != 0 ? 1u : 0u;
+    }
+    uint32_t complete = live & (lm >> (N - 1)) & 1u;
+    if constexpr (N > 1) complete &= hit[N - 2];
+    if (complete) {
+      complete_class(1u, t);
+      if ((mem[0] & ~fin) == 0u) mem[0] = 0u;
+      return fin != kAll;
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j)
+      m[0][j] |= (Bits)(live & (lm >> j) & (j == 0 ? 1u : hit[j > 0 ? j - 1 : 0]));
+    fin = over ? kAll : fin;
+    return !over;
+  }
+
   __device__ bool step(int32_t t, uint32_t lm) { return single ? step_one(t, lm) : step_many(t, lm); }
 
   // The tuples of the (segment, episode): one per machine lane (MCH = 1), or
@@ -1026,7 +1068,7 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
           const int4 w = cur[k >> 1];
           const int32_t t = (k & 1) ? w.z : w.x;
           const uint32_t lm = (uint32_t)((k & 1) ? w.w : w.y);
-          if (go && idx >= first && idx < n_end && (int64_t)t > lo_t) go = lane.step_one(t, lm);
+          go = lane.step_one_if(go && idx >= first && idx < n_end && (int64_t)t > lo_t, t, lm) && go;
         }
 #pragma unroll
         for (int q = 0; q < kD / 2; ++q) cur[q] = nxt[q];

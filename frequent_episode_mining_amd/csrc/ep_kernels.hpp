@@ -144,8 +144,11 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
 // kListBlock * max_share entries (max_share: most episodes one type is on), so
 // blocks need nothing from each other.  A thread takes 16 consecutive events;
 // its per-episode counts are packed two to a 32-bit word (16-bit fields; a
-// block holds at most 4096), so one scan serves two episodes.
+// block holds at most 4096), so one scan serves two episodes.  Where every
+// node type is below kFilterTab, a byte table maps types to slots directly;
+// otherwise the 65,536-bit set of node types and per-word ranks do.
 constexpr int kFilterPer = kListBlock / kBlock;  // 16
+constexpr int kFilterTab = 9216;                  // LDS bytes of the type table
 constexpr int kMaxListEpisodes = 32;
 constexpr double kMaxListBytes = 32.0 * (1ull << 30);  // list scratch bound of the list path
 
@@ -159,6 +162,7 @@ struct FilterArgs {
   const uint16_t* slot_levels;   // [256 * S] node levels of episode e with slot u's type
   int32_t S;                     // <= kMaxListEpisodes
   int32_t max_share;
+  int32_t type_cap;              // node types are below this (direct table when <= kFilterTab)
   int2* lists;
   int32_t* list_off;             // [blocks * S]
   int32_t* list_cnt;             // [blocks * S]
@@ -167,12 +171,16 @@ struct FilterArgs {
 // One workgroup loops over blocks b = blockIdx.x, + gridDim.x, ...: the LDS
 // tables are loaded once, and the next block's events are loaded before the
 // current block is classified and written.  G packed count words serve up to
-// 4 G episodes.
-template <int G>
+// 4 G episodes.  A thread keeps its events in LDS ([k][thread]) so that the
+// write loop visits only its events of node types, in order.
+template <int G, bool DIRECT>
 __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
   constexpr int kE = 4 * G;  // episodes this instance serves at most
-  __shared__ uint64_t s_seen[1024];
-  __shared__ uint8_t s_rank[1024];
+  __shared__ __align__(8) uint8_t s_tab[kFilterTab];  // type -> slot, or the set + ranks
+  uint64_t* s_seen = (uint64_t*)s_tab;
+  uint8_t* s_rank = s_tab + 8192;
+  __shared__ int32_t s_st[kFilterPer][kBlock];       // thread's event k: time
+  __shared__ uint32_t s_ss[kFilterPer / 4][kBlock];  // and slot (a byte of word k / 4)
   __shared__ uint32_t s_eps[256];
   __shared__ uint16_t s_lv[256 * kE];
   __shared__ uint16_t s_pre[kE][kBlock];  // thread's next rank per episode
@@ -182,9 +190,14 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int S = A.S;
-  for (int i = tid; i < 1024; i += kBlock) {
-    s_seen[i] = A.type_seen[i];
-    s_rank[i] = A.type_rank[i];
+  if (DIRECT) {
+    for (int i = tid; i < A.type_cap; i += kBlock)
+      s_tab[i] = (uint8_t)type_slot(A.type_seen, A.type_rank, (uint32_t)i);
+  } else {
+    for (int i = tid; i < 1024; i += kBlock) {
+      s_seen[i] = A.type_seen[i];
+      s_rank[i] = A.type_rank[i];
+    }
   }
   for (int i = tid; i < 256; i += kBlock) s_eps[i] = A.slot_eps[i];
   for (int i = tid; i < 256 * S; i += kBlock) s_lv[(i / S) * kE + i % S] = A.slot_levels[i];
@@ -241,23 +254,34 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
     // events of this thread that exist (the last block may be partial)
     const int64_t left = A.n - first;
     const int n_valid = left >= kFilterPer ? kFilterPer : (left > 0 ? (int)left : 0);
-    uint32_t sl[kFilterPer], ep[kFilterPer];
     // per-thread counts in 8-bit fields, four episodes to a word (at most 16
     // each): x * 0x204081 puts bit i of a 4-bit x at bit 8i with no carries
     uint32_t c8[G];
+    uint32_t rel = 0;  // bit k: event k has a node type
 #pragma unroll
     for (int g = 0; g < G; ++g) c8[g] = 0;
 #pragma unroll
     for (int k = 0; k < kFilterPer; ++k) {
       const uint32_t yk = y[k];
-      const uint64_t w = s_seen[yk >> 6];
-      const uint32_t sh = yk & 63u;
-      const bool on = k < n_valid && ((w >> sh) & 1ull);
-      const uint32_t below = (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
-      sl[k] = on ? (uint32_t)s_rank[yk >> 6] + below + 1u : 0u;
-      ep[k] = s_eps[sl[k]];
+      uint32_t u;
+      if (DIRECT) {
+        u = (k < n_valid && yk < (uint32_t)A.type_cap) ? (uint32_t)s_tab[yk] : 0u;
+      } else {
+        const uint64_t w = s_seen[yk >> 6];
+        const uint32_t sh = yk & 63u;
+        const bool on = k < n_valid && ((w >> sh) & 1ull);
+        const uint32_t below = (uint32_t)__popcll(w & ((1ull << sh) - 1ull));
+        u = on ? (uint32_t)s_rank[yk >> 6] + below + 1u : 0u;
+      }
+      const uint32_t ep = s_eps[u];
+      rel |= (u != 0u ? 1u : 0u) << k;
 #pragma unroll
-      for (int g = 0; g < G; ++g) c8[g] += __umul24((ep[k] >> (4 * g)) & 15u, 0x204081u) & 0x01010101u;
+      for (int g = 0; g < G; ++g) c8[g] += __umul24((ep >> (4 * g)) & 15u, 0x204081u) & 0x01010101u;
+      s_st[k][tid] = t[k];
+      if ((k & 3) == 0)
+        s_ss[k / 4][tid] = u;
+      else
+        s_ss[k / 4][tid] |= u << (8 * (k & 3));
     }
     // widen to two 16-bit fields per word: word 2g + h holds episodes 4g + 2h
     // and 4g + 2h + 1
@@ -271,14 +295,8 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
     uint32_t incl[2 * G];
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) {
-      uint32_t v = c[g];
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-      }
-      incl[g] = v;
-      if (lane == kWave - 1) s_wsum[wave][g] = v;
+      incl[g] = wave_incl_scan(c[g]);
+      if (lane == kWave - 1) s_wsum[wave][g] = incl[g];
     }
     __syncthreads();
 #pragma unroll
@@ -312,18 +330,22 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
     }
     __syncthreads();
     int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
-#pragma unroll
-    for (int k = 0; k < kFilterPer; ++k) {
-      uint32_t m = ep[k];
+    // this thread's events of node types, in order, from its LDS copy
+    while (rel) {
+      const int k = __ffs((int)rel) - 1;
+      rel &= rel - 1;
+      const int32_t tk = s_st[k][tid];
+      const uint32_t u = (s_ss[k >> 2][tid] >> (8 * (k & 3))) & 0xffu;
+      uint32_t m = s_eps[u];
       while (m) {
         const int e = __ffs((int)m) - 1;
         m &= m - 1;
         const uint16_t r = s_pre[e][tid];
         s_pre[e][tid] = (uint16_t)(r + 1);
-        region[s_off[e] + r] = make_int2(t[k], (int32_t)s_lv[sl[k] * kE + e]);
+        region[s_off[e] + r] = make_int2(tk, (int32_t)s_lv[u * kE + e]);
       }
     }
-    __syncthreads();  // s_wsum, s_pre and s_off are rewritten by the next block
+    __syncthreads();  // s_wsum, s_pre, s_off, s_st and s_ss are rewritten by the next block
   }
 }
 
