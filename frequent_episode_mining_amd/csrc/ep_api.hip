@@ -221,6 +221,7 @@ int prof_record_start(ProfRecord* r, int which, hipStream_t s) {
 // Lanes per (segment, episode) of the counting kernels: one lane carries all N
 // machines up to N = 8, one machine per lane beyond.
 constexpr int kMaxClassNodes = 8;
+constexpr int64_t kStreamSegEvents = 4096;  // a stream batch's segments hold about this many events at most
 
 // The hybrid rule (hybrid-algorithm section): the GPU is fully utilised by
 // PTPE when the episodes alone give every resident lane of every CU work.
@@ -562,7 +563,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   plan_rule(S, N, n_events, sh ? EP_MODE_MAPCONCAT : mode, opt ? opt->n_segments : 0,
             info->cu_count, lanes_per_cu_est, &pmode, &P);
   if (sh) {
-    // a batch of a stream: segments longer than maxSpan ticks (see the tail)
+    // a batch of a stream: the entry and tail kernels scan segment 0 and the
+    // last segment with one wave per episode, so segments of at most about
+    // kStreamSegEvents events unless the caller fixed P; and segments longer
+    // than maxSpan ticks (see the tail)
+    if (!(opt && opt->n_segments > 0))
+      P = (int32_t)std::max<int64_t>(P, std::min<int64_t>((n_events + kStreamSegEvents - 1) / kStreamSegEvents,
+                                                         INT32_MAX));
     const int64_t cap = std::max<int64_t>(1, (sh->t_end - sh->t_first + 1) / (max_span + 1));
     P = (int32_t)std::min<int64_t>(P, cap);
   }
@@ -1152,18 +1159,21 @@ struct ep_stream {
   int64_t* total = nullptr;         // device [S] running counts
   int64_t* reset[2] = {nullptr, nullptr};  // device [S] carried reset times (ping-pong)
   int cur = 0;                      // reset[cur] holds the times to carry into the next push
-  int64_t* scalar = nullptr;        // device scratch word
-  int32_t* halo_t = nullptr;        // device halo: events within maxSpan of t_last
-  uint16_t* halo_y = nullptr;
-  int64_t halo_n = 0, halo_cap = 0;
-  int32_t* comb_t = nullptr;        // device: halo followed by the batch
-  uint16_t* comb_y = nullptr;
-  int64_t comb_cap = 0;
+  int64_t* scalar = nullptr;        // device [2]: the pending halo's first index in the last
+                                    // combined buffer and its size
+  int64_t* info = nullptr;          // host-mapped [4]: what stream_info_kernel reports
+  int64_t* info_dev = nullptr;      // its device address
+  int32_t* comb_t[2] = {nullptr, nullptr};  // device: halo followed by the batch (ping-pong)
+  uint16_t* comb_y[2] = {nullptr, nullptr};
+  int64_t comb_cap[2] = {0, 0};
+  int cb = 0;                       // comb[cb] holds the pending halo at its head
 };
 
 namespace {
 
-int grow(int32_t** t, uint16_t** y, int64_t* cap, int64_t need) {
+// Room for `need` events in a combined buffer; its first `keep` events are
+// kept (copied on the stream before the old buffer is freed).
+int grow(int32_t** t, uint16_t** y, int64_t* cap, int64_t need, int64_t keep, hipStream_t stream) {
   if (need <= *cap) return EP_OK;
   const int64_t c = std::max<int64_t>(need + need / 4, 1 << 16);
   int32_t* nt = nullptr;
@@ -1172,6 +1182,13 @@ int grow(int32_t** t, uint16_t** y, int64_t* cap, int64_t need) {
   if (hipMalloc((void**)&ny, (size_t)c * sizeof(uint16_t)) != hipSuccess) {
     (void)hipFree(nt);
     return EP_ERR_WORKSPACE;
+  }
+  if (keep > 0 &&
+      (hipMemcpyAsync(nt, *t, (size_t)keep * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+       hipMemcpyAsync(ny, *y, (size_t)keep * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)) {
+    (void)hipFree(nt);
+    (void)hipFree(ny);
+    return EP_ERR_HIP;
   }
   // the old buffers may still be read by queued work: wait for the device first
   if (*t && (hipDeviceSynchronize() != hipSuccess || hipFree(*t) != hipSuccess || hipFree(*y) != hipSuccess)) {
@@ -1237,10 +1254,14 @@ extern "C" int ep_stream_create(ep_episodes episodes, int64_t n_episodes, const 
     const size_t b = (size_t)std::max<int64_t>(S, 1) * sizeof(int64_t);
     if (hipMalloc((void**)&st->total, b) != hipSuccess || hipMalloc((void**)&st->reset[0], b) != hipSuccess ||
         hipMalloc((void**)&st->reset[1], b) != hipSuccess ||
-        hipMalloc((void**)&st->scalar, sizeof(int64_t)) != hipSuccess) {
+        hipMalloc((void**)&st->scalar, 2 * sizeof(int64_t)) != hipSuccess ||
+        hipHostMalloc((void**)&st->info, 4 * sizeof(int64_t), hipHostMallocMapped | hipHostMallocCoherent) !=
+            hipSuccess) {
       status = EP_ERR_WORKSPACE;
       break;
     }
+    if (hipHostGetDevicePointer((void**)&st->info_dev, st->info, 0) != hipSuccess) { status = EP_ERR_HIP; break; }
+    hipLaunchKernelGGL(fill_i64_kernel, dim3(1), dim3(kBlock), 0, stream, st->scalar, (int64_t)2, (int64_t)0);
     if (S > 0) {
       hipLaunchKernelGGL(fill_i64_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, st->total, S, (int64_t)0);
       hipLaunchKernelGGL(fill_i64_kernel, dim3(grid_for(S)), dim3(kBlock), 0, stream, st->reset[0], S, kNoReset);
@@ -1267,48 +1288,44 @@ extern "C" int ep_stream_push(ep_stream* st, const int32_t* times, const uint16_
   int dev = 0;
   EP_HIP(hipGetDevice(&dev));
   if (dev != st->dev) return EP_ERR_ARG;
-  // the batch's first and last times
-  int32_t ends[2] = {0, 0};
-  EP_HIP(hipMemcpyAsync(&ends[0], times, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
-  EP_HIP(hipMemcpyAsync(&ends[1], times + n_events - 1, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
+  // the batch's first and last times and the pending halo (one synchronisation)
+  const int cb = st->cb;
+  hipLaunchKernelGGL(stream_info_kernel, dim3(1), dim3(kWave), 0, stream, times, n_events, st->scalar + 1,
+                     st->comb_t[cb], st->info_dev);
+  EP_HIP(hipGetLastError());
   EP_HIP(hipStreamSynchronize(stream));
-  if (st->t_last != INT64_MIN && (int64_t)ends[0] < st->t_last) return EP_ERR_UNSORTED;
-  const int64_t n = st->halo_n + n_events;
+  const int64_t t_first = st->info[0], t_end = st->info[1], halo_n = st->info[2], halo_first = st->info[3];
+  if (st->t_last != INT64_MIN && t_first < st->t_last) return EP_ERR_UNSORTED;
+  const int64_t n = halo_n + n_events;
   if (n > INT32_MAX) return EP_ERR_ARG;
-  if (int s = grow(&st->comb_t, &st->comb_y, &st->comb_cap, n)) return s;
-  int32_t halo_first = 0;
-  if (st->halo_n > 0) {
-    EP_HIP(hipMemcpyAsync(st->comb_t, st->halo_t, (size_t)st->halo_n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
-    EP_HIP(hipMemcpyAsync(st->comb_y, st->halo_y, (size_t)st->halo_n * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
-    EP_HIP(hipMemcpyAsync(&halo_first, st->halo_t, sizeof(int32_t), hipMemcpyDeviceToHost, stream));
-  }
-  EP_HIP(hipMemcpyAsync(st->comb_t + st->halo_n, times, (size_t)n_events * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
-  EP_HIP(hipMemcpyAsync(st->comb_y + st->halo_n, types, (size_t)n_events * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
+  if (int s = grow(&st->comb_t[cb], &st->comb_y[cb], &st->comb_cap[cb], n, halo_n, stream)) return s;
+  EP_HIP(hipMemcpyAsync(st->comb_t[cb] + halo_n, times, (size_t)n_events * sizeof(int32_t),
+                        hipMemcpyDeviceToDevice, stream));
+  EP_HIP(hipMemcpyAsync(st->comb_y[cb] + halo_n, types, (size_t)n_events * sizeof(uint16_t),
+                        hipMemcpyDeviceToDevice, stream));
   StreamHook hook;
   hook.entry = st->reset[st->cur];
   hook.total = st->total;
   hook.reset_out = st->reset[1 - st->cur];
-  if (st->halo_n > 0) EP_HIP(hipStreamSynchronize(stream));
-  hook.t_first = st->halo_n > 0 ? (int64_t)halo_first : (int64_t)ends[0];
-  hook.t_end = ends[1];
+  hook.t_first = halo_n > 0 ? halo_first : t_first;
+  hook.t_end = t_end;
   ep_episodes eps{st->N, st->types.data(), st->N > 1 ? st->lo.data() : nullptr,
                   st->N > 1 ? st->hi.data() : nullptr};
-  if (int s = count_episodes_impl(st->comb_t, st->comb_y, n, eps, st->S, st->total, stream, &st->opt, &hook))
+  if (int s = count_episodes_impl(st->comb_t[cb], st->comb_y[cb], n, eps, st->S, st->total, stream, &st->opt,
+                                  &hook))
     return s;
   st->cur = 1 - st->cur;
-  // the new halo: events within maxSpan of the last one
-  hipLaunchKernelGGL(lower_bound_kernel, dim3(1), dim3(64), 0, stream, st->comb_t, n, hook.t_end - st->max_span,
-                     st->scalar);
+  // the next halo (events within maxSpan of the last one) to the head of the
+  // other combined buffer; its size stays on the device until the next push
+  const int nb = 1 - cb;
+  if (int s = grow(&st->comb_t[nb], &st->comb_y[nb], &st->comb_cap[nb], n, 0, stream)) return s;
+  hipLaunchKernelGGL(halo_find_kernel, dim3(1), dim3(kWave), 0, stream, st->comb_t[cb], n, t_end - st->max_span,
+                     st->scalar, st->scalar + 1);
+  hipLaunchKernelGGL(halo_move_kernel, dim3((unsigned)std::min<int64_t>(grid_for(n), 256)), dim3(kBlock), 0, stream,
+                     st->comb_t[cb], st->comb_y[cb], st->scalar, st->scalar + 1, st->comb_t[nb], st->comb_y[nb]);
   EP_HIP(hipGetLastError());
-  int64_t h0 = 0;
-  EP_HIP(hipMemcpyAsync(&h0, st->scalar, sizeof(int64_t), hipMemcpyDeviceToHost, stream));
-  EP_HIP(hipStreamSynchronize(stream));
-  const int64_t hn = n - h0;
-  if (int s = grow(&st->halo_t, &st->halo_y, &st->halo_cap, hn)) return s;
-  EP_HIP(hipMemcpyAsync(st->halo_t, st->comb_t + h0, (size_t)hn * sizeof(int32_t), hipMemcpyDeviceToDevice, stream));
-  EP_HIP(hipMemcpyAsync(st->halo_y, st->comb_y + h0, (size_t)hn * sizeof(uint16_t), hipMemcpyDeviceToDevice, stream));
-  st->halo_n = hn;
-  st->t_last = hook.t_end;
+  st->cb = nb;
+  st->t_last = t_end;
   st->events += n_events;
   return EP_OK;
 }
@@ -1324,10 +1341,11 @@ extern "C" int64_t ep_stream_events(const ep_stream* st) { return st ? st->event
 
 extern "C" void ep_stream_destroy(ep_stream* st) {
   if (!st) return;
-  if (st->total || st->comb_t || st->halo_t) (void)hipDeviceSynchronize();
+  if (st->total || st->comb_t[0] || st->comb_t[1]) (void)hipDeviceSynchronize();
   for (void* p : {(void*)st->total, (void*)st->reset[0], (void*)st->reset[1], (void*)st->scalar,
-                  (void*)st->halo_t, (void*)st->halo_y, (void*)st->comb_t, (void*)st->comb_y})
+                  (void*)st->comb_t[0], (void*)st->comb_y[0], (void*)st->comb_t[1], (void*)st->comb_y[1]})
     if (p) (void)hipFree(p);
+  if (st->info) (void)hipHostFree(st->info);
   delete st;
 }
 

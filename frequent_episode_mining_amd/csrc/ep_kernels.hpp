@@ -478,8 +478,23 @@ __global__ __launch_bounds__(kMergeBlock) void two_pass_merge_kernel(const int64
   }
 }
 
-// First index with times[i] >= bound (one thread: a binary search).
-__global__ void lower_bound_kernel(const int32_t* times, int64_t n, int64_t bound, int64_t* out) {
+// Streaming: the scalars a push needs on the host, in one launch, written to
+// host-mapped memory: the batch's first and last times, the size of the halo
+// waiting at the head of the combined buffer, and the halo's first time.
+__global__ void stream_info_kernel(const int32_t* batch, int64_t n, const int64_t* halo_n,
+                                   const int32_t* halo, int64_t* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int64_t hn = *halo_n;
+  out[0] = batch[0];
+  out[1] = batch[n - 1];
+  out[2] = hn;
+  out[3] = hn > 0 ? (int64_t)halo[0] : 0;
+}
+
+// Streaming: the next halo, the events of [0, n) at or after time `bound`
+// (times sorted): its first index and its size.
+__global__ void halo_find_kernel(const int32_t* times, int64_t n, int64_t bound, int64_t* first,
+                                 int64_t* size) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
   int64_t lo = 0, hi = n;
   while (lo < hi) {
@@ -489,7 +504,20 @@ __global__ void lower_bound_kernel(const int32_t* times, int64_t n, int64_t boun
     else
       hi = mid;
   }
-  *out = lo;
+  *first = lo;
+  *size = n - lo;
+}
+
+// Streaming: the halo halo_find_kernel found, copied to the head of the other
+// combined buffer (a grid-stride loop: the halo is usually short).
+__global__ __launch_bounds__(kBlock) void halo_move_kernel(const int32_t* st, const uint16_t* sy,
+                                                           const int64_t* first, const int64_t* size,
+                                                           int32_t* dt, uint16_t* dy) {
+  const int64_t h0 = *first, hn = *size;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < hn; i += (int64_t)gridDim.x * kBlock) {
+    dt[i] = st[h0 + i];
+    dy[i] = sy[h0 + i];
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void check_sorted_kernel(const int32_t* times, int64_t n,
