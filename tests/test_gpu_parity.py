@@ -112,6 +112,34 @@ def test_fuzz_small_streams(fem, split, monkeypatch):
     assert checked > 200
 
 
+@pytest.mark.parametrize("split", ["auto", "positions"])
+def test_fuzz_large_type_values(fem, split, monkeypatch):
+    # node types spread over the whole uint16 range (the filter then maps
+    # types to slots through the 65,536-bit type set instead of a byte table),
+    # next to small ones (the byte table)
+    _split_env(monkeypatch, split)
+    rng = np.random.default_rng(43)
+    for trial in range(24):
+        n = int(rng.integers(1, 5000))
+        n_types = int(rng.integers(2, 9))
+        times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 6)))
+        if trial % 2 == 0:
+            alphabet = rng.choice(np.arange(9000, 65536), size=n_types, replace=False)
+        else:
+            alphabet = rng.choice(np.arange(0, 600), size=n_types, replace=False)
+        types = alphabet[types].astype(np.uint16)
+        S = int(rng.integers(1, 33))
+        N = int(rng.integers(2, 6))
+        ep = alphabet[rng.integers(0, n_types, size=(S, N))].astype(np.uint16)
+        hi = rng.integers(1, 30, size=(S, N - 1)).astype(np.int32)
+        lo = (rng.random(size=hi.shape) * hi).astype(np.int32)
+        lo = np.minimum(lo, hi - 1)
+        want = oracle.count(times, types, ep, lo, hi)
+        for mode, P in [("auto", 0), ("mapconcat", 3), ("mapconcat", 64)]:
+            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
+                   "large types trial %d n=%d S=%d %s P=%d" % (trial, n, S, mode, P))
+
+
 def test_empty_stream_and_no_episodes(fem):
     e = np.zeros(0, np.int32)
     got = _gpu(fem, e, e.astype(np.uint16), np.array([[1, 2]], np.uint16), np.array([[0]], np.int32),
