@@ -221,7 +221,8 @@ int prof_record_start(ProfRecord* r, int which, hipStream_t s) {
 // Lanes per (segment, episode) of the counting kernels: one lane carries all N
 // machines up to N = 8, one machine per lane beyond.
 constexpr int kMaxClassNodes = 8;
-constexpr int64_t kStreamSegEvents = 4096;  // a stream batch's segments hold about this many events at most
+constexpr int64_t kStreamSegEvents = 4096;
+constexpr int64_t kListMinEvents = 1 << 20;  // the list path pays off from streams of about this size  // a stream batch's segments hold about this many events at most
 
 // The hybrid rule (hybrid-algorithm section): the GPU is fully utilised by
 // PTPE when the episodes alone give every resident lane of every CU work.
@@ -588,8 +589,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
     // few episodes: sparse segments read the filter kernel's per-episode lists
     // (one lane per (segment, episode) walks only its episode's events)
+    // (on short streams the position kernel, which stages events in LDS, is
+    // faster than a filter pass plus lanes reading lists)
     L.list = S <= kMaxListEpisodes && L.split != 1 && list_bytes <= kMaxListBytes &&
-             !getenv("EP_NO_LIST");
+             (n_events >= kListMinEvents || getenv("EP_FORCE_LIST")) && !getenv("EP_NO_LIST");
     L.all_mach = L.n_machines > 1 && N <= kMaxClassNodes && (L.list || S * (int64_t)P * 4 >= target);
     const char* lanes_env = getenv("EP_LANES");
     if (lanes_env && N <= kMaxClassNodes && L.n_machines > 1)

@@ -55,13 +55,16 @@ MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 1), ("mapconcat", 2), ("mapconc
 
 def _split_env(monkeypatch, split):
     """Route segments: 'ticks' / 'positions' force one kernel for every segment
-    ('positions' means the list kernel where the call qualifies for it);
+    ('positions' means the list kernel where the call qualifies for it, also
+    on streams shorter than the planner's list-path minimum);
     'position-kernel' forces the position kernel itself."""
     if split == "position-kernel":
         monkeypatch.setenv("EP_SPLIT", "positions")
         monkeypatch.setenv("EP_NO_LIST", "1")
     elif split != "auto":
         monkeypatch.setenv("EP_SPLIT", split)
+        if split == "positions":
+            monkeypatch.setenv("EP_FORCE_LIST", "1")
 
 
 SPLITS = ["auto", "ticks", "positions", "position-kernel"]
@@ -206,6 +209,7 @@ def test_config_small_other_kernels(fem, name, layout, monkeypatch):
         monkeypatch.setenv("EP_SPLIT", "ticks")
     if layout.startswith("positions"):
         monkeypatch.setenv("EP_SPLIT", "positions")
+        monkeypatch.setenv("EP_FORCE_LIST", "1")
     if layout.startswith("position-kernel"):
         monkeypatch.setenv("EP_SPLIT", "positions")
         monkeypatch.setenv("EP_NO_LIST", "1")

@@ -68,8 +68,13 @@ def test_stream_golden_every_split(fem, case):
         _run(fem, times, types, ep, lo, hi, [c], "%s cut %d" % (case["name"], c))
 
 
-@pytest.mark.parametrize("mode", ["auto", "mapconcat"])
-def test_stream_fuzz(fem, mode):
+@pytest.mark.parametrize("mode", ["auto", "mapconcat", "mapconcat-list"])
+def test_stream_fuzz(fem, mode, monkeypatch):
+    if mode == "mapconcat-list":
+        # few episodes through the filter and the list kernel on every segment
+        monkeypatch.setenv("EP_SPLIT", "positions")
+        monkeypatch.setenv("EP_FORCE_LIST", "1")
+        mode = "mapconcat"
     rng = np.random.default_rng(71)
     for trial in range(40):
         n = int(rng.integers(1, 1500))

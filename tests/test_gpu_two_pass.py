@@ -48,6 +48,8 @@ def _split_env(monkeypatch, split):
         monkeypatch.setenv("EP_FORCE_SCAN", "1")
     elif split != "auto":
         monkeypatch.setenv("EP_SPLIT", split)
+        if split == "positions":
+            monkeypatch.setenv("EP_FORCE_LIST", "1")
 
 
 def _upper(fem, times, types, ep, hi, mode, P=0):
