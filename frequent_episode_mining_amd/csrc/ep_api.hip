@@ -461,9 +461,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       span += hi;
       max_hi = std::max(max_hi, hi);
       if (hi <= 63) dil_k = std::max(dil_k, dil_steps((uint32_t)lo, (uint32_t)hi));
-      // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1
-      const int64_t runs = hi / (hi - lo + 1) + 1;
-      while (K < runs && K <= EP_MAX_RUNS) K <<= 1;
+      // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1;
+      // K < that bound iff K * (hi - lo + 1) <= hi
+      while (K <= EP_MAX_RUNS && (int64_t)K * (hi - lo + 1) <= hi) K <<= 1;
     }
     if (span > INT32_MAX) return EP_ERR_INTERVAL;
     max_span = std::max(max_span, span);

@@ -10,9 +10,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
-#include <map>
 #include <vector>
 
 #include "epcount.h"
@@ -55,6 +57,9 @@ int count_level(const int32_t* times, const uint16_t* types, int64_t n, const Ca
     return EP_ERR_WORKSPACE;
   ep_options eo{};
   eo.mode = o.mode;
+  ep_stats stats{};
+  static const bool log_stats = getenv("EP_LOG_TIME") != nullptr;
+  if (log_stats) eo.stats = &stats;
   int st;
   if (two) {
     st = ep_count_two_pass(times, types, n, eps, S, o.threshold, d, d + S, nullptr, stream, &eo);
@@ -68,6 +73,9 @@ int count_level(const int32_t* times, const uint16_t* types, int64_t n, const Ca
        hipStreamSynchronize(stream) != hipSuccess))
     st = EP_ERR_HIP;
   if (hipFreeAsync(d, stream) != hipSuccess && st == EP_OK) st = EP_ERR_HIP;
+  if (log_stats && st == EP_OK)
+    fprintf(stderr, "ep_mine: size %d: P = %d, kernels %d, repairs %lld, fallbacks %lld\n", (int)k,
+            (int)stats.n_segments, (int)stats.kernels, (long long)stats.repairs, (long long)stats.fallbacks);
   // two passes: a dropped episode reads -1, below any threshold >= 1
   return st;
 }
@@ -105,6 +113,9 @@ extern "C" int ep_mine(const int32_t* times, const uint16_t* types, int64_t n_ev
     cur.types = a;
   }
   int status = EP_OK;
+  // per-size host timings on stderr when EP_LOG_TIME is set
+  static const bool log_time = getenv("EP_LOG_TIME") != nullptr;
+  using clk = std::chrono::steady_clock;
   while (cur.size() > 0) {
     const int32_t k = cur.k;
     const int64_t S = cur.size();
@@ -113,7 +124,9 @@ extern "C" int ep_mine(const int32_t* times, const uint16_t* types, int64_t n_ev
       break;
     }
     std::vector<int64_t> cnt;
+    const auto t0 = clk::now();
     status = count_level(times, types, n_events, cur, o, stream, cnt);
+    const auto t1 = clk::now();
     if (status != EP_OK) break;
     ep_mined::Level lv;
     lv.k = k;
@@ -146,21 +159,52 @@ extern "C" int ep_mine(const int32_t* times, const uint16_t* types, int64_t n_ev
             nxt.bins.push_back(b);
           }
     } else {
-      // key of an episode's first k-1 nodes (types and the k-2 bins between
-      // them), and of its last k-1 nodes
-      auto key = [&](int64_t i, int from) {
-        std::vector<int32_t> v;
-        v.reserve(2 * k);
-        for (int j = 0; j < k - 1; ++j) v.push_back(cur.types[(size_t)(i * k + from + j)]);
-        for (int j = 0; j < k - 2; ++j) v.push_back(cur.bins[(size_t)(i * (k - 1) + from + j)]);
-        return v;
+      // The frequent episodes are in key order (t1, b1, t2, ..., tk), so
+      // those sharing their first k-1 nodes (t1, b1, ..., t_{k-1}: the key's
+      // first 2k-3 entries) are contiguous.  Group starts, then for each
+      // episode a the group whose first k-1 nodes equal a's last k-1 nodes.
+      const int kl = 2 * k - 3;  // entries of a (k-1)-node key
+      auto at = [&](int64_t i, int from, int x) -> int32_t {
+        // entry x of the (k-1)-node key of episode i starting at node `from`
+        return (x & 1) ? cur.bins[(size_t)(i * (k - 1) + from + x / 2)]
+                       : (int32_t)cur.types[(size_t)(i * k + from + x / 2)];
       };
-      std::map<std::vector<int32_t>, std::vector<int64_t>> by_prefix;
-      for (int64_t i : keep) by_prefix[key(i, 0)].push_back(i);
-      for (int64_t ia : keep) {
-        auto it = by_prefix.find(key(ia, 1));
-        if (it == by_prefix.end()) continue;
-        for (int64_t ib : it->second) {
+      auto cmp = [&](int64_t i, int fi, int64_t j, int fj) {
+        for (int x = 0; x < kl; ++x) {
+          const int32_t u = at(i, fi, x), v = at(j, fj, x);
+          if (u != v) return u < v ? -1 : 1;
+        }
+        return 0;
+      };
+      std::vector<int64_t> starts;  // index into keep of each group's first episode
+      for (size_t q = 0; q < keep.size(); ++q)
+        if (q == 0 || cmp(keep[q - 1], 0, keep[q], 0) != 0) starts.push_back((int64_t)q);
+      starts.push_back((int64_t)keep.size());
+      int64_t total = 0;
+      std::vector<int64_t> hit_group(keep.size(), -1);
+      for (size_t qa = 0; qa < keep.size(); ++qa) {
+        const int64_t ia = keep[qa];
+        int64_t lo = 0, hi = (int64_t)starts.size() - 1;  // search groups [lo, hi)
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) / 2;
+          if (cmp(keep[(size_t)starts[(size_t)mid]], 0, ia, 1) < 0)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+        if (lo < (int64_t)starts.size() - 1 && cmp(keep[(size_t)starts[(size_t)lo]], 0, ia, 1) == 0) {
+          hit_group[qa] = lo;
+          total += starts[(size_t)lo + 1] - starts[(size_t)lo];
+        }
+      }
+      nxt.types.reserve((size_t)total * (k + 1));
+      nxt.bins.reserve((size_t)total * k);
+      for (size_t qa = 0; qa < keep.size(); ++qa) {
+        if (hit_group[qa] < 0) continue;
+        const int64_t ia = keep[qa];
+        const int64_t g = hit_group[qa];
+        for (int64_t qb = starts[(size_t)g]; qb < starts[(size_t)g + 1]; ++qb) {
+          const int64_t ib = keep[(size_t)qb];
           for (int j = 0; j < k; ++j) nxt.types.push_back(cur.types[(size_t)(ia * k + j)]);
           nxt.types.push_back(cur.types[(size_t)(ib * k + k - 1)]);
           for (int j = 0; j < k - 1; ++j) nxt.bins.push_back(cur.bins[(size_t)(ia * (k - 1) + j)]);
@@ -169,6 +213,10 @@ extern "C" int ep_mine(const int32_t* times, const uint16_t* types, int64_t n_ev
       }
     }
     cur = std::move(nxt);
+    if (log_time)
+      fprintf(stderr, "ep_mine: size %d, %lld candidates: count %.1f us, next size %.1f us\n", (int)k,
+              (long long)S, std::chrono::duration<double, std::micro>(t1 - t0).count(),
+              std::chrono::duration<double, std::micro>(clk::now() - t1).count());
   }
   if (status != EP_OK) {
     delete res;
