@@ -227,7 +227,8 @@ constexpr int64_t kListMinEvents = 1 << 20;  // the list path pays off from stre
 // The hybrid rule (hybrid-algorithm section): the GPU is fully utilised by
 // PTPE when the episodes alone give every resident lane of every CU work.
 // Otherwise MapConcatenate with the smallest power-of-two P that does, kept
-// to >= 256 events per segment on average and P <= 2^20.
+// to >= 256 events per segment on average (>= 64 with fewer than 256
+// episodes, where the lanes are few) and P <= 2^20.
 int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments, int32_t cu_count,
               int32_t lanes_per_cu, int32_t* out_mode, int32_t* out_segments) {
   const int64_t full = (int64_t)std::max(cu_count, 1) * std::max(lanes_per_cu, 1);
@@ -240,7 +241,7 @@ int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments,
     } else {
       const int64_t per_seg = std::max<int64_t>(S, 1) * (N <= kMaxClassNodes ? 1 : N);
       const int64_t need = (full + per_seg - 1) / per_seg;
-      const int64_t cap_by_events = std::max<int64_t>(1, n / 256);
+      const int64_t cap_by_events = std::max<int64_t>(1, n / (S < 256 ? 64 : 256));
       P = 2;
       while (P < need && P < (1 << 20)) P <<= 1;
       // keep segments to <= 65,536 events on average: a repair rescans one segment

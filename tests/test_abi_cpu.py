@@ -185,8 +185,10 @@ def test_planner_rule():
     assert fem.plan(16384, 2, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 256)
     # beyond 8 nodes a lane carries one machine: S * N * P lanes
     assert fem.plan(100, 12, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
-    # the segment count is capped so a segment keeps >= 256 events on average
-    assert fem.plan(1, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 32)
+    # the segment count is capped so a segment keeps >= 256 events on average,
+    # >= 64 when there are fewer than 256 episodes
+    assert fem.plan(1, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 128)
+    assert fem.plan(300, 2, 10_000, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 32)
     # forced choices pass through
     assert fem.plan(8, 5, 10 ** 8, mode="mapconcat", n_segments=4096) == ("mapconcat", 4096)
     assert fem.plan(8, 5, 10 ** 8, mode="ptpe") == ("ptpe", 1)
