@@ -244,8 +244,8 @@ int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments,
       const int64_t cap_by_events = std::max<int64_t>(1, n / (S < 256 ? 64 : 256));
       P = 2;
       while (P < need && P < (1 << 20)) P <<= 1;
-      // keep segments to <= 65,536 events on average: a repair rescans one segment
-      while (P * 65536 < n && P < (1 << 20)) P <<= 1;
+      // keep segments to <= 32,768 events on average: a repair rescans one segment
+      while (P * 32768 < n && P < (1 << 20)) P <<= 1;
       while (P > 1 && P > cap_by_events) P >>= 1;
     }
   }

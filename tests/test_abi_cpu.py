@@ -181,8 +181,8 @@ def test_planner_rule():
     assert mode == "mapconcat" and P == 512 and 1024 * P >= 256 * 2048 > 1024 * P // 2
     # few episodes, long stream
     assert fem.plan(8, 5, 10 ** 8, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 65536)
-    # many episodes, long stream: segments are kept to <= 65,536 events
-    assert fem.plan(16384, 2, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 256)
+    # many episodes, long stream: segments are kept to <= 32,768 events
+    assert fem.plan(16384, 2, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
     # beyond 8 nodes a lane carries one machine: S * N * P lanes
     assert fem.plan(100, 12, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("mapconcat", 512)
     # the segment count is capped so a segment keeps >= 256 events on average,
