@@ -377,8 +377,11 @@ def main():
         return out, None
 
     if scheme == "stream":
-        st = {"mode": "mapconcat per batch", "n_segments": 0, "max_runs": 0, "kernels": 1 | 2,
-              "repairs": 0, "fallbacks": 0}
+        # the stream reports no plan: the first batch counted alone has the
+        # same kernels (the list rule looks at the episodes and the batch size)
+        _, st = fem.count_episodes(times[cuts[0]:cuts[1]], types[cuts[0]:cuts[1]], table, mode="mapconcat",
+                                   n_segments=seg, stats=True, stream=stream)
+        st = dict(st, mode="mapconcat per batch", n_segments=0, repairs=0, fallbacks=0)
     elif scheme == "two-pass":
         _, _, _, st = fem.count_two_pass(times, types, table, threshold=args.threshold, mode=mode,
                                          n_segments=seg, stats=True, stream=stream)

@@ -328,9 +328,9 @@ void ep_stream_destroy(ep_stream* st);
  * that lanes(P) >= cu_count * lanes_per_cu, where a lane carries the N
  * machines of one (segment, episode) for N <= 8 (lanes = n_episodes * P) and
  * one machine beyond (lanes = n_episodes * n_nodes * P); P is then raised
- * until segments hold <= 65,536 events on average (a boundary repair rescans
- * one segment), and capped so that a segment keeps >= 256 events on average
- * and P <= 2^20.
+ * until segments hold <= 32,768 events on average (a boundary repair rescans
+ * one segment), and capped so that a segment keeps on average >= 64 events
+ * when n_episodes < 256, >= 256 events otherwise, and P <= 2^20.
  */
 int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, int32_t mode,
             int32_t n_segments, int32_t cu_count, int32_t lanes_per_cu,
