@@ -38,6 +38,9 @@ HBM_PEAK_GBS = 8000.0
 # Algorithmic work of the counting machine per (episode, relevant event): the
 # node-type test, the window check and the window update, ~10 int32 ops.
 OPS_PER_RELEVANT_PAIR = 10
+# the Map-step phases the library times, and the name profile_begin_kernel takes
+PHASES = {"map_filter_ms": "filter", "map_prune_ms": "prune", "map_ticks_ms": "ticks",
+          "map_positions_ms": "positions"}
 # Device code of every kernel (host code is not hashed: a change there leaves
 # the kernels and their traffic as they were).
 KERNEL_SOURCES = ["frequent_episode_mining_amd/csrc/ep_device.hpp",
@@ -202,12 +205,12 @@ def main_mine(args):
     for _ in range(args.steps):
         step()
     prof = fem.profile_end()
-    per = {k: prof[k] / args.steps for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
+    per = {k: prof[k] / args.steps for k in PHASES}
     top = max(per, key=per.get)
-    which = {"map_filter_ms": "filter", "map_ticks_ms": "ticks", "map_positions_ms": "positions"}[top]
-    log("phases per step: map %.4f (filter %.4f, ticks %.4f, positions %.4f) closure %.4f "
+    which = PHASES[top]
+    log("phases per step: map %.4f (filter %.4f, prune %.4f, ticks %.4f, positions %.4f) closure %.4f "
         "concat %.4f other %.4f ms; %.1f counting calls per step"
-        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_ticks_ms"],
+        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_prune_ms"], per["map_ticks_ms"],
            per["map_positions_ms"], prof["closure_ms"] / args.steps, prof["concat_ms"] / args.steps,
            prof["other_ms"] / args.steps, prof["calls"] / args.steps))
     fem.profile_begin_kernel(which, 1)
@@ -228,8 +231,8 @@ def main_mine(args):
     rel = int(cnt[np.unique(wl.alphabet)].sum())  # size 1: each type's own events
     for k, lst in mining_candidates(mined, wl.bins).items():
         rel += sum(int(cnt[np.unique(np.array(t))].sum()) for t in lst)
-    names = {"map_filter_ms": "filter_kernel", "map_ticks_ms": "map_ticks_kernel",
-             "map_positions_ms": "map_bits_kernel"}
+    names = {"map_filter_ms": "filter_kernel", "map_prune_ms": "list_prune_kernel",
+             "map_ticks_ms": "map_ticks_kernel", "map_positions_ms": "map_bits_kernel"}
     achieved = OPS_PER_RELEVANT_PAIR * rel / (kernel_ms / 1000.0) / 1e12 if kernel_ms > 0 else 0.0
     roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
                 "frac": achieved / ALU_PEAK_TOPS, "traffic": None,
@@ -400,14 +403,16 @@ def main():
     for _ in range(args.steps):
         step()
     prof = fem.profile_end()
-    per = {k: prof[k] / args.steps for k in ("map_filter_ms", "map_ticks_ms", "map_positions_ms")}
+    per = {k: prof[k] / args.steps for k in PHASES}
     if not st["kernels"] & 4:
         per["map_filter_ms"] = 0.0  # no filter launched: the interval is two bare events
+    if not st["kernels"] & 8:
+        per["map_prune_ms"] = 0.0  # no pruning launched: likewise
     top = max(per, key=per.get)
-    which = {"map_filter_ms": "filter", "map_ticks_ms": "ticks", "map_positions_ms": "positions"}[top]
-    log("phases per step: map %.4f (filter %.4f, ticks %.4f, positions %.4f) closure %.4f "
+    which = PHASES[top]
+    log("phases per step: map %.4f (filter %.4f, prune %.4f, ticks %.4f, positions %.4f) closure %.4f "
         "concat %.4f other %.4f ms"
-        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_ticks_ms"],
+        % (prof["map_ms"] / args.steps, per["map_filter_ms"], per["map_prune_ms"], per["map_ticks_ms"],
            per["map_positions_ms"], prof["closure_ms"] / args.steps,
            prof["concat_ms"] / args.steps, prof["other_ms"] / args.steps))
 
@@ -449,8 +454,8 @@ def main():
         pos_name = "map_list_kernel" if st["kernels"] & 4 else "map_bits_kernel"
     else:
         pos_name = "map_scan_kernel"
-    names = {"map_filter_ms": "filter_kernel", "map_ticks_ms": "map_ticks_kernel",
-             "map_positions_ms": pos_name}
+    names = {"map_filter_ms": "filter_kernel", "map_prune_ms": "list_prune_kernel",
+             "map_ticks_ms": "map_ticks_kernel", "map_positions_ms": pos_name}
     kernel, kernel_ms = names[top], kprof[top] / max(kprof["calls"], 1)
     map_s = kernel_ms / 1000.0
     rel = relevant_pairs(wl)
@@ -467,7 +472,14 @@ def main():
     traffic = stored_traffic(wl.name if scheme == "alpha" else "%s-%s" % (wl.name, scheme), kernel)
     if traffic is not None and scheme == "two-pass":
         traffic *= 2  # the stored figure is per dispatch; a step launches the kernel twice
-    if kernel == "filter_kernel":
+    if kernel == "list_prune_kernel":
+        # every entry read once (the kept ones are written back in place)
+        moved = 8.0 * rel
+        achieved = moved / map_s / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                    "work": "8 B x %d entries read" % rel}
+    elif kernel == "filter_kernel":
         # one read of the stream, one {time, levels} entry written per
         # (episode, relevant event) pair
         moved = 6.0 * n + 8.0 * rel

@@ -57,7 +57,8 @@ class EpProfile(ctypes.Structure):
     _fields_ = [("map_ms", ctypes.c_double), ("closure_ms", ctypes.c_double),
                 ("concat_ms", ctypes.c_double), ("other_ms", ctypes.c_double),
                 ("calls", ctypes.c_int64), ("map_ticks_ms", ctypes.c_double),
-                ("map_positions_ms", ctypes.c_double), ("map_filter_ms", ctypes.c_double)]
+                ("map_positions_ms", ctypes.c_double), ("map_filter_ms", ctypes.c_double),
+                ("map_prune_ms", ctypes.c_double)]
 
 
 class EpError(RuntimeError):
@@ -387,11 +388,11 @@ def profile_begin():
     _check(load_library().ep_profile_begin())
 
 
-PROFILE_KERNELS = {"filter": 0, "ticks": 1, "positions": 2}
+PROFILE_KERNELS = {"filter": 0, "ticks": 1, "positions": 2, "prune": 3}
 
 
 def profile_begin_kernel(which: str, every: int = 1) -> None:
-    """Time one Map kernel ('filter', 'ticks' or 'positions') on one call in
+    """Time one Map kernel ('filter', 'prune', 'ticks' or 'positions') on one call in
     `every`, recording nothing else."""
     _check(load_library().ep_profile_begin_kernel(PROFILE_KERNELS[which], every))
 
@@ -402,7 +403,8 @@ def profile_end() -> dict:
     _check(load_library().ep_profile_end(ctypes.byref(p)))
     return {"map_ms": p.map_ms, "closure_ms": p.closure_ms, "concat_ms": p.concat_ms,
             "other_ms": p.other_ms, "calls": p.calls, "map_ticks_ms": p.map_ticks_ms,
-            "map_positions_ms": p.map_positions_ms, "map_filter_ms": p.map_filter_ms}
+            "map_positions_ms": p.map_positions_ms, "map_filter_ms": p.map_filter_ms,
+            "map_prune_ms": p.map_prune_ms}
 
 
 def segment_cut(t_min: int, t_max: int, n_segments: int, p: int) -> int:

@@ -178,10 +178,11 @@ int scratch_release(int dev, ScratchBlock* b, hipStream_t stream) {
 // Profiling session: per counting call, events around its phases.  Events
 // come from a pool that lives as long as the process, so recording adds no
 // event creation to the timed calls once the pool is warm.
-constexpr int kProfEvents = 7;
+constexpr int kProfEvents = 8;
 struct ProfRecord {
-  // start, before Map (the filter), before the tick Map kernel, after it,
-  // after Map, after closure, after Concatenate
+  // start, before Map (the filter), after the filter, after the list
+  // pruning (before the tick Map kernel), after it, after Map, after closure,
+  // after Concatenate
   hipEvent_t ev[kProfEvents];
   hipEvent_t end;
   int which;  // -1: every phase; else the one Map kernel timed (EP_PROFILE_*)
@@ -191,6 +192,16 @@ bool g_prof_on = false;
 int g_prof_which = -1;   // -1: every phase of every call
 int g_prof_every = 1;    // one call in this many is recorded
 int64_t g_prof_calls = 0;
+
+// the event before one timed Map kernel (EP_PROFILE_*); the next one follows it
+int prof_first(int which) {
+  switch (which) {
+    case EP_PROFILE_FILTER: return 1;
+    case EP_PROFILE_PRUNE: return 2;
+    case EP_PROFILE_TICKS: return 3;
+    default: return 4;
+  }
+}
 std::vector<ProfRecord> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -404,6 +415,7 @@ struct Launch {
   size_t lds_ticks;
   int split;       // 0: per-segment choice between tick and position kernels; 1: ticks; 2: positions
   bool list;       // sparse segments through the filter + list Map kernels (else the position kernel)
+  bool prune;      // list path: the filter's lists pruned before the list Map kernel
   int slots;
   int n_machines;
 };
@@ -599,6 +611,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     if (lanes_env && N <= kMaxClassNodes && L.n_machines > 1)
       L.all_mach = strcmp(lanes_env, "machine") != 0;
     L.M = L.all_mach ? 1 : L.n_machines;
+    // pruning the lists pays where the list kernel has too few lanes (under
+    // two waves per SIMD) to hide their serial walks: it shortens every walk;
+    // with more lanes the list kernel is bound by its total work, which
+    // pruning cuts by less than pruning itself costs per block
+    const int64_t list_lanes = (int64_t)P * S * L.M;
+    L.prune = L.list && ((list_lanes < (int64_t)info->cu_count * 4 * 2 * kWave && !getenv("EP_NO_PRUNE")) ||
+                         getenv("EP_FORCE_PRUNE"));
     L.G = (int)std::min<int64_t>(S, L.block / L.M);
     L.R = (L.G == S) ? std::max(1, L.block / (L.G * L.M)) : 1;
     L.R = (int)std::min<int64_t>(L.R, P);
@@ -622,6 +641,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     L.lds_ticks = (size_t)L.R * L.CW * U * 8;
   } else {
     L.list = false;
+    L.prune = false;
     L.all_mach = false;
     L.M = L.n_machines;
     L.G = (int)std::min<int64_t>(S, L.block / L.M);
@@ -765,7 +785,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     // records boundary i when the session times it (every boundary, or the
     // two around the one Map kernel it times)
     auto rec_at = [&](int i) {
-      if (prof && (prof_which < 0 || i == prof_which + 1 || i == prof_which + 2))
+      if (prof && (prof_which < 0 || i == prof_first(prof_which) || i == prof_first(prof_which) + 1))
         (void)hipEventRecord(rec.ev[i], stream);
     };
     SetupArgs sa;
@@ -850,22 +870,42 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       le = hipGetLastError();
     }
     rec_at(2);
+    if (L.prune && !skip_map && le == hipSuccess) {
+      PruneArgs pa;
+      pa.times = times; pa.n = n_events; pa.n_blocks = n_lblocks; pa.ep_lo = d_lo; pa.ep_hi = d_hi;
+      pa.S = (int32_t)S; pa.N = N; pa.max_share = max_share;
+      pa.lists = d_lists; pa.list_off = d_loff; pa.list_cnt = d_lcnt;
+      // persistent workgroups: as many as are resident at once
+      static int prune_per_cu = 0;
+      if (prune_per_cu == 0) {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, list_prune_kernel, kBlock, 0) != hipSuccess) {
+          status = EP_ERR_HIP;
+          break;
+        }
+        prune_per_cu = std::max(v, 1);
+      }
+      const int64_t pgrid = std::min<int64_t>(n_lblocks, (int64_t)info->cu_count * prune_per_cu);
+      hipLaunchKernelGGL(list_prune_kernel, dim3((unsigned)pgrid), dim3(kBlock), 0, stream, pa);
+      le = hipGetLastError();
+    }
+    rec_at(3);
     if (skip_map) {
-      rec_at(3);
+      rec_at(4);
     } else if (le == hipSuccess && !L.bits) {
-      rec_at(3);  // no tick kernel: an empty interval
+      rec_at(4);  // no tick kernel: an empty interval
       le = Lr->map_scan(ma, L.win, mgrid, dim3(L.block), stream);
     } else if (le == hipSuccess) {
       // each segment goes to the tick kernel or, by segment_uses_ticks, to the
       // list or the position kernel
       if (L.split != 2) le = Lr->map_ticks(ma, L.all_mach, mgrid, dim3(L.block), L.lds_ticks, stream);
-      rec_at(3);
+      rec_at(4);
       if (le == hipSuccess && L.split != 1)
         le = L.list ? Lr->map_list(ma, L.win, L.all_mach, mgrid, dim3(L.block), stream)
                     : Lr->map_bits(ma, L.win, L.all_mach, mgrid, dim3(L.block), L.lds, stream);
     }
     if (le != hipSuccess) { status = EP_ERR_HIP; break; }
-    rec_at(4);
+    rec_at(5);
     StreamArgs stra{};
     if (sh) {
       ClosureArgs& c = stra.c;
@@ -909,7 +949,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         status = EP_ERR_HIP;
         break;
       }
-      rec_at(5);
+      rec_at(6);
     }
     if (P > 1 && !fused) {
       ClosureArgs ca;
@@ -922,7 +962,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         status = EP_ERR_HIP;
         break;
       }
-      rec_at(5);
+      rec_at(6);
       // Concatenate tree: each launch joins groups of `members` blocks in LDS
       // a stream's batch joins all but the last segment (the tail runs that one)
       const int32_t Pt = sh ? P - 1 : P;
@@ -940,8 +980,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       if (status != EP_OK) break;
     }
-    if (P <= 1 && !fused) rec_at(5);
-    rec_at(6);
+    if (P <= 1 && !fused) rec_at(6);
+    rec_at(7);
     mark();  // closure + tree launches
     if (sh) {
       if (Lr->stream_tail(stra, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
@@ -976,7 +1016,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       opt->stats->mode = pmode;
       opt->stats->n_segments = P;
       opt->stats->max_runs = L.win >= kBits32 ? (L.win == kBits32 ? 32 : 64) : K;
-      opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0);
+      opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0) | (L.prune ? 8 : 0);
       opt->stats->repairs = (int64_t)cnt[0];
       opt->stats->fallbacks = (int64_t)cnt[1];
     }
@@ -1001,7 +1041,7 @@ extern "C" int ep_profile_begin(void) {
 }
 
 extern "C" int ep_profile_begin_kernel(int32_t which, int32_t every) {
-  if (which < EP_PROFILE_FILTER || which > EP_PROFILE_POSITIONS || every < 1) return EP_ERR_ARG;
+  if (which < EP_PROFILE_FILTER || which > EP_PROFILE_PRUNE || every < 1) return EP_ERR_ARG;
   std::lock_guard<std::mutex> lock(g_prof_mu);
   g_prof.clear();
   g_prof_on = true;
@@ -1025,12 +1065,14 @@ extern "C" int ep_profile_end(ep_profile* out) {
     if (r.which >= 0) {
       // one Map kernel: the interval between its two boundaries
       float k_ms = 0.f;
-      if (hipEventSynchronize(r.ev[r.which + 2]) != hipSuccess ||
-          hipEventElapsedTime(&k_ms, r.ev[r.which + 1], r.ev[r.which + 2]) != hipSuccess)
+      const int f = prof_first(r.which);
+      if (hipEventSynchronize(r.ev[f + 1]) != hipSuccess ||
+          hipEventElapsedTime(&k_ms, r.ev[f], r.ev[f + 1]) != hipSuccess)
         status = EP_ERR_HIP;
-      double* field = r.which == EP_PROFILE_FILTER
-                          ? &acc.map_filter_ms
-                          : (r.which == EP_PROFILE_TICKS ? &acc.map_ticks_ms : &acc.map_positions_ms);
+      double* field = r.which == EP_PROFILE_FILTER  ? &acc.map_filter_ms
+                      : r.which == EP_PROFILE_PRUNE ? &acc.map_prune_ms
+                      : r.which == EP_PROFILE_TICKS ? &acc.map_ticks_ms
+                                                    : &acc.map_positions_ms;
       *field += k_ms;
       acc.map_ms += k_ms;
       acc.calls += 1;
@@ -1046,13 +1088,14 @@ extern "C" int ep_profile_end(ep_profile* out) {
     seq[kProfEvents] = r.end;
     for (int i = 0; i < kProfEvents && status == EP_OK; ++i)
       if (hipEventElapsedTime(&ms[i], seq[i], seq[i + 1]) != hipSuccess) status = EP_ERR_HIP;
-    acc.other_ms += ms[0] + ms[6];
+    acc.other_ms += ms[0] + ms[7];
     acc.map_filter_ms += ms[1];
-    acc.map_ticks_ms += ms[2];
-    acc.map_positions_ms += ms[3];
-    acc.map_ms += ms[1] + ms[2] + ms[3];
-    acc.closure_ms += ms[4];
-    acc.concat_ms += ms[5];
+    acc.map_prune_ms += ms[2];
+    acc.map_ticks_ms += ms[3];
+    acc.map_positions_ms += ms[4];
+    acc.map_ms += ms[1] + ms[2] + ms[3] + ms[4];
+    acc.closure_ms += ms[5];
+    acc.concat_ms += ms[6];
     acc.calls += 1;
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (int i = 0; i < kProfEvents; ++i) g_event_pool.push_back(r.ev[i]);

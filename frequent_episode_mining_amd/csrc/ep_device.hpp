@@ -386,6 +386,16 @@ struct MapArgs {
                        // groups when its segments fit one chunk each
 };
 
+// A workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every global load the thread has in flight (its release fence
+// covers all memory), which would end any prefetch into registers issued
+// before it; kernels whose threads share data only through LDS use this one.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (every lane active): the
 // shifts 1, 2, 4 and 8 within each row of 16 lanes, then the last lane of
 // rows 0 and 2 added to rows 1 and 3, then lane 31 to rows 2 and 3.

@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
 // One pass over the stream for the list Map kernel.  Block b holds events
 // [b * kListBlock, (b + 1) * kListBlock); each event gets its node-type slot
 // and the set of episodes with that type, and for each episode its events are
-// written in order to the block's region as {time, node levels}: episode e's
+// written in order to the block's region as {time, node levels | e << 16}
+// (the Map kernels read only the level bits, 0..15): episode e's
 // entries start at list_off[b][e] and number list_cnt[b][e].  The region holds
 // kListBlock * max_share entries (max_share: most episodes one type is on), so
 // blocks need nothing from each other.  A thread takes 16 consecutive events;
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
   };
   int64_t b = blockIdx.x;
   if (b < n_blocks) load(b, tn, yn);
-  __syncthreads();  // tables in LDS
+  lds_barrier();  // tables in LDS
 
   for (; b < n_blocks; b += gridDim.x) {
     const int64_t first = b * kListBlock + (int64_t)tid * kFilterPer;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
       incl[g] = wave_incl_scan(c[g]);
       if (lane == kWave - 1) s_wsum[wave][g] = incl[g];
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int g = 0; g < 2 * G; ++g) {
       uint32_t before = 0;
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
     // this thread's events of node types, in order, from its LDS copy
     while (rel) {
@@ -342,10 +343,187 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
         m &= m - 1;
         const uint16_t r = s_pre[e][tid];
         s_pre[e][tid] = (uint16_t)(r + 1);
-        region[s_off[e] + r] = make_int2(tk, (int32_t)s_lv[u * kE + e]);
+        region[s_off[e] + r] = make_int2(tk, (int32_t)((uint32_t)s_lv[u * kE + e] | (uint32_t)e << 16));
       }
     }
-    __syncthreads();  // s_wsum, s_pre, s_off, s_st and s_ss are rewritten by the next block
+    lds_barrier();  // s_wsum, s_pre, s_off, s_st and s_ss are rewritten by the next block
+  }
+}
+
+// ------------------------------------------------------------- list pruning
+
+// Leaves out of the filter's lists the entries that cannot change what the
+// counting machines output.  An event of node j's type acts only through a
+// node-j candidate: for j > 0 it becomes one only if a node j-1 candidate
+// lies in [t - hi_{j-1}, t - lo_{j-1} - 1], and node j-1 candidates are
+// events of node j-1's type, which sit in the same episode's list with bit
+// j-1 in their levels; for j < N-1 the candidate is used only by an event of
+// node j+1's type in [t + lo_j + 1, t + hi_j].  An entry with no such
+// neighbour is dropped: the machines' windows age by elapsed time, not by
+// entries, and every completion and reset happens at an entry that stays.
+// Each side is decided by the nearest kPruneLook entries of the list on that
+// side: the search ends at an entry past the range or at the list's end
+// (nothing found), at a match, or undecided after kPruneLook entries; an
+// undecided side, a range the block may not hold whole (not strictly between
+// its first and last time) and an entry on several levels count as having
+// the neighbour.  Persistent workgroups loop over blocks, a block's lists
+// read into registers one iteration ahead; a block is staged in LDS, each
+// entry tested by one thread (entries carry their episode in bits 16..), and
+// the kept entries are written back in place, list by list, with new offsets
+// and counts.  A block with more than kPruneCap entries is left as it is.
+constexpr int kPruneCap = 2048;   // entries a block may have to be pruned
+constexpr int kPruneLook = 3;     // entries a neighbour search visits on one side
+constexpr int kPrunePer = kPruneCap / kBlock;
+
+struct PruneArgs {
+  const int32_t* times;
+  int64_t n;
+  int64_t n_blocks;
+  const int32_t* ep_lo;  // [S * (N - 1)] delay intervals (lo, hi]
+  const int32_t* ep_hi;
+  int32_t S;
+  int32_t N;
+  int32_t max_share;
+  int2* lists;
+  int32_t* list_off;     // [blocks * S]
+  int32_t* list_cnt;     // [blocks * S]
+};
+
+__global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
+  __shared__ int2 s_e[kPruneCap];
+  __shared__ uint8_t s_keep[kPruneCap];             // entry i is kept
+  __shared__ int32_t s_off[kMaxListEpisodes + 1];
+  __shared__ uint32_t s_iv[kMaxListEpisodes * 16];  // interval j of episode e: lo | hi << 8
+  __shared__ uint32_t s_wsum[kBlock / kWave];
+  __shared__ int32_t s_pre[kBlock + 1];             // kept entries before thread t's chunk
+  __shared__ uint8_t s_kb[kBlock];                  // thread t's kept entries (bit q)
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int S = A.S, N = A.N;
+  for (int i = tid; i < S * (N - 1); i += kBlock)
+    s_iv[(i / (N - 1)) * 16 + i % (N - 1)] = (uint32_t)A.ep_lo[i] | (uint32_t)A.ep_hi[i] << 8;
+  const int64_t grid = gridDim.x;
+  // the lists lie one after the other from the region's start, episode by
+  // episode: a block's entries are its last list's offset plus count (kept
+  // apart until used, so that loading them waits for nothing)
+  auto total_of = [&](int64_t bb) -> int2 {
+    return bb < A.n_blocks ? make_int2(A.list_off[bb * S + S - 1], A.list_cnt[bb * S + S - 1]) : make_int2(0, 0);
+  };
+  int2 ent[kPrunePer];
+  int32_t off_r = 0, tf_r = 0, tl_r = 0;
+  // block bb's entries (entry tid + q * kBlock in ent[q]), offsets and ends
+  auto fetch = [&](int64_t bb, int32_t tot) {
+    const int2* region = A.lists + bb * (int64_t)kListBlock * A.max_share;
+    const bool run = tot > 0 && tot <= kPruneCap;
+#pragma unroll
+    for (int q = 0; q < kPrunePer; ++q) {
+      const int i = tid + q * kBlock;
+      ent[q] = (run && i < tot) ? region[i] : make_int2(0, 0);
+    }
+    off_r = tid < S ? A.list_off[bb * S + tid] : 0;
+    tf_r = A.times[bb * kListBlock];
+    tl_r = A.times[min(A.n, (bb + 1) * (int64_t)kListBlock) - 1];
+  };
+  int64_t b = blockIdx.x;
+  const int2 t0 = total_of(b);
+  int32_t tot = __builtin_amdgcn_readfirstlane(t0.x + t0.y);
+  int2 tot_next = total_of(b + grid);
+  if (b < A.n_blocks) fetch(b, tot);
+
+  for (; b < A.n_blocks; b += grid) {
+    const int32_t total = tot;
+    const int64_t t_first = tf_r, t_last = tl_r;
+    const bool run = total > 0 && total <= kPruneCap;
+    if (run) {
+#pragma unroll
+      for (int q = 0; q < kPrunePer; ++q) {
+        const int i = tid + q * kBlock;
+        if (i < total) s_e[i] = ent[q];
+      }
+      if (tid < S) s_off[tid] = off_r;
+      if (tid == 0) s_off[S] = total;
+    }
+    // the next block's loads in flight meanwhile
+    tot = __builtin_amdgcn_readfirstlane(tot_next.x + tot_next.y);
+    if (b + grid < A.n_blocks) fetch(b + grid, tot);
+    tot_next = total_of(b + 2 * grid);
+    lds_barrier();
+
+    if (run) {
+      // entries tid, tid + kBlock, ...: which of them pass
+      for (int i = tid; i < total; i += kBlock) {
+        const int2 me = s_e[i];
+        const int64_t t = me.x;
+        const int e = min((int)((uint32_t)me.y >> 16), S - 1);
+        const uint32_t lm = (uint32_t)me.y & 0xffffu;
+        const int j = __ffs((int)lm) - 1;
+        const int32_t beg = s_off[e], end = s_off[e + 1];
+        // predecessor side: node j-1 in [t - hi, t - lo - 1]; successor side:
+        // node j+1 in [t + lo + 1, t + hi]; each decided by the nearest
+        // kPruneLook entries of the list on its side
+        const uint32_t ivp = s_iv[e * 16 + max(j - 1, 0)], ivs = s_iv[e * 16 + max(j, 0)];
+        const int64_t p_lo = t - (int64_t)(ivp >> 8), p_hi = t - (int64_t)(ivp & 0xffu) - 1;
+        const int64_t s_lo = t + (int64_t)(ivs & 0xffu) + 1, s_hi = t + (int64_t)(ivs >> 8);
+        bool p_found = false, p_done = false, s_found = false, s_done = false;
+#pragma unroll
+        for (int d = 1; d <= kPruneLook; ++d) {
+          const int kp = i - d, ks = i + d;
+          const int2 op = s_e[max(kp, 0)];
+          const int2 os = s_e[min(ks, total - 1)];
+          const bool p_in = kp >= beg, s_in = ks < end;
+          const bool p_past = !p_in || (int64_t)op.x < p_lo;
+          const bool s_past = !s_in || (int64_t)os.x > s_hi;
+          const bool p_hit = !p_past && (int64_t)op.x <= p_hi && ((op.y >> max(j - 1, 0)) & 1);
+          const bool s_hit = !s_past && (int64_t)os.x >= s_lo && ((os.y >> (j + 1)) & 1);
+          p_found = p_found || (!p_done && p_hit);
+          s_found = s_found || (!s_done && s_hit);
+          p_done = p_done || p_past || p_hit;
+          s_done = s_done || s_past || s_hit;
+        }
+        // a side passes when found, undecided, without a node on it, or
+        // reaching past the ticks the block holds whole
+        const bool p_ok = j <= 0 || p_lo <= t_first || p_found || !p_done;
+        const bool s_ok = j >= N - 1 || s_hi >= t_last || s_found || !s_done;
+        const bool keep = (lm & (lm - 1)) != 0u || lm == 0u || (p_ok && s_ok);
+        s_keep[i] = keep ? 1 : 0;
+      }
+      lds_barrier();
+
+      // ranks of the kept entries: thread t's chunk is [8 t, 8 t + 8)
+      const int c0 = tid * kPrunePer;
+      uint32_t kb = 0;
+#pragma unroll
+      for (int q = 0; q < kPrunePer; ++q) kb |= (c0 + q < total && s_keep[c0 + q] ? 1u : 0u) << q;
+      const uint32_t cnt = (uint32_t)__popc(kb);
+      const uint32_t incl = wave_incl_scan(cnt);
+      if (lane == kWave - 1) s_wsum[wave] = incl;
+      lds_barrier();
+      uint32_t before = 0;
+#pragma unroll
+      for (int w = 0; w < kBlock / kWave; ++w) before += w < wave ? s_wsum[w] : 0u;
+      uint32_t r = before + incl - cnt;
+      s_pre[tid] = (int32_t)r;
+      s_kb[tid] = (uint8_t)kb;
+      if (tid == kBlock - 1) s_pre[kBlock] = (int32_t)(r + cnt);
+      int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
+#pragma unroll
+      for (int q = 0; q < kPrunePer; ++q)
+        if ((kb >> q) & 1u) region[r++] = s_e[c0 + q];
+      lds_barrier();
+      // each list's new offset and count: kept entries before its start and end
+      auto rank = [&](int32_t i) -> int32_t {
+        const int c = i / kPrunePer;
+        if (c >= kBlock) return s_pre[kBlock];
+        return s_pre[c] + __popc(s_kb[c] & ((1u << (i - c * kPrunePer)) - 1u));
+      };
+      if (tid < S) {
+        const int32_t a0 = rank(s_off[tid]), z = rank(s_off[tid + 1]);
+        A.list_off[b * S + tid] = a0;
+        A.list_cnt[b * S + tid] = z - a0;
+      }
+    }
+    lds_barrier();  // LDS is rewritten by the next block
   }
 }
 

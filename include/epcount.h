@@ -129,7 +129,8 @@ typedef struct {
   int32_t kernels;      /* bit 0: bit-window Map kernels (tick/list/position), else the
                            scan kernel; bit 1: one lane holds every machine of a
                            (segment, episode); bit 2: sparse segments through the event
-                           filter and the list Map kernel (else the position kernel) */
+                           filter and the list Map kernel (else the position kernel);
+                           bit 3: the filter's lists pruned of entries that cannot act */
   int64_t repairs;      /* repair tuples made for unmatched segment exits */
   int64_t fallbacks;    /* episodes recounted by the whole-stream fallback */
 } ep_stats;
@@ -359,6 +360,8 @@ int64_t ep_segment_cut(int32_t t_min, int32_t t_max, int32_t n_segments, int32_t
  *                     when windows are runs (part of map_ms)
  *   map_filter_ms     the event filter feeding the list Map kernel (part of
  *                     map_ms; 0 when the call does not use it)
+ *   map_prune_ms      the pruning of the filter's lists (part of map_ms; 0
+ *                     when the call does not use them)
  */
 typedef struct {
   double map_ms;
@@ -369,6 +372,7 @@ typedef struct {
   double map_ticks_ms;
   double map_positions_ms;
   double map_filter_ms;
+  double map_prune_ms;
 } ep_profile;
 
 int ep_profile_begin(void);
@@ -382,7 +386,7 @@ int ep_profile_end(ep_profile* out);
  * ep_profile_end() then fills map_ms, the chosen kernel's field and calls
  * (= calls recorded).  Returns EP_ERR_ARG for an unknown kernel or every < 1.
  */
-enum { EP_PROFILE_FILTER = 0, EP_PROFILE_TICKS = 1, EP_PROFILE_POSITIONS = 2 };
+enum { EP_PROFILE_FILTER = 0, EP_PROFILE_TICKS = 1, EP_PROFILE_POSITIONS = 2, EP_PROFILE_PRUNE = 3 };
 int ep_profile_begin_kernel(int32_t which, int32_t every);
 
 /* Static text for a status code. */

@@ -143,6 +143,64 @@ def test_fuzz_large_type_values(fem, split, monkeypatch):
                    "large types trial %d n=%d S=%d %s P=%d" % (trial, n, S, mode, P))
 
 
+def _plant_edges(rng, times, types, ep, lo, hi, per_episode):
+    """Insert chains of each episode whose delays sit on and just past the
+    ends of the intervals (lo + 1 and hi count, lo and hi + 1 do not), some
+    started next to a 4,096-event block edge."""
+    S, N = ep.shape
+    add_t, add_y = [], []
+    edges = times[np.arange(4096, times.size, 4096)] if times.size > 4096 else times[-1:]
+    for e in range(S):
+        for c in range(per_episode):
+            t = int(edges[rng.integers(0, edges.size)]) - int(rng.integers(0, 70)) if c % 3 == 0 \
+                else int(rng.integers(times[0], times[-1] + 1))
+            for j in range(N):
+                add_t.append(t)
+                add_y.append(int(ep[e, j]))
+                if j < N - 1:
+                    choice = rng.integers(0, 5)
+                    d = [lo[e, j] + 1, hi[e, j], lo[e, j], hi[e, j] + 1,
+                         rng.integers(lo[e, j] + 1, hi[e, j] + 1)][choice]
+                    t += int(d)
+    tt = np.concatenate([times, np.array(add_t, np.int32)])
+    yy = np.concatenate([types, np.array(add_y, np.uint16)])
+    o = np.argsort(tt, kind="stable")
+    return tt[o], yy[o]
+
+
+@pytest.mark.parametrize("prune", ["on", "off"])
+def test_list_pruning_windows(fem, prune, monkeypatch):
+    # the list pruning drops entries with no neighbour entry in their windows:
+    # sparse multi-block streams over many types (most entries left out),
+    # chains planted on the interval ends and at block edges, dense and sparse
+    # blocks in time
+    _split_env(monkeypatch, "positions")
+    monkeypatch.setenv("EP_FORCE_PRUNE" if prune == "on" else "EP_NO_PRUNE", "1")
+    rng = np.random.default_rng(59)
+    for trial in range(36):
+        n = int(rng.integers(3000, 21000))
+        n_types = int(rng.integers(8, 400))
+        max_gap = [0, 1, 3, 30, 300][trial % 5]
+        times, types = W.random_stream(rng, n, n_types, max_gap=max_gap)
+        S = int(rng.integers(1, 33))
+        N = int(rng.integers(1, 9))
+        ep = rng.integers(0, n_types, size=(S, N)).astype(np.uint16)
+        if trial % 4 == 0 and N > 2:
+            ep[:, 2] = ep[:, 0]  # a type on two levels
+        hi = rng.integers(1, 64, size=(S, max(N - 1, 0))).astype(np.int32)
+        lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
+        if trial % 3 == 0:
+            lo[:] = 0
+        times, types = _plant_edges(rng, times, types, ep, lo, hi, int(rng.integers(1, 12)))
+        want = oracle.count(times, types, ep, lo, hi)
+        for P in (1, 3, 64):
+            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True)
+            assert st["kernels"] & 4, "the list path was not taken"
+            assert bool(st["kernels"] & 8) == (prune == "on")
+            _check(got, want, "pruning %s trial %d n=%d S=%d N=%d gap<=%d P=%d"
+                   % (prune, trial, times.size, S, N, max_gap, P))
+
+
 def test_empty_stream_and_no_episodes(fem):
     e = np.zeros(0, np.int32)
     got = _gpu(fem, e, e.astype(np.uint16), np.array([[1, 2]], np.uint16), np.array([[0]], np.int32),
@@ -195,12 +253,13 @@ def test_config_small(fem, name):
 
 @pytest.mark.parametrize("layout", ["scan", "machine-lanes", "ticks", "positions", "ticks-machine-lanes",
                                     "position-kernel", "position-kernel-machine-lanes",
-                                    "positions-machine-lanes"])
+                                    "positions-machine-lanes", "positions-unpruned"])
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "longchain"])
 def test_config_small_other_kernels(fem, name, layout, monkeypatch):
     # the same counts from the scan Map kernel (run windows, every event), the
     # tick kernel, the list kernel ('positions' where the call has few
-    # episodes), the position kernel, each with one machine per lane too
+    # episodes; with the lists pruned, or not), the position kernel, each
+    # with one machine per lane too
     if layout == "scan":
         monkeypatch.setenv("EP_FORCE_SCAN", "1")
     if "machine-lanes" in layout:
@@ -210,6 +269,7 @@ def test_config_small_other_kernels(fem, name, layout, monkeypatch):
     if layout.startswith("positions"):
         monkeypatch.setenv("EP_SPLIT", "positions")
         monkeypatch.setenv("EP_FORCE_LIST", "1")
+        monkeypatch.setenv("EP_NO_PRUNE" if layout.endswith("unpruned") else "EP_FORCE_PRUNE", "1")
     if layout.startswith("position-kernel"):
         monkeypatch.setenv("EP_SPLIT", "positions")
         monkeypatch.setenv("EP_NO_LIST", "1")
