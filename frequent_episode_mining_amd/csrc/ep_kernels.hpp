@@ -366,13 +366,15 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
 // (nothing found), at a match, or undecided after kPruneLook entries; an
 // undecided side, a range the block may not hold whole (not strictly between
 // its first and last time) and an entry on several levels count as having
-// the neighbour.  Persistent workgroups loop over blocks, a block's lists
+// the neighbour.  Times are compared relative to the block's first, in 32
+// bits: blocks spanning 2^30 ticks or more are left as they are.  Persistent
+// workgroups loop over blocks, a block's lists
 // read into registers one iteration ahead; a block is staged in LDS, each
 // entry tested by one thread (entries carry their episode in bits 16..), and
 // the kept entries are written back in place, list by list, with new offsets
 // and counts.  A block with more than kPruneCap entries is left as it is.
 constexpr int kPruneCap = 2048;   // entries a block may have to be pruned
-constexpr int kPruneLook = 3;     // entries a neighbour search visits on one side
+constexpr int kPruneLook = 2;     // entries a neighbour search visits on one side
 constexpr int kPrunePer = kPruneCap / kBlock;
 
 struct PruneArgs {
@@ -433,8 +435,10 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
 
   for (; b < A.n_blocks; b += grid) {
     const int32_t total = tot;
-    const int64_t t_first = tf_r, t_last = tl_r;
-    const bool run = total > 0 && total <= kPruneCap;
+    const int32_t tf = tf_r;
+    const int64_t span64 = (int64_t)tl_r - (int64_t)tf_r;
+    const int32_t span = (int32_t)span64;
+    const bool run = total > 0 && total <= kPruneCap && span64 >= 0 && span64 < (1ll << 30);
     if (run) {
 #pragma unroll
       for (int q = 0; q < kPrunePer; ++q) {
@@ -454,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
       // entries tid, tid + kBlock, ...: which of them pass
       for (int i = tid; i < total; i += kBlock) {
         const int2 me = s_e[i];
-        const int64_t t = me.x;
+        const int32_t t = (int32_t)((uint32_t)me.x - (uint32_t)tf);  // 0 .. span
         const int e = min((int)((uint32_t)me.y >> 16), S - 1);
         const uint32_t lm = (uint32_t)me.y & 0xffffu;
         const int j = __ffs((int)lm) - 1;
@@ -463,19 +467,21 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
         // node j+1 in [t + lo + 1, t + hi]; each decided by the nearest
         // kPruneLook entries of the list on its side
         const uint32_t ivp = s_iv[e * 16 + max(j - 1, 0)], ivs = s_iv[e * 16 + max(j, 0)];
-        const int64_t p_lo = t - (int64_t)(ivp >> 8), p_hi = t - (int64_t)(ivp & 0xffu) - 1;
-        const int64_t s_lo = t + (int64_t)(ivs & 0xffu) + 1, s_hi = t + (int64_t)(ivs >> 8);
+        const int32_t p_lo = t - (int32_t)(ivp >> 8), p_hi = t - (int32_t)(ivp & 0xffu) - 1;
+        const int32_t s_lo = t + (int32_t)(ivs & 0xffu) + 1, s_hi = t + (int32_t)(ivs >> 8);
         bool p_found = false, p_done = false, s_found = false, s_done = false;
 #pragma unroll
         for (int d = 1; d <= kPruneLook; ++d) {
           const int kp = i - d, ks = i + d;
           const int2 op = s_e[max(kp, 0)];
           const int2 os = s_e[min(ks, total - 1)];
+          const int32_t tp = (int32_t)((uint32_t)op.x - (uint32_t)tf);
+          const int32_t ts = (int32_t)((uint32_t)os.x - (uint32_t)tf);
           const bool p_in = kp >= beg, s_in = ks < end;
-          const bool p_past = !p_in || (int64_t)op.x < p_lo;
-          const bool s_past = !s_in || (int64_t)os.x > s_hi;
-          const bool p_hit = !p_past && (int64_t)op.x <= p_hi && ((op.y >> max(j - 1, 0)) & 1);
-          const bool s_hit = !s_past && (int64_t)os.x >= s_lo && ((os.y >> (j + 1)) & 1);
+          const bool p_past = !p_in || tp < p_lo;
+          const bool s_past = !s_in || ts > s_hi;
+          const bool p_hit = !p_past && tp <= p_hi && ((op.y >> max(j - 1, 0)) & 1);
+          const bool s_hit = !s_past && ts >= s_lo && ((os.y >> (j + 1)) & 1);
           p_found = p_found || (!p_done && p_hit);
           s_found = s_found || (!s_done && s_hit);
           p_done = p_done || p_past || p_hit;
@@ -483,8 +489,8 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
         }
         // a side passes when found, undecided, without a node on it, or
         // reaching past the ticks the block holds whole
-        const bool p_ok = j <= 0 || p_lo <= t_first || p_found || !p_done;
-        const bool s_ok = j >= N - 1 || s_hi >= t_last || s_found || !s_done;
+        const bool p_ok = j <= 0 || p_lo <= 0 || p_found || !p_done;
+        const bool s_ok = j >= N - 1 || s_hi >= span || s_found || !s_done;
         const bool keep = (lm & (lm - 1)) != 0u || lm == 0u || (p_ok && s_ok);
         s_keep[i] = keep ? 1 : 0;
       }
