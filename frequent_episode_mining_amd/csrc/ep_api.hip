@@ -659,6 +659,39 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
             win_name(L.win), L.bits ? "bits" : "scan", L.all_mach ? "class" : "machine", L.M, L.G, L.R,
             L.CH, L.lds, (long long)max_span);
 
+  // tick kernel: episodes ordered by their doubling steps, so that an episode
+  // group of narrow windows runs fewer steps than the call's widest needs
+  // (only where the steps differ, there are several groups, and the tick
+  // kernel's work, about episodes x events, is large enough to repay the
+  // ordering's host time)
+  std::vector<int32_t> ep_perm, group_k;
+  if (L.bits && L.split != 2 && S > L.G &&
+      ((double)S * (double)n_events >= 4294967296.0 || getenv("EP_FORCE_GROUP_STEPS"))) {
+    std::vector<int32_t> steps((size_t)S, 0);
+    int32_t lo_k = INT32_MAX, hi_k = 0;
+    for (int64_t e = 0; e < S; ++e) {
+      int32_t k = 0;
+      for (int j = 0; j < N - 1; ++j)
+        k = std::max(k, dil_steps((uint32_t)episodes.t_low[e * (N - 1) + j],
+                                  (uint32_t)episodes.t_high[e * (N - 1) + j]));
+      steps[(size_t)e] = k;
+      lo_k = std::min(lo_k, k);
+      hi_k = std::max(hi_k, k);
+    }
+    if (lo_k < hi_k && !getenv("EP_NO_GROUP_STEPS")) {
+      // a counting sort (steps are 0 .. 6), stable
+      int64_t at[8] = {0};
+      for (int64_t e = 0; e < S; ++e) ++at[steps[(size_t)e] + 1];
+      for (int k = 1; k < 8; ++k) at[k] += at[k - 1];
+      ep_perm.resize((size_t)S);
+      for (int64_t e = 0; e < S; ++e) ep_perm[(size_t)at[steps[(size_t)e]]++] = (int32_t)e;
+      const int64_t groups = (S + L.G - 1) / L.G;
+      group_k.assign((size_t)groups, 0);
+      for (int64_t i = 0; i < S; ++i)
+        group_k[(size_t)(i / L.G)] = std::max(group_k[(size_t)(i / L.G)], steps[(size_t)ep_perm[(size_t)i]]);
+    }
+  }
+
   // ---- scratch layout (one stream-ordered allocation)
   const size_t sz_types = align_up(sizeof(uint16_t) * S * N, 256);
   const size_t sz_lohi = align_up(sizeof(int32_t) * S * std::max(N - 1, 1), 256);
@@ -668,8 +701,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_rank = 1024;                       // set bits before each 64-bit word
   const size_t sz_seps = L.list ? sizeof(uint32_t) * 256 : 0;
   const size_t sz_slv = L.list ? align_up(sizeof(uint16_t) * 256 * S, 256) : 0;
+  const size_t sz_perm = align_up(sizeof(int32_t) * ep_perm.size(), 256);
+  const size_t sz_gk = align_up(sizeof(int32_t) * group_k.size(), 256);
   const size_t host_bytes =
-      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv;
+      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv + sz_perm + sz_gk;
   // (+ slack: the list kernel's aligned batches may read two entries past the
   // last block's region)
   const size_t sz_lists = L.list ? align_up((size_t)list_bytes + 4 * sizeof(int2), 256) : 0;
@@ -703,6 +738,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     uint8_t* d_rank = (uint8_t*)(ws + off); off += sz_rank;
     uint32_t* d_seps = (uint32_t*)(ws + off); off += sz_seps;
     uint16_t* d_slv = (uint16_t*)(ws + off); off += sz_slv;
+    int32_t* d_perm = (int32_t*)(ws + off); off += sz_perm;
+    int32_t* d_gk = (int32_t*)(ws + off); off += sz_gk;
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
@@ -745,6 +782,11 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         char* at = host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank;
         memcpy(at, slot_eps, sz_seps);
         memcpy(at + sz_seps, slot_levels, sizeof(uint16_t) * 256 * S);
+      }
+      if (!ep_perm.empty()) {
+        char* at = host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv;
+        memcpy(at, ep_perm.data(), sizeof(int32_t) * ep_perm.size());
+        memcpy(at + sz_perm, group_k.data(), sizeof(int32_t) * group_k.size());
       }
     }
 
@@ -812,6 +854,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ma.S = S; ma.P = P; ma.M = L.M; ma.G = L.G; ma.R = L.R; ma.CH = L.CH;
     ma.U = U; ma.n_machines = L.n_machines;
     ma.max_span = max_span; ma.CW = L.CW; ma.split = L.split; ma.dil_steps = dil_k;
+    ma.ep_perm = ep_perm.empty() ? nullptr : d_perm;
+    ma.group_k = ep_perm.empty() ? nullptr : d_gk;
     ma.lists = d_lists; ma.list_off = d_loff; ma.list_cnt = d_lcnt; ma.max_share = max_share;
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;

@@ -378,6 +378,11 @@ struct MapArgs {
   int32_t split;       // 0: each segment to the kernel segment_uses_ticks picks; 1: all to
                        // the tick kernel; 2: all to the position kernel
   int32_t dil_steps;   // tick kernel: doubling steps of the widest interval of the call
+  // tick kernel, optional: episode group eg covers episodes ep_perm[eg * G ..
+  // eg * G + G) and runs group_k[eg] doubling steps (episodes ordered by their
+  // steps, so that groups of narrow windows skip the wide ones' steps)
+  const int32_t* ep_perm;
+  const int32_t* group_k;
   const int2* lists;        // list kernel: per event block, each episode's entries {time, levels}
   const int32_t* list_off;  // [blocks * S] start of episode e's entries in block b's region
   const int32_t* list_cnt;  // [blocks * S] their number
@@ -1285,7 +1290,6 @@ void map_ticks_kernel(MapArgs A) {
   const int64_t p = seg_group * A.R + r_idx;
   const bool seg_here = tid < A.R * per_seg && p < A.P && segment_uses_ticks(A, p, N);
   const int CW = A.CW;
-  const int K = A.dil_steps;
   const int CE = kPer * nthr;
   const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
 
@@ -1314,8 +1318,10 @@ void map_ticks_kernel(MapArgs A) {
   const int64_t eg_step = fit ? A.eg_blocks : A.n_egroups;
 
   for (int64_t eg = eg_id; eg < A.n_egroups; eg += eg_step) {
-    const int64_t e = eg * A.G + g;
-    const bool active = seg_here && e < A.S;
+    const int64_t eo = eg * A.G + g;
+    const bool active = seg_here && eo < A.S;
+    const int64_t e = (A.ep_perm && eo < A.S) ? A.ep_perm[eo] : eo;
+    const int K = A.group_k ? A.group_k[eg] : A.dil_steps;
     if (tid < A.R) {
       const int64_t pp = seg_group * A.R + tid;
       s_ev[tid] = s_seg_end[tid] ? A.seg_beg[pp] : 0;

@@ -201,6 +201,29 @@ def test_list_pruning_windows(fem, prune, monkeypatch):
                    % (prune, trial, times.size, S, N, max_gap, P))
 
 
+@pytest.mark.parametrize("order", ["grouped", "plain"])
+def test_tick_kernel_episode_groups_by_steps(fem, order, monkeypatch):
+    # the tick kernel may take episodes ordered by their doubling steps, each
+    # workgroup running its own group's steps: many episodes with windows of
+    # every width (1 to 63 ticks), mixed in the table
+    monkeypatch.setenv("EP_SPLIT", "ticks")
+    monkeypatch.setenv("EP_FORCE_GROUP_STEPS" if order == "grouped" else "EP_NO_GROUP_STEPS", "1")
+    rng = np.random.default_rng(67)
+    for trial in range(6):
+        n = int(rng.integers(2000, 20000))
+        n_types = int(rng.integers(2, 12))
+        times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(1, 6)))
+        N = int(rng.integers(2, 5))
+        S = int(rng.integers(300, 1400))
+        ep = rng.integers(0, n_types, size=(S, N)).astype(np.uint16)
+        hi = rng.integers(1, 64, size=(S, N - 1)).astype(np.int32)
+        lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
+        want = oracle.count(times, types, ep, lo, hi)
+        for P in (0, 7, 64):
+            got = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P)
+            _check(got, want, "steps %s trial %d n=%d S=%d N=%d P=%d" % (order, trial, n, S, N, P))
+
+
 def test_empty_stream_and_no_episodes(fem):
     e = np.zeros(0, np.int32)
     got = _gpu(fem, e, e.astype(np.uint16), np.array([[1, 2]], np.uint16), np.array([[0]], np.int32),
