@@ -717,8 +717,11 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_nslots = align_up(sizeof(int32_t) * (size_t)P * S, 256);  // also nmap
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
+  // closure misses queued for repair_kernel (more are repaired where found)
+  const int64_t queue_cap = P > 1 ? 65536 : 0;
+  const size_t sz_queue = align_up(sizeof(uint64_t) * (size_t)queue_cap, 256);
   const size_t total =
-      host_bytes + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt + sz_lists +
+      host_bytes + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt + sz_queue + sz_lists +
       2 * sz_lidx;
 
   mark();  // plan
@@ -751,6 +754,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ts.T0 = d_t0; ts.TX = d_tx; ts.nmap = d_nmap; ts.nslots = d_nslots; ts.P = P; ts.slots = L.slots;
     int32_t* d_flags = (int32_t*)(ws + off); off += sz_flags;
     unsigned long long* d_cnt = (unsigned long long*)(ws + off); off += sz_cnt;
+    uint64_t* d_queue = (uint64_t*)(ws + off); off += sz_queue;
     int2* d_lists = (int2*)(ws + off); off += sz_lists;
     int32_t* d_loff = (int32_t*)(ws + off); off += sz_lidx;
     int32_t* d_lcnt = (int32_t*)(ws + off); off += sz_lidx;
@@ -958,6 +962,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       c.tau = d_tau; c.seg_beg = d_beg; c.seg_end = d_end;
       c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
       c.S = S; c.P = P;
+      c.queue = nullptr; c.queue_cap = 0; c.queue_n = c.queue_head = nullptr; c.repair_blocks = 0;
       stra.entry = sh->entry; stra.total = sh->total; stra.reset_out = sh->reset_out;
       stra.n = n_events; stra.t_end = sh->t_end; stra.max_span = max_span;
       if (P > 1 && Lr->stream_entry(stra, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
@@ -987,6 +992,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       c.tau = d_tau; c.seg_beg = d_beg; c.seg_end = d_end;
       c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
       c.S = S; c.P = P;
+      c.queue = nullptr; c.queue_cap = 0; c.queue_n = c.queue_head = nullptr; c.repair_blocks = 0;
       ra.fallbacks = d_cnt + 1; ra.out = out_counts; ra.n = n_events;
       if (Lr->reduce(ra, L.win, dim3((unsigned)S), dim3((unsigned)members), lds, stream) !=
           hipSuccess) {
@@ -1002,6 +1008,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
       ca.ts = ts; ca.flags = d_flags; ca.repairs = d_cnt;
       ca.S = S; ca.P = P;
+      ca.queue = d_queue; ca.queue_cap = getenv("EP_NO_REPAIR_QUEUE") ? 0 : queue_cap;
+      ca.queue_n = d_cnt + 2; ca.queue_head = d_cnt + 3;
+      ca.repair_blocks = info->cu_count * 2;
       if (Lr->closure(ca, L.win, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;

@@ -1812,6 +1812,14 @@ struct ClosureArgs {
   unsigned long long* repairs;  // repair-tuple counter
   int64_t S;
   int32_t P;
+  // unmatched exits queued for repair_kernel: item << 5 | machine, queue_n
+  // of them (slots past queue_cap are repaired where they are found);
+  // queue_head hands them out
+  uint64_t* queue;
+  int64_t queue_cap;
+  unsigned long long* queue_n;
+  unsigned long long* queue_head;
+  int32_t repair_blocks;  // workgroups of repair_kernel
 };
 
 // The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
@@ -1847,6 +1855,38 @@ __device__ bool has_map_key(const ClosureArgs& A, int64_t q, int64_t e, int32_t 
   return hit;
 }
 
+// Repairs one unmatched exit (machine k of boundary p of episode e) by the
+// whole wave: a machine reset at the exit runs over segment p + 1, and on
+// while its own exit finds no key in the next segment.
+template <int N, class Mach>
+__device__ void repair_exit(const ClosureArgs& A, const typename Mach::Params& prm, int64_t e, int64_t p,
+                            int k, int lane) {
+  int32_t x_off = A.ts.at(e, p, k)->b;
+  int64_t q = p + 1;
+  for (;;) {
+    if (x_off <= 0) {  // a sentinel exit always has a sentinel key; never repair it
+      if (lane == 0) atomicOr(&A.flags[e], 1);
+      break;
+    }
+    const Tuple tu = repair_tuple<Mach>(A, prm, q, A.tau[q] + x_off);
+    int slot = 0;
+    if (lane == 0) slot = atomicAdd(&A.ts.nslots[A.ts.idx(e, q)], 1);
+    slot = __shfl(slot, 0);
+    if (slot >= A.ts.slots) {
+      if (lane == 0) atomicOr(&A.flags[e], 1);
+      break;
+    }
+    if (lane == 0) {
+      *A.ts.at(e, q, slot) = tu;
+      atomicAdd(A.repairs, 1ull);
+    }
+    if (q + 1 >= A.P) break;
+    if (has_map_key<N>(A, q + 1, e, tu.b)) break;
+    x_off = tu.b;
+    ++q;
+  }
+}
+
 template <int N, class Mach>
 __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
   // items episode-major: consecutive lanes take consecutive boundaries of one
@@ -1877,6 +1917,21 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
       for (int j = 0; j < k; ++j) dup |= exits[j] == exits[k];
       if (k < nl && !hit && !dup) missing |= 1u << k;
     }
+    // queue the misses for repair_kernel, which spreads them over every
+    // wave; those past the queue's capacity are repaired below
+    if (missing != 0u && A.queue_cap > 0) {
+      const uint32_t n_m = (uint32_t)__popc(missing);
+      const unsigned long long base = atomicAdd(A.queue_n, (unsigned long long)n_m);
+      uint32_t left = 0, i = 0;
+      for (uint32_t m = missing; m; m &= m - 1, ++i) {
+        const int k = __ffs((int)m) - 1;
+        if (base + i < (unsigned long long)A.queue_cap)
+          A.queue[base + i] = (uint64_t)item << 5 | (uint64_t)k;
+        else
+          left |= 1u << k;
+      }
+      missing = left;
+    }
   }
   uint64_t wmask = __ballot(missing != 0u);
   const int lane = threadIdx.x & (kWave - 1);
@@ -1892,31 +1947,31 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
     while (miss != 0u) {
       const int k = __ffs((int)miss) - 1;
       miss &= miss - 1;
-      int32_t x_off = A.ts.at(e, p, k)->b;
-      int64_t q = p + 1;
-      for (;;) {
-        if (x_off <= 0) {  // a sentinel exit always has a sentinel key; never repair it
-          if (lane == 0) atomicOr(&A.flags[e], 1);
-          break;
-        }
-        const Tuple tu = repair_tuple<Mach>(A, prm, q, A.tau[q] + x_off);
-        int slot = 0;
-        if (lane == 0) slot = atomicAdd(&A.ts.nslots[A.ts.idx(e, q)], 1);
-        slot = __shfl(slot, 0);
-        if (slot >= A.ts.slots) {
-          if (lane == 0) atomicOr(&A.flags[e], 1);
-          break;
-        }
-        if (lane == 0) {
-          *A.ts.at(e, q, slot) = tu;
-          atomicAdd(A.repairs, 1ull);
-        }
-        if (q + 1 >= A.P) break;
-        if (has_map_key<N>(A, q + 1, e, tu.b)) break;
-        x_off = tu.b;
-        ++q;
-      }
+      repair_exit<N, Mach>(A, prm, e, p, k, lane);
     }
+  }
+}
+
+// The queued repairs, one at a time per wave, taken in order from a shared
+// head: every wave leaves once the head has passed the queue's end.
+template <int N, class Mach>
+__global__ __launch_bounds__(kBlock) void repair_kernel(ClosureArgs A) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const unsigned long long n = *A.queue_n;
+  const unsigned long long count = n < (unsigned long long)A.queue_cap ? n : (unsigned long long)A.queue_cap;
+  for (;;) {
+    unsigned long long idx = 0;
+    if (lane == 0) idx = atomicAdd(A.queue_head, 1ull);
+    idx = (unsigned long long)__shfl((long long)idx, 0);
+    if (idx >= count) break;
+    const uint64_t w = A.queue[idx];
+    const int64_t it = (int64_t)(w >> 5);
+    const int k = (int)(w & 31u);
+    const int64_t e = it / (A.P - 1);
+    const int64_t p = it - e * (A.P - 1);
+    typename Mach::Params prm;
+    prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
+    repair_exit<N, Mach>(A, prm, e, p, k, lane);
   }
 }
 

@@ -358,8 +358,13 @@ def test_config_small_separate_closure_and_tree(fem, name, monkeypatch):
         assert st["fallbacks"] == 0
 
 
-def test_fuzz_separate_closure_and_tree(fem, monkeypatch):
+@pytest.mark.parametrize("repairs", ["queued", "inline"])
+def test_fuzz_separate_closure_and_tree(fem, repairs, monkeypatch):
+    # misses are queued for the repair kernel, or (past the queue's capacity,
+    # forced here) repaired by the closure kernel where they are found
     monkeypatch.setenv("EP_NO_REDUCE", "1")
+    if repairs == "inline":
+        monkeypatch.setenv("EP_NO_REPAIR_QUEUE", "1")
     rng = np.random.default_rng(37)
     for trial in range(30):
         n = int(rng.integers(1, 400))
