@@ -1959,6 +1959,7 @@ __global__ __launch_bounds__(kBlock) void repair_kernel(ClosureArgs A) {
   const int lane = threadIdx.x & (kWave - 1);
   const unsigned long long n = *A.queue_n;
   const unsigned long long count = n < (unsigned long long)A.queue_cap ? n : (unsigned long long)A.queue_cap;
+  if (count == 0) return;  // (no wave touches the head: nothing was queued)
   for (;;) {
     unsigned long long idx = 0;
     if (lane == 0) idx = atomicAdd(A.queue_head, 1ull);
