@@ -345,6 +345,37 @@ def test_ptpe_config_full_size(fem):
     assert want[0] >= 200  # the planted chains
 
 
+@pytest.mark.parametrize("name", ["mapconcat", "longchain"])
+def test_list_configs_full_size(fem, name):
+    # the few-episode workloads at full size, with the workload's segment count
+    # as bench.py times them: mapconcat through the filter, the list pruning
+    # and the list kernel; longchain through the filter and the list kernel
+    wl = W.make(name)
+    _log("config %s full: n=%d S=%d P=%d" % (name, wl.n_events, wl.n_episodes, wl.n_segments))
+    t0 = time.time()
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    _log("oracle %.1fs" % (time.time() - t0))
+    got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "mapconcat", wl.n_segments,
+                   stats=True)
+    _log("gpu plan %s" % st)
+    assert st["kernels"] & 4
+    assert bool(st["kernels"] & 8) == (name == "mapconcat")
+    _check(got, want, "%s full" % name)
+
+
+def test_level2_full_size_sampled(fem):
+    # the level-2 sweep at full size, AUTO launch (episodes grouped by their
+    # doubling steps, closure misses queued for the repair kernel), checked on
+    # evenly spaced episodes
+    wl = W.make("level2")
+    got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "auto", stats=True)
+    _log("level2 full: plan %s" % st)
+    assert st["repairs"] > 0
+    idx = np.linspace(0, wl.n_episodes - 1, 96).astype(int)
+    want = oracle.count(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx], wl.t_high[idx])
+    _check(got[idx], want, "level2 full sampled")
+
+
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "level2", "longchain"])
 def test_config_small_separate_closure_and_tree(fem, name, monkeypatch):
     # the three-launch path (closure kernel, tree launches, finish kernel) that
