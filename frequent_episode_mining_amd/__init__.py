@@ -37,13 +37,36 @@ class EpEpisodes(ctypes.Structure):
 class EpStats(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
                 ("max_runs", ctypes.c_int32), ("kernels", ctypes.c_int32),
-                ("repairs", ctypes.c_int64), ("fallbacks", ctypes.c_int64)]
+                ("repairs", ctypes.c_int64), ("fallbacks", ctypes.c_int64),
+                ("groups", ctypes.c_int32), ("pad", ctypes.c_int32)]
 
 
 class EpOptions(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_segments", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("upper_only", ctypes.c_int32),
-                ("stats", ctypes.POINTER(EpStats))]
+                ("stats", ctypes.POINTER(EpStats)), ("plan", ctypes.c_uint32),
+                ("pad", ctypes.c_int32)]
+
+
+# EP_PLAN_* switches of ep_options.plan: which kernels produce the (same) counts
+PLAN = {"ticks": 1 << 0, "positions": 1 << 1, "list": 1 << 2, "no-list": 1 << 3,
+        "prune": 1 << 4, "no-prune": 1 << 5, "group-steps": 1 << 6, "no-group-steps": 1 << 7,
+        "run-windows": 1 << 8, "ring-windows": 1 << 9, "machine-lanes": 1 << 10,
+        "no-reduce": 1 << 11, "no-repair-queue": 1 << 12, "recount": 1 << 13, "no-split": 1 << 14}
+
+
+def plan_bits(plan) -> int:
+    """EP_PLAN_* bits from an int or an iterable of PLAN names."""
+    if plan is None:
+        return 0
+    if isinstance(plan, int):
+        return plan
+    if isinstance(plan, str):
+        plan = [plan]
+    bits = 0
+    for name in plan:
+        bits |= PLAN[name]
+    return bits
 
 
 class EpMineOptions(ctypes.Structure):
@@ -203,21 +226,22 @@ def _on_device(device, fn):
 def _stats_dict(st):
     return {"mode": MODE_NAMES.get(st.mode, st.mode), "n_segments": st.n_segments,
             "max_runs": st.max_runs, "kernels": st.kernels, "repairs": st.repairs,
-            "fallbacks": st.fallbacks}
+            "fallbacks": st.fallbacks, "groups": st.groups}
 
 
 def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str = "auto",
                    n_segments: int = 0, validate: bool = False, stats: bool = False,
-                   upper_only: bool = False, out=None, stream=None):
+                   upper_only: bool = False, plan=None, out=None, stream=None):
     """Counts of S episodes over one GPU-resident event stream.
 
     times: int32 [n] GPU tensor, non-decreasing.  types: uint16 (or int16, same
     bits) [n] GPU tensor.  ep_types: [S, N] host array (or an EpisodeTable);
     t_low/t_high: [S, N-1] host arrays.  ``upper_only`` counts the relaxed
-    episodes (every lower bound taken as 0; ``t_low`` may be None).  Returns an
-    int64 [S] GPU tensor (and the ep_stats dict if ``stats``).  Enqueued on
-    ``stream`` (default: torch's current stream); ``validate``/``stats``
-    synchronise that stream.
+    episodes (every lower bound taken as 0; ``t_low`` may be None).  ``plan``:
+    EP_PLAN_* switches (names of ``PLAN`` or an int) choosing the kernels.
+    Returns an int64 [S] GPU tensor (and the ep_stats dict if ``stats``).
+    Enqueued on ``stream`` (default: torch's current stream);
+    ``validate``/``stats`` synchronise that stream.
     """
     import torch
     if upper_only and t_low is None and not isinstance(ep_types, EpisodeTable):
@@ -232,7 +256,7 @@ def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str
     lib = load_library()
     st = EpStats()
     opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), int(bool(upper_only)),
-                    ctypes.pointer(st) if stats else None)
+                    ctypes.pointer(st) if stats else None, plan_bits(plan), 0)
     status = _on_device(times.device, lambda: lib.ep_count_episodes_ex(
         tp, yp, n, table.as_struct(), S, op, sp, ctypes.byref(opt)))
     _check(status)
@@ -243,7 +267,7 @@ def count_episodes(times, types, ep_types, t_low=None, t_high=None, *, mode: str
 
 def count_two_pass(times, types, ep_types, t_low=None, t_high=None, *, threshold: int,
                    mode: str = "auto", n_segments: int = 0, validate: bool = False,
-                   stats: bool = False, stream=None):
+                   stats: bool = False, plan=None, stream=None):
     """Two-pass elimination (A2 then A1) for a support threshold.
 
     Returns ``(counts, upper, n_kept)`` (plus the second pass's ep_stats dict
@@ -265,7 +289,7 @@ def count_two_pass(times, types, ep_types, t_low=None, t_high=None, *, threshold
     lib = load_library()
     st = EpStats()
     opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), 0,
-                    ctypes.pointer(st) if stats else None)
+                    ctypes.pointer(st) if stats else None, plan_bits(plan), 0)
     kept = ctypes.c_int64(0)
     status = _on_device(times.device, lambda: lib.ep_count_two_pass(
         tp, yp, n, table.as_struct(), S, int(threshold), cp, up, ctypes.byref(kept), sp,
@@ -327,7 +351,8 @@ class EpisodeStream:
     """
 
     def __init__(self, ep_types, t_low=None, t_high=None, *, mode: str = "auto", n_segments: int = 0,
-                 validate: bool = False, upper_only: bool = False, device="cuda", stream=None):
+                 validate: bool = False, upper_only: bool = False, plan=None, device="cuda",
+                 stream=None):
         import torch
         if upper_only and t_low is None and not isinstance(ep_types, EpisodeTable):
             t_low = np.zeros_like(np.asarray(t_high, dtype=np.int32))
@@ -337,7 +362,8 @@ class EpisodeStream:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self._lib = load_library()
         self._handle = ctypes.c_void_p()
-        opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), int(bool(upper_only)), None)
+        opt = EpOptions(MODES[mode], int(n_segments), int(bool(validate)), int(bool(upper_only)), None,
+                        plan_bits(plan), 0)
         sp = _stream_handle(stream, self.device)
         status = _on_device(self.device, lambda: self._lib.ep_stream_create(
             self.table.as_struct(), self.table.n_episodes, ctypes.byref(opt), sp, ctypes.byref(self._handle)))

@@ -74,6 +74,8 @@ struct DeviceInfo {
   // resident lanes per CU of the tick kernel with one lane per (segment,
   // episode), as its registers allow (the planner's T_B * B_MP), by N
   int plan_lanes[EP_MAX_NODES + 1] = {};
+  // resident list-pruning workgroups per CU (0: not queried yet)
+  int prune_per_cu = 0;
 };
 
 std::mutex g_info_mu;
@@ -118,6 +120,13 @@ struct ScratchPool {
 };
 ScratchPool g_scratch[64];
 
+// Hands a held block back after a failed acquire (under the pool's lock).
+int scratch_abandon(ScratchPool& pool, ScratchBlock* b, int status) {
+  std::lock_guard<std::mutex> lock(pool.mu);
+  b->held = false;
+  return status;
+}
+
 int scratch_acquire(int dev, size_t bytes, hipStream_t stream, ScratchBlock** out) {
   ScratchPool& pool = g_scratch[dev];
   ScratchBlock* b = nullptr;
@@ -137,31 +146,23 @@ int scratch_acquire(int dev, size_t bytes, hipStream_t stream, ScratchBlock** ou
     }
     b->held = true;
   }
-  if (b->used && b->last_stream != stream && hipStreamWaitEvent(stream, b->ev, 0) != hipSuccess) {
-    b->held = false;
-    return EP_ERR_HIP;
-  }
+  if (b->used && b->last_stream != stream && hipStreamWaitEvent(stream, b->ev, 0) != hipSuccess)
+    return scratch_abandon(pool, b, EP_ERR_HIP);
   if (b->cap < bytes) {
     // the old block may still be read by kernels queued on `stream` (ordered
     // after the wait above): free it stream-ordered, then take a bigger one
-    if (b->ptr && hipFreeAsync(b->ptr, stream) != hipSuccess) {
-      b->held = false;
-      return EP_ERR_HIP;
-    }
+    if (b->ptr && hipFreeAsync(b->ptr, stream) != hipSuccess) return scratch_abandon(pool, b, EP_ERR_HIP);
     b->ptr = nullptr;
     b->cap = 0;
     const size_t cap = bytes + bytes / 4;
     if (hipMallocAsync(&b->ptr, cap, stream) != hipSuccess || !b->ptr) {
       b->ptr = nullptr;
-      b->held = false;
-      return EP_ERR_WORKSPACE;
+      return scratch_abandon(pool, b, EP_ERR_WORKSPACE);
     }
     b->cap = cap;
   }
-  if (!b->ev && hipEventCreateWithFlags(&b->ev, hipEventDisableTiming) != hipSuccess) {
-    b->held = false;
-    return EP_ERR_HIP;
-  }
+  if (!b->ev && hipEventCreateWithFlags(&b->ev, hipEventDisableTiming) != hipSuccess)
+    return scratch_abandon(pool, b, EP_ERR_HIP);
   *out = b;
   return EP_OK;
 }
@@ -303,11 +304,17 @@ extern "C" int ep_plan(int64_t n_episodes, int32_t n_nodes, int64_t n_events, in
 
 namespace {
 
+// EP_LOG (read once): print each call's plan and the HIP failures on stderr
+bool log_on() {
+  static const bool on = getenv("EP_LOG") != nullptr;
+  return on;
+}
+
 #define EP_HIP(call)                                      \
   do {                                                    \
     hipError_t err_ = (call);                             \
     if (err_ != hipSuccess) {                             \
-      if (getenv("EP_LOG"))                               \
+      if (log_on())                                       \
         fprintf(stderr, "epcount: %s failed: %s\n", #call, \
                 hipGetErrorString(err_));                 \
       return EP_ERR_HIP;                                  \
@@ -345,7 +352,7 @@ int staging_acquire(int dev, size_t bytes, char** out, const void** dout) {
     s.pending = false;
   }
   if (status == EP_OK && s.cap < bytes) {
-    if (s.buf) hipHostFree(s.buf);
+    if (s.buf) (void)hipHostFree(s.buf);
     s.buf = nullptr;
     s.dbuf = nullptr;
     s.cap = 0;
@@ -354,7 +361,7 @@ int staging_acquire(int dev, size_t bytes, char** out, const void** dout) {
       s.buf = nullptr;
       status = EP_ERR_HIP;
     } else if (hipHostGetDevicePointer(&s.dbuf, s.buf, 0) != hipSuccess || !s.dbuf) {
-      hipHostFree(s.buf);
+      (void)hipHostFree(s.buf);
       s.buf = nullptr;
       s.dbuf = nullptr;
       status = EP_ERR_HIP;
@@ -396,6 +403,7 @@ const char* win_name(int w) {
     case kRuns4: return "runs4";
     case kBits32: return "bits32";
     case kBits64: return "bits64";
+    case kRing: return "ring";
     default: return "?";
   }
 }
@@ -441,9 +449,80 @@ struct StreamHook {
   int64_t t_end;
 };
 
+// Window kind each episode needs: bit windows when every t_high <= 63, run
+// windows in registers when every interval's live-run bound
+// floor(t_high / (t_high - t_low + 1)) + 1 is at most EP_MAX_RUNS, ring
+// windows otherwise.
+enum { kClsBits = 0, kClsRuns = 1, kClsRing = 2, kNumCls = 3 };
+
+// Largest ring-window arena a call plans for: MapConcatenate's P is lowered
+// until every Map machine's rings fit (a caller's fixed P is kept).
+constexpr double kRingBudget = 2.0 * (1ull << 30);
+
 int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
-                        hipStream_t stream, const ep_options* opt, const StreamHook* sh = nullptr) {
+                        hipStream_t stream, const ep_options* opt, const StreamHook* sh = nullptr,
+                        const int32_t* out_map = nullptr);
+
+// A call whose episodes need different window kinds: one sub-call per kind,
+// each over its own episodes and writing their counts through an index map
+// into the caller's out_counts (the sub-calls' outputs are disjoint).
+int count_split(const int32_t* times, const uint16_t* types, int64_t n_events, ep_episodes episodes,
+                int64_t S, int64_t* out_counts, hipStream_t stream, const ep_options* opt,
+                const std::vector<uint8_t>& cls) {
+  const int32_t N = episodes.n_nodes;
+  const int NI = N - 1;
+  ep_stats acc{};
+  int64_t most = -1;
+  bool first = true;
+  for (int c = 0; c < kNumCls; ++c) {
+    std::vector<int32_t> idx;
+    for (int64_t e = 0; e < S; ++e)
+      if (cls[(size_t)e] == c) idx.push_back((int32_t)e);
+    if (idx.empty()) continue;
+    const int64_t Sc = (int64_t)idx.size();
+    std::vector<uint16_t> ty((size_t)(Sc * N));
+    std::vector<int32_t> lo((size_t)(Sc * NI)), hi((size_t)(Sc * NI));
+    for (int64_t i = 0; i < Sc; ++i) {
+      const int64_t e = idx[(size_t)i];
+      memcpy(ty.data() + i * N, episodes.types + e * N, sizeof(uint16_t) * N);
+      if (NI > 0) {
+        memcpy(lo.data() + i * NI, episodes.t_low + e * NI, sizeof(int32_t) * NI);
+        memcpy(hi.data() + i * NI, episodes.t_high + e * NI, sizeof(int32_t) * NI);
+      }
+    }
+    ep_episodes sub{N, ty.data(), NI > 0 ? lo.data() : nullptr, NI > 0 ? hi.data() : nullptr};
+    ep_options o{};
+    if (opt) o = *opt;
+    o.upper_only = 0;  // the table passed in already holds the relaxed bounds
+    o.validate = first && opt ? opt->validate : 0;
+    ep_stats st{};
+    o.stats = (opt && opt->stats) ? &st : nullptr;
+    if (int status = count_episodes_impl(times, types, n_events, sub, Sc, out_counts, stream, &o, nullptr,
+                                         idx.data()))
+      return status;
+    first = false;
+    if (opt && opt->stats) {
+      if (Sc > most) {
+        most = Sc;
+        acc.mode = st.mode;
+        acc.n_segments = st.n_segments;
+        acc.max_runs = st.max_runs;
+      }
+      acc.kernels |= st.kernels;
+      acc.repairs += st.repairs;
+      acc.fallbacks += st.fallbacks;
+      acc.groups += 1;
+    }
+  }
+  if (opt && opt->stats) *opt->stats = acc;
+  return EP_OK;
+}
+
+int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
+                        ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                        hipStream_t stream, const ep_options* opt, const StreamHook* sh,
+                        const int32_t* out_map) {
   // ---- host-side argument checks (nothing is enqueued before they pass)
   const int32_t N = episodes.n_nodes;
   const int64_t S = n_episodes;
@@ -461,37 +540,51 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const int mode = opt ? opt->mode : EP_MODE_AUTO;
   if (mode < EP_MODE_AUTO || mode > EP_MODE_MAPCONCAT) return EP_ERR_ARG;
   if (opt && opt->n_segments < 0) return EP_ERR_ARG;
+  const uint32_t plan = opt ? opt->plan : 0u;
 
   int64_t max_span = 0, max_hi = 0;
-  int K = 1;
+  int64_t max_bound = 1;  // most live runs any window can hold
   int dil_k = 0;  // doubling steps of the tick kernel's dilation (windows up to 63 ticks)
+  std::vector<uint8_t> cls((size_t)S);
+  int cls_seen = 0;  // bit c: some episode needs window kind c
   for (int64_t e = 0; e < S; ++e) {
-    int64_t span = 0;
+    int64_t span = 0, ep_hi = 0, ep_bound = 1;
     for (int j = 0; j < N - 1; ++j) {
       const int64_t lo = episodes.t_low[e * (N - 1) + j];
       const int64_t hi = episodes.t_high[e * (N - 1) + j];
       if (lo < 0 || lo >= hi) return EP_ERR_INTERVAL;
       span += hi;
-      max_hi = std::max(max_hi, hi);
+      ep_hi = std::max(ep_hi, hi);
       if (hi <= 63) dil_k = std::max(dil_k, dil_steps((uint32_t)lo, (uint32_t)hi));
-      // live disjoint runs of a window are bounded by floor(hi / (hi - lo + 1)) + 1;
-      // K < that bound iff K * (hi - lo + 1) <= hi
-      while (K <= EP_MAX_RUNS && (int64_t)K * (hi - lo + 1) <= hi) K <<= 1;
+      // live disjoint runs of a window: at most floor(hi / (hi - lo + 1)) + 1
+      ep_bound = std::max(ep_bound, hi / (hi - lo + 1) + 1);
     }
     if (span > INT32_MAX) return EP_ERR_INTERVAL;
     max_span = std::max(max_span, span);
+    max_hi = std::max(max_hi, ep_hi);
+    max_bound = std::max(max_bound, ep_bound);
+    int c = ep_hi <= 63 ? kClsBits : (ep_bound <= EP_MAX_RUNS ? kClsRuns : kClsRing);
+    if (plan & EP_PLAN_RUN_WINDOWS) c = ep_bound <= EP_MAX_RUNS ? kClsRuns : kClsRing;
+    if (plan & EP_PLAN_RING_WINDOWS) c = kClsRing;
+    cls[(size_t)e] = (uint8_t)c;
+    cls_seen |= 1 << c;
   }
-  // window kind: bit windows when every t_high fits one mask, else run windows
-  int win;
-  if (max_hi <= 31)
-    win = kBits32;
-  else if (max_hi <= 63)
-    win = kBits64;
-  else if (K <= EP_MAX_RUNS)
-    win = K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4);
-  else
-    return EP_ERR_UNSUPPORTED;
   if (S == 0) return EP_OK;
+  if (!sh && !out_map && !(plan & EP_PLAN_NO_SPLIT) && n_events > 0 && __builtin_popcount(cls_seen) > 1)
+    return count_split(times, types, n_events, episodes, S, out_counts, stream, opt, cls);
+  // window kind of the call: the widest any of its episodes needs
+  const int K = max_bound <= 1 ? 1 : (max_bound <= 2 ? 2 : 4);
+  const int run_win = max_bound <= EP_MAX_RUNS ? (K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4)) : kRing;
+  int win;
+  if (cls_seen == (1 << kClsBits))
+    win = max_hi <= 31 ? kBits32 : kBits64;
+  else if (cls_seen & (1 << kClsRing))
+    win = kRing;
+  else
+    win = run_win;
+  // ring capacity: the live-run bound, and never more runs than events
+  uint32_t ring_cap = 1;
+  while ((int64_t)ring_cap < std::min<int64_t>(max_bound, std::max<int64_t>(n_events, 1))) ring_cap <<= 1;
 
   // distinct node types -> slots 1..U by rank (a 65,536-bit set with prefix counts)
   uint64_t seen[1024];
@@ -539,7 +632,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       memset(opt->stats, 0, sizeof(ep_stats));
       opt->stats->mode = EP_MODE_PTPE;
       opt->stats->n_segments = 1;
-      opt->stats->max_runs = win >= kBits32 ? (win == kBits32 ? 32 : 64) : K;
+      opt->stats->max_runs = win == kBits32 ? 32 : win == kBits64 ? 64 : win == kRing ? (int32_t)ring_cap : K;
+      opt->stats->groups = 1;
     }
     return EP_OK;
   }
@@ -552,12 +646,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   // ---- plan: scheme, segments, kernel and workgroup layout
   Launch L{};
   L.win = win;
-  L.bits = (win == kBits32 || win == kBits64) && U <= 255 && !getenv("EP_FORCE_SCAN");
-  if (!L.bits && win >= kBits32) {
-    // many node types: the scan kernel with bit windows is not built; use runs if they fit
-    if (K > EP_MAX_RUNS) return EP_ERR_UNSUPPORTED;
-    L.win = K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4);
-  }
+  L.bits = (win == kBits32 || win == kBits64) && U <= 255;
+  // many node types: the scan kernel with bit windows is not built; runs or rings
+  if (!L.bits && (win == kBits32 || win == kBits64)) L.win = run_win;
   // lanes one CU holds for the counting kernel (the hybrid rule's T_B * B_MP):
   // the tick kernel's workgroups per CU as its registers allow, times its
   // threads, for bit windows; 8 waves on each of 4 SIMDs otherwise
@@ -587,6 +678,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     const int64_t cap = std::max<int64_t>(1, (sh->t_end - sh->t_first + 1) / (max_span + 1));
     P = (int32_t)std::min<int64_t>(P, cap);
   }
+  // ring windows: every Map machine owns N-1 rings of ring_cap runs
+  const double ring_slot_bytes = (double)std::max(N - 1, 1) * ring_cap * sizeof(int2);
+  if (L.win == kRing && !(opt && opt->n_segments > 0)) {
+    const double per_p = (double)S * (pmode == EP_MODE_PTPE ? 1 : N) * ring_slot_bytes;
+    while (P > 1 && (double)P * per_p > kRingBudget) P >>= 1;
+  }
   L.mode = pmode;
   L.P = P;
   L.n_machines = (pmode == EP_MODE_PTPE) ? 1 : N;
@@ -595,29 +692,23 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     // one lane per (segment, episode) holding every machine, unless that
     // leaves the GPU with too few lanes for a fixed segment count
     const int64_t target = (int64_t)info->cu_count * lanes_per_cu_est;
-    L.split = 0;
-    if (const char* sp = getenv("EP_SPLIT")) {
-      if (!strcmp(sp, "ticks")) L.split = 1;
-      if (!strcmp(sp, "positions")) L.split = 2;
-    }
+    L.split = (plan & EP_PLAN_TICKS) ? 1 : ((plan & EP_PLAN_POSITIONS) ? 2 : 0);
     // few episodes: sparse segments read the filter kernel's per-episode lists
     // (one lane per (segment, episode) walks only its episode's events)
     // (on short streams the position kernel, which stages events in LDS, is
     // faster than a filter pass plus lanes reading lists)
     L.list = S <= kMaxListEpisodes && L.split != 1 && list_bytes <= kMaxListBytes &&
-             (n_events >= kListMinEvents || getenv("EP_FORCE_LIST")) && !getenv("EP_NO_LIST");
+             (n_events >= kListMinEvents || (plan & EP_PLAN_LIST)) && !(plan & EP_PLAN_NO_LIST);
     L.all_mach = L.n_machines > 1 && N <= kMaxClassNodes && (L.list || S * (int64_t)P * 4 >= target);
-    const char* lanes_env = getenv("EP_LANES");
-    if (lanes_env && N <= kMaxClassNodes && L.n_machines > 1)
-      L.all_mach = strcmp(lanes_env, "machine") != 0;
+    if (plan & EP_PLAN_MACHINE_LANES) L.all_mach = false;
     L.M = L.all_mach ? 1 : L.n_machines;
     // pruning the lists pays where the list kernel has too few lanes (under
     // two waves per SIMD) to hide their serial walks: it shortens every walk;
     // with more lanes the list kernel is bound by its total work, which
     // pruning cuts by less than pruning itself costs per block
     const int64_t list_lanes = (int64_t)P * S * L.M;
-    L.prune = L.list && ((list_lanes < (int64_t)info->cu_count * 4 * 2 * kWave && !getenv("EP_NO_PRUNE")) ||
-                         getenv("EP_FORCE_PRUNE"));
+    L.prune = L.list && ((list_lanes < (int64_t)info->cu_count * 4 * 2 * kWave && !(plan & EP_PLAN_NO_PRUNE)) ||
+                         (plan & EP_PLAN_PRUNE));
     L.G = (int)std::min<int64_t>(S, L.block / L.M);
     L.R = (L.G == S) ? std::max(1, L.block / (L.G * L.M)) : 1;
     L.R = (int)std::min<int64_t>(L.R, P);
@@ -651,13 +742,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     L.lds = 0;
   }
   L.slots = (pmode == EP_MODE_PTPE) ? 1 : 2 * N;
-  if (getenv("EP_LOG"))
+  if (log_on())
     fprintf(stderr,
             "epcount: S=%lld N=%d n=%lld U=%d mode=%s P=%d win=%s kernel=%s lanes=%s M=%d G=%d R=%d "
-            "CH=%d lds=%zu maxSpan=%lld\n",
+            "CH=%d lds=%zu maxSpan=%lld ring=%u\n",
             (long long)S, N, (long long)n_events, U, pmode == EP_MODE_PTPE ? "ptpe" : "mapconcat", P,
             win_name(L.win), L.bits ? "bits" : "scan", L.all_mach ? "class" : "machine", L.M, L.G, L.R,
-            L.CH, L.lds, (long long)max_span);
+            L.CH, L.lds, (long long)max_span, L.win == kRing ? ring_cap : 0u);
 
   // tick kernel: episodes ordered by their doubling steps, so that an episode
   // group of narrow windows runs fewer steps than the call's widest needs
@@ -666,7 +757,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   // ordering's host time)
   std::vector<int32_t> ep_perm, group_k;
   if (L.bits && L.split != 2 && S > L.G &&
-      ((double)S * (double)n_events >= 4294967296.0 || getenv("EP_FORCE_GROUP_STEPS"))) {
+      ((double)S * (double)n_events >= 4294967296.0 || (plan & EP_PLAN_GROUP_STEPS))) {
     std::vector<int32_t> steps((size_t)S, 0);
     int32_t lo_k = INT32_MAX, hi_k = 0;
     for (int64_t e = 0; e < S; ++e) {
@@ -678,7 +769,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       lo_k = std::min(lo_k, k);
       hi_k = std::max(hi_k, k);
     }
-    if (lo_k < hi_k && !getenv("EP_NO_GROUP_STEPS")) {
+    if (lo_k < hi_k && !(plan & EP_PLAN_NO_GROUP_STEPS)) {
       // a counting sort (steps are 0 .. 6), stable
       int64_t at[8] = {0};
       for (int64_t e = 0; e < S; ++e) ++at[steps[(size_t)e] + 1];
@@ -703,8 +794,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_slv = L.list ? align_up(sizeof(uint16_t) * 256 * S, 256) : 0;
   const size_t sz_perm = align_up(sizeof(int32_t) * ep_perm.size(), 256);
   const size_t sz_gk = align_up(sizeof(int32_t) * group_k.size(), 256);
+  const size_t sz_omap = out_map ? align_up(sizeof(int32_t) * S, 256) : 0;
   const size_t host_bytes =
-      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv + sz_perm + sz_gk;
+      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv + sz_perm + sz_gk + sz_omap;
   // (+ slack: the list kernel's aligned batches may read two entries past the
   // last block's region)
   const size_t sz_lists = L.list ? align_up((size_t)list_bytes + 4 * sizeof(int2), 256) : 0;
@@ -720,9 +812,28 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   // closure misses queued for repair_kernel (more are repaired where found)
   const int64_t queue_cap = P > 1 ? 65536 : 0;
   const size_t sz_queue = align_up(sizeof(uint64_t) * (size_t)queue_cap, 256);
+  // ring windows: a slot per Map machine (scan kernel) and per wave of the
+  // kernels that run one machine per wave (closure, repair, result, fused
+  // reduction, stream entry and tail); the kernels run one after another
+  RingArena ring{nullptr, 0, 1, 0};
+  if (L.win == kRing) {
+    int red_waves = 1;
+    while (red_waves * kWave < P) red_waves <<= 1;
+    int64_t slots = (int64_t)P * S * L.M;
+    slots = std::max<int64_t>(slots, ((S + 3) / 4) * 4);             // finish, stream entry and tail
+    slots = std::max<int64_t>(slots, S * (int64_t)red_waves);          // fused reduction
+    if (P > 1) {
+      slots = std::max<int64_t>(slots, grid_for((int64_t)(P - 1) * S) * (kBlock / kWave));  // closure
+      slots = std::max<int64_t>(slots, (int64_t)info->cu_count * 2 * (kBlock / kWave));      // repair
+    }
+    ring.stride = (int64_t)std::max(N - 1, 1) * ring_cap;
+    ring.cap = ring_cap;
+    ring.slots = slots;
+  }
+  const size_t sz_ring = L.win == kRing ? align_up(sizeof(int2) * (size_t)ring.slots * ring.stride, 256) : 0;
   const size_t total =
       host_bytes + sz_tau + 2 * sz_seg + sz_tuples + 2 * sz_nslots + sz_flags + sz_cnt + sz_queue + sz_lists +
-      2 * sz_lidx;
+      2 * sz_lidx + sz_ring;
 
   mark();  // plan
   ScratchBlock* block = nullptr;
@@ -743,6 +854,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     uint16_t* d_slv = (uint16_t*)(ws + off); off += sz_slv;
     int32_t* d_perm = (int32_t*)(ws + off); off += sz_perm;
     int32_t* d_gk = (int32_t*)(ws + off); off += sz_gk;
+    int32_t* d_omap = (int32_t*)(ws + off); off += sz_omap;
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
     int32_t* d_end = (int32_t*)(ws + off); off += sz_seg;
@@ -758,6 +870,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     int2* d_lists = (int2*)(ws + off); off += sz_lists;
     int32_t* d_loff = (int32_t*)(ws + off); off += sz_lidx;
     int32_t* d_lcnt = (int32_t*)(ws + off); off += sz_lidx;
+    ring.base = (int2*)(ws + off); off += sz_ring;
 
     // episode table, spans, node slots and the node-type set, written
     // straight into pinned staging; the set-up kernel copies it to the device
@@ -792,6 +905,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         memcpy(at, ep_perm.data(), sizeof(int32_t) * ep_perm.size());
         memcpy(at + sz_perm, group_k.data(), sizeof(int32_t) * group_k.size());
       }
+      if (out_map)
+        memcpy(host + (host_bytes - sz_omap), out_map, sizeof(int32_t) * S);
     }
 
     if (opt && opt->validate) {
@@ -838,6 +953,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     sa.times = times; sa.n = n_events; sa.P = P; sa.max_span = max_span;
     sa.tau = d_tau; sa.beg = d_beg; sa.end = d_end;
     sa.flags = d_flags; sa.S = S; sa.counters = d_cnt;
+    sa.flag_init = (plan & EP_PLAN_RECOUNT) ? 1 : 0;
     sa.wave_search = P <= kWaveSearchMaxP ? 1 : 0;
     sa.tab_src = (const uint4*)tab_dev;
     sa.tab_dst = (uint4*)ws;
@@ -861,6 +977,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ma.ep_perm = ep_perm.empty() ? nullptr : d_perm;
     ma.group_k = ep_perm.empty() ? nullptr : d_gk;
     ma.lists = d_lists; ma.list_off = d_loff; ma.list_cnt = d_lcnt; ma.max_share = max_share;
+    ma.ring = ring;
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;
     dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));
@@ -924,14 +1041,19 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       pa.S = (int32_t)S; pa.N = N; pa.max_share = max_share;
       pa.lists = d_lists; pa.list_off = d_loff; pa.list_cnt = d_lcnt;
       // persistent workgroups: as many as are resident at once
-      static int prune_per_cu = 0;
-      if (prune_per_cu == 0) {
-        int v = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, list_prune_kernel, kBlock, 0) != hipSuccess) {
-          status = EP_ERR_HIP;
-          break;
+      int prune_per_cu = 0;
+      {
+        std::lock_guard<std::mutex> lock(g_info_mu);
+        if (info->prune_per_cu == 0) {
+          int v = 0;
+          if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, list_prune_kernel, kBlock, 0) == hipSuccess)
+            info->prune_per_cu = std::max(v, 1);
         }
-        prune_per_cu = std::max(v, 1);
+        prune_per_cu = info->prune_per_cu;
+      }
+      if (prune_per_cu == 0) {
+        status = EP_ERR_HIP;
+        break;
       }
       const int64_t pgrid = std::min<int64_t>(n_lblocks, (int64_t)info->cu_count * prune_per_cu);
       hipLaunchKernelGGL(list_prune_kernel, dim3((unsigned)pgrid), dim3(kBlock), 0, stream, pa);
@@ -963,6 +1085,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
       c.S = S; c.P = P;
       c.queue = nullptr; c.queue_cap = 0; c.queue_n = c.queue_head = nullptr; c.repair_blocks = 0;
+      c.ring = ring;
       stra.entry = sh->entry; stra.total = sh->total; stra.reset_out = sh->reset_out;
       stra.n = n_events; stra.t_end = sh->t_end; stra.max_span = max_span;
       if (P > 1 && Lr->stream_entry(stra, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
@@ -981,7 +1104,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     // (S x P <= 2^20 tuples); beyond, the closure kernel spreads each
     // episode's repairs over the whole grid and wins
     const bool fused = !sh && P <= kReduceMembers && red_lds <= 65536 && S * (int64_t)P <= (1 << 20) &&
-                       !getenv("EP_NO_REDUCE");
+                       !(plan & EP_PLAN_NO_REDUCE);
     if (fused) {
       const int members = red_members;
       const size_t lds = red_lds;
@@ -993,7 +1116,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       c.ts = ts; c.flags = d_flags; c.repairs = d_cnt;
       c.S = S; c.P = P;
       c.queue = nullptr; c.queue_cap = 0; c.queue_n = c.queue_head = nullptr; c.repair_blocks = 0;
+      c.ring = ring;
       ra.fallbacks = d_cnt + 1; ra.out = out_counts; ra.n = n_events;
+      ra.out_map = out_map ? d_omap : nullptr;
       if (Lr->reduce(ra, L.win, dim3((unsigned)S), dim3((unsigned)members), lds, stream) !=
           hipSuccess) {
         status = EP_ERR_HIP;
@@ -1008,9 +1133,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
       ca.ts = ts; ca.flags = d_flags; ca.repairs = d_cnt;
       ca.S = S; ca.P = P;
-      ca.queue = d_queue; ca.queue_cap = getenv("EP_NO_REPAIR_QUEUE") ? 0 : queue_cap;
+      ca.queue = d_queue; ca.queue_cap = (plan & EP_PLAN_NO_REPAIR_QUEUE) ? 0 : queue_cap;
       ca.queue_n = d_cnt + 2; ca.queue_head = d_cnt + 3;
       ca.repair_blocks = info->cu_count * 2;
+      ca.ring = ring;
       if (Lr->closure(ca, L.win, dim3(grid_for((int64_t)(P - 1) * S)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
@@ -1047,7 +1173,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       fa.ep_types = d_types; fa.ep_lo = d_lo; fa.ep_hi = d_hi; fa.ep_span = d_span;
       fa.flags = d_flags; fa.T0 = d_t0; fa.P = P;
       fa.fallbacks = d_cnt + 1; fa.out = out_counts;
-      fa.n = n_events; fa.S = S;
+      fa.out_map = out_map ? d_omap : nullptr;
+      fa.n = n_events; fa.S = S; fa.ring = ring;
       if (Lr->finish(fa, L.win, dim3((unsigned)((S + 3) / 4)), stream) != hipSuccess) {
         status = EP_ERR_HIP;
         break;
@@ -1068,10 +1195,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       opt->stats->mode = pmode;
       opt->stats->n_segments = P;
-      opt->stats->max_runs = L.win >= kBits32 ? (L.win == kBits32 ? 32 : 64) : K;
-      opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0) | (L.prune ? 8 : 0);
+      opt->stats->max_runs = L.win == kBits32 ? 32 : L.win == kBits64 ? 64 : L.win == kRing ? (int32_t)ring_cap : K;
+      opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0) | (L.prune ? 8 : 0) |
+                            (L.win == kRing ? 16 : 0);
       opt->stats->repairs = (int64_t)cnt[0];
       opt->stats->fallbacks = (int64_t)cnt[1];
+      opt->stats->groups = 1;
     }
   } while (0);
 

@@ -20,6 +20,13 @@
 //                candidate (f, l) and covering (f+t_low, l+t_high].  At most
 //                floor(t_high/(t_high-t_low+1)) + 1 runs are ever live, so a
 //                capacity of K runs is exact when that bound is <= K.
+//   ring windows (any t_high, any number of live runs): the same runs kept
+//                in a ring of device memory owned by the machine, with the
+//                oldest and the newest run in registers.  Runs leave at the
+//                front (expiry) and enter at the back (new candidates), so
+//                every operation touches only the two ends; the ring holds
+//                min(that bound, events of the call) runs, which no window
+//                can exceed (every run holds at least one event).
 //
 // All time differences are formed as uint32 of non-negative differences of
 // int32 times, and cut arithmetic is int64, so nothing can overflow.
@@ -65,6 +72,23 @@ struct TupleStore {
     return k == 0 ? T0 + i : TX + i * (slots - 1) + (k - 1);
   }
 };
+
+// Device memory of the ring windows: `slots` machines, each owning N-1 rings
+// of `cap` runs {first, last} (a power of two), `stride` entries apart.  A
+// kernel running one machine per lane gives each lane its own slot; a kernel
+// running one machine per wave (all lanes holding the same machine) gives
+// the wave its slot, its lanes writing identical values to identical places.
+struct RingArena {
+  int2* base;
+  int64_t stride;
+  uint32_t cap;
+  int64_t slots;
+};
+
+// The slot of the calling wave in a kernel that runs one machine per wave.
+__device__ inline int64_t wave_slot() {
+  return ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+}
 
 template <int W>
 struct BitsOf;
@@ -193,6 +217,8 @@ struct RunMachine {
   int64_t r;  // time of the last reset (last completion, or the start)
   RunWindow<K> w[N > 1 ? N - 1 : 1];
 
+  __device__ void attach(const RingArena&, int64_t) {}
+
   __device__ void reset(int64_t at) {
     r = at;
 #pragma unroll
@@ -219,6 +245,98 @@ struct RunMachine {
         bool ok = true;
         if (j > 0) ok = w[j - 1].contains(t, P.lo[j - 1], P.hi[j - 1]);
         if (ok) w[j].insert(t, P.hi[j], P.width[j]);
+      }
+    }
+    return false;
+  }
+};
+
+// Run windows of any capacity: each node's runs in a ring of device memory.
+// The oldest live run (the only one the extension test reads) and the newest
+// (the only one a new candidate can merge into) stay in registers; a run is
+// written to the ring when a newer run is started behind it, and read back
+// when the runs before it have expired.  Same semantics as RunMachine.
+template <int N>
+struct RingMachine {
+  using Params = RunParams<N>;
+  static constexpr int NI = N > 1 ? N - 1 : 1;
+  int64_t r;
+  int2* ring;        // node j's ring at ring + j * cap
+  uint32_t cap;
+  uint32_t head[NI];  // ring position of the oldest live run
+  uint32_t cnt[NI];   // live runs
+  int32_t of[NI], ol[NI];  // the oldest live run (first, last candidate)
+  int32_t nf[NI], nl[NI];  // the newest live run
+
+  __device__ void attach(const RingArena& A, int64_t slot) {
+    ring = A.base + slot * A.stride;
+    cap = A.cap;
+  }
+
+  __device__ void reset(int64_t at) {
+    r = at;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      cnt[j] = 0;
+      head[j] = 0;
+    }
+  }
+
+  // Drop node j's runs that ended before t (t - last > hi).
+  __device__ __forceinline__ void expire(int j, int32_t t, uint32_t hi) {
+    while (cnt[j] > 0 && ((uint32_t)t - (uint32_t)ol[j]) > hi) {
+      --cnt[j];
+      ++head[j];
+      if (cnt[j] == 1) {
+        of[j] = nf[j];
+        ol[j] = nl[j];
+      } else if (cnt[j] > 1) {
+        const int2 v = ring[(size_t)j * cap + (head[j] & (cap - 1))];
+        of[j] = v.x;
+        ol[j] = v.y;
+      }
+    }
+  }
+
+  __device__ __forceinline__ bool contains(int j, int32_t t, uint32_t lo, uint32_t hi) {
+    expire(j, t, hi);
+    return cnt[j] > 0 && ((uint32_t)t - (uint32_t)of[j]) > lo;
+  }
+
+  __device__ __forceinline__ void insert(int j, int32_t t, uint32_t hi, uint32_t width) {
+    expire(j, t, hi);
+    if (cnt[j] > 0 && ((uint32_t)t - (uint32_t)nl[j]) <= width) {
+      nl[j] = t;
+      if (cnt[j] == 1) ol[j] = t;
+      return;
+    }
+    if (cnt[j] > 0) {
+      ring[(size_t)j * cap + ((head[j] + cnt[j] - 1) & (cap - 1))] = make_int2(nf[j], nl[j]);
+    } else {
+      of[j] = t;
+      ol[j] = t;
+    }
+    nf[j] = t;
+    nl[j] = t;
+    ++cnt[j];
+  }
+
+  __device__ bool step(int32_t t, uint32_t lm, const Params& P) {
+    if ((int64_t)t <= r) return false;
+    if ((lm >> (N - 1)) & 1u) {
+      bool done = true;
+      if constexpr (N > 1) done = contains(N - 2, t, P.lo[N - 2], P.hi[N - 2]);
+      if (done) {
+        reset(t);
+        return true;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      if ((lm >> j) & 1u) {
+        bool ok = true;
+        if (j > 0) ok = contains(j - 1, t, P.lo[j - 1], P.hi[j - 1]);
+        if (ok) insert(j, t, P.hi[j], P.width[j]);
       }
     }
     return false;
@@ -263,6 +381,8 @@ struct BitMachine {
   int64_t r;
   int32_t B;
   Bits m[N > 1 ? N - 1 : 1];
+
+  __device__ void attach(const RingArena&, int64_t) {}
 
   __device__ void reset(int64_t at) {
     r = at;
@@ -311,6 +431,9 @@ struct SegMachine {
   bool first_found;
   bool finished;
   int64_t last;  // the last completion in (tau_lo, tau_hi] (INT64_MIN: none)
+
+  // give a ring-window machine its ring slot (no-op for the other machines)
+  __device__ void attach(const RingArena& A, int64_t slot) { m.attach(A, slot); }
 
   __device__ void init(int64_t reset_at, int64_t lo_cut, int64_t hi_cut, int32_t span) {
     m.reset(reset_at);
@@ -389,6 +512,7 @@ struct MapArgs {
   int32_t max_share;        // most episodes one node type belongs to (region = kListBlock * this)
   int64_t eg_blocks;   // tick kernel: workgroups that loop over a segment group's episode
                        // groups when its segments fit one chunk each
+  RingArena ring;      // scan kernel with ring windows: slot ((p * S) + e) * M + k
 };
 
 // A workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -441,12 +565,12 @@ __device__ inline bool segment_uses_ticks(const MapArgs& A, int64_t p, int N) {
   return tick_span * (int64_t)(N > 1 ? N - 1 : 1) <= 4 * events;
 }
 
-// Scan Map kernel (run windows): one lane = one machine (segment p, episode e,
-// machine k).  A workgroup holds R consecutive segments x G episodes x M
-// machines; it streams the R segments' event ranges through LDS in lockstep
-// chunks of CH events, and every lane feeds each event of its own segment's
-// chunk to its machine.
-template <int N, int K>
+// Scan Map kernel (run or ring windows): one lane = one machine (segment p,
+// episode e, machine k).  A workgroup holds R consecutive segments x G
+// episodes x M machines; it streams the R segments' event ranges through LDS
+// in lockstep chunks of CH events, and every lane feeds each event of its own
+// segment's chunk to its machine.
+template <int N, class Mach>
 __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   __shared__ int32_t s_t[kTile];
   __shared__ uint16_t s_y[kTile];
@@ -479,10 +603,10 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
     atomicMax(&s_chunks, (len + A.CH - 1) / A.CH);
   }
 
-  using Mach = RunMachine<N, K>;
   typename Mach::Params prm;
   SegMachine<Mach> sm;
   if (active) {
+    sm.attach(A.ring, (p * A.S + e) * A.M + k);
     prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
     const int64_t lo_cut = A.tau[p];
     const int64_t hi_cut = A.tau[p + 1];
@@ -1820,6 +1944,7 @@ struct ClosureArgs {
   unsigned long long* queue_n;
   unsigned long long* queue_head;
   int32_t repair_blocks;  // workgroups of repair_kernel
+  RingArena ring;         // ring windows: one slot per wave (wave_slot)
 };
 
 // The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
@@ -1839,6 +1964,7 @@ __device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params&
     return tu;
   }
   SegMachine<Mach> sm;
+  sm.attach(A.ring, wave_slot());
   sm.init(x, lo_cut, hi_cut, prm.span);
   const int64_t i0 = upper_bound_time(A.times, A.seg_beg[q], A.seg_end[q], x);
   wave_feed_range<Mach>(A.times, A.types, i0, A.seg_end[q], sm, prm);
@@ -1990,8 +2116,10 @@ struct FallbackArgs {
   int64_t P;
   unsigned long long* fallbacks;
   int64_t* out;
+  const int32_t* out_map;  // [S] or null: episode e's count goes to out[out_map[e]]
   int64_t n;
   int64_t S;
+  RingArena ring;
 };
 
 // Result extraction, one wave per episode.  The answer is the chain entering
@@ -2005,18 +2133,20 @@ __global__ __launch_bounds__(kBlock) void finish_kernel(FallbackArgs A) {
   const int64_t e = (int64_t)blockIdx.x * (kBlock / kWave) + threadIdx.x / kWave;
   if (e >= A.S) return;
   const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
+  const int64_t oe = A.out_map ? (int64_t)A.out_map[e] : e;
   if (A.flags[e] == 0) {
-    if (lane0) A.out[e] = A.T0[e * A.P].c;
+    if (lane0) A.out[oe] = A.T0[e * A.P].c;
     return;
   }
   typename Mach::Params prm;
   prm.load(A.ep_types, A.ep_lo, A.ep_hi, A.ep_span, e);
   const int64_t before = (int64_t)A.times[0] - 1;
   SegMachine<Mach> sm;
+  sm.attach(A.ring, wave_slot());
   sm.init(before, before, INT64_MAX / 4, prm.span);
   wave_feed_range<Mach>(A.times, A.types, 0, A.n, sm, prm);
   if (lane0) {
-    A.out[e] = sm.count;
+    A.out[oe] = sm.count;
     atomicAdd(A.fallbacks, 1ull);
   }
 }
@@ -2046,6 +2176,7 @@ struct ReduceArgs {
   ClosureArgs c;
   unsigned long long* fallbacks;
   int64_t* out;
+  const int32_t* out_map;  // [S] or null: episode e's count goes to out[out_map[e]]
   int64_t n;
 };
 
@@ -2193,8 +2324,9 @@ __global__ __launch_bounds__(kReduceMembers) void reduce_kernel(ReduceArgs A) {
     }
     __syncthreads();
   }
+  const int64_t oe = A.out_map ? (int64_t)A.out_map[e] : e;
   if (s_bad == 0) {
-    if (i == 0) A.out[e] = s_c[0];
+    if (i == 0) A.out[oe] = s_c[0];
     return;
   }
   if (i >= kWave) return;
@@ -2202,18 +2334,20 @@ __global__ __launch_bounds__(kReduceMembers) void reduce_kernel(ReduceArgs A) {
   prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
   const int64_t before = (int64_t)A.c.times[0] - 1;
   SegMachine<Mach> sm;
+  sm.attach(A.c.ring, wave_slot());
   sm.init(before, before, INT64_MAX / 4, prm.span);
   wave_feed_range<Mach>(A.c.times, A.c.types, 0, A.n, sm, prm);
   if (lane == 0) {
-    A.out[e] = sm.count;
+    A.out[oe] = sm.count;
     atomicAdd(A.fallbacks, 1ull);
   }
 }
 
 // ----------------------------------------------------------- launchers
 
-// Window kinds: run windows with K = 1, 2, 4 runs, or bit windows of 32 / 64 bits.
-enum WinKind { kRuns1 = 0, kRuns2 = 1, kRuns4 = 2, kBits32 = 3, kBits64 = 4, kNumWin = 5 };
+// Window kinds: run windows with K = 1, 2, 4 runs in registers, bit windows of
+// 32 / 64 bits, or ring windows (runs in device memory, any number).
+enum WinKind { kRuns1 = 0, kRuns2 = 1, kRuns4 = 2, kBits32 = 3, kBits64 = 4, kRing = 5, kNumWin = 6 };
 
 // Per-N entry points, defined in ep_inst.hip (one translation unit per N).
 // ------------------------------------------------------------- streaming
@@ -2328,6 +2462,7 @@ __global__ __launch_bounds__(kBlock) void stream_tail_kernel(StreamArgs A) {
     i0 = upper_bound_time(A.c.times, 0, A.n, reset_t);
   }
   SegMachine<Mach> sm;
+  sm.attach(A.c.ring, wave_slot());
   sm.init(reset_t, reset_t, A.t_end, prm.span);
   wave_feed_range<Mach>(A.c.times, A.c.types, i0, A.n, sm, prm);
   if (!lane0) return;
@@ -2345,7 +2480,7 @@ __global__ __launch_bounds__(kBlock) void stream_tail_kernel(StreamArgs A) {
 }
 
 struct Launchers {
-  // scan Map kernel (run windows; win must be a run kind)
+  // scan Map kernel (run windows; win must be a run or ring kind)
   hipError_t (*map_scan)(const MapArgs&, int win, dim3 grid, dim3 block, hipStream_t);
   // bit Map kernel (win must be a bit kind); all_machines: one lane holds N machines
   hipError_t (*map_bits)(const MapArgs&, int win, bool all_machines, dim3 grid, dim3 block,

@@ -16,17 +16,18 @@ namespace {
 constexpr int kMaxClassNodes = 8;
 constexpr int kClassMch = EP_N <= kMaxClassNodes ? EP_N : 1;
 
-template <int K>
-hipError_t launch_scan_k(const MapArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((map_scan_kernel<EP_N, K>), grid, block, 0, s, a);
+template <class Mach>
+hipError_t launch_scan_m(const MapArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  hipLaunchKernelGGL((map_scan_kernel<EP_N, Mach>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const MapArgs& a, int win, dim3 grid, dim3 block, hipStream_t s) {
   switch (win) {
-    case kRuns1: return launch_scan_k<1>(a, grid, block, s);
-    case kRuns2: return launch_scan_k<2>(a, grid, block, s);
-    case kRuns4: return launch_scan_k<4>(a, grid, block, s);
+    case kRuns1: return launch_scan_m<RunMachine<EP_N, 1>>(a, grid, block, s);
+    case kRuns2: return launch_scan_m<RunMachine<EP_N, 2>>(a, grid, block, s);
+    case kRuns4: return launch_scan_m<RunMachine<EP_N, 4>>(a, grid, block, s);
+    case kRing: return launch_scan_m<RingMachine<EP_N>>(a, grid, block, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -92,6 +93,7 @@ hipError_t launch_closure(const ClosureArgs& a, int win, dim3 grid, hipStream_t 
     case kRuns4: return launch_closure_m<RunMachine<EP_N, 4>>(a, grid, s);
     case kBits32: return launch_closure_m<BitMachine<EP_N, 32>>(a, grid, s);
     case kBits64: return launch_closure_m<BitMachine<EP_N, 64>>(a, grid, s);
+    case kRing: return launch_closure_m<RingMachine<EP_N>>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -109,6 +111,7 @@ hipError_t launch_finish(const FallbackArgs& a, int win, dim3 grid, hipStream_t 
     case kRuns4: return launch_finish_m<RunMachine<EP_N, 4>>(a, grid, s);
     case kBits32: return launch_finish_m<BitMachine<EP_N, 32>>(a, grid, s);
     case kBits64: return launch_finish_m<BitMachine<EP_N, 64>>(a, grid, s);
+    case kRing: return launch_finish_m<RingMachine<EP_N>>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -126,6 +129,7 @@ hipError_t launch_reduce(const ReduceArgs& a, int win, dim3 grid, dim3 block, si
     case kRuns4: return launch_reduce_m<RunMachine<EP_N, 4>>(a, grid, block, lds, s);
     case kBits32: return launch_reduce_m<BitMachine<EP_N, 32>>(a, grid, block, lds, s);
     case kBits64: return launch_reduce_m<BitMachine<EP_N, 64>>(a, grid, block, lds, s);
+    case kRing: return launch_reduce_m<RingMachine<EP_N>>(a, grid, block, lds, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -146,6 +150,7 @@ hipError_t launch_stream(const StreamArgs& a, int win, bool tail, dim3 grid, hip
     case kRuns4: return launch_stream_m<RunMachine<EP_N, 4>>(a, tail, grid, s);
     case kBits32: return launch_stream_m<BitMachine<EP_N, 32>>(a, tail, grid, s);
     case kBits64: return launch_stream_m<BitMachine<EP_N, 64>>(a, tail, grid, s);
+    case kRing: return launch_stream_m<RingMachine<EP_N>>(a, tail, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -166,9 +171,10 @@ hipError_t occ(F f, int block, size_t lds, int* out) {
 hipError_t occupancy(int win, bool all_machines, int block, size_t lds, int* out) {
   if (all_machines && EP_N > kMaxClassNodes) return hipErrorInvalidValue;
   switch (win) {
-    case kRuns1: return occ(map_scan_kernel<EP_N, 1>, block, 0, out);
-    case kRuns2: return occ(map_scan_kernel<EP_N, 2>, block, 0, out);
-    case kRuns4: return occ(map_scan_kernel<EP_N, 4>, block, 0, out);
+    case kRuns1: return occ(map_scan_kernel<EP_N, RunMachine<EP_N, 1>>, block, 0, out);
+    case kRuns2: return occ(map_scan_kernel<EP_N, RunMachine<EP_N, 2>>, block, 0, out);
+    case kRuns4: return occ(map_scan_kernel<EP_N, RunMachine<EP_N, 4>>, block, 0, out);
+    case kRing: return occ(map_scan_kernel<EP_N, RingMachine<EP_N>>, block, 0, out);
     case kBits32:
       return all_machines ? occ(map_bits_kernel<EP_N, 32, kClassMch>, block, lds, out)
                           : occ(map_bits_kernel<EP_N, 32, 1>, block, lds, out);

@@ -37,6 +37,7 @@ struct SetupArgs {
   int32_t* beg;
   int32_t* end;
   int32_t* flags;  // [S + 1]
+  int32_t flag_init;  // episodes' flags start at this (1: every episode takes the whole-stream recount)
   int64_t S;
   unsigned long long* counters;  // [4]
   int32_t wave_search;  // range ends by one wave each (small P) or one thread each
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
   }
   i -= (int64_t)A.P + 1;
   if (i <= A.S) {
-    A.flags[i] = 0;
+    A.flags[i] = i < A.S ? A.flag_init : 0;
     return;
   }
   i -= A.S + 1;

@@ -73,14 +73,18 @@ typedef enum {
   EP_ERR_UNSORTED = -4,    /* validate: times are not non-decreasing */
   EP_ERR_WORKSPACE = -5,   /* scratch allocation failed */
   EP_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
-  EP_ERR_UNSUPPORTED = -7  /* a delay window needs more candidate runs than the kernels hold (see EP_MAX_RUNS) */
+  EP_ERR_UNSUPPORTED = -7  /* ep_mine only: a size has more candidates than max_candidates */
 } ep_status;
 
 /*
- * Candidate runs per node window.  A node window holds the union of the
- * intervals (t'+t_low, t'+t_high] over the candidate times t' of the previous
- * node; at most floor(t_high/(t_high-t_low+1)) + 1 disjoint runs of it can
- * be live at once, and the kernels keep up to EP_MAX_RUNS of them per node.
+ * Candidate runs per node window kept in registers.  A node window holds the
+ * union of the intervals (t'+t_low, t'+t_high] over the candidate times t' of
+ * the previous node; at most floor(t_high/(t_high-t_low+1)) + 1 disjoint runs
+ * of it can be live at once.  Windows up to 63 ticks are bit masks; longer
+ * ones whose bound is <= EP_MAX_RUNS keep their runs in registers; the rest
+ * keep them in a ring of device memory sized by that bound (and by the
+ * number of events, which no window can exceed), so every interval with
+ * 0 <= t_low < t_high is counted exactly.
  */
 #define EP_MAX_RUNS 4
 
@@ -121,22 +125,55 @@ int ep_count_episodes(const int32_t* times, const uint16_t* types, int64_t n_eve
 /* Scheme selection for ep_count_episodes_ex. */
 enum { EP_MODE_AUTO = 0, EP_MODE_PTPE = 1, EP_MODE_MAPCONCAT = 2 };
 
-/* Optional statistics filled by ep_count_episodes_ex when `stats` is set. */
+/* Optional statistics filled by ep_count_episodes_ex when `stats` is set.  A
+ * call whose episodes need different window kinds runs one group per kind
+ * (see EP_PLAN_NO_SPLIT); mode, n_segments and max_runs then describe the
+ * group with the most episodes, kernels is the union over the groups and
+ * repairs and fallbacks are their sums. */
 typedef struct {
   int32_t mode;         /* scheme that ran: EP_MODE_PTPE or EP_MODE_MAPCONCAT */
   int32_t n_segments;   /* P (1 for PTPE) */
-  int32_t max_runs;     /* run capacity per node window the kernels were built with */
+  int32_t max_runs;     /* window capacity: 32 / 64 (bit masks), else candidate runs per node */
   int32_t kernels;      /* bit 0: bit-window Map kernels (tick/list/position), else the
                            scan kernel; bit 1: one lane holds every machine of a
                            (segment, episode); bit 2: sparse segments through the event
                            filter and the list Map kernel (else the position kernel);
-                           bit 3: the filter's lists pruned of entries that cannot act */
+                           bit 3: the filter's lists pruned of entries that cannot act;
+                           bit 4: ring windows (runs in device memory) */
   int64_t repairs;      /* repair tuples made for unmatched segment exits */
   int64_t fallbacks;    /* episodes recounted by the whole-stream fallback */
+  int32_t groups;       /* window-kind groups the call ran (1 unless split) */
+  int32_t pad;
 } ep_stats;
 
 /*
- * Options for ep_count_episodes_ex.
+ * Planner switches for ep_options.plan (bit flags, 0 = the planner decides).
+ * None of them changes a result: they choose which kernels produce it, so
+ * that tests can reach every kernel on small inputs and measurements can
+ * compare schemes.
+ */
+enum {
+  EP_PLAN_TICKS = 1 << 0,            /* every segment to the tick Map kernel */
+  EP_PLAN_POSITIONS = 1 << 1,        /* every segment to the list or position Map kernel */
+  EP_PLAN_LIST = 1 << 2,             /* the event filter + list kernel at any stream length */
+  EP_PLAN_NO_LIST = 1 << 3,          /* never the list path (the position kernel instead) */
+  EP_PLAN_PRUNE = 1 << 4,            /* list path: always prune the lists */
+  EP_PLAN_NO_PRUNE = 1 << 5,         /* list path: never prune them */
+  EP_PLAN_GROUP_STEPS = 1 << 6,      /* tick kernel: always order episodes by doubling steps */
+  EP_PLAN_NO_GROUP_STEPS = 1 << 7,   /* tick kernel: never */
+  EP_PLAN_RUN_WINDOWS = 1 << 8,      /* run windows and the scan kernel where bit windows fit */
+  EP_PLAN_RING_WINDOWS = 1 << 9,     /* ring windows and the scan kernel for every episode */
+  EP_PLAN_MACHINE_LANES = 1 << 10,   /* one Map machine per lane */
+  EP_PLAN_NO_REDUCE = 1 << 11,       /* separate closure, tree and result launches */
+  EP_PLAN_NO_REPAIR_QUEUE = 1 << 12, /* closure misses repaired where they are found */
+  EP_PLAN_RECOUNT = 1 << 13,         /* every episode taken through the whole-stream recount
+                                        that guards repair-list overflow and tree misses */
+  EP_PLAN_NO_SPLIT = 1 << 14         /* one window kind for the whole call: the widest one
+                                        any episode needs (else one group per kind) */
+};
+
+/*
+ * Options for ep_count_episodes_ex (a zeroed struct gives the defaults).
  *   mode        EP_MODE_AUTO, EP_MODE_PTPE or EP_MODE_MAPCONCAT.
  *   n_segments  MAPCONCAT only: P >= 1, 0 = chosen by the planner.  Any P is
  *               valid; the planner picks powers of two (Concatenate section).
@@ -149,10 +186,10 @@ typedef struct {
  *               `episodes.t_low` is then not read (it may be NULL); every
  *               t_high must be > 0.  Every occurrence of an episode is one of
  *               its relaxed version, so count(alpha') >= count(alpha).  The
- *               relaxed windows never need more than one candidate run, so
- *               this mode never returns EP_ERR_UNSUPPORTED.
+ *               relaxed windows never need more than one candidate run.
  *   stats       if non-NULL, filled after the work completes.  Synchronises
  *               `stream`.
+ *   plan        EP_PLAN_* switches (0: the planner's choice).
  */
 typedef struct {
   int32_t mode;
@@ -160,6 +197,8 @@ typedef struct {
   int32_t validate;
   int32_t upper_only;
   ep_stats* stats;
+  uint32_t plan;
+  int32_t pad;
 } ep_options;
 
 /* ep_count_episodes with explicit options (opt may be NULL = defaults). */

@@ -59,9 +59,6 @@ def test_host_argument_errors():
     assert _call(lo=(5,), hi=(5,)) == -3
     assert _call(lo=(-1,), hi=(5,)) == -3
     assert _call(N=3, lo=(0, 0), hi=(2 ** 31 - 1, 2)) == -3
-    # a window longer than 63 ticks with more live runs than EP_MAX_RUNS:
-    # (99,100] can hold 51 disjoint runs; (9,10] fits a bit window and is fine
-    assert _call(lo=(99,), hi=(100,)) == -7
     bad_mode = fem.EpOptions(7, 0, 0, 0, None)
     assert _call(opt=ctypes.byref(bad_mode)) == -1
     bad_p = fem.EpOptions(2, -4, 0, 0, None)
@@ -206,3 +203,33 @@ def test_segment_cut_rule():
     cuts = [fem.segment_cut(-2 ** 31, 2 ** 31 - 1, 1024, p) for p in range(1025)]
     assert cuts[0] == -2 ** 31 - 1 and cuts[-1] == 2 ** 31 - 1
     assert all(b >= a for a, b in zip(cuts, cuts[1:]))
+
+
+def test_struct_layouts_match_header(tmp_path):
+    # the binding's ctypes mirrors of the option and statistics structs have
+    # the sizes and field offsets the C compiler gives the header's structs
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "epcount.h"\n'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(ep_options), sizeof(ep_stats),'
+        ' offsetof(ep_options, plan), offsetof(ep_stats, groups), sizeof(ep_episodes),'
+        ' sizeof(ep_mine_options)); return 0; }\n')
+    exe = tmp_path / "layout"
+    inc = os.path.dirname(HEADER)
+    import subprocess
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include", str(src),
+                           "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    want = [ctypes.sizeof(fem.EpOptions), ctypes.sizeof(fem.EpStats), fem.EpOptions.plan.offset,
+            fem.EpStats.groups.offset, ctypes.sizeof(fem.EpEpisodes), ctypes.sizeof(fem.EpMineOptions)]
+    assert got == want
+
+
+def test_plan_switch_names():
+    # every EP_PLAN_* flag of the header has a name in the binding, with its value
+    text = open(HEADER).read()
+    flags = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"EP_PLAN_(\w+)\s*=\s*1 << (\d+)", text))
+    assert len(flags) == len(fem.PLAN)
+    for name, bit in flags.items():
+        assert fem.PLAN[name.lower().replace("_", "-")] == 1 << bit
+    assert fem.plan_bits(["ring-windows", "recount"]) == fem.PLAN["ring-windows"] | fem.PLAN["recount"]

@@ -59,6 +59,24 @@ def test_mine_random_streams(fem, mode, two_pass):
         _same(got, want, "random %d %s two_pass=%s" % (trial, mode, two_pass))
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
+def test_mine_mixed_bins(fem, two_pass):
+    # bins needing every window kind in one level: short ones (bit masks), a
+    # long wide one (one run in registers) and narrow ones far from zero (ring
+    # windows); each level is counted in one call split by window kind
+    rng = np.random.default_rng(67)
+    for trial in range(4):
+        n_types = int(rng.integers(2, 4))
+        gaps = rng.integers(1, 4, size=int(rng.integers(500, 2500)))
+        times = np.cumsum(gaps).astype(np.int32)
+        types = rng.integers(0, n_types, size=times.size).astype(np.uint16)
+        bins = [(0, 3), (10, 11), (0, 100), (99, 100), (60, 64)]
+        threshold = int(rng.integers(3, 20))
+        want = oracle.mine(times, types, range(n_types), bins, 4, threshold)
+        got = _mine(fem, times, types, range(n_types), bins, 4, threshold, two_pass=two_pass)
+        _same(got, want, "mixed bins %d two_pass=%s" % (trial, two_pass))
+
+
 @pytest.mark.parametrize("seconds", [10, 60])
 @pytest.mark.parametrize("two_pass", [False, True])
 def test_mine_sym26(fem, seconds, two_pass):

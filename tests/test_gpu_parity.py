@@ -29,9 +29,9 @@ def fem():
     return m
 
 
-def _gpu(fem, times, types, ep, lo, hi, mode, P=0, stats=False):
+def _gpu(fem, times, types, ep, lo, hi, mode, P=0, stats=False, plan=None):
     t, y = fem.to_device(times, types, "cuda")
-    res = fem.count_episodes(t, y, ep, lo, hi, mode=mode, n_segments=P, stats=stats)
+    res = fem.count_episodes(t, y, ep, lo, hi, mode=mode, n_segments=P, stats=stats, plan=plan)
     torch.cuda.synchronize()
     if stats:
         return res[0].cpu().numpy(), res[1]
@@ -53,32 +53,29 @@ MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 1), ("mapconcat", 2), ("mapconc
          ("mapconcat", 4), ("mapconcat", 7), ("mapconcat", 16), ("mapconcat", 64)]
 
 
-def _split_env(monkeypatch, split):
+def _split_plan(split):
     """Route segments: 'ticks' / 'positions' force one kernel for every segment
     ('positions' means the list kernel where the call qualifies for it, also
     on streams shorter than the planner's list-path minimum);
-    'position-kernel' forces the position kernel itself."""
-    if split == "position-kernel":
-        monkeypatch.setenv("EP_SPLIT", "positions")
-        monkeypatch.setenv("EP_NO_LIST", "1")
-    elif split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
-        if split == "positions":
-            monkeypatch.setenv("EP_FORCE_LIST", "1")
+    'position-kernel' forces the position kernel itself; 'runs' and 'rings'
+    take the scan kernel with run windows in registers (rings where a window
+    needs more runs than they hold) or with ring windows for every episode."""
+    return {"auto": [], "ticks": ["ticks"], "positions": ["positions", "list"],
+            "position-kernel": ["positions", "no-list"], "runs": ["run-windows"],
+            "rings": ["ring-windows"]}[split]
 
 
-SPLITS = ["auto", "ticks", "positions", "position-kernel"]
+SPLITS = ["auto", "ticks", "positions", "position-kernel", "runs", "rings"]
 
 
 @pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("case", all_cases(), ids=lambda c: c["name"])
-def test_golden(fem, case, split, monkeypatch):
-    _split_env(monkeypatch, split)
+def test_golden(fem, case, split):
     _log("golden %s %s" % (case["name"], split))
     want = np.array(case["expect"]["count"], np.int64)
     for mode, P in MODES:
         got = _gpu(fem, case["times"], case["types"], case["ep_types"][None], case["t_low"][None],
-                   case["t_high"][None], mode, P)
+                   case["t_high"][None], mode, P, plan=_split_plan(split))
         _check(got, want, "%s %s P=%d" % (case["name"], mode, P))
 
 
@@ -91,8 +88,7 @@ def test_boundary_miss_is_repaired(fem):
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_fuzz_small_streams(fem, split, monkeypatch):
-    _split_env(monkeypatch, split)
+def test_fuzz_small_streams(fem, split):
     rng = np.random.default_rng(31)
     checked = 0
     for trial in range(60):
@@ -100,27 +96,21 @@ def test_fuzz_small_streams(fem, split, monkeypatch):
         n_types = int(rng.integers(1, 6))
         N = int(rng.integers(1, 6))
         times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 4)))
-        # windows whose live runs fit the kernels (at most 4)
         ep, lo, hi = W.random_episodes(rng, int(rng.integers(1, 80)), N, n_types, max_hi=6)
-        ok = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1) if N > 1 else np.ones(ep.shape[0], bool)
-        ep, lo, hi = ep[ok], lo[ok], hi[ok]
-        if ep.shape[0] == 0:
-            continue
         want = oracle.count(times, types, ep, lo, hi)
         for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 2), ("mapconcat", 5),
                         ("mapconcat", 16), ("mapconcat", max(1, n))]:
-            got = _gpu(fem, times, types, ep, lo, hi, mode, P)
+            got = _gpu(fem, times, types, ep, lo, hi, mode, P, plan=_split_plan(split))
             _check(got, want, "fuzz trial %d n=%d N=%d %s P=%d" % (trial, n, N, mode, P))
             checked += 1
     assert checked > 200
 
 
 @pytest.mark.parametrize("split", ["auto", "positions"])
-def test_fuzz_large_type_values(fem, split, monkeypatch):
+def test_fuzz_large_type_values(fem, split):
     # node types spread over the whole uint16 range (the filter then maps
     # types to slots through the 65,536-bit type set instead of a byte table),
     # next to small ones (the byte table)
-    _split_env(monkeypatch, split)
     rng = np.random.default_rng(43)
     for trial in range(24):
         n = int(rng.integers(1, 5000))
@@ -139,7 +129,7 @@ def test_fuzz_large_type_values(fem, split, monkeypatch):
         lo = np.minimum(lo, hi - 1)
         want = oracle.count(times, types, ep, lo, hi)
         for mode, P in [("auto", 0), ("mapconcat", 3), ("mapconcat", 64)]:
-            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
+            _check(_gpu(fem, times, types, ep, lo, hi, mode, P, plan=_split_plan(split)), want,
                    "large types trial %d n=%d S=%d %s P=%d" % (trial, n, S, mode, P))
 
 
@@ -169,13 +159,12 @@ def _plant_edges(rng, times, types, ep, lo, hi, per_episode):
 
 
 @pytest.mark.parametrize("prune", ["on", "off"])
-def test_list_pruning_windows(fem, prune, monkeypatch):
+def test_list_pruning_windows(fem, prune):
     # the list pruning drops entries with no neighbour entry in their windows:
     # sparse multi-block streams over many types (most entries left out),
     # chains planted on the interval ends and at block edges, dense and sparse
     # blocks in time
-    _split_env(monkeypatch, "positions")
-    monkeypatch.setenv("EP_FORCE_PRUNE" if prune == "on" else "EP_NO_PRUNE", "1")
+    plan = _split_plan("positions") + ["prune" if prune == "on" else "no-prune"]
     rng = np.random.default_rng(59)
     for trial in range(36):
         n = int(rng.integers(3000, 21000))
@@ -194,7 +183,7 @@ def test_list_pruning_windows(fem, prune, monkeypatch):
         times, types = _plant_edges(rng, times, types, ep, lo, hi, int(rng.integers(1, 12)))
         want = oracle.count(times, types, ep, lo, hi)
         for P in (1, 3, 64):
-            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True)
+            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True, plan=plan)
             assert st["kernels"] & 4, "the list path was not taken"
             assert bool(st["kernels"] & 8) == (prune == "on")
             _check(got, want, "pruning %s trial %d n=%d S=%d N=%d gap<=%d P=%d"
@@ -202,12 +191,11 @@ def test_list_pruning_windows(fem, prune, monkeypatch):
 
 
 @pytest.mark.parametrize("order", ["grouped", "plain"])
-def test_tick_kernel_episode_groups_by_steps(fem, order, monkeypatch):
+def test_tick_kernel_episode_groups_by_steps(fem, order):
     # the tick kernel may take episodes ordered by their doubling steps, each
     # workgroup running its own group's steps: many episodes with windows of
     # every width (1 to 63 ticks), mixed in the table
-    monkeypatch.setenv("EP_SPLIT", "ticks")
-    monkeypatch.setenv("EP_FORCE_GROUP_STEPS" if order == "grouped" else "EP_NO_GROUP_STEPS", "1")
+    plan = ["ticks", "group-steps" if order == "grouped" else "no-group-steps"]
     rng = np.random.default_rng(67)
     for trial in range(6):
         n = int(rng.integers(2000, 20000))
@@ -220,7 +208,7 @@ def test_tick_kernel_episode_groups_by_steps(fem, order, monkeypatch):
         lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
         want = oracle.count(times, types, ep, lo, hi)
         for P in (0, 7, 64):
-            got = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P)
+            got = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, plan=plan)
             _check(got, want, "steps %s trial %d n=%d S=%d N=%d P=%d" % (order, trial, n, S, N, P))
 
 
@@ -243,8 +231,7 @@ def test_validate_rejects_unsorted(fem):
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_extreme_times(fem, split, monkeypatch):
-    _split_env(monkeypatch, split)
+def test_extreme_times(fem, split):
     # times at both ends of the int32 range: cut and window arithmetic must not overflow
     lo32, hi32 = -2 ** 31, 2 ** 31 - 1
     times = np.array([lo32, lo32, lo32 + 1, lo32 + 3, 0, 1, 2, hi32 - 3, hi32 - 1, hi32, hi32], np.int32)
@@ -257,7 +244,8 @@ def test_extreme_times(fem, split, monkeypatch):
         hi = np.array([hi], np.int32)
         want = oracle.count(times, types, e, lo, hi)
         for mode, P in MODES:
-            _check(_gpu(fem, times, types, e, lo, hi, mode, P), want, "extreme %s %s P=%d" % (row, mode, P))
+            _check(_gpu(fem, times, types, e, lo, hi, mode, P, plan=_split_plan(split)), want,
+                   "extreme %s %s P=%d" % (row, mode, P))
 
 
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "level2", "longchain"])
@@ -274,39 +262,43 @@ def test_config_small(fem, name):
         assert st["fallbacks"] == 0
 
 
-@pytest.mark.parametrize("layout", ["scan", "machine-lanes", "ticks", "positions", "ticks-machine-lanes",
+@pytest.mark.parametrize("layout", ["scan", "scan-rings", "machine-lanes", "ticks", "positions",
+                                    "ticks-machine-lanes",
                                     "position-kernel", "position-kernel-machine-lanes",
                                     "positions-machine-lanes", "positions-unpruned"])
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "longchain"])
-def test_config_small_other_kernels(fem, name, layout, monkeypatch):
-    # the same counts from the scan Map kernel (run windows, every event), the
-    # tick kernel, the list kernel ('positions' where the call has few
-    # episodes; with the lists pruned, or not), the position kernel, each
-    # with one machine per lane too
+def test_config_small_other_kernels(fem, name, layout):
+    # the same counts from the scan Map kernel (run or ring windows, every
+    # event), the tick kernel, the list kernel ('positions' where the call
+    # has few episodes; with the lists pruned, or not), the position kernel,
+    # each with one machine per lane too
+    plan = []
     if layout == "scan":
-        monkeypatch.setenv("EP_FORCE_SCAN", "1")
+        plan.append("run-windows")
+    if layout == "scan-rings":
+        plan.append("ring-windows")
     if "machine-lanes" in layout:
-        monkeypatch.setenv("EP_LANES", "machine")
+        plan.append("machine-lanes")
     if layout.startswith("ticks"):
-        monkeypatch.setenv("EP_SPLIT", "ticks")
+        plan.append("ticks")
     if layout.startswith("positions"):
-        monkeypatch.setenv("EP_SPLIT", "positions")
-        monkeypatch.setenv("EP_FORCE_LIST", "1")
-        monkeypatch.setenv("EP_NO_PRUNE" if layout.endswith("unpruned") else "EP_FORCE_PRUNE", "1")
+        plan += ["positions", "list", "no-prune" if layout.endswith("unpruned") else "prune"]
     if layout.startswith("position-kernel"):
-        monkeypatch.setenv("EP_SPLIT", "positions")
-        monkeypatch.setenv("EP_NO_LIST", "1")
+        plan += ["positions", "no-list"]
     wl = W.make_small(name)
     want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
     for mode, P in [("auto", 0), ("mapconcat", 64), ("mapconcat", 1000)]:
-        got = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P)
+        got = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, plan=plan)
         _check(got, want, "%s %s %s P=%d" % (name, layout, mode, P))
 
 
-@pytest.mark.parametrize("split", ["auto", "ticks", "position-kernel"])
-def test_fuzz_wide_windows(fem, split, monkeypatch):
-    _split_env(monkeypatch, split)
-    # t_high up to 60 (64-bit windows) and beyond 63 (run windows), t_low near t_high
+@pytest.mark.parametrize("split", ["auto", "ticks", "position-kernel", "runs", "rings", "no-split"])
+def test_fuzz_wide_windows(fem, split):
+    # t_high up to 60 (64-bit windows) and beyond 63 (run windows in registers
+    # or rings), t_low near t_high; every episode of the table is counted (a
+    # call mixing window kinds runs one group per kind, or with 'no-split' the
+    # widest kind for all)
+    plan = ["no-split"] if split == "no-split" else _split_plan(split)
     rng = np.random.default_rng(41)
     for trial in range(30):
         n = int(rng.integers(50, 3000))
@@ -316,20 +308,10 @@ def test_fuzz_wide_windows(fem, split, monkeypatch):
         hi = rng.integers(20, 120, size=(40, N - 1)).astype(np.int32)
         lo = (hi - rng.integers(1, 60, size=hi.shape)).clip(0).astype(np.int32)
         lo = np.minimum(lo, hi - 1)
-        if trial % 2 == 0:
-            # within 64-bit windows: any t_low works
-            sel = (hi <= 63).all(axis=1)
-        else:
-            # a call with a window beyond 63 ticks uses run windows for every
-            # episode, so each must fit 4 runs
-            sel = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1)
-        ep, lo, hi = ep[sel], lo[sel], hi[sel]
-        if ep.shape[0] == 0:
-            continue
         want = oracle.count(times, types, ep, lo, hi)
         for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 7), ("mapconcat", 64)]:
-            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
-                   "wide trial %d %s P=%d" % (trial, mode, P))
+            got = _gpu(fem, times, types, ep, lo, hi, mode, P, plan=plan)
+            _check(got, want, "wide trial %d %s P=%d" % (trial, mode, P))
 
 
 def test_ptpe_config_full_size(fem):
@@ -363,39 +345,38 @@ def test_list_configs_full_size(fem, name):
     _check(got, want, "%s full" % name)
 
 
-def test_level2_full_size_sampled(fem):
+def test_level2_full_size(fem):
     # the level-2 sweep at full size, AUTO launch (episodes grouped by their
-    # doubling steps, closure misses queued for the repair kernel), checked on
-    # evenly spaced episodes
+    # doubling steps, closure misses queued for the repair kernel), every one
+    # of the 16,384 episodes against the oracle
     wl = W.make("level2")
     got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "auto", stats=True)
     _log("level2 full: plan %s" % st)
     assert st["repairs"] > 0
-    idx = np.linspace(0, wl.n_episodes - 1, 96).astype(int)
-    want = oracle.count(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx], wl.t_high[idx])
-    _check(got[idx], want, "level2 full sampled")
+    t0 = time.time()
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    _log("oracle %.1fs" % (time.time() - t0))
+    _check(got, want, "level2 full")
 
 
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "level2", "longchain"])
-def test_config_small_separate_closure_and_tree(fem, name, monkeypatch):
+def test_config_small_separate_closure_and_tree(fem, name):
     # the three-launch path (closure kernel, tree launches, finish kernel) that
     # calls with more than 512 segments take, forced for every segment count
-    monkeypatch.setenv("EP_NO_REDUCE", "1")
     wl = W.make_small(name)
     want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
     for mode, P in [("auto", 0), ("mapconcat", 2), ("mapconcat", 64), ("mapconcat", 300)]:
-        got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, stats=True)
+        got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, stats=True,
+                       plan=["no-reduce"])
         _check(got, want, "%s separate %s P=%d" % (name, mode, P))
         assert st["fallbacks"] == 0
 
 
 @pytest.mark.parametrize("repairs", ["queued", "inline"])
-def test_fuzz_separate_closure_and_tree(fem, repairs, monkeypatch):
+def test_fuzz_separate_closure_and_tree(fem, repairs):
     # misses are queued for the repair kernel, or (past the queue's capacity,
     # forced here) repaired by the closure kernel where they are found
-    monkeypatch.setenv("EP_NO_REDUCE", "1")
-    if repairs == "inline":
-        monkeypatch.setenv("EP_NO_REPAIR_QUEUE", "1")
+    plan = ["no-reduce"] + (["no-repair-queue"] if repairs == "inline" else [])
     rng = np.random.default_rng(37)
     for trial in range(30):
         n = int(rng.integers(1, 400))
@@ -403,11 +384,121 @@ def test_fuzz_separate_closure_and_tree(fem, repairs, monkeypatch):
         N = int(rng.integers(1, 6))
         times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 4)))
         ep, lo, hi = W.random_episodes(rng, int(rng.integers(1, 60)), N, n_types, max_hi=6)
-        ok = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1) if N > 1 else np.ones(ep.shape[0], bool)
-        ep, lo, hi = ep[ok], lo[ok], hi[ok]
-        if ep.shape[0] == 0:
-            continue
         want = oracle.count(times, types, ep, lo, hi)
         for mode, P in [("mapconcat", 3), ("mapconcat", 16), ("mapconcat", max(1, n))]:
-            _check(_gpu(fem, times, types, ep, lo, hi, mode, P), want,
+            _check(_gpu(fem, times, types, ep, lo, hi, mode, P, plan=plan), want,
                    "separate fuzz %d n=%d %s P=%d" % (trial, n, mode, P))
+
+
+def _narrow_long_stream(rng, n, n_types, spacing):
+    """Events on a sparse time axis: gaps U{1..spacing}, so that a window far
+    from zero holds many separate candidate runs."""
+    gaps = rng.integers(1, spacing + 1, size=n)
+    times = np.cumsum(gaps).astype(np.int32)
+    types = rng.integers(0, n_types, size=n).astype(np.uint16)
+    return times, types
+
+
+LONG_WINDOWS = [(60, 64), (90, 100), (99, 100), (0, 1000), (999, 1000), (500, 510), (37, 200), (250, 251)]
+
+
+@pytest.mark.parametrize("split", ["auto", "rings", "no-split", "no-reduce", "positions"])
+def test_long_narrow_windows(fem, split):
+    # windows beyond 63 ticks whose candidates can form more live runs than
+    # registers hold (floor(t_high / (t_high - t_low + 1)) + 1 > 4): the ring
+    # windows count them exactly, next to bit-window and register-run episodes
+    plan = {"no-split": ["no-split"], "no-reduce": ["no-reduce"]}.get(split) or _split_plan(split)
+    rng = np.random.default_rng(71)
+    for trial in range(16):
+        n = int(rng.integers(200, 4000))
+        n_types = int(rng.integers(2, 5))
+        times, types = _narrow_long_stream(rng, n, n_types, int(rng.integers(1, 4)))
+        N = int(rng.integers(2, 5))
+        S = int(rng.integers(4, 40))
+        ep = rng.integers(0, n_types, size=(S, N)).astype(np.uint16)
+        pick = rng.integers(0, len(LONG_WINDOWS) + 1, size=(S, N - 1))
+        lo = np.zeros((S, N - 1), np.int32)
+        hi = np.zeros((S, N - 1), np.int32)
+        for (e, j), w in np.ndenumerate(pick):
+            if w < len(LONG_WINDOWS):
+                lo[e, j], hi[e, j] = LONG_WINDOWS[w]
+            else:  # a short window (bit masks when the whole episode stays under 64)
+                hi[e, j] = int(rng.integers(1, 40))
+                lo[e, j] = int(rng.integers(0, hi[e, j]))
+        want = oracle.count(times, types, ep, lo, hi)
+        _log("long windows trial %d n=%d S=%d N=%d" % (trial, n, S, N))
+        for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 3), ("mapconcat", 64)]:
+            got, st = _gpu(fem, times, types, ep, lo, hi, mode, P, stats=True, plan=plan)
+            _check(got, want, "long windows %s trial %d %s P=%d" % (split, trial, mode, P))
+            assert st["groups"] == 1 or split != "no-split"
+
+
+def test_ring_window_at_capacity(fem):
+    # (99,100] over events of one type on every other tick: 51 runs live at
+    # once, the bound, in every segment layout
+    times = np.arange(0, 4000, 2, dtype=np.int32)
+    types = np.zeros(times.size, np.uint16)
+    types[rng_pick(times.size)] = 1
+    ep = np.array([[0, 1], [0, 0], [1, 0]], np.uint16)
+    lo = np.array([[99], [99], [99]], np.int32)
+    hi = np.array([[100], [100], [100]], np.int32)
+    want = oracle.count(times, types, ep, lo, hi)
+    assert want[1] > 0
+    for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 2), ("mapconcat", 33), ("mapconcat", 500)]:
+        got, st = _gpu(fem, times, types, ep, lo, hi, mode, P, stats=True)
+        _check(got, want, "ring at capacity %s P=%d" % (mode, P))
+        assert st["kernels"] & 16 and st["max_runs"] >= 51
+
+
+def rng_pick(n):
+    return np.random.default_rng(5).choice(n, size=n // 7, replace=False)
+
+
+def test_mixed_window_kinds(fem):
+    # one table needing bit windows, runs in registers and rings: split into
+    # one group per kind, or counted with the widest kind for all
+    rng = np.random.default_rng(73)
+    times, types = _narrow_long_stream(rng, 3000, 2, 2)
+    ep = np.array([[0, 1], [0, 1], [0, 1], [1, 0], [0, 0]], np.uint16)
+    lo = np.array([[10], [0], [20], [0], [99]], np.int32)
+    hi = np.array([[11], [100], [21], [64], [100]], np.int32)
+    want = oracle.count(times, types, ep, lo, hi)
+    for plan, groups in [([], 3), (["no-split"], 1)]:
+        for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 16)]:
+            got, st = _gpu(fem, times, types, ep, lo, hi, mode, P, stats=True, plan=plan)
+            _check(got, want, "mixed %s %s P=%d" % (plan, mode, P))
+            assert st["groups"] == groups
+
+
+@pytest.mark.parametrize("reduce", ["fused", "separate"])
+@pytest.mark.parametrize("name", ["tiny", "ptpe", "longchain"])
+def test_whole_stream_recount(fem, name, reduce):
+    # the whole-stream recount that guards repair-list overflow and tree
+    # misses, forced for every episode: the reduction kernel's recount and
+    # the result kernel's (three-launch path)
+    wl = W.make_small(name)
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    plan = ["recount"] + (["no-reduce"] if reduce == "separate" else [])
+    for mode, P in [("ptpe", 0), ("mapconcat", 2), ("mapconcat", 64)]:
+        got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, stats=True,
+                       plan=plan)
+        _check(got, want, "%s recount %s %s P=%d" % (name, reduce, mode, P))
+        assert st["fallbacks"] == wl.n_episodes
+
+
+def test_plain_entry_point(fem):
+    # ep_count_episodes itself (no options: the planner's choice), on torch's
+    # current stream
+    import ctypes
+    wl = W.make_small("ptpe")
+    want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
+    t, y = fem.to_device(wl.times, wl.types, "cuda")
+    out = torch.full((wl.n_episodes,), -5, dtype=torch.int64, device="cuda")
+    table = fem.EpisodeTable(wl.ep_types, wl.t_low, wl.t_high)
+    lib = fem.load_library()
+    status = lib.ep_count_episodes(t.data_ptr(), y.data_ptr(), wl.n_events, table.as_struct(),
+                                   wl.n_episodes, out.data_ptr(),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert status == 0
+    torch.cuda.synchronize()
+    _check(out.cpu().numpy(), want, "plain entry point")

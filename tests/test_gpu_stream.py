@@ -39,9 +39,9 @@ def _check(got, want, label):
             label, int((got != want).sum()), bad.tolist(), got[bad].tolist(), want[bad].tolist()))
 
 
-def _run(fem, times, types, ep, lo, hi, cuts, label, mode="auto", upper_only=False, every=True):
+def _run(fem, times, types, ep, lo, hi, cuts, label, mode="auto", upper_only=False, every=True, plan=None):
     """Push the stream cut at `cuts` (sorted indices) and check after each push."""
-    st = fem.EpisodeStream(ep, None if upper_only else lo, hi, mode=mode, upper_only=upper_only)
+    st = fem.EpisodeStream(ep, None if upper_only else lo, hi, mode=mode, upper_only=upper_only, plan=plan)
     bounds = [0] + list(cuts) + [times.size]
     try:
         for i in range(len(bounds) - 1):
@@ -68,13 +68,15 @@ def test_stream_golden_every_split(fem, case):
         _run(fem, times, types, ep, lo, hi, [c], "%s cut %d" % (case["name"], c))
 
 
-@pytest.mark.parametrize("mode", ["auto", "mapconcat", "mapconcat-list"])
-def test_stream_fuzz(fem, mode, monkeypatch):
+@pytest.mark.parametrize("mode", ["auto", "mapconcat", "mapconcat-list", "mapconcat-rings"])
+def test_stream_fuzz(fem, mode):
+    plan = None
     if mode == "mapconcat-list":
         # few episodes through the filter and the list kernel on every segment
-        monkeypatch.setenv("EP_SPLIT", "positions")
-        monkeypatch.setenv("EP_FORCE_LIST", "1")
-        mode = "mapconcat"
+        plan = ["positions", "list"]
+    if mode == "mapconcat-rings":
+        plan = ["ring-windows"]
+    mode = "auto" if mode == "auto" else "mapconcat"
     rng = np.random.default_rng(71)
     for trial in range(40):
         n = int(rng.integers(1, 1500))
@@ -83,18 +85,14 @@ def test_stream_fuzz(fem, mode, monkeypatch):
         times, types = W.random_stream(rng, n, n_types, max_gap=int(rng.integers(0, 5)))
         S = int(rng.integers(1, 40))
         ep = rng.integers(0, n_types, size=(S, N)).astype(np.uint16)
-        top = 12 if trial % 3 else 90  # some windows beyond 63 ticks (run windows)
+        # some windows beyond 63 ticks, narrow ones too (runs in registers or rings)
+        top = 12 if trial % 3 else 120
         hi = rng.integers(1, top, size=(S, N - 1)).astype(np.int32)
         lo = (hi - rng.integers(1, 12, size=hi.shape)).clip(0).astype(np.int32)
         lo = np.minimum(lo, hi - 1)
-        if top > 63:
-            ok = (hi // (hi - lo + 1) + 1 <= 4).all(axis=1) if N > 1 else np.ones(S, bool)
-            ep, lo, hi = ep[ok], lo[ok], hi[ok]
-            if ep.shape[0] == 0:
-                continue
         k = int(rng.integers(1, 8))
         cuts = np.sort(rng.integers(0, n + 1, size=k))  # repeats give empty batches
-        _run(fem, times, types, ep, lo, hi, cuts.tolist(), "fuzz %d %s" % (trial, mode), mode=mode)
+        _run(fem, times, types, ep, lo, hi, cuts.tolist(), "fuzz %d %s" % (trial, mode), mode=mode, plan=plan)
 
 
 def test_stream_upper_only(fem):

@@ -40,53 +40,45 @@ def _check(got, want, label):
             label, int((got != want).sum()), bad.tolist(), got[bad].tolist(), want[bad].tolist()))
 
 
-def _split_env(monkeypatch, split):
-    if split == "position-kernel":
-        monkeypatch.setenv("EP_SPLIT", "positions")
-        monkeypatch.setenv("EP_NO_LIST", "1")
-    elif split == "scan":
-        monkeypatch.setenv("EP_FORCE_SCAN", "1")
-    elif split != "auto":
-        monkeypatch.setenv("EP_SPLIT", split)
-        if split == "positions":
-            monkeypatch.setenv("EP_FORCE_LIST", "1")
+def _split_plan(split):
+    return {"auto": [], "ticks": ["ticks"], "positions": ["positions", "list"],
+            "position-kernel": ["positions", "no-list"], "scan": ["run-windows"],
+            "rings": ["ring-windows"]}[split]
 
 
-def _upper(fem, times, types, ep, hi, mode, P=0):
+def _upper(fem, times, types, ep, hi, mode, P=0, plan=None):
     t, y = fem.to_device(times, types, "cuda")
-    got = fem.count_episodes(t, y, ep, None, hi, mode=mode, n_segments=P, upper_only=True)
+    got = fem.count_episodes(t, y, ep, None, hi, mode=mode, n_segments=P, upper_only=True, plan=plan)
     torch.cuda.synchronize()
     return got.cpu().numpy()
 
 
-def _two_pass(fem, times, types, ep, lo, hi, theta, mode="auto", P=0):
+def _two_pass(fem, times, types, ep, lo, hi, theta, mode="auto", P=0, plan=None):
     t, y = fem.to_device(times, types, "cuda")
     counts, upper, kept = fem.count_two_pass(t, y, ep, lo, hi, threshold=theta, mode=mode,
-                                             n_segments=P)
+                                             n_segments=P, plan=plan)
     torch.cuda.synchronize()
     return counts.cpu().numpy(), upper.cpu().numpy(), kept
 
 
-SPLITS = ["auto", "ticks", "positions", "position-kernel", "scan"]
+SPLITS = ["auto", "ticks", "positions", "position-kernel", "scan", "rings"]
 MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 2), ("mapconcat", 7), ("mapconcat", 64)]
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_upper_only_golden(fem, split, monkeypatch):
-    _split_env(monkeypatch, split)
+def test_upper_only_golden(fem, split):
     for case in all_cases():
         ep, hi = case["ep_types"][None], case["t_high"][None]
         want = oracle.count_upper(case["times"], case["types"], ep, hi)
         if "upper" in case["expect"]:
             assert want[0] == case["expect"]["upper"][0]
         for mode, P in MODES:
-            _check(_upper(fem, case["times"], case["types"], ep, hi, mode, P), want,
+            _check(_upper(fem, case["times"], case["types"], ep, hi, mode, P, _split_plan(split)), want,
                    "upper %s %s %s P=%d" % (case["name"], split, mode, P))
 
 
 @pytest.mark.parametrize("split", SPLITS)
-def test_upper_only_fuzz(fem, split, monkeypatch):
-    _split_env(monkeypatch, split)
+def test_upper_only_fuzz(fem, split):
     rng = np.random.default_rng(53)
     for trial in range(30):
         n = int(rng.integers(1, 2000))
@@ -100,7 +92,7 @@ def test_upper_only_fuzz(fem, split, monkeypatch):
         hi = rng.integers(1, top, size=(S, N - 1)).astype(np.int32)
         want = oracle.count_upper(times, types, ep, hi)
         for mode, P in MODES:
-            _check(_upper(fem, times, types, ep, hi, mode, P), want,
+            _check(_upper(fem, times, types, ep, hi, mode, P, _split_plan(split)), want,
                    "upper fuzz %d %s %s P=%d" % (trial, split, mode, P))
 
 
@@ -167,25 +159,28 @@ def test_two_pass_edge_cases(fem):
     c, u, k = fem.count_two_pass(t, y, np.zeros((0, 2), np.uint16), np.zeros((0, 1), np.int32),
                                  np.zeros((0, 1), np.int32), threshold=1)
     assert c.numel() == 0 and u.numel() == 0 and k == 0
-    # a window A1 cannot hold ((99,100] needs 51 runs) is fine for a dropped episode
+    # a narrow window far from zero ((99,100]: up to 51 live candidate runs,
+    # ring windows in the exact pass): dropped at threshold 5, counted at 1
     times = np.array([0, 50, 100, 200], np.int32)
     types = np.array([0, 1, 0, 1], np.uint16)
     c, u, k = _two_pass(fem, times, types, ep, np.array([[99]], np.int32), np.array([[100]], np.int32), 5)
     assert c.tolist() == [-1] and u.tolist() == [2] and k == 0
+    c, u, k = _two_pass(fem, times, types, ep, np.array([[99]], np.int32), np.array([[100]], np.int32), 1)
+    want = oracle.count(times, types, ep, np.array([[99]], np.int32), np.array([[100]], np.int32))
+    assert c.tolist() == want.tolist() == [1] and u.tolist() == [2] and k == 1
 
 
-def test_two_pass_level2_full_size_sampled(fem):
-    # the level-2 sweep at full size, AUTO launch, checked on evenly spaced episodes
+def test_two_pass_level2_full_size(fem):
+    # the level-2 sweep at full size, AUTO launch, every one of the 16,384
+    # episodes against the oracle's two passes
     wl = W.make("level2")
     _log("two-pass level2 full: n=%d S=%d theta=%d" % (wl.n_events, wl.n_episodes, LEVEL2_THRESHOLD))
     got_c, got_u, kept = _two_pass(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high,
                                    LEVEL2_THRESHOLD)
     assert kept == int((got_u >= LEVEL2_THRESHOLD).sum())
-    idx = np.linspace(0, wl.n_episodes - 1, 96).astype(int)
     t0 = time.time()
-    want_c, want_u = oracle.two_pass(wl.times, wl.types, wl.ep_types[idx], wl.t_low[idx],
-                                     wl.t_high[idx], LEVEL2_THRESHOLD)
-    _log("oracle on %d sampled episodes %.1fs" % (idx.size, time.time() - t0))
-    _check(got_u[idx], want_u, "level2 two-pass upper")
-    _check(got_c[idx], want_c, "level2 two-pass counts")
+    want_c, want_u = oracle.two_pass(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, LEVEL2_THRESHOLD)
+    _log("oracle two passes %.1fs" % (time.time() - t0))
+    _check(got_u, want_u, "level2 two-pass upper")
+    _check(got_c, want_c, "level2 two-pass counts")
     assert 0 < kept < wl.n_episodes
