@@ -23,7 +23,9 @@ EP_OK = 0
 STATUS = {
     0: "EP_OK", -1: "EP_ERR_ARG", -2: "EP_ERR_NODES", -3: "EP_ERR_INTERVAL",
     -4: "EP_ERR_UNSORTED", -5: "EP_ERR_WORKSPACE", -6: "EP_ERR_HIP", -7: "EP_ERR_UNSUPPORTED",
+    -8: "EP_ERR_SCRATCH_LIMIT",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MODES = {"auto": 0, "ptpe": 1, "mapconcat": 2}
 MODE_NAMES = {v: k for k, v in MODES.items()}
 MAX_NODES = 16
@@ -108,6 +110,9 @@ def load_library(path: str | None = None):
     lib.ep_count_episodes_ex.restype = ctypes.c_int
     lib.ep_count_episodes_ex.argtypes = [vp, vp, i64, EpEpisodes, i64, vp, vp,
                                          ctypes.POINTER(EpOptions)]
+    lib.ep_count_episodes_noalloc.restype = ctypes.c_int
+    lib.ep_count_episodes_noalloc.argtypes = [vp, vp, i64, EpEpisodes, i64, vp, vp,
+                                              ctypes.POINTER(EpOptions)]
     lib.ep_count_two_pass.restype = ctypes.c_int
     lib.ep_count_two_pass.argtypes = [vp, vp, i64, EpEpisodes, i64, i64, vp, vp,
                                       ctypes.POINTER(ctypes.c_int64), vp, ctypes.POINTER(EpOptions)]

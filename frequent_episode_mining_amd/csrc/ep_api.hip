@@ -176,6 +176,30 @@ int scratch_release(int dev, ScratchBlock* b, hipStream_t stream) {
   return ok ? EP_OK : EP_ERR_HIP;
 }
 
+// Scratch of ep_count_episodes_noalloc: one fixed array per device, in the
+// library's code object (the loader places it when the code object is loaded
+// on a device, and it stays until the process ends).  Host code never passes
+// the array's name to a kernel: it takes the array's device address once per
+// device with hipGetSymbolAddress and uses that address everywhere.  Calls
+// share the array; calls that overlap on one device race.
+constexpr size_t kNoAllocScratchBytes = EP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[64] = {};
+
+// The device address of `scratch` on device `dev` (current), taken on first use.
+int noalloc_scratch(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EP_ERR_HIP;
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return EP_OK;
+}
+
 // Profiling session: per counting call, events around its phases.  Events
 // come from a pool that lives as long as the process, so recording adds no
 // event creation to the timed calls once the pool is warm.
@@ -280,7 +304,8 @@ extern "C" const char* ep_status_string(int status) {
     case EP_ERR_UNSORTED: return "event times are not non-decreasing";
     case EP_ERR_WORKSPACE: return "scratch allocation failed";
     case EP_ERR_HIP: return "HIP runtime error";
-    case EP_ERR_UNSUPPORTED: return "a delay window needs more candidate runs than EP_MAX_RUNS";
+    case EP_ERR_UNSUPPORTED: return "more candidates than max_candidates";
+    case EP_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the fixed array of ep_count_episodes_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -462,14 +487,14 @@ constexpr double kRingBudget = 2.0 * (1ull << 30);
 int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
                         hipStream_t stream, const ep_options* opt, const StreamHook* sh = nullptr,
-                        const int32_t* out_map = nullptr);
+                        const int32_t* out_map = nullptr, bool no_alloc = false);
 
 // A call whose episodes need different window kinds: one sub-call per kind,
 // each over its own episodes and writing their counts through an index map
 // into the caller's out_counts (the sub-calls' outputs are disjoint).
 int count_split(const int32_t* times, const uint16_t* types, int64_t n_events, ep_episodes episodes,
                 int64_t S, int64_t* out_counts, hipStream_t stream, const ep_options* opt,
-                const std::vector<uint8_t>& cls) {
+                const std::vector<uint8_t>& cls, bool no_alloc) {
   const int32_t N = episodes.n_nodes;
   const int NI = N - 1;
   ep_stats acc{};
@@ -499,7 +524,7 @@ int count_split(const int32_t* times, const uint16_t* types, int64_t n_events, e
     ep_stats st{};
     o.stats = (opt && opt->stats) ? &st : nullptr;
     if (int status = count_episodes_impl(times, types, n_events, sub, Sc, out_counts, stream, &o, nullptr,
-                                         idx.data()))
+                                         idx.data(), no_alloc))
       return status;
     first = false;
     if (opt && opt->stats) {
@@ -522,7 +547,7 @@ int count_split(const int32_t* times, const uint16_t* types, int64_t n_events, e
 int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_events,
                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
                         hipStream_t stream, const ep_options* opt, const StreamHook* sh,
-                        const int32_t* out_map) {
+                        const int32_t* out_map, bool no_alloc) {
   // ---- host-side argument checks (nothing is enqueued before they pass)
   const int32_t N = episodes.n_nodes;
   const int64_t S = n_episodes;
@@ -571,7 +596,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   }
   if (S == 0) return EP_OK;
   if (!sh && !out_map && !(plan & EP_PLAN_NO_SPLIT) && n_events > 0 && __builtin_popcount(cls_seen) > 1)
-    return count_split(times, types, n_events, episodes, S, out_counts, stream, opt, cls);
+    return count_split(times, types, n_events, episodes, S, out_counts, stream, opt, cls, no_alloc);
   // window kind of the call: the widest any of its episodes needs
   const int K = max_bound <= 1 ? 1 : (max_bound <= 2 ? 2 : 4);
   const int run_win = max_bound <= EP_MAX_RUNS ? (K == 1 ? kRuns1 : (K == 2 ? kRuns2 : kRuns4)) : kRing;
@@ -683,6 +708,15 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   if (L.win == kRing && !(opt && opt->n_segments > 0)) {
     const double per_p = (double)S * (pmode == EP_MODE_PTPE ? 1 : N) * ring_slot_bytes;
     while (P > 1 && (double)P * per_p > kRingBudget) P >>= 1;
+  }
+  // the fixed scratch array of ep_count_episodes_noalloc: fewer segments
+  // until the tuple store (and the rings) fit beside the lists and the table
+  if (no_alloc && !(opt && opt->n_segments > 0) && pmode == EP_MODE_MAPCONCAT) {
+    const double fixed = (S <= kMaxListEpisodes ? list_bytes + 2.0 * n_lblocks * S * 4 : 0.0) +
+                         (double)S * (N * 2 + 24) + 2048 * 8 + 65536 * 8 + (1 << 20);
+    const double per_p = (double)S * (16.0 * 2 * N + 8) + 16 +
+                         (L.win == kRing ? (double)S * N * ring_slot_bytes : 0.0);
+    while (P > 1 && fixed + (double)P * per_p > (double)kNoAllocScratchBytes) P >>= 1;
   }
   L.mode = pmode;
   L.P = P;
@@ -837,8 +871,17 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
 
   mark();  // plan
   ScratchBlock* block = nullptr;
-  if (int st = scratch_acquire(dev, total, stream, &block)) return st;
-  char* ws = (char*)block->ptr;
+  char* ws = nullptr;
+  if (no_alloc) {
+    // the fixed array: nothing is allocated, a call that needs more is refused
+    if (total > kNoAllocScratchBytes) return EP_ERR_SCRATCH_LIMIT;
+    void* base = nullptr;
+    if (int st = noalloc_scratch(dev, &base)) return st;
+    ws = (char*)base;
+  } else {
+    if (int st = scratch_acquire(dev, total, stream, &block)) return st;
+    ws = (char*)block->ptr;
+  }
   int status = EP_OK;
   mark();  // malloc
   do {
@@ -874,10 +917,25 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
 
     // episode table, spans, node slots and the node-type set, written
     // straight into pinned staging; the set-up kernel copies it to the device
+    // (no_alloc: written into a host buffer of the calling thread and copied
+    // to the scratch array ahead of the set-up kernel, on the stream)
     const void* tab_dev = nullptr;
+    bool staged = false;  // a staging slot is held (released after the set-up launch)
+    thread_local std::vector<char> na_host;
+    auto release_staging = [&](bool used) -> int {
+      if (!staged) return EP_OK;
+      staged = false;
+      return staging_release(dev, used, stream);
+    };
     {
       char* host = nullptr;
-      if ((status = staging_acquire(dev, host_bytes, &host, &tab_dev))) break;
+      if (no_alloc) {
+        if (na_host.size() < host_bytes) na_host.resize(host_bytes);
+        host = na_host.data();
+      } else {
+        if ((status = staging_acquire(dev, host_bytes, &host, &tab_dev))) break;
+        staged = true;
+      }
       memcpy(host, episodes.types, sizeof(uint16_t) * S * N);
       if (N > 1) {
         memcpy(host + sz_types, episodes.t_low, sizeof(int32_t) * S * (N - 1));
@@ -907,6 +965,11 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       }
       if (out_map)
         memcpy(host + (host_bytes - sz_omap), out_map, sizeof(int32_t) * S);
+      // pageable source: the copy has read it before the call returns
+      if (no_alloc && hipMemcpyAsync(ws, host, host_bytes, hipMemcpyHostToDevice, stream) != hipSuccess) {
+        status = EP_ERR_HIP;
+        break;
+      }
     }
 
     if (opt && opt->validate) {
@@ -918,12 +981,12 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       if (hipMemcpyAsync(&bad, d_cnt, sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
           hipStreamSynchronize(stream) != hipSuccess) {
         status = EP_ERR_HIP;
-        staging_release(dev, false, stream);
+        release_staging(false);
         break;
       }
       if (bad) {
         status = EP_ERR_UNSORTED;
-        staging_release(dev, false, stream);
+        release_staging(false);
         break;
       }
     }
@@ -934,13 +997,13 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ProfRecord rec{};
     {
       std::lock_guard<std::mutex> lock(g_prof_mu);
-      if (g_prof_on) {
+      if (g_prof_on && !no_alloc) {  // (events come from a pool that may grow)
         prof_which = g_prof_which;
         prof = (g_prof_calls++ % g_prof_every) == 0;
       }
     }
     if (prof && (status = prof_record_start(&rec, prof_which, stream))) {
-      staging_release(dev, false, stream);
+      release_staging(false);
       break;
     }
     // records boundary i when the session times it (every boundary, or the
@@ -957,10 +1020,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     sa.wave_search = P <= kWaveSearchMaxP ? 1 : 0;
     sa.tab_src = (const uint4*)tab_dev;
     sa.tab_dst = (uint4*)ws;
-    sa.tab_words = (int64_t)(host_bytes / sizeof(uint4));
+    sa.tab_words = no_alloc ? 0 : (int64_t)(host_bytes / sizeof(uint4));
     hipLaunchKernelGGL(setup_kernel, dim3(grid_for(setup_items(sa))), dim3(kBlock), 0, stream, sa);
     const bool launched = hipGetLastError() == hipSuccess;
-    if (int st = staging_release(dev, launched, stream)) status = st;
+    if (int st = release_staging(launched)) status = st;
     if (!launched) status = EP_ERR_HIP;
     if (status != EP_OK) break;
 
@@ -1205,7 +1268,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   } while (0);
 
   mark();  // finish launch
-  if (scratch_release(dev, block, stream) != EP_OK && status == EP_OK) status = EP_ERR_HIP;
+  if (block && scratch_release(dev, block, stream) != EP_OK && status == EP_OK) status = EP_ERR_HIP;
   mark();  // free
   return status;
 }
@@ -1305,6 +1368,13 @@ extern "C" int ep_count_episodes_ex(const int32_t* times, const uint16_t* types,
   }
   fprintf(stderr, "\n");
   return st;
+}
+
+extern "C" int ep_count_episodes_noalloc(const int32_t* times, const uint16_t* types, int64_t n_events,
+                                         ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                                         hipStream_t stream, const ep_options* opt) {
+  return count_episodes_impl(times, types, n_events, episodes, n_episodes, out_counts, stream, opt, nullptr,
+                             nullptr, true);
 }
 
 extern "C" int ep_count_two_pass(const int32_t* times, const uint16_t* types, int64_t n_events,

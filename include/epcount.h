@@ -73,7 +73,8 @@ typedef enum {
   EP_ERR_UNSORTED = -4,    /* validate: times are not non-decreasing */
   EP_ERR_WORKSPACE = -5,   /* scratch allocation failed */
   EP_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
-  EP_ERR_UNSUPPORTED = -7  /* ep_mine only: a size has more candidates than max_candidates */
+  EP_ERR_UNSUPPORTED = -7,   /* ep_mine only: a size has more candidates than max_candidates */
+  EP_ERR_SCRATCH_LIMIT = -8  /* ep_count_episodes_noalloc: the call needs more than EP_NOALLOC_SCRATCH_BYTES */
 } ep_status;
 
 /*
@@ -205,6 +206,32 @@ typedef struct {
 int ep_count_episodes_ex(const int32_t* times, const uint16_t* types, int64_t n_events,
                          ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
                          hipStream_t stream, const ep_options* opt);
+
+/*
+ * For callers that cannot allocate device memory (code being captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc): the same
+ * counts as ep_count_episodes_ex with the same arguments and options, but all
+ * scratch comes from one fixed array of EP_NOALLOC_SCRATCH_BYTES per device
+ * that the library's code object holds (placed when the library is first
+ * used on the device, kept until the process ends), and the call allocates
+ * nothing: no hipMalloc/hipFree, no pinned staging, no profiling events.  The
+ * episode table reaches the device by a stream-ordered copy from pageable
+ * host memory, which HIP reads before the call returns.
+ *   When opt leaves n_segments to the planner, MapConcatenate's P is lowered
+ *   until the plan fits the array (a speed trade, never a change of counts).
+ *   Returns EP_ERR_SCRATCH_LIMIT, before anything is enqueued, when the plan
+ *   still needs more scratch than the array holds (the need grows with
+ *   episodes x segments and, on the list path, with the stream length);
+ *   otherwise as ep_count_episodes_ex.
+ *   Every call on a device uses that device's one array, which keeps the last
+ *   call's contents: calls enqueued on one stream run one after another, but
+ *   calls that overlap on a device (other streams, other host threads without
+ *   ordering) race and give unspecified counts.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ep_count_episodes_noalloc(const int32_t* times, const uint16_t* types, int64_t n_events,
+                              ep_episodes episodes, int64_t n_episodes, int64_t* out_counts,
+                              hipStream_t stream, const ep_options* opt);
 
 /*
  * Two-pass elimination A2+A1 for a support threshold (two-pass elimination
