@@ -321,6 +321,9 @@ def main():
                          "(default: the workload's)")
     ap.add_argument("--two-pass-mining", action="store_true",
                     help="sym26: count every size from 2 on with the two-pass elimination")
+    ap.add_argument("--plan", default="",
+                    help="comma-separated planner switches (EP_PLAN_* names, e.g. prune,no-reduce); "
+                         "they choose kernels, never results")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -363,12 +366,13 @@ def main():
 
     scheme = args.scheme
     kept_box = [0]
+    plan = [p for p in args.plan.split(",") if p]
 
     cuts = np.linspace(0, wl.n_events, max(1, args.batches) + 1).astype(np.int64)
 
     def step():
         if scheme == "stream":
-            st = fem.EpisodeStream(table, mode=mode, n_segments=seg, stream=stream)
+            st = fem.EpisodeStream(table, mode=mode, n_segments=seg, stream=stream, plan=plan)
             for i in range(cuts.size - 1):
                 st.push(times[cuts[i]:cuts[i + 1]], types[cuts[i]:cuts[i + 1]], stream=stream)
             c = st.counts(stream=stream)
@@ -376,24 +380,24 @@ def main():
             return c, None
         if scheme == "two-pass":
             c, u, kept_box[0] = fem.count_two_pass(times, types, table, threshold=args.threshold,
-                                                   mode=mode, n_segments=seg, stream=stream)
+                                                   mode=mode, n_segments=seg, stream=stream, plan=plan)
             return c, u
         fem.count_episodes(times, types, table, mode=mode, n_segments=seg, out=out, stream=stream,
-                           upper_only=(scheme == "upper"))
+                           upper_only=(scheme == "upper"), plan=plan)
         return out, None
 
     if scheme == "stream":
         # the stream reports no plan: the first batch counted alone has the
         # same kernels (the list rule looks at the episodes and the batch size)
         _, st = fem.count_episodes(times[cuts[0]:cuts[1]], types[cuts[0]:cuts[1]], table, mode="mapconcat",
-                                   n_segments=seg, stats=True, stream=stream)
+                                   n_segments=seg, stats=True, stream=stream, plan=plan)
         st = dict(st, mode="mapconcat per batch", n_segments=0, repairs=0, fallbacks=0)
     elif scheme == "two-pass":
         _, _, _, st = fem.count_two_pass(times, types, table, threshold=args.threshold, mode=mode,
-                                         n_segments=seg, stats=True, stream=stream)
+                                         n_segments=seg, stats=True, stream=stream, plan=plan)
     else:
         _, st = fem.count_episodes(times, types, table, mode=mode, n_segments=seg, stats=True,
-                                   out=out, upper_only=(scheme == "upper"))
+                                   out=out, upper_only=(scheme == "upper"), plan=plan)
     log("plan: %s" % st)
     for _ in range(args.warmup):
         step()
@@ -537,6 +541,7 @@ def main():
                    "n_episodes": S, "n_nodes": wl.n_nodes, "mode": st["mode"],
                    "segments": st["n_segments"], "window_runs": st["max_runs"],
                    "repairs": st["repairs"], "fallbacks": st["fallbacks"],
+                   "plan": plan,
                    "scheme": {"alpha": "exact counts",
                               "upper": "relaxed episodes (lower bounds 0)",
                               "two-pass": "two-pass elimination, threshold %d, %d kept"

@@ -768,6 +768,30 @@ struct ClassLane {
 #pragma unroll
         for (int j = 0; j < N - 1; ++j) m[c][j] = age<W>(m[c][j], d);
       }
+    {
+      // classes with every window empty whose resets lie before t have
+      // identical futures (no candidate, and every later event is after both
+      // resets): merge them.  At a segment's first events this joins the
+      // machines started before the first event of the lane's list.
+      uint32_t empty = 0, acc = 0;
+#pragma unroll
+      for (int c = 0; c < MCH; ++c)
+        if (mem[c] && (int64_t)t > r[c]) {
+          Bits any = 0;
+#pragma unroll
+          for (int j = 0; j < N - 1; ++j) any |= m[c][j];
+          if (any == 0) {
+            empty |= 1u << c;
+            acc |= mem[c];
+          }
+        }
+      if (__popc(empty) >= 2) {
+        const int lowest = __ffs((int)empty) - 1;
+#pragma unroll
+        for (int c = 0; c < MCH; ++c)
+          if ((empty >> c) & 1u) mem[c] = (c == lowest) ? acc : 0u;
+      }
+    }
     if ((int64_t)t >= check_at) {
       // classes whose last reset lies more than Span back are identical: merge
       uint32_t stale = 0, acc = 0;
@@ -1181,40 +1205,78 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
     // one class: batches of kD entries read as kD / 2 aligned 16-byte loads
     // (a lane reads its list in whole lines, which stay useful even when the
     // L1 cannot hold every lane's line), the next batch's loads in flight.
-    // A batch starts at an even entry of the region (region starts are
-    // 16-byte aligned); entries before i or past the list are read (they lie
-    // in the region, or in the buffer's slack) and skipped.  The loads are
+    // A batch starts at an even entry of its block's region (region starts
+    // are 16-byte aligned); entries before the lane's cursor or past the list
+    // are read (they lie in the region, or in the buffer's slack) and skipped.
+    // Each lane carries its own cursor (block, region index) across blocks:
+    // the batch after a block's last one is the next block's first, loaded
+    // ahead like any other, so a wave's lanes never wait for one another at
+    // block ends.  Entries of the list lie after lo_t from the cursor on (the
+    // search above skipped the first block's earlier ones).  The loads are
     // unconditional so that the compiler can count them and wait only for the
     // batch about to be stepped through.
-    while (go && lane.single) {
-      const int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
-      const int32_t rel = (int32_t)(list - region);   // the list's first entry in the region
-      const int32_t first = i;                         // entries before it are done
-      const int32_t n_end = n_here;
-      int32_t j0 = (rel + i) & ~1;                     // even region index of the first batch
-      const int32_t j_last = (rel + n_end + 1) & ~1;   // clamp for the loads
-      const int4* v = (const int4*)region;
+    if (go && lane.single) {
+      const int64_t region_len = (int64_t)kListBlock * A.max_share;
+      const int4* v = (const int4*)(A.lists + b * region_len);  // the cursor's block region
+      int32_t rel = (int32_t)(list - A.lists - b * region_len);  // the list's first entry in it
+      int32_t n_end = n_here;
+      int32_t first = i;  // entries before it are done
+      int32_t j0 = (rel + i) & ~1;  // even region index of the current batch
+      if (j0 >= rel + n_end) {
+        // the first block holds nothing more for this lane: the next one
+        if (b < b_last) {
+          ++b;
+          open();
+          v = (const int4*)(A.lists + b * region_len);
+          rel = (int32_t)(list - A.lists - b * region_len);
+          n_end = n_here;
+          first = 0;
+          j0 = rel & ~1;
+        } else {
+          go = false;
+        }
+      }
       int4 cur[kD / 2];
 #pragma unroll
-      for (int q = 0; q < kD / 2; ++q) cur[q] = v[min(j0 + 2 * q, j_last) >> 1];
-      for (; go && j0 < rel + n_end; j0 += kD) {
+      for (int q = 0; q < kD / 2; ++q) cur[q] = v[min(j0 + 2 * q, (rel + n_end + 1) & ~1) >> 1];
+      while (go) {
+        // the batch after this one: the rest of this block, or the next block
+        const bool same = j0 + kD < rel + n_end;
+        const bool more = same || b < b_last;
+        const int4* nv = v;
+        int32_t n_rel = rel, n_n = n_end, n_j0 = j0 + kD;
+        if (!same && more) {
+          nv = (const int4*)(A.lists + (b + 1) * region_len);
+          n_rel = off_next;
+          n_n = cnt_next;
+          n_j0 = off_next & ~1;
+        }
         int4 nxt[kD / 2];
 #pragma unroll
-        for (int q = 0; q < kD / 2; ++q) nxt[q] = v[min(j0 + kD + 2 * q, j_last) >> 1];
+        for (int q = 0; q < kD / 2; ++q) nxt[q] = nv[min(n_j0 + 2 * q, (n_rel + n_n + 1) & ~1) >> 1];
 #pragma unroll
         for (int k = 0; k < kD; ++k) {
           const int32_t idx = j0 + k - rel;  // index within this episode's list
           const int4 w = cur[k >> 1];
           const int32_t t = (k & 1) ? w.z : w.x;
           const uint32_t lm = (uint32_t)((k & 1) ? w.w : w.y);
-          go = lane.step_one_if(go && idx >= first && idx < n_end && (int64_t)t > lo_t, t, lm) && go;
+          go = lane.step_one_if(go && idx >= first && idx < n_end, t, lm) && go;
         }
 #pragma unroll
         for (int q = 0; q < kD / 2; ++q) cur[q] = nxt[q];
+        if (!more) break;
+        if (same) {
+          j0 += kD;
+        } else {
+          ++b;
+          open();  // (list, n_here and the following block's bounds)
+          v = nv;
+          rel = n_rel;
+          n_end = n_n;
+          first = 0;
+          j0 = n_j0;
+        }
       }
-      if (!go || b >= b_last) break;
-      ++b;
-      open();
     }
   }
   lane.write(A, e, p, k_lane);
