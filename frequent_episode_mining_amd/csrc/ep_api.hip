@@ -260,16 +260,22 @@ constexpr int kMaxClassNodes = 8;
 constexpr int64_t kStreamSegEvents = 4096;
 constexpr int64_t kListMinEvents = 1 << 20;  // the list path pays off from streams of about this size  // a stream batch's segments hold about this many events at most
 
-// The hybrid rule (hybrid-algorithm section): the GPU is fully utilised by
-// PTPE when the episodes alone give every resident lane of every CU work.
-// Otherwise MapConcatenate with the smallest power-of-two P that does, kept
-// to >= 256 events per segment on average (>= 64 with fewer than 256
-// episodes, where the lanes are few) and P <= 2^20.
+// The hybrid rule (hybrid-algorithm section): PTPE when the episodes alone
+// give every resident lane of every CU work, here kPtpeFill times over;
+// otherwise MapConcatenate with the smallest power-of-two P that gives every
+// lane work, kept to >= 256 events per segment on average (>= 64 with fewer
+// than 256 episodes, where the lanes are few) and P <= 2^20.  The factor is
+// measured: on MI355X (196,608 resident tick-kernel lanes, 1M events, four
+// nodes) MapConcatenate was faster at every episode count up to 1,048,576
+// (5.3 x the lanes) and PTPE at 2,097,152 (10.7 x); a segment shares its
+// type bitmaps over all episodes of a workgroup, so PTPE's one pass per lane
+// over the whole stream pays off only far beyond one lane per episode.
+constexpr int64_t kPtpeFill = 6;
 int plan_rule(int64_t S, int32_t N, int64_t n, int32_t mode, int32_t n_segments, int32_t cu_count,
               int32_t lanes_per_cu, int32_t* out_mode, int32_t* out_segments) {
   const int64_t full = (int64_t)std::max(cu_count, 1) * std::max(lanes_per_cu, 1);
   int m = mode;
-  if (m == EP_MODE_AUTO) m = (S >= full) ? EP_MODE_PTPE : EP_MODE_MAPCONCAT;
+  if (m == EP_MODE_AUTO) m = (S >= kPtpeFill * full) ? EP_MODE_PTPE : EP_MODE_MAPCONCAT;
   int64_t P = 1;
   if (m == EP_MODE_MAPCONCAT) {
     if (n_segments > 0) {

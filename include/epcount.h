@@ -30,9 +30,10 @@
  *              tuples (Map rules 1-4, Figs. 4-5); a log-depth tree joins
  *              adjacent segments where the left exit b equals the right key a
  *              (Concatenate rules 1-3, Fig. 6).
- * AUTO picks PTPE when the episodes alone fill the GPU and MAPCONCAT
- * otherwise (hybrid-algorithm section: "fully utilized" test on episodes,
- * threads per block, multiprocessors and resident blocks per multiprocessor).
+ * AUTO picks PTPE when the episodes alone fill the GPU many times over and
+ * MAPCONCAT otherwise (hybrid-algorithm section: "fully utilized" test on
+ * episodes, threads per block, multiprocessors and resident blocks per
+ * multiprocessor; the margin is measured, see ep_plan).
  *
  * Conventions shared by all calls:
  *   - Device pointers point into memory of the current HIP device; host
@@ -390,8 +391,10 @@ void ep_stream_destroy(ep_stream* st);
  *   lanes_per_cu                   resident lanes per multiprocessor of the
  *                                  counting kernel (T_B * B_MP).
  *   out_mode, out_segments         results (host pointers).
- * Rule (hybrid-algorithm section): PTPE iff n_episodes >= cu_count *
- * lanes_per_cu; otherwise MAPCONCAT with the smallest power-of-two P such
+ * Rule (hybrid-algorithm section): PTPE iff n_episodes >= 6 * cu_count *
+ * lanes_per_cu (the factor measured on MI355X: MAPCONCAT was faster up to
+ * 5.3 times the resident lanes, PTPE from 10.7 times); otherwise MAPCONCAT
+ * with the smallest power-of-two P such
  * that lanes(P) >= cu_count * lanes_per_cu, where a lane carries the N
  * machines of one (segment, episode) for N <= 8 (lanes = n_episodes * P) and
  * one machine beyond (lanes = n_episodes * n_nodes * P); P is then raised

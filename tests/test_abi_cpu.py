@@ -170,8 +170,11 @@ def test_stream_host_errors():
 
 
 def test_planner_rule():
-    # episodes alone fill 256 CUs x 2048 lanes -> PTPE
-    assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
+    # episodes alone fill 256 CUs x 2048 lanes six times over -> PTPE; the
+    # measured crossover lies above one lane per episode
+    assert fem.plan(6 * 256 * 2048, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048) == ("ptpe", 1)
+    assert fem.plan(6 * 256 * 2048 - 1, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048)[0] == "mapconcat"
+    assert fem.plan(600_000, 4, 10 ** 7, cu_count=256, lanes_per_cu=2048)[0] == "mapconcat"
     # 1,024 four-node episodes: MapConcatenate; a lane carries the N machines of
     # one (segment, episode), so P is the smallest 2^q with S * P filling the device
     mode, P = fem.plan(1024, 4, 10 ** 6, cu_count=256, lanes_per_cu=2048)

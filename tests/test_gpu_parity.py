@@ -502,3 +502,27 @@ def test_plain_entry_point(fem):
     assert status == 0
     torch.cuda.synchronize()
     _check(out.cpu().numpy(), want, "plain entry point")
+
+
+def test_auto_takes_ptpe_when_episodes_fill_the_gpu(fem):
+    # AUTO chooses PTPE when the episodes fill every resident lane six times
+    # over (lanes per CU are at most 2,048, so this many always do); the
+    # counts are the oracle's either way
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = 6 * cus * 2048
+    rng = np.random.default_rng(89)
+    times, types = W.random_stream(rng, 200, 6, max_gap=3)
+    ep = rng.integers(0, 6, size=(S, 2)).astype(np.uint16)
+    hi = rng.integers(1, 8, size=(S, 1)).astype(np.int32)
+    lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
+    got, st = _gpu(fem, times, types, ep, lo, hi, "auto", stats=True)
+    assert st["mode"] == "ptpe" and st["n_segments"] == 1
+    t0 = time.time()
+    want = oracle.count(times, types, ep, lo, hi)
+    _log("auto ptpe: S=%d, oracle %.1fs" % (S, time.time() - t0))
+    _check(got, want, "auto ptpe")
+    # one episode fewer than the bound on a 2,048-lane device is still
+    # MapConcatenate on this one (its resident lanes per CU are fewer)
+    got2, st2 = _gpu(fem, times, types, ep[:S // 8], lo[:S // 8], hi[:S // 8], "auto", stats=True)
+    assert st2["mode"] == "mapconcat"
+    _check(got2, want[:S // 8], "auto mapconcat")
