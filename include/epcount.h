@@ -49,8 +49,27 @@
  *   - Inputs outside the documented domain (unsorted times) give unspecified
  *     counts unless `validate` is set in ep_options.
  *   - The library is thread-safe: concurrent calls never share a scratch
- *     block, and the pinned staging ring for the episode table is guarded by
- *     a lock.
+ *     block; the pinned staging ring for the episode table and each cached
+ *     per-device figure are guarded by locks.
+ *
+ * Where this boundary differs from an all-device, allocate-per-call design,
+ * and why:
+ *   - The episode table is HOST memory.  The planner must read every delay
+ *     bound before any launch: the window kind (bit masks, runs in registers,
+ *     rings) and capacity follow from each interval ("Design of
+ *     MapConcatenate": (t_low, t_high] per node pair; a window can hold up to
+ *     floor(t_high / (t_high - t_low + 1)) + 1 separate runs), the segment
+ *     halos from the largest Span (Map rules: machines start up to Span before
+ *     a cut), and the hybrid choice from the episode count.  Reading a device
+ *     table would cost a synchronisation per call; the library uploads the
+ *     table itself, stream-ordered.
+ *   - Scratch is cached per device (blocks grown on demand and kept) instead
+ *     of allocated and freed in every call: a stream-ordered allocation and
+ *     free per call cost more than the small workloads' whole count.  Callers
+ *     that must not allocate at all use ep_count_episodes_noalloc.
+ *   - Status codes beyond argument errors: EP_ERR_UNSUPPORTED (ep_mine's
+ *     candidate limit) and EP_ERR_SCRATCH_LIMIT (the fixed array of
+ *     ep_count_episodes_noalloc).  Every valid interval is counted.
  */
 #ifndef EPCOUNT_H
 #define EPCOUNT_H
