@@ -48,7 +48,8 @@ PHASES = {"map_filter_ms": "filter", "map_prune_ms": "prune", "map_ticks_ms": "t
 # the kernels and their traffic as they were).
 KERNEL_SOURCES = ["frequent_episode_mining_amd/csrc/ep_device.hpp",
                   "frequent_episode_mining_amd/csrc/ep_inst.hip",
-                  "frequent_episode_mining_amd/csrc/ep_kernels.hpp"]
+                  "frequent_episode_mining_amd/csrc/ep_kernels.hpp",
+                  "frequent_episode_mining_amd/csrc/ep_slice.hpp"]
 
 
 def log(msg):
@@ -234,8 +235,10 @@ def main_mine(args):
     rel = int(cnt[np.unique(wl.alphabet)].sum())  # size 1: each type's own events
     for k, lst in mining_candidates(mined, wl.bins).items():
         rel += sum(int(cnt[np.unique(np.array(t))].sum()) for t in lst)
+    # (the ticks phase: the tick kernel, and the type-sliced kernel for the
+    # two-node candidates)
     names = {"map_filter_ms": "filter_kernel", "map_prune_ms": "list_prune_kernel",
-             "map_ticks_ms": "map_ticks_kernel", "map_positions_ms": "map_bits_kernel"}
+             "map_ticks_ms": "map_ticks_kernel+map_slice_kernel", "map_positions_ms": "map_bits_kernel"}
     achieved = OPS_PER_RELEVANT_PAIR * rel / (kernel_ms / 1000.0) / 1e12 if kernel_ms > 0 else 0.0
     roofline = {"bound": "alu", "achieved": achieved, "peak": ALU_PEAK_TOPS, "unit": "TOP/s",
                 "frac": achieved / ALU_PEAK_TOPS, "traffic": None,
@@ -461,8 +464,10 @@ def main():
         pos_name = "map_list_kernel" if st["kernels"] & 4 else "map_bits_kernel"
     else:
         pos_name = "map_scan_kernel"
+    # (two-node episodes on the type-sliced kernel: it takes the tick kernel's slot)
     names = {"map_filter_ms": "filter_kernel", "map_prune_ms": "list_prune_kernel",
-             "map_ticks_ms": "map_ticks_kernel", "map_positions_ms": pos_name}
+             "map_ticks_ms": "map_slice_kernel" if st["kernels"] & 32 else "map_ticks_kernel",
+             "map_positions_ms": pos_name}
     kernel, kernel_ms = names[top], kprof[top] / max(kprof["calls"], 1)
     map_s = kernel_ms / 1000.0
     rel = relevant_pairs(wl)

@@ -13,10 +13,12 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "ep_device.hpp"
 #include "ep_kernels.hpp"
+#include "ep_slice.hpp"
 #include "epcount.h"
 
 namespace epk {
@@ -455,6 +457,7 @@ struct Launch {
   int split;       // 0: per-segment choice between tick and position kernels; 1: ticks; 2: positions
   bool list;       // sparse segments through the filter + list Map kernels (else the position kernel)
   bool prune;      // list path: the filter's lists pruned before the list Map kernel
+  bool slice;      // two-node episodes: every segment through the type-sliced kernel
   int slots;
   int n_machines;
 };
@@ -479,6 +482,106 @@ struct StreamHook {
   int64_t t_first;
   int64_t t_end;
 };
+
+// Tables of the type-sliced two-node kernel (map_slice_kernel): episodes
+// grouped by (node-0 type word, node-1 type, lo, hi), node-0 types ranked and
+// cut into words of 64 bits; groups of one word padded to whole workgroups.
+struct SliceHost {
+  std::vector<SliceGroup> groups;
+  std::vector<uint64_t> mask;
+  std::vector<int32_t> ep;    // 64 per group
+  std::vector<uint16_t> tab;  // kSliceTypes per workgroup
+  int64_t real_groups = 0;
+  int wg_groups = 0, n_wg = 0, n_brows = 0;
+};
+
+// Average episodes per group from which the planner takes the sliced kernel
+// (a group's lane steps its word of node-0 types at every node-1 tick).
+constexpr int64_t kSliceMinFill = 8;
+
+// false when the call does not fit the kernel: a node type >= kSliceTypes,
+// an episode given twice, or a window wider than 63 ticks
+bool slice_plan(const ep_episodes& eps, int64_t S, int n_machines, SliceHost* out) {
+  if (eps.n_nodes != 2 || S <= 0 || S >= (1 << 30)) return false;
+  std::vector<int32_t> a_rank((size_t)kSliceTypes, -1);
+  for (int64_t e = 0; e < S; ++e) {
+    const int a = eps.types[e * 2], b = eps.types[e * 2 + 1];
+    if (a >= kSliceTypes || b >= kSliceTypes || eps.t_high[e] > 63) return false;
+    a_rank[(size_t)a] = 0;
+  }
+  int32_t r = 0;
+  for (int y = 0; y < kSliceTypes; ++y)
+    if (a_rank[(size_t)y] == 0) a_rank[(size_t)y] = r++;
+  // one sort key per episode: group (word, node-1 type, lo, hi: 28 bits), then
+  // node-0 bit (6), then the episode (30)
+  std::vector<uint64_t> keyed((size_t)S);
+  for (int64_t e = 0; e < S; ++e) {
+    const uint64_t ra = (uint64_t)a_rank[eps.types[e * 2]];
+    const uint64_t gk = (((ra >> 6) * kSliceTypes + eps.types[e * 2 + 1]) * 64 + (uint64_t)eps.t_low[e]) * 64 +
+                        (uint64_t)eps.t_high[e];
+    keyed[(size_t)e] = (((gk << 6) | (ra & 63)) << 30) | (uint64_t)e;
+  }
+  std::sort(keyed.begin(), keyed.end());
+  const int wg = kBlock / n_machines;
+  SliceHost& h = *out;
+  h = SliceHost();
+  h.wg_groups = wg;
+  h.groups.reserve((size_t)S);
+  h.mask.reserve((size_t)S);
+  std::vector<int32_t> g_word;  // node-0 word of each group (-1: padding)
+  int32_t word = -1;
+  uint64_t prev_gk = ~0ull;
+  int prev_bit = -1;
+  auto add_group = [&](SliceGroup sg, int32_t wd) {
+    h.groups.push_back(sg);
+    h.mask.push_back(0ull);
+    h.ep.resize(h.ep.size() + 64, -1);
+    g_word.push_back(wd);
+  };
+  for (size_t i = 0; i < keyed.size(); ++i) {
+    const uint64_t gk = keyed[i] >> 36;
+    const int bit = (int)((keyed[i] >> 30) & 63);
+    const int64_t e = (int64_t)(keyed[i] & ((1ull << 30) - 1));
+    if (gk == prev_gk && bit == prev_bit) return false;  // an episode given twice
+    if (gk != prev_gk) {
+      const int32_t wd = (int32_t)(gk / ((uint64_t)kSliceTypes * 64 * 64));
+      if (wd != word) {
+        // a new node-0 word starts a new workgroup
+        while (!h.groups.empty() && h.groups.size() % wg) add_group(SliceGroup{0, 1, 0, 0}, -1);
+        word = wd;
+      }
+      add_group(SliceGroup{eps.t_low[e], eps.t_high[e], 0, (int32_t)eps.types[e * 2 + 1]}, word);
+      ++h.real_groups;
+      prev_gk = gk;
+    }
+    prev_bit = bit;
+    h.mask.back() |= 1ull << bit;
+    h.ep[(h.groups.size() - 1) * 64 + bit] = (int32_t)e;
+  }
+  const int64_t ng = (int64_t)h.groups.size();
+  h.n_wg = (int)((ng + wg - 1) / wg);
+  h.tab.assign((size_t)h.n_wg * kSliceTypes, 0);
+  h.n_brows = 1;
+  for (int w = 0; w < h.n_wg; ++w) {
+    uint16_t* tab = h.tab.data() + (size_t)w * kSliceTypes;
+    int32_t wword = -1, rows = 0;
+    for (int64_t g = (int64_t)w * wg; g < std::min<int64_t>(ng, (int64_t)(w + 1) * wg); ++g) {
+      if (g_word[(size_t)g] < 0) continue;
+      wword = g_word[(size_t)g];
+      // the node-1 type is parked in pad until its row is known
+      const int32_t b = h.groups[(size_t)g].pad;
+      if ((tab[b] >> 7) == 0) tab[b] = (uint16_t)(tab[b] | ((rows++ + 1) << 7));
+      h.groups[(size_t)g].brow = (tab[b] >> 7) - 1;
+      h.groups[(size_t)g].pad = 0;
+    }
+    if (wword >= 0)
+      for (int y = 0; y < kSliceTypes; ++y)
+        if (a_rank[(size_t)y] >= 0 && (a_rank[(size_t)y] >> 6) == wword)
+          tab[y] = (uint16_t)(tab[y] | ((a_rank[(size_t)y] & 63) + 1));
+    h.n_brows = std::max(h.n_brows, rows);
+  }
+  return true;
+}
 
 // Window kind each episode needs: bit windows when every t_high <= 63, run
 // windows in registers when every interval's live-run bound
@@ -782,13 +885,31 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     L.lds = 0;
   }
   L.slots = (pmode == EP_MODE_PTPE) ? 1 : 2 * N;
+  // two-node episodes: the type-sliced kernel takes every segment where the
+  // episodes fill its words (or where a plan switch asks for it; the switches
+  // that force another Map kernel keep it out)
+  SliceHost slc;
+  L.slice = false;
+  {
+    const uint32_t other = EP_PLAN_TICKS | EP_PLAN_POSITIONS | EP_PLAN_LIST | EP_PLAN_MACHINE_LANES |
+                           EP_PLAN_NO_SLICE;
+    const bool wanted = (plan & EP_PLAN_SLICE) || !(plan & other);
+    if (N == 2 && L.bits && wanted && slice_plan(episodes, S, L.n_machines, &slc) &&
+        ((plan & EP_PLAN_SLICE) || S >= kSliceMinFill * slc.real_groups)) {
+      L.slice = true;
+      L.list = false;
+      L.prune = false;
+      L.split = 1;
+    }
+  }
   if (log_on())
     fprintf(stderr,
             "epcount: S=%lld N=%d n=%lld U=%d mode=%s P=%d win=%s kernel=%s lanes=%s M=%d G=%d R=%d "
-            "CH=%d lds=%zu maxSpan=%lld ring=%u\n",
+            "CH=%d lds=%zu maxSpan=%lld ring=%u slice=%d groups=%lld wg=%d rows=%d\n",
             (long long)S, N, (long long)n_events, U, pmode == EP_MODE_PTPE ? "ptpe" : "mapconcat", P,
             win_name(L.win), L.bits ? "bits" : "scan", L.all_mach ? "class" : "machine", L.M, L.G, L.R,
-            L.CH, L.lds, (long long)max_span, L.win == kRing ? ring_cap : 0u);
+            L.CH, L.lds, (long long)max_span, L.win == kRing ? ring_cap : 0u, L.slice ? 1 : 0,
+            (long long)slc.real_groups, slc.n_wg, slc.n_brows);
 
   // tick kernel: episodes ordered by their doubling steps, so that an episode
   // group of narrow windows runs fewer steps than the call's widest needs
@@ -796,7 +917,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   // kernel's work, about episodes x events, is large enough to repay the
   // ordering's host time)
   std::vector<int32_t> ep_perm, group_k;
-  if (L.bits && L.split != 2 && S > L.G &&
+  if (L.bits && !L.slice && L.split != 2 && S > L.G &&
       ((double)S * (double)n_events >= 4294967296.0 || (plan & EP_PLAN_GROUP_STEPS))) {
     std::vector<int32_t> steps((size_t)S, 0);
     int32_t lo_k = INT32_MAX, hi_k = 0;
@@ -834,9 +955,14 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_slv = L.list ? align_up(sizeof(uint16_t) * 256 * S, 256) : 0;
   const size_t sz_perm = align_up(sizeof(int32_t) * ep_perm.size(), 256);
   const size_t sz_gk = align_up(sizeof(int32_t) * group_k.size(), 256);
+  const size_t sz_sgrp = L.slice ? align_up(sizeof(SliceGroup) * slc.groups.size(), 256) : 0;
+  const size_t sz_smask = L.slice ? align_up(sizeof(uint64_t) * slc.mask.size(), 256) : 0;
+  const size_t sz_sep = L.slice ? align_up(sizeof(int32_t) * slc.ep.size(), 256) : 0;
+  const size_t sz_stab = L.slice ? align_up(sizeof(uint16_t) * slc.tab.size(), 256) : 0;
+  const size_t sz_slice = sz_sgrp + sz_smask + sz_sep + sz_stab;
   const size_t sz_omap = out_map ? align_up(sizeof(int32_t) * S, 256) : 0;
-  const size_t host_bytes =
-      sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv + sz_perm + sz_gk + sz_omap;
+  const size_t host_bytes = sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv +
+                            sz_perm + sz_gk + sz_slice + sz_omap;
   // (+ slack: the list kernel's aligned batches may read two entries past the
   // last block's region)
   const size_t sz_lists = L.list ? align_up((size_t)list_bytes + 4 * sizeof(int2), 256) : 0;
@@ -903,6 +1029,10 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     uint16_t* d_slv = (uint16_t*)(ws + off); off += sz_slv;
     int32_t* d_perm = (int32_t*)(ws + off); off += sz_perm;
     int32_t* d_gk = (int32_t*)(ws + off); off += sz_gk;
+    SliceGroup* d_sgrp = (SliceGroup*)(ws + off); off += sz_sgrp;
+    uint64_t* d_smask = (uint64_t*)(ws + off); off += sz_smask;
+    int32_t* d_sep = (int32_t*)(ws + off); off += sz_sep;
+    uint16_t* d_stab = (uint16_t*)(ws + off); off += sz_stab;
     int32_t* d_omap = (int32_t*)(ws + off); off += sz_omap;
     int64_t* d_tau = (int64_t*)(ws + off); off += sz_tau;
     int32_t* d_beg = (int32_t*)(ws + off); off += sz_seg;
@@ -968,6 +1098,14 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         char* at = host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv;
         memcpy(at, ep_perm.data(), sizeof(int32_t) * ep_perm.size());
         memcpy(at + sz_perm, group_k.data(), sizeof(int32_t) * group_k.size());
+      }
+      if (L.slice) {
+        char* at = host + sz_types + 2 * sz_lohi + sz_span + sz_slot + sz_seen + sz_rank + sz_seps + sz_slv +
+                   sz_perm + sz_gk;
+        memcpy(at, slc.groups.data(), sizeof(SliceGroup) * slc.groups.size());
+        memcpy(at + sz_sgrp, slc.mask.data(), sizeof(uint64_t) * slc.mask.size());
+        memcpy(at + sz_sgrp + sz_smask, slc.ep.data(), sizeof(int32_t) * slc.ep.size());
+        memcpy(at + sz_sgrp + sz_smask + sz_sep, slc.tab.data(), sizeof(uint16_t) * slc.tab.size());
       }
       if (out_map)
         memcpy(host + (host_bytes - sz_omap), out_map, sizeof(int32_t) * S);
@@ -1055,7 +1193,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     // bitmaps once each (the kernel decides per group; the grid is mgrid)
     const int64_t seg_groups = (P + L.R - 1) / L.R;
     ma.eg_blocks = ma.n_egroups;
-    if (L.bits && L.split != 2) {
+    if (L.bits && !L.slice && L.split != 2) {
       int per_cu = 0;
       {
         std::lock_guard<std::mutex> lock(g_info_mu);
@@ -1130,6 +1268,17 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     }
     rec_at(3);
     if (skip_map) {
+      rec_at(4);
+    } else if (le == hipSuccess && L.slice) {
+      SliceArgs sl;
+      sl.times = times; sl.types = types; sl.tau = d_tau; sl.seg_beg = d_beg; sl.seg_end = d_end;
+      sl.ts = ts; sl.P = P; sl.n_machines = L.n_machines; sl.max_span = (int32_t)max_span;
+      sl.n_groups = (int32_t)slc.groups.size(); sl.wg_groups = slc.wg_groups; sl.n_wg = slc.n_wg;
+      sl.n_brows = slc.n_brows;
+      sl.groups = d_sgrp; sl.g_mask = d_smask; sl.g_ep = d_sep; sl.wg_tab = d_stab;
+      hipLaunchKernelGGL(map_slice_kernel, dim3((unsigned)((int64_t)P * slc.n_wg)), dim3(kBlock),
+                         slice_lds(slc.n_brows), stream, sl);
+      le = hipGetLastError();
       rec_at(4);
     } else if (le == hipSuccess && !L.bits) {
       rec_at(4);  // no tick kernel: an empty interval
@@ -1266,7 +1415,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       opt->stats->n_segments = P;
       opt->stats->max_runs = L.win == kBits32 ? 32 : L.win == kBits64 ? 64 : L.win == kRing ? (int32_t)ring_cap : K;
       opt->stats->kernels = (L.bits ? 1 : 0) | (L.all_mach ? 2 : 0) | (L.list ? 4 : 0) | (L.prune ? 8 : 0) |
-                            (L.win == kRing ? 16 : 0);
+                            (L.win == kRing ? 16 : 0) | (L.slice ? 32 : 0);
       opt->stats->repairs = (int64_t)cnt[0];
       opt->stats->fallbacks = (int64_t)cnt[1];
       opt->stats->groups = 1;

@@ -160,7 +160,10 @@ typedef struct {
                            (segment, episode); bit 2: sparse segments through the event
                            filter and the list Map kernel (else the position kernel);
                            bit 3: the filter's lists pruned of entries that cannot act;
-                           bit 4: ring windows (runs in device memory) */
+                           bit 4: ring windows (runs in device memory); bit 5: two-node
+                           episodes through the type-sliced kernel (episodes sharing a
+                           node-1 type and interval stepped together, one bit per
+                           node-0 type) */
   int64_t repairs;      /* repair tuples made for unmatched segment exits */
   int64_t fallbacks;    /* episodes recounted by the whole-stream fallback */
   int32_t groups;       /* window-kind groups the call ran (1 unless split) */
@@ -189,8 +192,13 @@ enum {
   EP_PLAN_NO_REPAIR_QUEUE = 1 << 12, /* closure misses repaired where they are found */
   EP_PLAN_RECOUNT = 1 << 13,         /* every episode taken through the whole-stream recount
                                         that guards repair-list overflow and tree misses */
-  EP_PLAN_NO_SPLIT = 1 << 14         /* one window kind for the whole call: the widest one
+  EP_PLAN_NO_SPLIT = 1 << 14,        /* one window kind for the whole call: the widest one
                                         any episode needs (else one group per kind) */
+  EP_PLAN_SLICE = 1 << 15,           /* two-node episodes: the type-sliced kernel whenever the
+                                        call fits it (node types below 2,048, windows up to
+                                        63 ticks, no episode twice), however few episodes
+                                        share a node-1 type and interval */
+  EP_PLAN_NO_SLICE = 1 << 16         /* two-node episodes: never the type-sliced kernel */
 };
 
 /*

@@ -59,13 +59,14 @@ def _split_plan(split):
     on streams shorter than the planner's list-path minimum);
     'position-kernel' forces the position kernel itself; 'runs' and 'rings'
     take the scan kernel with run windows in registers (rings where a window
-    needs more runs than they hold) or with ring windows for every episode."""
+    needs more runs than they hold) or with ring windows for every episode;
+    'slice' takes the type-sliced kernel wherever a two-node call fits it."""
     return {"auto": [], "ticks": ["ticks"], "positions": ["positions", "list"],
             "position-kernel": ["positions", "no-list"], "runs": ["run-windows"],
-            "rings": ["ring-windows"]}[split]
+            "rings": ["ring-windows"], "slice": ["slice"]}[split]
 
 
-SPLITS = ["auto", "ticks", "positions", "position-kernel", "runs", "rings"]
+SPLITS = ["auto", "ticks", "positions", "position-kernel", "runs", "rings", "slice"]
 
 
 @pytest.mark.parametrize("split", SPLITS)
@@ -353,6 +354,7 @@ def test_level2_full_size(fem):
     got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "auto", stats=True)
     _log("level2 full: plan %s" % st)
     assert st["repairs"] > 0
+    assert st["kernels"] & 32
     t0 = time.time()
     want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
     _log("oracle %.1fs" % (time.time() - t0))

@@ -43,7 +43,7 @@ def _check(got, want, label):
 def _split_plan(split):
     return {"auto": [], "ticks": ["ticks"], "positions": ["positions", "list"],
             "position-kernel": ["positions", "no-list"], "scan": ["run-windows"],
-            "rings": ["ring-windows"]}[split]
+            "rings": ["ring-windows"], "slice": ["slice"]}[split]
 
 
 def _upper(fem, times, types, ep, hi, mode, P=0, plan=None):
@@ -61,7 +61,7 @@ def _two_pass(fem, times, types, ep, lo, hi, theta, mode="auto", P=0, plan=None)
     return counts.cpu().numpy(), upper.cpu().numpy(), kept
 
 
-SPLITS = ["auto", "ticks", "positions", "position-kernel", "scan", "rings"]
+SPLITS = ["auto", "ticks", "positions", "position-kernel", "scan", "rings", "slice"]
 MODES = [("auto", 0), ("ptpe", 0), ("mapconcat", 2), ("mapconcat", 7), ("mapconcat", 64)]
 
 
