@@ -112,13 +112,30 @@ __device__ inline uint64_t slice_or(const uint64_t* st, int32_t l, int32_t r) {
   return ok ? v : 0ull;
 }
 
-// bits of `src` where `m` is set, the rest from `dst` (one bitfield insert per half)
-__device__ inline uint64_t slice_insert(uint64_t m, uint64_t src, uint64_t dst) {
-  return (src & m) | (dst & ~m);
+// bit i of v as 0 or all ones
+__device__ inline uint32_t slice_sbit(int32_t v, int i) {
+  return (uint32_t)(-((v >> i) & 1));
 }
 
-__device__ inline uint64_t slice_ones_if(int32_t v, int i) {
-  return ((v >> i) & 1) ? ~0ull : 0ull;
+// the bits of `m` set to s (0 or all ones), the rest from d: one bitfield
+// insert per 32-bit half
+__device__ inline uint64_t slice_set(uint64_t m, uint32_t s, uint64_t d) {
+  const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+  const uint32_t lo = (ml & s) | (~ml & (uint32_t)d);
+  const uint32_t hi = (mh & s) | (~mh & (uint32_t)(d >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// the bits of `m` whose six planes spell v (mod 64)
+__device__ inline uint64_t slice_match(uint64_t m, const uint64_t (&pl)[6], int32_t v) {
+  uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const uint32_t s = slice_sbit(v, i);
+    ml &= ~((uint32_t)pl[i] ^ s);
+    mh &= ~((uint32_t)(pl[i] >> 32) ^ s);
+  }
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // value of bit j over `n` planes
@@ -197,7 +214,8 @@ void map_slice_kernel(SliceArgs A) {
 #pragma unroll
   for (int i = 0; i < kSlicePlanes; ++i) cp[i] = 0ull;
   int32_t xprev = -kFar, lastb = -kFar;
-  int32_t n_in = 0;
+  uint64_t q0 = 0ull, q1 = 0ull;        // small counter: completions since the last merge (<= 3)
+  int32_t n_in = 0;                     // counted B ticks since the last flush
   bool flushed = false;
   // the cuts and the stop tick: from their 64-bit values at every new base
   // (a clamped offset must not be moved again)
@@ -231,15 +249,35 @@ void map_slice_kernel(SliceArgs A) {
       const int32_t tp = l + __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
       PT &= ~(1ull << (tp & 63));
-      uint64_t Dp = PA;
-#pragma unroll
-      for (int i = 0; i < 6; ++i) Dp &= ~(pp[i] ^ slice_ones_if(tp, i));
+      const uint64_t Dp = slice_match(PA, pp, tp);
       PA &= ~Dp;
       if (tp >= exp_t) {
         DS |= Dp & ~slice_or(s_st, tp + 1, x);
         tS = tp;
       }
     }
+  };
+
+  // the small counter added into the planes (every third step of a wave and
+  // before the planes are read); a lane near 255 counted steps flushes
+  auto merge_small = [&]() {
+    // plane 0 + q0; plane 1 + q1 + carry; the carry rippled up
+    uint64_t c = cp[0] & q0;
+    cp[0] ^= q0;
+    const uint64_t x1 = cp[1] ^ q1;
+    const uint64_t c2 = (cp[1] & q1) | (c & x1);
+    cp[1] = x1 ^ c;
+    c = c2;
+#pragma unroll
+    for (int i = 2; i < kSlicePlanes; ++i) {
+      const uint64_t carry = cp[i] & c;
+      cp[i] ^= c;
+      c = carry;
+    }
+    q0 = q1 = 0ull;
+    // every lane of the wave flushes once one needs to (one pass of the
+    // flush loop per wave, not one per lane)
+    if (__ballot(n_in >= kSliceFlush - 3)) flush();
   };
 
   // bring the reset state to x (t: the B tick about to be stepped, or the
@@ -259,40 +297,60 @@ void map_slice_kernel(SliceArgs A) {
     xprev = x;
   };
 
-  // one B tick t
+  // one B tick t.  The reads of the three ORs it needs (W, the settled
+  // entry's pruning, the first pending reset that settles) are issued
+  // together; a second settling reset at one step is rare and takes the
+  // general loop
   auto step = [&](int32_t t) {
     const int32_t x = t - lo - 1;
-    advance(t, x);
-    const uint64_t hit = slice_or(s_st, t - hi, x) & gmask & ~(DS | PA);
+    const int32_t e = t - hi;
+    const int32_t top = x < lastb ? x : lastb;
+    const int32_t len = top - xprev;  // < 64
+    // pending ticks in (xprev, top], bit j for tick xprev + 1 + j (branch-free:
+    // the common path of a step takes no branch but the rare ones)
+    const uint64_t rot = __builtin_rotateright64(PT, (uint32_t)(xprev + 1) & 63u);
+    const uint64_t sm = len > 0 ? rot & ((~0ull) >> (64 - (len > 63 ? 63 : (len < 1 ? 1 : len)))) : 0ull;
+    const int32_t tp = xprev + __ffsll((unsigned long long)sm);
+    const bool live = sm != 0ull && tp >= e;
+    const bool expired = tS < e;
+    const uint64_t w_or = slice_or(s_st, e, x);
+    const uint64_t s_or = slice_or(s_st, expired ? x + 1 : tS + 1, x);
+    const uint64_t p_or = slice_or(s_st, live ? tp + 1 : x + 1, x);
+    DS = expired ? 0ull : (DS & ~s_or);
+    // the first settling reset
+    const uint64_t Dp = sm ? slice_match(PA, pp, tp) : 0ull;
+    PA &= ~Dp;
+    PT &= sm ? ~(1ull << (tp & 63)) : ~0ull;
+    DS |= live ? (Dp & ~p_or) : 0ull;
+    tS = live ? tp : tS;
+    if (sm & (sm - 1)) settle_range(tp + 1, top, x, e);  // rare
+    xprev = x;
+    const uint64_t hit = w_or & gmask & ~(DS | PA);
     lastb = t;
-    if (!hit) return;
+    // (a zero hit leaves all of this unchanged)
     PA |= hit;
-    PT |= 1ull << (t & 63);
+    PT |= hit ? (1ull << (t & 63)) : 0ull;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) pp[i] = slice_insert(hit, slice_ones_if(t, i), pp[i]);
-    if (t > tlo) {
+    for (int i = 0; i < 6; ++i) pp[i] = slice_set(hit, slice_sbit(t, i), pp[i]);
+    const bool counted = t > tlo && t <= thi;
+    const uint64_t hc = counted ? hit : 0ull;
+    q1 ^= q0 & hc;
+    q0 ^= hc;
+    n_in += counted ? 1 : 0;
+    if (hit && t > tlo) {
       if (t <= tlo + hi) {
         const uint64_t nw = hit & ~fa;
         fa |= hit;
         const int32_t av = t - tlo;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) ap[i] = slice_insert(nw, slice_ones_if(av, i), ap[i]);
+        for (int i = 0; i < 6; ++i) ap[i] = slice_set(nw, slice_sbit(av, i), ap[i]);
       }
-      if (t <= thi) {
-        uint64_t c = hit;
-#pragma unroll
-        for (int i = 0; i < kSlicePlanes; ++i) {
-          const uint64_t carry = cp[i] & c;
-          cp[i] ^= c;
-          c = carry;
-        }
-        if (++n_in == kSliceFlush) flush();
-      } else {
+      if (t > thi) {
         const uint64_t nw = hit & ~fb;
         fb |= hit;
         const int32_t bv = t - thi;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) bp[i] = slice_insert(nw, slice_ones_if(bv, i), bp[i]);
+        for (int i = 0; i < 6; ++i) bp[i] = slice_set(nw, slice_sbit(bv, i), bp[i]);
       }
     }
   };
@@ -360,11 +418,20 @@ void map_slice_kernel(SliceArgs A) {
     // that a wave steps as often as its busiest lane, not the sum over words
     // of each word's busiest), then its state as of the next chunk
     if (!done) {
-      int wi = 1;
-      uint64_t bits = brow[1];
+      // the chunk's non-empty words of the lane's node-1 row
+      uint32_t occ = 0;
+#pragma unroll
+      for (int i = 1; i < kSliceWords; ++i) occ |= (brow[i] != 0ull ? 1u : 0u) << i;
+      int wi = 0;
+      uint64_t bits = 0ull;
+      int it = 0;  // steps of this loop: the same in every lane still in it
       for (;;) {
-        while (!bits && wi < kSliceWords - 1) bits = brow[++wi];
-        if (!bits) break;
+        if (!bits) {
+          if (!occ) break;
+          wi = __ffs(occ) - 1;
+          occ &= occ - 1;
+          bits = brow[wi];
+        }
         const int32_t t = wi * 64 + __ffsll((unsigned long long)bits) - 1;
         bits &= bits - 1;
         if (t > stop) {
@@ -372,7 +439,13 @@ void map_slice_kernel(SliceArgs A) {
           break;
         }
         step(t);
+        // (the same count in every lane still in the loop: a scalar branch)
+        if (__builtin_amdgcn_readfirstlane(++it) == 3) {
+          it = 0;
+          merge_small();
+        }
       }
+      merge_small();
       if (!done) advance(kSliceWin, kSliceWin - lo - 1);
     }
     // machine-1 lanes that match their twin's state stop (the chunk ends past
