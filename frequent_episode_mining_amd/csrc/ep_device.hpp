@@ -214,6 +214,7 @@ struct RunWindow {
 template <int N, int K>
 struct RunMachine {
   using Params = RunParams<N>;
+  static constexpr bool kComparable = false;  // (no same_future test)
   int64_t r;  // time of the last reset (last completion, or the start)
   RunWindow<K> w[N > 1 ? N - 1 : 1];
 
@@ -259,6 +260,7 @@ struct RunMachine {
 template <int N>
 struct RingMachine {
   using Params = RunParams<N>;
+  static constexpr bool kComparable = false;
   static constexpr int NI = N > 1 ? N - 1 : 1;
   int64_t r;
   int2* ring;        // node j's ring at ring + j * cap
@@ -378,11 +380,22 @@ template <int N, int W>
 struct BitMachine {
   using Params = BitParams<N, W>;
   using Bits = typename BitsOf<W>::type;
+  static constexpr bool kComparable = true;
   int64_t r;
   int32_t B;
   Bits m[N > 1 ? N - 1 : 1];
 
   __device__ void attach(const RingArena&, int64_t) {}
+
+  // Both machines of one episode, fed the same events, behave alike from here
+  // on: windows on one base time with the same candidates, and either both
+  // or neither reset at that time (a reset ignores later events on its tick).
+  __device__ bool same_future(const BitMachine& o) const {
+    bool eq = B == o.B && ((r == (int64_t)B) == (o.r == (int64_t)o.B));
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) eq = eq && m[j] == o.m[j];
+    return eq;
+  }
 
   __device__ void reset(int64_t at) {
     r = at;
@@ -1935,15 +1948,62 @@ void map_ticks_kernel(MapArgs A) {
 
 // ------------------------------------------- wave-cooperative single machine
 
-// All 64 lanes hold the same machine; they load 64 events at a time with one
-// coalesced access, ballot the events whose type sits on a node of the
-// episode, and feed those, in order, to the (uniform) machine.
+// All 64 lanes hold the same machine(s); they load 64 events at a time with
+// one coalesced access, ballot the events whose type sits on a node of the
+// episode, and hand those, in order, to on_event(t, level mask), which returns
+// false to stop the scan.
+// Blocks of kDepth x 64 events; the next block's loads are issued before the
+// current one is fed, so one load latency covers kDepth x 64 events (a
+// repair rescans a whole segment, thousands of events of which a few percent
+// are the episode's: such a scan is bound by load latency).
+template <class Mach, int kDepth, class OnEvent>
+__device__ __forceinline__ void wave_scan(const int32_t* times, const uint16_t* types, int64_t i0,
+                                          int64_t i1, const typename Mach::Params& prm, OnEvent on_event) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int32_t t_cur[kDepth], t_nxt[kDepth];
+  uint32_t y_cur[kDepth], y_nxt[kDepth];
+  auto load = [&](int64_t base, int32_t* tt, uint32_t* yy) {
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      const int64_t i = base + q * kWave + lane;
+      const bool valid = i < i1;
+      tt[q] = valid ? times[i] : 0;
+      yy[q] = valid ? (uint32_t)types[i] : 0xffffffffu;
+    }
+  };
+  if (i0 >= i1) return;
+  load(i0, t_cur, y_cur);
+  bool go = true;
+  for (int64_t base = i0; base < i1 && go; base += kDepth * kWave) {
+    const int64_t nb = base + kDepth * kWave;
+    if (nb < i1) load(nb, t_nxt, y_nxt);
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      const uint32_t lm = y_cur[q] == 0xffffffffu ? 0u : prm.level_mask(y_cur[q]);
+      uint64_t mask = __ballot(lm != 0u);
+      while (mask != 0 && go) {
+        const int src = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        const int32_t tt = __shfl(t_cur[q], src);
+        const uint32_t ll = (uint32_t)__shfl((int)lm, src);
+        go = on_event(tt, ll);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kDepth; ++q) {
+      t_cur[q] = t_nxt[q];
+      y_cur[q] = y_nxt[q];
+    }
+  }
+}
+
+// One machine over events [i0, i1) (the loop of wave_scan, written out so
+// that the machine stays in registers): deeper prefetch for the machines with
+// little state (two nodes), 4 blocks for the rest as their registers allow.
 template <class Mach>
 __device__ void wave_feed_range(const int32_t* times, const uint16_t* types, int64_t i0, int64_t i1,
                                 SegMachine<Mach>& sm, const typename Mach::Params& prm) {
-  // Blocks of kDepth x 64 events; the next block's loads are issued before
-  // the current one is fed, so one load latency covers kDepth x 64 events.
-  constexpr int kDepth = 4;
+  constexpr int kDepth = sizeof(SegMachine<Mach>) <= 72 ? 16 : 4;
   const int lane = threadIdx.x & (kWave - 1);
   int32_t t_cur[kDepth], t_nxt[kDepth];
   uint32_t y_cur[kDepth], y_nxt[kDepth];
@@ -2012,8 +2072,18 @@ struct ClosureArgs {
 // The tuple of a chain that completed at x, x in (tau_q, tau_q + Span]: a
 // machine reset at x runs over segment q.  Its count includes the completion
 // at x itself when x <= tau_{q+1}.
+//
+// Bit-window machines take a shortcut: the machine reset at x runs in
+// lockstep with segment q's machine 0 (reset at tau_q) until both behave
+// alike (BitMachine::same_future), after machine 0's a-window has closed and
+// before tau_{q+1}; from there on both complete at the same events, so the
+// repair's count is its own so far plus what machine 0's Map tuple (found by
+// its key a) counts after that point, and its b is machine 0's.  On this
+// path a repair scans the events of a few Spans instead of a whole segment;
+// if the machines never meet, or no Map tuple has machine 0's key, the
+// machine reset at x runs to the end alone.
 template <class Mach>
-__device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params& prm, int64_t q,
+__device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params& prm, int64_t e, int64_t q,
                               int64_t x) {
   const int64_t lo_cut = A.tau[q];
   const int64_t hi_cut = A.tau[q + 1];
@@ -2024,6 +2094,39 @@ __device__ Tuple repair_tuple(const ClosureArgs& A, const typename Mach::Params&
     tu.c = 0;
     tu.b = (int32_t)(x - hi_cut);
     return tu;
+  }
+  if constexpr (Mach::kComparable) {
+    if (x > lo_cut) {
+      SegMachine<Mach> R, M;
+      R.init(x, lo_cut, hi_cut, prm.span);
+      M.init(lo_cut, lo_cut, hi_cut, prm.span);
+      const int64_t a_closed = lo_cut + prm.span;  // machine 0's a is final after this tick
+      bool met = false;
+      const int64_t i0 = upper_bound_time(A.times, A.seg_beg[q], A.seg_end[q], lo_cut);
+      wave_scan<Mach, 4>(A.times, A.types, i0, A.seg_end[q], prm, [&](int32_t t, uint32_t lm) __attribute__((always_inline)) {
+        R.feed(t, lm, prm);
+        M.feed(t, lm, prm);
+        if ((int64_t)t > a_closed && (int64_t)t > x && (int64_t)t < hi_cut && R.m.same_future(M.m)) {
+          met = true;
+          return false;
+        }
+        return !R.finished;
+      });
+      if (!met) {
+        tu.c = R.count + 1;
+        tu.b = R.b_off;
+        return tu;
+      }
+      const int nm = A.ts.nmap[A.ts.idx(e, q)];
+      for (int m = 0; m < nm && m < A.ts.slots; ++m) {
+        const Tuple t0 = *A.ts.at(e, q, m);
+        if (t0.a == M.a_off) {
+          tu.c = R.count + (t0.c - M.count) + 1;
+          tu.b = t0.b;
+          return tu;
+        }
+      }
+    }
   }
   SegMachine<Mach> sm;
   sm.attach(A.ring, wave_slot());
@@ -2056,7 +2159,7 @@ __device__ void repair_exit(const ClosureArgs& A, const typename Mach::Params& p
       if (lane == 0) atomicOr(&A.flags[e], 1);
       break;
     }
-    const Tuple tu = repair_tuple<Mach>(A, prm, q, A.tau[q] + x_off);
+    const Tuple tu = repair_tuple<Mach>(A, prm, e, q, A.tau[q] + x_off);
     int slot = 0;
     if (lane == 0) slot = atomicAdd(&A.ts.nslots[A.ts.idx(e, q)], 1);
     slot = __shfl(slot, 0);
@@ -2333,7 +2436,7 @@ __global__ __launch_bounds__(kReduceMembers) void reduce_kernel(ReduceArgs A) {
         }
         go = __shfl(go, 0);
         if (!go) break;
-        const Tuple tu = repair_tuple<Mach>(A.c, prm, q, A.c.tau[q] + x_off);
+        const Tuple tu = repair_tuple<Mach>(A.c, prm, e, q, A.c.tau[q] + x_off);
         int next = 0;
         if (lane == 0) {
           lock(q);
@@ -2459,7 +2562,7 @@ __global__ __launch_bounds__(kBlock) void stream_entry_kernel(StreamArgs A) {
   const bool lane0 = (threadIdx.x & (kWave - 1)) == 0;
   typename Mach::Params prm;
   prm.load(A.c.ep_types, A.c.ep_lo, A.c.ep_hi, A.c.ep_span, e);
-  const Tuple tu = repair_tuple<Mach>(A.c, prm, 0, x);
+  const Tuple tu = repair_tuple<Mach>(A.c, prm, e, 0, x);
   if (!lane0) return;
   const TupleStore& ts = A.c.ts;
   const int64_t pe = ts.idx(e, 0);
