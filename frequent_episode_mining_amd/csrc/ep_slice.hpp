@@ -549,16 +549,22 @@ void map_slice_kernel(SliceArgs A) {
       *tp = tu;
       if (k == 0) {
         const int64_t pe = A.ts.idx(e, p);
-        A.ts.nmap[pe] = A.n_machines;
-        A.ts.nslots[pe] = A.n_machines;
+        int32_t n_map = A.n_machines;
         if (stopped) {
           // the stopped twin: its count so far minus ours at the stop, plus
-          // our final count; our b
+          // our final count; our b.  With our key it is our tuple (equal
+          // keys, identical tuples): the pair keeps one Map tuple
           Tuple* t1 = A.ts.at(e, p, 1);
-          t1->c += c;
-          t1->b = tu.b;
-          t1->pad = 0;
+          if (t1->a == tu.a) {
+            n_map = 1;
+          } else {
+            t1->c += c;
+            t1->b = tu.b;
+            t1->pad = 0;
+          }
         }
+        A.ts.nmap[pe] = n_map;
+        A.ts.nslots[pe] = n_map;
       }
     }
   }
