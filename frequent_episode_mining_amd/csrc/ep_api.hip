@@ -1185,6 +1185,7 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
     ma.group_k = ep_perm.empty() ? nullptr : d_gk;
     ma.lists = d_lists; ma.list_off = d_loff; ma.list_cnt = d_lcnt; ma.max_share = max_share;
     ma.ring = ring;
+    ma.lazy = L.prune ? 0 : 1;  // pruned lists: nearly every entry left changes the machine
     // workgroups: (segment group, episode group), episode group fastest
     ma.n_egroups = (S + L.G - 1) / L.G;
     dim3 mgrid((unsigned)(((P + L.R - 1) / L.R) * ma.n_egroups));

@@ -526,6 +526,7 @@ struct MapArgs {
   int64_t eg_blocks;   // tick kernel: workgroups that loop over a segment group's episode
                        // groups when its segments fit one chunk each
   RingArena ring;      // scan kernel with ring windows: slot ((p * S) + e) * M + k
+  int32_t lazy;        // list kernel: the lazily aged single-class walk (unpruned lists)
 };
 
 // A workgroup barrier that orders LDS accesses only.  __syncthreads() also
@@ -663,6 +664,33 @@ __global__ __launch_bounds__(kBlock) void map_scan_kernel(MapArgs A) {
   }
 }
 
+// The distinct tuples of the M machines of a (segment, episode): equal keys
+// (a) mean identical tuples (the same first completion after the cut, or none
+// within Span), so one of each is kept; machine 0's tuple stays first.
+template <int M>
+__device__ inline void write_class_tuples(const MapArgs& A, int64_t e, int64_t p, const int32_t* a_off,
+                                          const int32_t* cnt, const int32_t* b_off) {
+  int d = 0;
+#pragma unroll
+  for (int c = 0; c < M; ++c) {
+    bool dup = false;
+#pragma unroll
+    for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
+    if (!dup) {
+      Tuple tu;
+      tu.a = a_off[c];
+      tu.c = cnt[c];
+      tu.b = b_off[c];
+      tu.pad = 0;
+      *A.ts.at(e, p, d) = tu;
+      ++d;
+    }
+  }
+  const int64_t pe = A.ts.idx(e, p);
+  A.ts.nmap[pe] = d;
+  A.ts.nslots[pe] = d;
+}
+
 // The Map machines of one (segment, episode) held by one lane (MCH = N) as
 // equivalence classes, or one Map machine per lane (MCH = 1), on bit windows.
 // Machines that reset at the same time are identical from then on, and so
@@ -687,6 +715,12 @@ struct ClassLane {
   int64_t tau_lo, tau_hi, stop, check_at;
   int32_t B;
   bool single;  // exactly one class left, held in slot 0
+  // the lazily aged single class (step_lazy_if): window 0 anchored at B0, the
+  // later windows at B; hiw[j] = interval j's upper bound; dl0 / dlr = a tick
+  // after which no candidate of window 0 / of any later window lies within
+  // its interval's upper bound any more (INT32_MIN: no candidate)
+  int32_t B0, dl0, dlr;
+  int32_t hiw[NI];
 
   __device__ void init(const MapArgs& A, int64_t e, int64_t p, int k_lane, bool active) {
     found = 0;
@@ -695,6 +729,10 @@ struct ClassLane {
     tau_lo = tau_hi = stop = 0;
     check_at = INT64_MAX;
     B = INT32_MIN;
+    B0 = INT32_MIN;
+    dl0 = dlr = INT32_MIN;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) hiw[j] = 0;
     single = MCH == 1;
     if (!active) {
       fin = kAll;
@@ -909,6 +947,103 @@ struct ClassLane {
     return true;
   }
 
+  // The last tick at which the newest candidate of window mm (anchored at
+  // `at`) still lies within the upper bound of the interval whose window
+  // mask is w (its highest bit): INT32_MIN for an empty window.
+  __device__ static int32_t deadline(Bits mm, int32_t at, Bits w) {
+    if (mm == 0) return INT32_MIN;
+    int newest, top;
+    if constexpr (W == 64) {
+      newest = __builtin_ctzll((unsigned long long)mm);
+      top = 63 - __builtin_clzll((unsigned long long)w);
+    } else {
+      newest = __builtin_ctz((unsigned)mm);
+      top = 31 - __builtin_clz((unsigned)w);
+    }
+    const int64_t d = (int64_t)at - newest + top;
+    return d > (int64_t)INT32_MAX ? INT32_MAX : (d < (int64_t)INT32_MIN ? INT32_MIN : (int32_t)d);
+  }
+
+  // Switch the single class to lazy ageing (windows as step_one leaves them).
+  __device__ void lazy_begin() {
+    B0 = B;
+    if constexpr (N > 1) {
+#pragma unroll
+      for (int j = 0; j < N - 1; ++j)
+        hiw[j] = (W == 64) ? 63 - __builtin_clzll((unsigned long long)win[j])
+                           : 31 - __builtin_clz((unsigned)win[j]);
+      dl0 = deadline(m[0][0], B, win[0]);
+      dlr = INT32_MIN;
+#pragma unroll
+      for (int j = 1; j < N - 1; ++j) dlr = max(dlr, deadline(m[0][j], B, win[j]));
+    }
+  }
+
+  // The exact step of step_one at t after the lazy windows are aged to t;
+  // the event is live (after the last reset) and not past stop.
+  __device__ bool step_exact(int32_t t, uint32_t lm) {
+    if constexpr (N > 1) m[0][0] = age<W>(m[0][0], (uint32_t)t - (uint32_t)B0);
+#pragma unroll
+    for (int j = 1; j < N - 1; ++j) m[0][j] = age<W>(m[0][j], (uint32_t)t - (uint32_t)B);
+    B0 = B = t;
+    bool hit[NI];
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) hit[j] = (m[0][j] & win[j]) != 0;
+    bool complete = (lm >> (N - 1)) & 1u;
+    if constexpr (N > 1) complete = complete && hit[N - 2];
+    if (complete) {
+      complete_class(1u, t);
+      if ((mem[0] & ~fin) == 0u) mem[0] = 0u;
+      dl0 = dlr = INT32_MIN;
+      return fin != kAll;
+    }
+    // a candidate added at t is its window's newest: the deadlines move to
+    // t + hi (the older candidates' deadlines are earlier)
+#pragma unroll
+    for (int j = 0; j < N - 1; ++j) {
+      const bool add = ((lm >> j) & 1u) && (j == 0 || hit[j > 0 ? j - 1 : 0]);
+      m[0][j] |= (Bits)(add ? 1u : 0u);
+      const int32_t dl = __builtin_elementwise_add_sat(t, hiw[j]);
+      if (j == 0)
+        dl0 = add ? dl : dl0;
+      else
+        dlr = add ? max(dlr, dl) : dlr;
+    }
+    return true;
+  }
+
+  // step_one for the lanes where `use` holds, with lazily aged windows (after
+  // lazy_begin).  The windows are relative to their anchors, so an event that
+  // changes no window needs no ageing at all.  An event on node levels >= 1
+  // only can change the state only through a hit, which needs a candidate of
+  // the previous node within that interval's upper bound: past dl0 (level 1)
+  // and dlr (levels >= 2) there is none, so nothing happens.  A node-0 event
+  // otherwise only adds a candidate to window 0.  Every other live event (a
+  // possible hit or completion) takes the exact step, a branch that the wave
+  // runs only while one of its lanes needs it.  Returns false once the lane
+  // has finished.
+  __device__ bool step_lazy_if(bool use, int32_t t, uint32_t lm) {
+    lm &= (1u << N) - 1u;
+    const bool over = use && (int64_t)t > stop;
+    const bool on = use && !over && (int64_t)t > r[0];
+    bool slow;
+    if constexpr (N == 1) {
+      slow = on && (lm & 1u);
+    } else {
+      slow = on && ((((lm >> 1) & 1u) && t <= dl0) || ((lm >> 2) != 0u && t <= dlr));
+      const bool add0 = on && !slow && (lm & 1u);
+      const Bits aged = age<W>(m[0][0], (uint32_t)t - (uint32_t)B0) | (Bits)1;
+      m[0][0] = add0 ? aged : m[0][0];
+      B0 = add0 ? t : B0;
+      dl0 = add0 ? __builtin_elementwise_add_sat(t, hiw[0]) : dl0;
+    }
+    if (slow) {
+      if (!step_exact(t, lm)) return false;
+    }
+    fin = over ? kAll : fin;
+    return !over;
+  }
+
   // step_one for the lanes where `use` holds, as predicated arithmetic (the
   // others keep their state): no branch but for the rare completion.
   // Returns false once the lane has finished.
@@ -958,24 +1093,7 @@ struct ClassLane {
         A.ts.nslots[pe] = A.n_machines;
       }
     } else {
-      int d = 0;
-#pragma unroll
-      for (int c = 0; c < MCH; ++c) {
-        bool dup = false;
-#pragma unroll
-        for (int c2 = 0; c2 < c; ++c2) dup |= a_off[c2] == a_off[c];
-        if (!dup) {
-          Tuple tu;
-          tu.a = a_off[c];
-          tu.c = cnt[c];
-          tu.b = b_off[c];
-          tu.pad = 0;
-          *A.ts.at(e, p, d) = tu;
-          ++d;
-        }
-      }
-      A.ts.nmap[pe] = d;
-      A.ts.nslots[pe] = d;
+      write_class_tuples<MCH>(A, e, p, a_off, cnt, b_off);
     }
   }
 };
@@ -1138,16 +1256,100 @@ __global__ __launch_bounds__(kBlock) void map_bits_kernel(MapArgs A) {
   if (active) lane.write(A, e, p, k_lane);
 }
 
+// The single-class walk of the list Map kernels: the lane's list from cursor
+// (block b, entry i of the list at region offset `off`, `cnt` entries; the
+// next block's bounds off_next / cnt_next) to its end or until step() reports
+// the lane finished.  Batches of kD entries are read as kD / 2 aligned 16-byte
+// loads (a lane reads its list in whole lines, which stay useful even when
+// the L1 cannot hold every lane's line), the next batch's loads in flight.  A
+// batch starts at an even entry of its block's region (region starts are
+// 16-byte aligned); entries before the lane's cursor or past the list are
+// read (they lie in the region, or in the buffer's slack) and skipped.  Each
+// lane carries its own cursor (block, region index) across blocks: the batch
+// after a block's last one is the next block's first, loaded ahead like any
+// other, so a wave's lanes never wait for one another at block ends.  The
+// loads are unconditional so that the compiler can count them and wait only
+// for the batch about to be stepped through.  step(use, t, lm) steps the
+// lanes where `use` holds and returns false once the lane has finished.
+template <class Step>
+__device__ __forceinline__ void list_walk(const MapArgs& A, int64_t e, int64_t b, int64_t b_last,
+                                          int32_t off, int32_t cnt, int32_t i, int32_t off_next,
+                                          int32_t cnt_next, Step&& step) {
+  constexpr int kD = 8;
+  const int64_t region_len = (int64_t)kListBlock * A.max_share;
+  const int4* v = (const int4*)(A.lists + b * region_len);  // the cursor's block region
+  int32_t rel = off;    // the list's first entry in it
+  int32_t n_end = cnt;
+  int32_t first = i;    // entries before it are done
+  int32_t j0 = (rel + i) & ~1;  // even region index of the current batch
+  bool go = true;
+  auto advance = [&]() {  // to block b + 1's list, its following block's bounds loaded
+    ++b;
+    v = (const int4*)(A.lists + b * region_len);
+    rel = off_next;
+    n_end = cnt_next;
+    first = 0;
+    j0 = rel & ~1;
+    if (b < b_last) {
+      off_next = A.list_off[(b + 1) * A.S + e];
+      cnt_next = A.list_cnt[(b + 1) * A.S + e];
+    }
+  };
+  if (j0 >= rel + n_end) {
+    // this block holds nothing more for the lane: the next one
+    if (b < b_last)
+      advance();
+    else
+      go = false;
+  }
+  if (!go) return;
+  int4 cur[kD / 2];
+#pragma unroll
+  for (int q = 0; q < kD / 2; ++q) cur[q] = v[min(j0 + 2 * q, (rel + n_end + 1) & ~1) >> 1];
+  while (go) {
+    // the batch after this one: the rest of this block, or the next block
+    const bool same = j0 + kD < rel + n_end;
+    const bool more = same || b < b_last;
+    const int4* nv = v;
+    int32_t n_rel = rel, n_n = n_end, n_j0 = j0 + kD;
+    if (!same && more) {
+      nv = (const int4*)(A.lists + (b + 1) * region_len);
+      n_rel = off_next;
+      n_n = cnt_next;
+      n_j0 = off_next & ~1;
+    }
+    int4 nxt[kD / 2];
+#pragma unroll
+    for (int q = 0; q < kD / 2; ++q) nxt[q] = nv[min(n_j0 + 2 * q, (n_rel + n_n + 1) & ~1) >> 1];
+#pragma unroll
+    for (int k = 0; k < kD; ++k) {
+      const int32_t idx = j0 + k - rel;  // index within this episode's list
+      const int4 w = cur[k >> 1];
+      const int32_t t = (k & 1) ? w.z : w.x;
+      const uint32_t lm = (uint32_t)((k & 1) ? w.w : w.y);
+      go = step(go && idx >= first && idx < n_end, t, lm) && go;
+    }
+#pragma unroll
+    for (int q = 0; q < kD / 2; ++q) cur[q] = nxt[q];
+    if (!more) break;
+    if (same)
+      j0 += kD;
+    else
+      advance();
+  }
+}
+
 // List Map kernel (bit windows): the ClassLane machines fed from the filter
 // kernel's per-episode event lists instead of a staged chunk.  The lane of
 // (segment, episode) reads, in time order, its episode's entries of the event
 // blocks its segment's range (tau_p - maxSpan, tau_{p+1} + maxSpan] covers;
-// no LDS and no barriers.  Entries are taken in batches of kD: the loads of
-// the next batch are issued before the current one is stepped through, and
-// the next block's list bounds before the current block's entries.
-template <int N, int W, int MCH>
+// no LDS and no barriers.  The segment's start, while several classes live,
+// is stepped one entry at a time; the single class left then walks the rest
+// (list_walk), with lazily aged windows where the lists are unpruned (most
+// entries then change nothing) and the branch-free step where they are pruned
+// (nearly every entry left is a hit).
+template <int N, int W, int MCH, bool LAZY>
 __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
-  constexpr int kD = 8;
   const int tid = threadIdx.x;
   const int per_seg = A.G * A.M;
   const int r_idx = tid / per_seg;
@@ -1170,12 +1372,13 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
     const int64_t b_last = (end - 1) / kListBlock;
     int64_t b = beg / kListBlock;
     const int2* list = nullptr;
-    int32_t n_here = 0, i = 0;
+    int32_t n_here = 0, i = 0, off = 0;
     // block b's list; the next block's bounds are loaded meanwhile
     int32_t off_next = A.list_off[b * A.S + e];
     int32_t cnt_next = A.list_cnt[b * A.S + e];
     auto open = [&]() {
-      list = A.lists + b * (int64_t)kListBlock * A.max_share + off_next;
+      off = off_next;
+      list = A.lists + b * (int64_t)kListBlock * A.max_share + off;
       n_here = cnt_next;
       i = 0;
       if (b < b_last) {
@@ -1198,9 +1401,9 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
       i = lo;
     }
     bool go = true;
-    // several classes (the segment's first events): one entry at a time, the
-    // next entry's load issued before the current one is stepped
-    if (MCH > 1) {
+    if constexpr (MCH > 1) {
+      // several classes (the segment's first events): one entry at a time,
+      // the next entry's load issued before the current one is stepped
       int2 en = i < n_here ? list[i] : make_int2(0, 0);
       while (go && !lane.single) {
         while (i >= n_here && b < b_last) {
@@ -1215,81 +1418,15 @@ __global__ __launch_bounds__(kBlock) void map_list_kernel(MapArgs A) {
         go = lane.step_many(cur.x, (uint32_t)cur.y);
       }
     }
-    // one class: batches of kD entries read as kD / 2 aligned 16-byte loads
-    // (a lane reads its list in whole lines, which stay useful even when the
-    // L1 cannot hold every lane's line), the next batch's loads in flight.
-    // A batch starts at an even entry of its block's region (region starts
-    // are 16-byte aligned); entries before the lane's cursor or past the list
-    // are read (they lie in the region, or in the buffer's slack) and skipped.
-    // Each lane carries its own cursor (block, region index) across blocks:
-    // the batch after a block's last one is the next block's first, loaded
-    // ahead like any other, so a wave's lanes never wait for one another at
-    // block ends.  Entries of the list lie after lo_t from the cursor on (the
-    // search above skipped the first block's earlier ones).  The loads are
-    // unconditional so that the compiler can count them and wait only for the
-    // batch about to be stepped through.
     if (go && lane.single) {
-      const int64_t region_len = (int64_t)kListBlock * A.max_share;
-      const int4* v = (const int4*)(A.lists + b * region_len);  // the cursor's block region
-      int32_t rel = (int32_t)(list - A.lists - b * region_len);  // the list's first entry in it
-      int32_t n_end = n_here;
-      int32_t first = i;  // entries before it are done
-      int32_t j0 = (rel + i) & ~1;  // even region index of the current batch
-      if (j0 >= rel + n_end) {
-        // the first block holds nothing more for this lane: the next one
-        if (b < b_last) {
-          ++b;
-          open();
-          v = (const int4*)(A.lists + b * region_len);
-          rel = (int32_t)(list - A.lists - b * region_len);
-          n_end = n_here;
-          first = 0;
-          j0 = rel & ~1;
-        } else {
-          go = false;
-        }
-      }
-      int4 cur[kD / 2];
-#pragma unroll
-      for (int q = 0; q < kD / 2; ++q) cur[q] = v[min(j0 + 2 * q, (rel + n_end + 1) & ~1) >> 1];
-      while (go) {
-        // the batch after this one: the rest of this block, or the next block
-        const bool same = j0 + kD < rel + n_end;
-        const bool more = same || b < b_last;
-        const int4* nv = v;
-        int32_t n_rel = rel, n_n = n_end, n_j0 = j0 + kD;
-        if (!same && more) {
-          nv = (const int4*)(A.lists + (b + 1) * region_len);
-          n_rel = off_next;
-          n_n = cnt_next;
-          n_j0 = off_next & ~1;
-        }
-        int4 nxt[kD / 2];
-#pragma unroll
-        for (int q = 0; q < kD / 2; ++q) nxt[q] = nv[min(n_j0 + 2 * q, (n_rel + n_n + 1) & ~1) >> 1];
-#pragma unroll
-        for (int k = 0; k < kD; ++k) {
-          const int32_t idx = j0 + k - rel;  // index within this episode's list
-          const int4 w = cur[k >> 1];
-          const int32_t t = (k & 1) ? w.z : w.x;
-          const uint32_t lm = (uint32_t)((k & 1) ? w.w : w.y);
-          go = lane.step_one_if(go && idx >= first && idx < n_end, t, lm) && go;
-        }
-#pragma unroll
-        for (int q = 0; q < kD / 2; ++q) cur[q] = nxt[q];
-        if (!more) break;
-        if (same) {
-          j0 += kD;
-        } else {
-          ++b;
-          open();  // (list, n_here and the following block's bounds)
-          v = nv;
-          rel = n_rel;
-          n_end = n_n;
-          first = 0;
-          j0 = n_j0;
-        }
-      }
+      if constexpr (LAZY) lane.lazy_begin();
+      list_walk(A, e, b, b_last, off, n_here, i, off_next, cnt_next,
+                [&](bool use, int32_t t, uint32_t lm) {
+                  if constexpr (LAZY)
+                    return lane.step_lazy_if(use, t, lm);
+                  else
+                    return lane.step_one_if(use, t, lm);
+                });
     }
   }
   lane.write(A, e, p, k_lane);

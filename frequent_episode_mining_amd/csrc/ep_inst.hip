@@ -52,7 +52,10 @@ hipError_t launch_bits(const MapArgs& a, int win, bool all_machines, dim3 grid, 
 
 template <int W, int MCH>
 hipError_t launch_list_wm(const MapArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((map_list_kernel<EP_N, W, MCH>), grid, block, 0, s, a);
+  if (a.lazy)
+    hipLaunchKernelGGL((map_list_kernel<EP_N, W, MCH, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((map_list_kernel<EP_N, W, MCH, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

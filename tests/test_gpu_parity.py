@@ -159,13 +159,16 @@ def _plant_edges(rng, times, types, ep, lo, hi, per_episode):
     return tt[o], yy[o]
 
 
-@pytest.mark.parametrize("prune", ["on", "off"])
+@pytest.mark.parametrize("prune", ["on", "off", "off-machine-lanes"])
 def test_list_pruning_windows(fem, prune):
     # the list pruning drops entries with no neighbour entry in their windows:
     # sparse multi-block streams over many types (most entries left out),
     # chains planted on the interval ends and at block edges, dense and sparse
-    # blocks in time
+    # blocks in time.  Unpruned lists take the lazily aged walk (with the
+    # machines as classes, or one machine per lane)
     plan = _split_plan("positions") + ["prune" if prune == "on" else "no-prune"]
+    if prune.endswith("machine-lanes"):
+        plan.append("machine-lanes")
     rng = np.random.default_rng(59)
     for trial in range(36):
         n = int(rng.integers(3000, 21000))
@@ -266,7 +269,8 @@ def test_config_small(fem, name):
 @pytest.mark.parametrize("layout", ["scan", "scan-rings", "machine-lanes", "ticks", "positions",
                                     "ticks-machine-lanes",
                                     "position-kernel", "position-kernel-machine-lanes",
-                                    "positions-machine-lanes", "positions-unpruned"])
+                                    "positions-machine-lanes", "positions-unpruned",
+                                    "positions-machine-lanes-unpruned"])
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "longchain"])
 def test_config_small_other_kernels(fem, name, layout):
     # the same counts from the scan Map kernel (run or ring windows, every

@@ -47,3 +47,71 @@ def test_model_matches_oracle_random():
             misses += st["misses"]
     # repairs are exercised, also with t_low = 0
     assert misses > 0
+
+
+class _LazyMachine:
+    """The machine with the list kernel's skip rule: an event on node levels
+    >= 1 only is skipped when it lies past the deadline of every window it
+    could extend (the newest interval end of window 0 for level 1, of the later
+    windows for levels >= 2); a node-0 event otherwise only opens an interval
+    in window 0.  Every other event takes the exact step."""
+
+    def __init__(self, ep, lo, hi, reset_at):
+        from model_mapconcat import Machine
+        self.m = Machine(ep, lo, hi, reset_at)
+        self.dl0 = self.dlr = -(1 << 60)
+        self.skipped = 0
+
+    def step(self, t, y):
+        m = self.m
+        if t <= m.r:
+            return False
+        levels = [k for k in range(m.N) if m.ep[k] == y]
+        if not levels:
+            return False
+        if m.N == 1:
+            slow = True
+        else:
+            slow = (1 in levels and t <= self.dl0) or (any(k >= 2 for k in levels) and t <= self.dlr)
+        if not slow:
+            self.skipped += 1
+            if 0 in levels:
+                m._insert(0, t)
+                self.dl0 = t + m.hi[0]
+            return False
+        ins = [k for k in levels if k < m.N - 1 and (k == 0 or m._in(k - 1, t))]
+        done = m.step(t, y)
+        if done:
+            self.dl0 = self.dlr = -(1 << 60)
+        else:
+            for k in ins:
+                if k == 0:
+                    self.dl0 = t + m.hi[0]
+                else:
+                    self.dlr = max(self.dlr, t + m.hi[k])
+        return done
+
+
+def test_lazy_skip_rule_matches_exact_machine():
+    # the skip rule changes no completion: random streams, one to eight nodes,
+    # types on several levels, lo = 0 and lo near hi, windows up to 63 ticks
+    from model_mapconcat import Machine
+    rng = np.random.default_rng(71)
+    total_skipped = 0
+    for trial in range(300):
+        n_types = int(rng.integers(2, 12))
+        times, types = W.random_stream(rng, int(rng.integers(50, 600)), n_types,
+                                       max_gap=int(rng.choice([0, 1, 3, 10])))
+        N = int(rng.integers(1, 9))
+        ep = rng.integers(0, n_types, size=N)
+        hi = rng.integers(1, 64, size=max(N - 1, 0))
+        lo = np.minimum((rng.random(size=hi.shape) * hi).astype(int), hi - 1)
+        if trial % 3 == 0:
+            lo[:] = 0
+        r0 = int(times[0]) - int(rng.integers(1, 5))
+        exact, lazy = Machine(ep, lo, hi, r0), _LazyMachine(ep, lo, hi, r0)
+        got = [int(t) for t, y in zip(times, types) if lazy.step(int(t), int(y))]
+        want = [int(t) for t, y in zip(times, types) if exact.step(int(t), int(y))]
+        assert got == want, (trial, N, ep.tolist(), lo.tolist(), hi.tolist())
+        total_skipped += lazy.skipped
+    assert total_skipped > 1000  # the rule did skip events
