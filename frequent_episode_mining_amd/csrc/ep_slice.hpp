@@ -533,38 +533,61 @@ void map_slice_kernel(SliceArgs A) {
   __syncthreads();  // a machine-1 lane's merge writes are seen by its twin
   const bool stopped = A.n_machines == 2 && gi < kBlock / 2 && s_merged[gi] != 0;
   if (active && !(k == 1 && stopped)) {
-    uint64_t m = gmask;
-    while (m) {
-      const int j = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int32_t e = A.g_ep[g * 64 + j];
-      Tuple* tp = A.ts.at(e, p, k);
-      int32_t c = slice_get<kSlicePlanes>(cp, j);
-      if (flushed) c += tp->c;
-      Tuple tu;
-      tu.a = slice_get<6>(ap, j);
-      tu.c = c;
-      tu.b = slice_get<6>(bp, j);
-      tu.pad = 0;
-      *tp = tu;
-      if (k == 0) {
-        const int64_t pe = A.ts.idx(e, p);
-        int32_t n_map = A.n_machines;
-        if (stopped) {
-          // the stopped twin: its count so far minus ours at the stop, plus
-          // our final count; our b.  With our key it is our tuple (equal
-          // keys, identical tuples): the pair keeps one Map tuple
-          Tuple* t1 = A.ts.at(e, p, 1);
-          if (t1->a == tu.a) {
-            n_map = 1;
-          } else {
-            t1->c += c;
-            t1->b = tu.b;
-            t1->pad = 0;
-          }
+    // eight node-0 bits at a time: their episodes (two 16-byte loads of the
+    // group's row) and the stored values the tuples add to (the flushed
+    // count, the stopped twin's tuple) are all loaded before any store, so a
+    // lane waits for memory twice per eight episodes instead of per episode
+    const int4* row = (const int4*)(A.g_ep + g * 64);
+#pragma unroll 1
+    for (int c8 = 0; c8 < 8; ++c8) {
+      const uint32_t mc = (uint32_t)(gmask >> (8 * c8)) & 0xffu;
+      if (mc == 0u) continue;
+      const int4 q0 = row[2 * c8], q1 = row[2 * c8 + 1];
+      const int32_t ev[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      int32_t prev[8];
+      int4 twin[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        prev[jj] = 0;
+        twin[jj] = make_int4(0, 0, 0, 0);
+        if ((mc >> jj) & 1u) {
+          if (flushed) prev[jj] = A.ts.at(ev[jj], p, k)->c;
+          if (k == 0 && stopped) twin[jj] = *(const int4*)A.ts.at(ev[jj], p, 1);
         }
-        A.ts.nmap[pe] = n_map;
-        A.ts.nslots[pe] = n_map;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (!((mc >> jj) & 1u)) continue;
+        const int j = 8 * c8 + jj;
+        const int32_t e = ev[jj];
+        Tuple tu;
+        tu.a = slice_get<6>(ap, j);
+        tu.c = slice_get<kSlicePlanes>(cp, j) + prev[jj];
+        tu.b = slice_get<6>(bp, j);
+        tu.pad = 0;
+        *A.ts.at(e, p, k) = tu;
+        if (k == 0) {
+          const int64_t pe = A.ts.idx(e, p);
+          int32_t n_map = A.n_machines;
+          if (stopped) {
+            // the stopped twin {a, c, b, -}: its count so far minus ours at
+            // the stop, plus our final count; our b.  With our key it is our
+            // tuple (equal keys, identical tuples): the pair keeps one Map
+            // tuple
+            if (twin[jj].x == tu.a) {
+              n_map = 1;
+            } else {
+              Tuple t1;
+              t1.a = twin[jj].x;
+              t1.c = twin[jj].y + tu.c;
+              t1.b = tu.b;
+              t1.pad = 0;
+              *A.ts.at(e, p, 1) = t1;
+            }
+          }
+          A.ts.nmap[pe] = n_map;
+          A.ts.nslots[pe] = n_map;
+        }
       }
     }
   }
