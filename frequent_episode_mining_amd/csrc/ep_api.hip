@@ -1361,19 +1361,28 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
         break;
       }
       rec_at(6);
-      // Concatenate tree: each launch joins groups of `members` blocks in LDS
+      // Concatenate tree: each launch joins groups of `members` blocks, a
+      // workgroup per group, each thread `per` consecutive members in order
+      // first, then the threads' lists in LDS
       // a stream's batch joins all but the last segment (the tail runs that one)
       const int32_t Pt = sh ? P - 1 : P;
-      // members per workgroup: the fewest powers of two covering Pt (less LDS,
-      // more resident workgroups), within 64 KiB of LDS
+      // members per workgroup: the fewest powers of two covering Pt, within
+      // 64 KiB of LDS at one member per thread
       int members = kConcatMembers;
       while (members > 1 && (size_t)members * (12 * L.slots + 4) > 65536) members >>= 1;
       while (members > 1 && members / 2 >= Pt) members >>= 1;
-      const size_t lds = (size_t)members * (12 * L.slots + 4);
       for (int64_t stride = 1; stride < Pt; stride *= members) {
         const int64_t groups = (Pt + stride * members - 1) / (stride * members);
-        hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(members), lds,
-                           stream, ts, d_flags, S, Pt, stride, members, groups);
+        // members each thread joins in order: as many as keep the launch at
+        // kConcatMinThreads threads or more
+        int per = 1;
+        while (per < kConcatPer && per * 2 <= members &&
+               (int64_t)members * groups * S / (per * 2) >= kConcatMinThreads)
+          per *= 2;
+        const int threads = members / per;
+        const size_t lds = (size_t)threads * (12 * L.slots + 4);
+        hipLaunchKernelGGL(concat_tree_kernel, dim3((unsigned)(groups * S)), dim3(threads), lds,
+                           stream, ts, d_flags, S, Pt, stride, members, groups, per);
         if (hipGetLastError() != hipSuccess) { status = EP_ERR_HIP; break; }
       }
       if (status != EP_OK) break;

@@ -536,44 +536,90 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
 
 // ------------------------------------------------------------- Concatenate
 
-// One workgroup joins G consecutive members (segments p0, p0 + stride, ...)
-// of one episode in LDS, level by level (Concatenate rules 1-3, Fig. 6), and
-// writes the merged tuples back to the first member.  Members hold their
-// tuple list keyed by their first segment's keys; joining left block L with
-// right block R maps each (a, c, b) of L to (a, c + c', b') for the tuple of R
-// whose key a' equals b.  Launched with stride 1, then `members`, then
-// members^2, ..., until one member is left.
-constexpr int kConcatMembers = 512;  // threads of a tree workgroup at most
+// One workgroup joins `members` consecutive members (segments p0, p0 +
+// stride, ...) of one episode (Concatenate rules 1-3, Fig. 6) and writes the
+// merged tuples back to the first member.  Members hold their tuple list keyed
+// by their first segment's keys; joining left block L with right block R maps
+// each (a, c, b) of L to (a, c + c', b') for the tuple of R whose key a'
+// equals b (no such tuple: a miss, flagged for the episode).  Launched with
+// stride 1, then `members`, then members^2, ..., until one member is left.
+//
+// Thread t first joins members t * per .. t * per + per - 1 in order (their
+// first tuples and tuple counts loaded together up front: with stride 1 that
+// is one contiguous read per thread), then the threads' lists are joined
+// level by level in LDS.  Where the launch has threads to spare (many
+// episodes), per = 8 makes a 512-member group one wave whose tree needs six
+// levels inside the wave, instead of nine workgroup barriers over 512 threads.
+constexpr int kConcatMembers = 512;  // members of a tree workgroup at most
+constexpr int kConcatPer = 8;        // members one thread joins in order at most
+constexpr int64_t kConcatMinThreads = 65536;  // threads a launch keeps when choosing per
 
 __global__ __launch_bounds__(kConcatMembers) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
                                                              int32_t P, int64_t stride, int32_t members,
-                                                             int64_t groups) {
+                                                             int64_t groups, int32_t per) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int slots = ts.slots;
-  int32_t* s_a = (int32_t*)smem;                      // [members][slots]
-  int32_t* s_c = s_a + members * slots;
-  int32_t* s_b = s_c + members * slots;
-  int32_t* s_n = s_b + members * slots;               // [members]
+  const int nt = blockDim.x;                          // members / per
+  int32_t* s_a = (int32_t*)smem;                      // [nt][slots]
+  int32_t* s_c = s_a + nt * slots;
+  int32_t* s_b = s_c + nt * slots;
+  int32_t* s_n = s_b + nt * slots;                    // [nt]
   __shared__ int32_t s_miss;
   const int64_t e = (int64_t)blockIdx.x / groups;
   const int64_t p0 = ((int64_t)blockIdx.x - e * groups) * stride * members;
   const int i = threadIdx.x;
-  const int64_t p = p0 + (int64_t)i * stride;
+  const int64_t span = stride * per;                  // segments between threads' first members
+  const int64_t p = p0 + (int64_t)i * span;
   if (i == 0) s_miss = 0;
+  bool miss = false;
   int n = 0;
   if (p < P) {
-    n = min(ts.nslots[ts.idx(e, p)], slots);
+    // the thread's members, first tuples and counts loaded together
+    Tuple t0[kConcatPer];
+    int32_t nm[kConcatPer];
+#pragma unroll
+    for (int q = 0; q < kConcatPer; ++q) {
+      const int64_t pq = p + (int64_t)q * stride;
+      const bool in = q < per && pq < P;
+      nm[q] = in ? min(ts.nslots[ts.idx(e, pq)], slots) : -1;
+      t0[q] = in ? *ts.at(e, pq, 0) : Tuple{0, 0, 0, 0};
+    }
+    n = nm[0];
     for (int k = 0; k < n; ++k) {
-      const Tuple tu = *ts.at(e, p, k);
+      const Tuple tu = k == 0 ? t0[0] : *ts.at(e, p, k);
       s_a[i * slots + k] = tu.a;
       s_c[i * slots + k] = tu.c;
       s_b[i * slots + k] = tu.b;
     }
+#pragma unroll
+    for (int q = 1; q < kConcatPer; ++q) {
+      if (nm[q] < 0) break;
+      const int64_t pq = p + (int64_t)q * stride;
+      for (int k = 0; k < n; ++k) {
+        const int32_t b = s_b[i * slots + k];
+        int hit = -1;
+        Tuple hr{0, 0, 0, 0};
+        for (int m = 0; m < nm[q] && hit < 0; ++m) {
+          const Tuple tr = m == 0 ? t0[q] : *ts.at(e, pq, m);
+          if (tr.a == b) {
+            hit = m;
+            hr = tr;
+          }
+        }
+        if (hit >= 0) {
+          s_c[i * slots + k] += hr.c;
+          s_b[i * slots + k] = hr.b;
+        } else {
+          miss = true;
+        }
+      }
+    }
   }
   s_n[i] = n;
   __syncthreads();
-  for (int h = 1; h < members; h <<= 1) {
-    if ((i & (2 * h - 1)) == 0 && i + h < members && p + (int64_t)h * stride < P) {
+  if (miss) s_miss = 1;
+  for (int h = 1; h < nt; h <<= 1) {
+    if ((i & (2 * h - 1)) == 0 && i + h < nt && p + (int64_t)h * span < P) {
       const int nl = s_n[i];
       const int nr = s_n[i + h];
       for (int k = 0; k < nl; ++k) {

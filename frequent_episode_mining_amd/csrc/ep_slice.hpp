@@ -162,8 +162,19 @@ void map_slice_kernel(SliceArgs A) {
   constexpr int32_t kFar = 1 << 30;  // offsets are clamped to +-kFar
   constexpr int kPer = 4;            // events per thread per fill batch
   const int tid = threadIdx.x;
-  const int64_t p = (int64_t)blockIdx.x / A.n_wg;
-  const int w = (int)((int64_t)blockIdx.x - p * A.n_wg);
+  // XCD-aware order: workgroups go to the eight XCDs round-robin by blockIdx,
+  // so XCD c takes a contiguous range of logical blocks (segment-major): the
+  // tuples of consecutive segments share cache lines of the episode-major
+  // tuple store, and written from one XCD they are merged in its L2 instead
+  // of reaching memory as partial lines from several
+  int64_t lb = blockIdx.x;
+  {
+    const int64_t nb = gridDim.x, q = nb / 8, r = nb % 8;
+    const int64_t c = lb % 8, slot = lb / 8;
+    lb = c * q + (c < r ? c : r) + slot;
+  }
+  const int64_t p = lb / A.n_wg;
+  const int w = (int)(lb - p * A.n_wg);
   const int k = tid / A.wg_groups;
   const int gi = tid - k * A.wg_groups;
   const int64_t g = (int64_t)w * A.wg_groups + gi;
