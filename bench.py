@@ -452,12 +452,6 @@ def main():
         log("two-pass: threshold %d, %d of %d episodes counted exactly, %d frequent"
             % (args.threshold, kept_box[0], wl.n_episodes, int((counts[0] >= args.threshold).sum())))
     log("host enqueue %.4f ms per call" % ((we - w0) * 1000.0 / args.steps))
-    log("step %.4f ms (gpu events %.4f, wall %.4f); %s kernel %.4f ms per launch (%d launches timed)"
-        % (ms_per_step, gpu_ms, wall_ms, which, kprof[top] / max(kprof["calls"], 1), kprof["calls"]))
-
-    n, S = wl.n_events, wl.n_episodes
-    value = n * S / (ms_per_step / 1000.0)
-
     # the dominant Map-step kernel of this workload, timed alone by the
     # library's events on the stream it runs on, during the timed calls
     if st["kernels"] & 1:
@@ -468,6 +462,12 @@ def main():
     names = {"map_filter_ms": "filter_kernel", "map_prune_ms": "list_prune_kernel",
              "map_ticks_ms": "map_slice_kernel" if st["kernels"] & 32 else "map_ticks_kernel",
              "map_positions_ms": pos_name}
+    log("step %.4f ms (gpu events %.4f, wall %.4f); %s %.4f ms per launch (%d launches timed)"
+        % (ms_per_step, gpu_ms, wall_ms, names[top], kprof[top] / max(kprof["calls"], 1), kprof["calls"]))
+
+    n, S = wl.n_events, wl.n_episodes
+    value = n * S / (ms_per_step / 1000.0)
+
     kernel, kernel_ms = names[top], kprof[top] / max(kprof["calls"], 1)
     map_s = kernel_ms / 1000.0
     rel = relevant_pairs(wl)
