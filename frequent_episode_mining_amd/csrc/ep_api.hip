@@ -498,6 +498,12 @@ struct SliceHost {
 // Average episodes per group from which the planner takes the sliced kernel
 // (a group's lane steps its word of node-0 types at every node-1 tick).
 constexpr int64_t kSliceMinFill = 8;
+// A workgroup of the sliced kernel steps one segment's events in order: the
+// kernel is taken where its workgroups (segments x workgroups per segment)
+// fill the CUs, or where segments are short enough that a few workgroups
+// finish quickly (PTPE's single segment over a long stream is neither: the
+// level-2 sweep took 476 ms there against 63 ms on the tick kernel).
+constexpr int64_t kSliceShortSegment = 1 << 16;  // events per segment
 
 // false when the call does not fit the kernel: a node type >= kSliceTypes,
 // an episode given twice, or a window wider than 63 ticks
@@ -895,7 +901,9 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
                            EP_PLAN_NO_SLICE;
     const bool wanted = (plan & EP_PLAN_SLICE) || !(plan & other);
     if (N == 2 && L.bits && wanted && slice_plan(episodes, S, L.n_machines, &slc) &&
-        ((plan & EP_PLAN_SLICE) || S >= kSliceMinFill * slc.real_groups)) {
+        ((plan & EP_PLAN_SLICE) ||
+         (S >= kSliceMinFill * slc.real_groups &&
+          ((int64_t)P * slc.n_wg >= info->cu_count || n_events <= (int64_t)P * kSliceShortSegment)))) {
       L.slice = true;
       L.list = false;
       L.prune = false;

@@ -351,9 +351,9 @@ def test_list_configs_full_size(fem, name):
 
 
 def test_level2_full_size(fem):
-    # the level-2 sweep at full size, AUTO launch (episodes grouped by their
-    # doubling steps, closure misses queued for the repair kernel), every one
-    # of the 16,384 episodes against the oracle
+    # the level-2 sweep at full size, AUTO launch (the type-sliced Map kernel,
+    # closure misses queued for the repair kernel), every one of the 16,384
+    # episodes against the oracle
     wl = W.make("level2")
     got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, "auto", stats=True)
     _log("level2 full: plan %s" % st)

@@ -157,10 +157,30 @@ def test_slice_not_taken_for_duplicates(fem):
 
 @pytest.mark.parametrize("plan", [[], ["no-slice"]], ids=["slice", "no-slice"])
 def test_level2_small(fem, plan):
-    # the level-2 sweep's shape: AUTO takes the sliced kernel unless switched off
+    # the level-2 sweep's shape: MapConcatenate takes the sliced kernel unless
+    # switched off; PTPE's one segment of 200,000 events goes to the tick
+    # kernel (a sliced workgroup steps a segment in order)
     wl = W.make_small("level2")
     want = oracle.count(wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high)
     for mode, P in [("auto", 0), ("ptpe", 0), ("mapconcat", 16), ("mapconcat", 256)]:
         got, st = _gpu(fem, wl.times, wl.types, wl.ep_types, wl.t_low, wl.t_high, mode, P, plan=plan)
         _check(got, want, "level2 small %s %s P=%d" % (plan, mode, P))
-        assert bool(st["kernels"] & 32) == (plan == []), st
+        assert bool(st["kernels"] & 32) == (plan == [] and mode != "ptpe"), (mode, P, st)
+
+
+def test_slice_not_taken_for_one_long_segment(fem):
+    # a workgroup steps one segment in order: PTPE's single segment over a
+    # long stream goes to the tick kernel instead; short segments keep it
+    rng = np.random.default_rng(14)
+    times, types = W.random_stream(rng, 200000, 16, max_gap=2)
+    ep, lo, hi = _sweep(range(16), range(16), [(0, 5), (5, 20)])
+    want = oracle.count(times, types, ep, lo, hi)
+    got, st = _gpu(fem, times, types, ep, lo, hi, "ptpe")
+    _check(got, want, "ptpe one segment")
+    assert not st["kernels"] & 32, st
+    got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", 64)
+    _check(got, want, "mapconcat 64 segments")
+    assert st["kernels"] & 32, st
+    got, st = _gpu(fem, times, types, ep, lo, hi, "ptpe", plan=["slice"])
+    _check(got, want, "ptpe one segment, forced")
+    assert st["kernels"] & 32, st
