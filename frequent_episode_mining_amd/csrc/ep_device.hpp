@@ -1604,7 +1604,7 @@ void map_ticks_kernel(MapArgs A) {
   __shared__ int32_t s_maxw[kBlock];    // last word of the chunk holding an event
   __shared__ int32_t s_seg_end[kBlock]; // segment r's event range end; 0 for a segment not counted here
   __shared__ int32_t s_built[kBlock];   // first event of the chunk the bitmaps hold (-1: none)
-  __shared__ int32_t s_more, s_reuse, s_fit;
+  __shared__ int32_t s_more, s_reuse, s_fit, s_any;
   __shared__ uint64_t s_seen[1024];     // node-type set and ranks (type_slot)
   __shared__ uint8_t s_rank[1024];
   uint64_t* s_tb = (uint64_t*)smem;     // [R*CW words][U], word-major
@@ -1629,12 +1629,16 @@ void map_ticks_kernel(MapArgs A) {
   const int CE = kPer * nthr;
   const uint32_t all = (MCH == 32) ? 0xffffffffu : ((1u << MCH) - 1u);
 
-  if (tid == 0) s_fit = 1;
+  if (tid == 0) {
+    s_fit = 1;
+    s_any = 0;
+  }
   __syncthreads();
   if (tid < A.R) {
     const int64_t pp = seg_group * A.R + tid;
     int32_t end = 0;
     if (pp < A.P && segment_uses_ticks(A, pp, N)) {
+      s_any = 1;
       end = A.seg_end[pp];
       const int32_t beg = A.seg_beg[pp];
       if (beg < end && (((int64_t)A.times[end - 1] - A.times[beg]) >> 6) >= CW) s_fit = 0;
@@ -1648,6 +1652,7 @@ void map_ticks_kernel(MapArgs A) {
     tau_hi = A.tau[p + 1];
   }
   __syncthreads();
+  if (!s_any) return;  // no segment of the group is counted here (whole workgroup)
   const bool fit = s_fit != 0;
   if (fit && eg_id >= A.eg_blocks) return;  // the group's looping workgroups cover it
   load_type_tables(A, s_seen, s_rank);  // first read after the chunk loop's barrier

@@ -40,7 +40,7 @@ struct SetupArgs {
   int32_t flag_init;  // episodes' flags start at this (1: every episode takes the whole-stream recount)
   int64_t S;
   unsigned long long* counters;  // [4]
-  int32_t wave_search;  // range ends by one wave each (small P) or one thread each
+  int32_t wave_search;  // range ends by one wave each (small P) or kSearchLanes lanes each
   const uint4* tab_src;  // the episode table in pinned host memory (device-visible)
   uint4* tab_dst;        // its device copy
   int64_t tab_words;     // 16-byte words
@@ -50,19 +50,28 @@ __device__ inline int64_t cut_of(int64_t t_min, int64_t t_max, int64_t p, int64_
   return t_min - 1 + (p * (t_max - t_min + 1)) / P;
 }
 
-// First index i in [0, n) with times[i] > v, n if none; every lane of the wave
-// calls it with the same arguments and gets the answer.  Invariant: the
-// answer lies in [lo, hi], times[lo-1] <= v and times[hi] > v (or hi = n).
-__device__ int64_t wave_upper_bound(const int32_t* times, int64_t n, int64_t v) {
+// First index i in [0, n) with times[i] > v, n if none, found by the G lanes
+// of an aligned group of a wave (G a power of two up to the wave size), every
+// lane of the group calling it with the same v and getting the answer.  Each
+// level probes G evenly spaced elements of the range and keeps the part
+// before the first one above v: about log_G(n) dependent loads.  Invariant:
+// the answer lies in [lo, hi], times[lo-1] <= v and times[hi] > v (or hi = n).
+// Groups of one wave may leave the loop at different levels: a ballot counts
+// the active lanes only, and each group reads its own bits.
+template <int G>
+__device__ int64_t group_upper_bound(const int32_t* times, int64_t n, int64_t v) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int gl = lane & (G - 1);  // lane in the group
+  const int gb = lane - gl;       // the group's first lane
+  const uint64_t mask = (G == kWave) ? ~0ull : (((1ull << G) - 1ull) << gb);
   int64_t lo = 0, hi = n;
-  while (hi - lo > kWave) {
-    const int64_t step = (hi - lo + kWave - 1) / kWave;
-    int64_t idx = lo + (int64_t)(lane + 1) * step - 1;
+  while (hi - lo > G) {
+    const int64_t step = (hi - lo + G - 1) / G;
+    int64_t idx = lo + (int64_t)(gl + 1) * step - 1;
     idx = idx < hi - 1 ? idx : hi - 1;
-    const uint64_t gt = __ballot((int64_t)times[idx] > v);
+    const uint64_t gt = (__ballot((int64_t)times[idx] > v) & mask) >> gb;
     if (gt == 0) {
-      lo = hi;  // lane 63 probed hi - 1
+      lo = hi;  // the group's last lane probed hi - 1
     } else {
       const int f = __ffsll((unsigned long long)gt) - 1;
       const int64_t idx_f = lo + (int64_t)(f + 1) * step - 1;
@@ -71,42 +80,39 @@ __device__ int64_t wave_upper_bound(const int32_t* times, int64_t n, int64_t v) 
       lo = new_lo;
     }
   }
-  const int64_t idx = lo + lane;
+  const int64_t idx = lo + gl;
   const bool in = idx < hi;  // lanes past the range read times[0] (n >= 1) and ignore it
-  const uint64_t gt = __ballot(in && (int64_t)times[in ? idx : 0] > v);
+  const uint64_t gt = (__ballot(in && (int64_t)times[in ? idx : 0] > v) & mask) >> gb;
   return gt ? lo + (__ffsll((unsigned long long)gt) - 1) : hi;
 }
 
+// Segment range ends: a wave per search for few segments, groups of
+// kSearchLanes lanes beyond (as many groups as keep the whole search one round
+// of resident waves on the largest segment counts)
 constexpr int32_t kWaveSearchMaxP = 4096;
+constexpr int kSearchLanes = 4;
 
 __host__ __device__ inline int64_t setup_search_threads(int32_t P, bool wave) {
-  return (int64_t)2 * P * (wave ? kWave : 1);
+  return (int64_t)2 * P * (wave ? kWave : kSearchLanes);
 }
 
 __global__ __launch_bounds__(kBlock) void setup_kernel(SetupArgs A) {
   int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   const int64_t n_search = setup_search_threads(A.P, A.wave_search != 0);
-  if (i < n_search && !A.wave_search) {
-    const int64_t p = i >> 1;
-    const int64_t t_min = A.times[0];
-    const int64_t t_max = A.times[A.n - 1];
-    if (i & 1)
-      A.end[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p + 1, A.P) + A.max_span);
-    else
-      A.beg[p] = (int32_t)upper_bound_time(A.times, 0, A.n, cut_of(t_min, t_max, p, A.P) - A.max_span);
-    return;
-  }
   if (i < n_search) {
-    // wave w: w even -> beg[w / 2], w odd -> end[w / 2] (whole waves: n_search is a
-    // multiple of the wave size)
-    const int64_t w = i / kWave;
+    // lane group w (a wave, or kSearchLanes lanes): w even -> beg[w / 2], w odd
+    // -> end[w / 2] (whole groups: n_search is a multiple of the group size,
+    // and the other lanes of a partly searching wave do other items)
+    const int G = A.wave_search ? kWave : kSearchLanes;
+    const int64_t w = i / G;
     const int64_t p = w >> 1;
     const int64_t t_min = A.times[0];
     const int64_t t_max = A.times[A.n - 1];
     const int64_t v = (w & 1) ? cut_of(t_min, t_max, p + 1, A.P) + A.max_span
                               : cut_of(t_min, t_max, p, A.P) - A.max_span;
-    const int64_t r = wave_upper_bound(A.times, A.n, v);
-    if ((threadIdx.x & (kWave - 1)) == 0) {
+    const int64_t r = A.wave_search ? group_upper_bound<kWave>(A.times, A.n, v)
+                                    : group_upper_bound<kSearchLanes>(A.times, A.n, v);
+    if ((threadIdx.x & (G - 1)) == 0) {
       if (w & 1)
         A.end[p] = (int32_t)r;
       else

@@ -252,6 +252,26 @@ def test_extreme_times(fem, split):
                    "extreme %s %s P=%d" % (row, mode, P))
 
 
+def test_many_segments(fem):
+    # beyond 4,096 segments the set-up kernel finds each segment's event range
+    # with groups of four lanes (a wave each below): segment counts on both
+    # sides of the switch, streams with ties, bursts and long gaps, and times
+    # at both ends of the int32 range
+    rng = np.random.default_rng(83)
+    for trial in range(6):
+        n = int(rng.integers(20000, 60000))
+        times, types = W.random_stream(rng, n, 12, max_gap=[0, 1, 3, 40, 300, 2][trial])
+        if trial == 5:
+            times = (times.astype(np.int64) - int(times[0]) - 2 ** 31).astype(np.int32)
+            times[-3:] = 2 ** 31 - 1
+        ep, lo, hi = W.random_episodes(rng, 6, 3, 12, max_hi=20)
+        want = oracle.count(times, types, ep, lo, hi)
+        for P in (4096, 4097, 5000, 8192, 30000):
+            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True)
+            _check(got, want, "many segments trial %d n=%d P=%d" % (trial, n, P))
+            assert st["fallbacks"] == 0
+
+
 @pytest.mark.parametrize("name", ["tiny", "ptpe", "mapconcat", "level2", "longchain"])
 def test_config_small(fem, name):
     wl = W.make_small(name)
