@@ -368,27 +368,38 @@ __global__ __launch_bounds__(kBlock) void filter_kernel(FilterArgs A) {
 // node j+1's type in [t + lo_j + 1, t + hi_j].  An entry with no such
 // neighbour is dropped: the machines' windows age by elapsed time, not by
 // entries, and every completion and reset happens at an entry that stays.
-// Each side is decided by the nearest kPruneLook entries of the list on that
-// side: the search ends at an entry past the range or at the list's end
-// (nothing found), at a match, or undecided after kPruneLook entries; an
-// undecided side, a range the block may not hold whole (not strictly between
-// its first and last time) and an entry on several levels count as having
-// the neighbour.  Times are compared relative to the block's first, in 32
-// bits: blocks spanning 2^30 ticks or more are left as they are.  Persistent
-// workgroups loop over blocks, a block's lists
-// read into registers one iteration ahead; a block is staged in LDS, each
-// entry tested by one thread (entries carry their episode in bits 16..), and
-// the kept entries are written back in place, list by list, with new offsets
-// and counts.  A block with more than kPruneCap entries is left as it is.
-constexpr int kPruneCap = 2048;   // entries a block may have to be pruned
-constexpr int kPruneLook = 2;     // entries a neighbour search visits on one side
-constexpr int kPrunePer = kPruneCap / kBlock;
+// Each side is decided by the two entries of the list nearest on that side
+// (a list is sorted by time, so an entry past the range means every further
+// one is too): the side has the neighbour when the nearest is a match, and
+// counts as undecided, so kept, when the second nearest still lies within
+// the range; an entry with no list entry on a side, or with both past the
+// range or failing it, has none there.  A range the block may not hold whole
+// (not strictly between its first and last time) and an entry on several
+// levels count as having the neighbour.  Times are compared by difference
+// in 32 bits: blocks spanning 2^30 ticks or more are left as they are, and
+// so is a block with more than kPruneCap entries.
+//
+// Persistent workgroups loop over blocks, a block's lists read into
+// registers one iteration ahead and copied to LDS.  Entry i is tested by
+// thread i mod 256, it and its neighbours read from LDS (list membership by
+// the episode field the filter writes in bits 16.., two sentinels before the
+// block's entries and two after them); a ballot per 64 entries gives the
+// kept entries' ranks, and each kept entry is written back in place at its
+// rank, consecutive threads to consecutive slots.  Each list's new offset
+// is the rank of its first entry.  Two workgroup barriers per block.  Each
+// thread copies the next block's entries, and the sentinels after them, into
+// LDS slots that no other thread reads after this block's second barrier;
+// the ballot words are rewritten only after the next block's first.
+constexpr int kPruneCap = 2048;                  // entries a block may have to be pruned
+constexpr int kPrunePer = kPruneCap / kBlock;    // entries per thread
+constexpr int kPruneWords = kPruneCap / kWave;   // ballot words per block
+constexpr int kPruneIv = 16;                     // interval words per episode (slot j: interval j-1)
 
 struct PruneArgs {
   const int32_t* times;
   int64_t n;
   int64_t n_blocks;
-  const int32_t* ep_lo;  // [S * (N - 1)] delay intervals (lo, hi]
+  const int32_t* ep_lo;  // [S * (N - 1)] delay intervals (lo, hi], hi <= 64
   const int32_t* ep_hi;
   int32_t S;
   int32_t N;
@@ -399,19 +410,27 @@ struct PruneArgs {
 };
 
 __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
-  __shared__ int2 s_e[kPruneCap];
-  __shared__ uint8_t s_keep[kPruneCap];             // entry i is kept
-  __shared__ int32_t s_off[kMaxListEpisodes + 1];
-  __shared__ uint32_t s_iv[kMaxListEpisodes * 16];  // interval j of episode e: lo | hi << 8
-  __shared__ uint32_t s_wsum[kBlock / kWave];
-  __shared__ int32_t s_pre[kBlock + 1];             // kept entries before thread t's chunk
-  __shared__ uint8_t s_kb[kBlock];                  // thread t's kept entries (bit q)
+  __shared__ int2 s_e[kPruneCap + 4];              // entry i at s_e[i + 2]; 0, 1: sentinels
+  __shared__ uint32_t s_iv[kMaxListEpisodes * kPruneIv + 1];
+  __shared__ uint64_t s_bal[kPruneWords + 1];     // kept entries 64 w .. 64 w + 63
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int S = A.S, N = A.N;
-  for (int i = tid; i < S * (N - 1); i += kBlock)
-    s_iv[(i / (N - 1)) * 16 + i % (N - 1)] = (uint32_t)A.ep_lo[i] | (uint32_t)A.ep_hi[i] << 8;
+  // interval j-1 of episode e in slot e * kPruneIv + j: lo + 1, hi - lo and
+  // hi, one byte each (slot 0 unused: node 0 has no predecessor; the slot
+  // after node N-1's is read for its successor side and not used)
+  for (int i = tid; i < S * kPruneIv; i += kBlock) {
+    const int e = i / kPruneIv, k = i - e * kPruneIv;
+    uint32_t v = 0;
+    if (k >= 1 && k <= N - 1) {
+      const int32_t lo = A.ep_lo[e * (N - 1) + k - 1], hi = A.ep_hi[e * (N - 1) + k - 1];
+      v = (uint32_t)(lo + 1) | (uint32_t)(hi - lo) << 8 | (uint32_t)hi << 16;
+    }
+    s_iv[i] = v;
+  }
+  const int2 sentinel = make_int2(0, (int32_t)0xffff0000u);  // episode field in no list
+  if (tid < 2) s_e[tid] = sentinel;
   const int64_t grid = gridDim.x;
   // the lists lie one after the other from the region's start, episode by
   // episode: a block's entries are its last list's offset plus count (kept
@@ -419,7 +438,7 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
   auto total_of = [&](int64_t bb) -> int2 {
     return bb < A.n_blocks ? make_int2(A.list_off[bb * S + S - 1], A.list_cnt[bb * S + S - 1]) : make_int2(0, 0);
   };
-  int2 ent[kPrunePer];
+  int2 ent[kPrunePer] = {};
   int32_t off_r = 0, tf_r = 0, tl_r = 0;
   // block bb's entries (entry tid + q * kBlock in ent[q]), offsets and ends
   auto fetch = [&](int64_t bb, int32_t tot) {
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
 #pragma unroll
     for (int q = 0; q < kPrunePer; ++q) {
       const int i = tid + q * kBlock;
-      ent[q] = (run && i < tot) ? region[i] : make_int2(0, 0);
+      if (run && i < tot) ent[q] = region[i];  // (the others are never read)
     }
     off_r = tid < S ? A.list_off[bb * S + tid] : 0;
     tf_r = A.times[bb * kListBlock];
@@ -443,6 +462,7 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
   for (; b < A.n_blocks; b += grid) {
     const int32_t total = tot;
     const int32_t tf = tf_r;
+    const int32_t off = off_r;
     const int64_t span64 = (int64_t)tl_r - (int64_t)tf_r;
     const int32_t span = (int32_t)span64;
     const bool run = total > 0 && total <= kPruneCap && span64 >= 0 && span64 < (1ll << 30);
@@ -450,93 +470,97 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
 #pragma unroll
       for (int q = 0; q < kPrunePer; ++q) {
         const int i = tid + q * kBlock;
-        if (i < total) s_e[i] = ent[q];
+        if (q * kBlock < total + 2) {
+          if (i < total)
+            s_e[i + 2] = ent[q];
+          else if (i < total + 2)
+            s_e[i + 2] = sentinel;
+        }
       }
-      if (tid < S) s_off[tid] = off_r;
-      if (tid == 0) s_off[S] = total;
+      // (sentinels past the last thread's slots: entries kPruneCap, kPruneCap + 1)
+      if (tid < 2 && kPruneCap + tid < total + 2) s_e[kPruneCap + 2 + tid] = sentinel;
     }
     // the next block's loads in flight meanwhile
     tot = __builtin_amdgcn_readfirstlane(tot_next.x + tot_next.y);
     if (b + grid < A.n_blocks) fetch(b + grid, tot);
     tot_next = total_of(b + 2 * grid);
+    if (!run) continue;
     lds_barrier();
 
-    if (run) {
-      // entries tid, tid + kBlock, ...: which of them pass
-      for (int i = tid; i < total; i += kBlock) {
-        const int2 me = s_e[i];
-        const int32_t t = (int32_t)((uint32_t)me.x - (uint32_t)tf);  // 0 .. span
-        const int e = min((int)((uint32_t)me.y >> 16), S - 1);
-        const uint32_t lm = (uint32_t)me.y & 0xffffu;
-        const int j = __ffs((int)lm) - 1;
-        const int32_t beg = s_off[e], end = s_off[e + 1];
-        // predecessor side: node j-1 in [t - hi, t - lo - 1]; successor side:
-        // node j+1 in [t + lo + 1, t + hi]; each decided by the nearest
-        // kPruneLook entries of the list on its side
-        const uint32_t ivp = s_iv[e * 16 + max(j - 1, 0)], ivs = s_iv[e * 16 + max(j, 0)];
-        const int32_t p_lo = t - (int32_t)(ivp >> 8), p_hi = t - (int32_t)(ivp & 0xffu) - 1;
-        const int32_t s_lo = t + (int32_t)(ivs & 0xffu) + 1, s_hi = t + (int32_t)(ivs >> 8);
-        bool p_found = false, p_done = false, s_found = false, s_done = false;
+    // entries tid, tid + kBlock, ...: which of them pass
 #pragma unroll
-        for (int d = 1; d <= kPruneLook; ++d) {
-          const int kp = i - d, ks = i + d;
-          const int2 op = s_e[max(kp, 0)];
-          const int2 os = s_e[min(ks, total - 1)];
-          const int32_t tp = (int32_t)((uint32_t)op.x - (uint32_t)tf);
-          const int32_t ts = (int32_t)((uint32_t)os.x - (uint32_t)tf);
-          const bool p_in = kp >= beg, s_in = ks < end;
-          const bool p_past = !p_in || tp < p_lo;
-          const bool s_past = !s_in || ts > s_hi;
-          const bool p_hit = !p_past && tp <= p_hi && ((op.y >> max(j - 1, 0)) & 1);
-          const bool s_hit = !s_past && ts >= s_lo && ((os.y >> (j + 1)) & 1);
-          p_found = p_found || (!p_done && p_hit);
-          s_found = s_found || (!s_done && s_hit);
-          p_done = p_done || p_past || p_hit;
-          s_done = s_done || s_past || s_hit;
-        }
-        // a side passes when found, undecided, without a node on it, or
-        // reaching past the ticks the block holds whole
-        const bool p_ok = j <= 0 || p_lo <= 0 || p_found || !p_done;
-        const bool s_ok = j >= N - 1 || s_hi >= span || s_found || !s_done;
-        const bool keep = (lm & (lm - 1)) != 0u || lm == 0u || (p_ok && s_ok);
-        s_keep[i] = keep ? 1 : 0;
+    for (int q = 0; q < kPrunePer; ++q) {
+      if (q * kBlock < total) {
+        const int i = tid + q * kBlock;
+        const int2 me = s_e[i + 2];
+        const uint32_t y = (uint32_t)me.y;
+        const uint32_t lm = y & 0xffffu;
+        const uint32_t e = y >> 16;
+        // every read below stays inside the arrays for any lane (a lane past
+        // the block's entries reads stale slots and keeps nothing), and the
+        // conditions are combined without branches, so that the LDS reads go
+        // out together
+        const int j = __builtin_ctz(lm | 0x8000u);  // the entry's level, if single
+        const int ie = (int)(min(e, (uint32_t)S - 1u) * kPruneIv) + j;
+        const uint32_t ivp = s_iv[ie], ivs = s_iv[ie + 1];
+        const int2 p1 = s_e[i + 1], p2 = s_e[i], s1 = s_e[i + 3], s2 = s_e[i + 4];
+        const int32_t tr = (int32_t)((uint32_t)me.x - (uint32_t)tf);  // 0 .. span
+        // predecessor side: a node j-1 entry at distance (lo, hi] before
+        const uint32_t dp1 = (uint32_t)me.x - (uint32_t)p1.x, dp2 = (uint32_t)me.x - (uint32_t)p2.x;
+        const bool p_hit = (((uint32_t)p1.y >> 16) == e) & (((uint32_t)p1.y & (lm >> 1)) != 0u) &
+                           (dp1 - (ivp & 0xffu) < ((ivp >> 8) & 0xffu));
+        const bool p_open = (((uint32_t)p2.y >> 16) == e) & ((int32_t)dp2 <= (int32_t)(ivp >> 16));
+        const bool p_ok = (j == 0) | (tr <= (int32_t)(ivp >> 16)) | p_hit | p_open;
+        // successor side: a node j+1 entry at distance (lo, hi] after
+        const uint32_t ds1 = (uint32_t)s1.x - (uint32_t)me.x, ds2 = (uint32_t)s2.x - (uint32_t)me.x;
+        const bool s_hit = (((uint32_t)s1.y >> 16) == e) & (((uint32_t)s1.y & (lm << 1)) != 0u) &
+                           (ds1 - (ivs & 0xffu) < ((ivs >> 8) & 0xffu));
+        const bool s_open = (((uint32_t)s2.y >> 16) == e) & ((int32_t)ds2 <= (int32_t)(ivs >> 16));
+        const bool s_ok = (j >= N - 1) | (tr + (int32_t)(ivs >> 16) >= span) | s_hit | s_open;
+        // several levels (or none): kept
+        bool keep = ((lm & (lm - 1u)) != 0u) | (lm == 0u) | (p_ok & s_ok);
+        keep = keep && i < total;
+        const uint64_t bal = __ballot(keep);
+        if (lane == 0) s_bal[q * (kBlock / kWave) + wave] = bal;
       }
-      lds_barrier();
+    }
+    lds_barrier();
 
-      // ranks of the kept entries: thread t's chunk is [8 t, 8 t + 8)
-      const int c0 = tid * kPrunePer;
-      uint32_t kb = 0;
+    // ranks: kept entries in the ballot words before this one, plus the
+    // lanes below in it
+    const int n_words = (total + kWave - 1) / kWave;
+    const uint64_t wv = lane < n_words ? s_bal[lane] : 0ull;
+    const uint32_t wc = (uint32_t)__popcll(wv);
+    const uint32_t before = wave_incl_scan(wc) - wc;
+    int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
 #pragma unroll
-      for (int q = 0; q < kPrunePer; ++q) kb |= (c0 + q < total && s_keep[c0 + q] ? 1u : 0u) << q;
-      const uint32_t cnt = (uint32_t)__popc(kb);
-      const uint32_t incl = wave_incl_scan(cnt);
-      if (lane == kWave - 1) s_wsum[wave] = incl;
-      lds_barrier();
-      uint32_t before = 0;
-#pragma unroll
-      for (int w = 0; w < kBlock / kWave; ++w) before += w < wave ? s_wsum[w] : 0u;
-      uint32_t r = before + incl - cnt;
-      s_pre[tid] = (int32_t)r;
-      s_kb[tid] = (uint8_t)kb;
-      if (tid == kBlock - 1) s_pre[kBlock] = (int32_t)(r + cnt);
-      int2* region = A.lists + b * (int64_t)kListBlock * A.max_share;
-#pragma unroll
-      for (int q = 0; q < kPrunePer; ++q)
-        if ((kb >> q) & 1u) region[r++] = s_e[c0 + q];
-      lds_barrier();
-      // each list's new offset and count: kept entries before its start and end
-      auto rank = [&](int32_t i) -> int32_t {
-        const int c = i / kPrunePer;
-        if (c >= kBlock) return s_pre[kBlock];
-        return s_pre[c] + __popc(s_kb[c] & ((1u << (i - c * kPrunePer)) - 1u));
+    for (int q = 0; q < kPrunePer; ++q)
+      if (q * kBlock < total) {
+        const int w = q * (kBlock / kWave) + wave;
+        const uint32_t base = __builtin_amdgcn_readlane(before, w);
+        const uint64_t bal = s_bal[w];  // (one address for the wave)
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if ((bal >> lane) & 1ull) region[base + below] = s_e[tid + q * kBlock + 2];
+      }
+    if (wave == 0) {
+      // each list's new offset and count: the ranks of its first entry and of
+      // the next list's (lists are consecutive; S <= 32 lanes of wave 0)
+      const int32_t nxt = __shfl_down(off, 1);
+      const int32_t end = tid == S - 1 ? total : nxt;
+      auto rank = [&](int32_t x) -> int32_t {
+        const int w = x >> 6, l = x & (kWave - 1);
+        const uint32_t base = (uint32_t)__shfl((int)before, w);
+        const uint64_t ww = (uint64_t)(uint32_t)__shfl((int)(uint32_t)wv, w) |
+                            (uint64_t)(uint32_t)__shfl((int)(uint32_t)(wv >> 32), w) << 32;
+        return (int32_t)(base + (uint32_t)__popcll(ww & ((1ull << l) - 1ull)));
       };
+      const int32_t a0 = rank(off), z = rank(end);
       if (tid < S) {
-        const int32_t a0 = rank(s_off[tid]), z = rank(s_off[tid + 1]);
         A.list_off[b * S + tid] = a0;
         A.list_cnt[b * S + tid] = z - a0;
       }
     }
-    lds_barrier();  // LDS is rewritten by the next block
   }
 }
 

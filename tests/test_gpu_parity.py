@@ -194,6 +194,34 @@ def test_list_pruning_windows(fem, prune):
                    % (prune, trial, times.size, S, N, max_gap, P))
 
 
+def test_list_pruning_block_sizes(fem):
+    # 4,096-event blocks holding a chosen number of list entries: around the
+    # pruning's per-block cap (2,048; blocks above it are left as they are),
+    # around its 256-entry rows, empty and single-entry blocks; each relevant
+    # event is on one episode, so a block's entries are its relevant events
+    plan = _split_plan("positions") + ["prune"]
+    rng = np.random.default_rng(83)
+    totals = [2048, 2047, 2046, 2049, 0, 1, 2, 255, 256, 257, 511, 1500, 4096, 2048, 1023]
+    S, N = 2, 3
+    ep = np.array([[0, 1, 2], [3, 4, 5]], np.uint16)
+    for trial in range(3):
+        types = []
+        for tb in totals:
+            blk = rng.integers(6, 10, size=4096)
+            at = rng.choice(4096, size=tb, replace=False)
+            blk[at] = rng.integers(0, 6, size=tb)
+            types.append(blk)
+        types = np.concatenate(types)[: len(totals) * 4096 - 1000].astype(np.uint16)
+        times = np.cumsum(rng.integers(0, [2, 4, 40][trial], size=types.size)).astype(np.int32)
+        hi = rng.integers(1, 64, size=(S, N - 1)).astype(np.int32)
+        lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
+        want = oracle.count(times, types, ep, lo, hi)
+        for P in (1, 3, 64):
+            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True, plan=plan)
+            assert st["kernels"] & 4 and st["kernels"] & 8, "the pruned list path was not taken"
+            _check(got, want, "pruning block sizes trial %d P=%d" % (trial, P))
+
+
 @pytest.mark.parametrize("order", ["grouped", "plain"])
 def test_tick_kernel_episode_groups_by_steps(fem, order):
     # the tick kernel may take episodes ordered by their doubling steps, each
