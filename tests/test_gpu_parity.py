@@ -222,6 +222,43 @@ def test_list_pruning_block_sizes(fem):
             _check(got, want, "pruning block sizes trial %d P=%d" % (trial, P))
 
 
+@pytest.mark.parametrize("N", [12, 16])
+def test_list_pruning_long_episodes(fem, N):
+    # the most episodes the list path takes (32) with up to 16 nodes: the
+    # pruning's interval table at its last slots, entries of the last level
+    # with no successor side, and chains planted on the interval ends
+    plan = _split_plan("positions") + ["prune"]
+    rng = np.random.default_rng(300 + N)
+    for trial in range(4):
+        n = int(rng.integers(9000, 20000))
+        n_types = int(rng.integers(N, 3 * N))
+        times, types = W.random_stream(rng, n, n_types, max_gap=[0, 2, 6, 20][trial])
+        S = 32
+        ep = np.stack([rng.permutation(n_types)[:N] for _ in range(S)]).astype(np.uint16)
+        hi = rng.integers(1, 64, size=(S, N - 1)).astype(np.int32)
+        lo = np.minimum((rng.random(size=hi.shape) * hi).astype(np.int32), hi - 1)
+        times, types = _plant_edges(rng, times, types, ep, lo, hi, 4)
+        # and whole chains with every delay on an interval end
+        add_t, add_y = [], []
+        for e in range(S):
+            for c in range(3):
+                t = int(rng.integers(times[0], times[-1] + 1))
+                for j in range(N):
+                    add_t.append(t)
+                    add_y.append(int(ep[e, j]))
+                    if j < N - 1:
+                        t += int(lo[e, j] + 1 if (j + c) % 2 else hi[e, j])
+        times = np.concatenate([times, np.array(add_t, np.int32)])
+        types = np.concatenate([types, np.array(add_y, np.uint16)])
+        o = np.argsort(times, kind="stable")
+        times, types = times[o], types[o]
+        want = oracle.count(times, types, ep, lo, hi)
+        for P in (1, 5, 64):
+            got, st = _gpu(fem, times, types, ep, lo, hi, "mapconcat", P, stats=True, plan=plan)
+            assert st["kernels"] & 4 and st["kernels"] & 8, "the pruned list path was not taken"
+            _check(got, want, "pruning N=%d trial %d P=%d" % (N, trial, P))
+
+
 @pytest.mark.parametrize("order", ["grouped", "plain"])
 def test_tick_kernel_episode_groups_by_steps(fem, order):
     # the tick kernel may take episodes ordered by their doubling steps, each
