@@ -1283,16 +1283,26 @@ __device__ __forceinline__ void list_walk(const MapArgs& A, int64_t e, int64_t b
   int32_t first = i;    // entries before it are done
   int32_t j0 = (rel + i) & ~1;  // even region index of the current batch
   bool go = true;
-  auto advance = [&]() {  // to block b + 1's list, its following block's bounds loaded
+  // the bounds of the list two blocks ahead as well: a batch's address then
+  // never waits on a bounds load issued in the iteration before it (on short
+  // lists, one block per batch, that would put two loads in a row per block)
+  int32_t off_next2 = 0, cnt_next2 = 0;
+  if (b + 1 < b_last) {
+    off_next2 = A.list_off[(b + 2) * A.S + e];
+    cnt_next2 = A.list_cnt[(b + 2) * A.S + e];
+  }
+  auto advance = [&]() {  // to block b + 1's list, the bounds two blocks ahead loaded
     ++b;
     v = (const int4*)(A.lists + b * region_len);
     rel = off_next;
     n_end = cnt_next;
     first = 0;
     j0 = rel & ~1;
-    if (b < b_last) {
-      off_next = A.list_off[(b + 1) * A.S + e];
-      cnt_next = A.list_cnt[(b + 1) * A.S + e];
+    off_next = off_next2;
+    cnt_next = cnt_next2;
+    if (b + 1 < b_last) {
+      off_next2 = A.list_off[(b + 2) * A.S + e];
+      cnt_next2 = A.list_cnt[(b + 2) * A.S + e];
     }
   };
   if (j0 >= rel + n_end) {
