@@ -578,10 +578,12 @@ __global__ __launch_bounds__(kBlock) void list_prune_kernel(PruneArgs A) {
 // first tuples and tuple counts loaded together up front: with stride 1 that
 // is one contiguous read per thread), then the threads' lists are joined
 // level by level in LDS.  Where the launch has threads to spare (many
-// episodes), per = 8 makes a 512-member group one wave whose tree needs six
-// levels inside the wave, instead of nine workgroup barriers over 512 threads.
+// episodes), per = 4 makes a 512-member group two waves: a chain of four
+// dependent joins per thread, then seven tree levels, instead of nine
+// workgroup barriers over 512 threads (per = 8, one wave, makes the chains of
+// joins the longer wait; per = 2 leaves more barriers).
 constexpr int kConcatMembers = 512;  // members of a tree workgroup at most
-constexpr int kConcatPer = 8;        // members one thread joins in order at most
+constexpr int kConcatPer = 4;        // members one thread joins in order at most
 constexpr int64_t kConcatMinThreads = 65536;  // threads a launch keeps when choosing per
 
 __global__ __launch_bounds__(kConcatMembers) void concat_tree_kernel(TupleStore ts, int32_t* flags, int64_t S,
