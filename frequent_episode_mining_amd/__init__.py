@@ -55,7 +55,7 @@ PLAN = {"ticks": 1 << 0, "positions": 1 << 1, "list": 1 << 2, "no-list": 1 << 3,
         "prune": 1 << 4, "no-prune": 1 << 5, "group-steps": 1 << 6, "no-group-steps": 1 << 7,
         "run-windows": 1 << 8, "ring-windows": 1 << 9, "machine-lanes": 1 << 10,
         "no-reduce": 1 << 11, "no-repair-queue": 1 << 12, "recount": 1 << 13, "no-split": 1 << 14,
-        "slice": 1 << 15, "no-slice": 1 << 16}
+        "slice": 1 << 15, "no-slice": 1 << 16, "tiny-repair-queue": 1 << 17}
 
 
 def plan_bits(plan) -> int:

@@ -984,7 +984,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
   const size_t sz_flags = align_up(sizeof(int32_t) * (S + 1), 256);
   const size_t sz_cnt = 256;
   // closure misses queued for repair_kernel (more are repaired where found)
-  const int64_t queue_cap = P > 1 ? 65536 : 0;
+  // misses past the queue send their episode to the whole-stream recount
+  const int64_t queue_cap = P > 1 ? 262144 : 0;
   const size_t sz_queue = align_up(sizeof(uint64_t) * (size_t)queue_cap, 256);
   // ring windows: a slot per Map machine (scan kernel) and per wave of the
   // kernels that run one machine per wave (closure, repair, result, fused
@@ -1360,7 +1361,8 @@ int count_episodes_impl(const int32_t* times, const uint16_t* types, int64_t n_e
       ca.tau = d_tau; ca.seg_beg = d_beg; ca.seg_end = d_end;
       ca.ts = ts; ca.flags = d_flags; ca.repairs = d_cnt;
       ca.S = S; ca.P = P;
-      ca.queue = d_queue; ca.queue_cap = (plan & EP_PLAN_NO_REPAIR_QUEUE) ? 0 : queue_cap;
+      ca.queue = d_queue;
+      ca.queue_cap = (plan & EP_PLAN_NO_REPAIR_QUEUE) ? 0 : ((plan & EP_PLAN_TINY_REPAIR_QUEUE) ? 1 : queue_cap);
       ca.queue_n = d_cnt + 2; ca.queue_head = d_cnt + 3;
       ca.repair_blocks = info->cu_count * 2;
       ca.ring = ring;

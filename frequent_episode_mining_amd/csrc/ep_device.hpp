@@ -2330,7 +2330,12 @@ __device__ void repair_exit(const ClosureArgs& A, const typename Mach::Params& p
   }
 }
 
-template <int N, class Mach>
+// INLINE: misses the queue cannot take are repaired here, one wave at a time
+// (the machine's code then sets the kernel's registers, and its occupancy:
+// 195 VGPRs for two nodes against 15 for the matching alone); otherwise
+// they send their episode to the whole-stream recount, as a full slot list
+// does.  The launch takes the inline form only where there is no queue.
+template <int N, class Mach, bool INLINE>
 __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
   // items episode-major: consecutive lanes take consecutive boundaries of one
   // episode, so their first tuples are contiguous
@@ -2375,7 +2380,11 @@ __global__ __launch_bounds__(kBlock) void closure_kernel(ClosureArgs A) {
       }
       missing = left;
     }
+    if constexpr (!INLINE) {
+      if (missing != 0u) atomicOr(&A.flags[item / (A.P - 1)], 1);
+    }
   }
+  if constexpr (!INLINE) return;
   uint64_t wmask = __ballot(missing != 0u);
   const int lane = threadIdx.x & (kWave - 1);
   while (wmask != 0) {

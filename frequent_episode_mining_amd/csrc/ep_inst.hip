@@ -83,7 +83,10 @@ hipError_t launch_ticks(const MapArgs& a, bool all_machines, dim3 grid, dim3 blo
 
 template <class Mach>
 hipError_t launch_closure_m(const ClosureArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((closure_kernel<EP_N, Mach>), grid, dim3(kBlock), 0, s, a);
+  if (a.queue_cap > 0)
+    hipLaunchKernelGGL((closure_kernel<EP_N, Mach, false>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((closure_kernel<EP_N, Mach, true>), grid, dim3(kBlock), 0, s, a);
   if (a.queue_cap > 0)  // the queued repairs, pulled one per wave
     hipLaunchKernelGGL((repair_kernel<EP_N, Mach>), dim3((unsigned)a.repair_blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();

@@ -189,7 +189,8 @@ enum {
   EP_PLAN_RING_WINDOWS = 1 << 9,     /* ring windows and the scan kernel for every episode */
   EP_PLAN_MACHINE_LANES = 1 << 10,   /* one Map machine per lane */
   EP_PLAN_NO_REDUCE = 1 << 11,       /* separate closure, tree and result launches */
-  EP_PLAN_NO_REPAIR_QUEUE = 1 << 12, /* closure misses repaired where they are found */
+  EP_PLAN_NO_REPAIR_QUEUE = 1 << 12, /* closure misses repaired where they are found (else queued
+                                        for the repair kernel; past the queue, recounted whole) */
   EP_PLAN_RECOUNT = 1 << 13,         /* every episode taken through the whole-stream recount
                                         that guards repair-list overflow and tree misses */
   EP_PLAN_NO_SPLIT = 1 << 14,        /* one window kind for the whole call: the widest one
@@ -198,7 +199,9 @@ enum {
                                         call fits it (node types below 2,048, windows up to
                                         63 ticks, no episode twice), however few episodes
                                         share a node-1 type and interval */
-  EP_PLAN_NO_SLICE = 1 << 16         /* two-node episodes: never the type-sliced kernel */
+  EP_PLAN_NO_SLICE = 1 << 16,        /* two-node episodes: never the type-sliced kernel */
+  EP_PLAN_TINY_REPAIR_QUEUE = 1 << 17 /* a one-entry repair queue: the closure's other misses send
+                                        their episodes to the whole-stream recount */
 };
 
 /*

@@ -463,12 +463,16 @@ def test_config_small_separate_closure_and_tree(fem, name):
         assert st["fallbacks"] == 0
 
 
-@pytest.mark.parametrize("repairs", ["queued", "inline"])
+@pytest.mark.parametrize("repairs", ["queued", "inline", "overflow"])
 def test_fuzz_separate_closure_and_tree(fem, repairs):
-    # misses are queued for the repair kernel, or (past the queue's capacity,
-    # forced here) repaired by the closure kernel where they are found
-    plan = ["no-reduce"] + (["no-repair-queue"] if repairs == "inline" else [])
+    # misses are queued for the repair kernel; with no queue (forced here) the
+    # closure kernel repairs them where they are found; past a queue's
+    # capacity (a one-entry queue, forced here) their episodes are recounted
+    # over the whole stream
+    plan = ["no-reduce"] + {"queued": [], "inline": ["no-repair-queue"],
+                            "overflow": ["tiny-repair-queue"]}[repairs]
     rng = np.random.default_rng(37)
+    recounted = 0
     for trial in range(30):
         n = int(rng.integers(1, 400))
         n_types = int(rng.integers(1, 6))
@@ -477,8 +481,11 @@ def test_fuzz_separate_closure_and_tree(fem, repairs):
         ep, lo, hi = W.random_episodes(rng, int(rng.integers(1, 60)), N, n_types, max_hi=6)
         want = oracle.count(times, types, ep, lo, hi)
         for mode, P in [("mapconcat", 3), ("mapconcat", 16), ("mapconcat", max(1, n))]:
-            _check(_gpu(fem, times, types, ep, lo, hi, mode, P, plan=plan), want,
-                   "separate fuzz %d n=%d %s P=%d" % (trial, n, mode, P))
+            got, st = _gpu(fem, times, types, ep, lo, hi, mode, P, stats=True, plan=plan)
+            _check(got, want, "separate fuzz %d n=%d %s P=%d" % (trial, n, mode, P))
+            recounted += st["fallbacks"]
+    if repairs == "overflow":
+        assert recounted > 0  # the recount past the queue was taken
 
 
 def _narrow_long_stream(rng, n, n_types, spacing):
